@@ -1,0 +1,211 @@
+/*
+ * isk.h - C ABI of the batch-invariant split-KV decode-attention library
+ * (libisk.so, built for AMD Instinct MI355X / gfx950).
+ *
+ * What the library computes.  For every batch row b and query head h it
+ * returns softmax attention of the row's query over the row's own keys and
+ * values, plus the natural-log log-sum-exp of the scaled scores:
+ *     s_t = scale * <q[b,h,:], k_t>,  lse = ln sum_t exp(s_t),
+ *     out[b,h,:] = sum_t exp(s_t - lse) * v_t.
+ * It computes this the split-KV way described on the FlashMLA issue page
+ * "Sparse MLA decode is not batch-invariant ..." (section "Where it comes
+ * from"): each row's keys are cut into splits, every split yields a partial
+ * output and its log-sum-exp, and a combine step merges the partials with
+ * log-sum-exp weights.  Unlike the scheduler that page describes, the
+ * default split rule here follows the request in that page's section
+ * "Question": a row's split count and split boundaries are a function of
+ * that row's own length (or top-k count) and fixed library constants only,
+ * never of batch-wide totals, and the combine runs in a fixed order.  A
+ * row's output bits therefore do not depend on its batchmates or its
+ * position in the batch.
+ *
+ * Kinds:
+ *   ISK_KIND_GQA  dense grouped-query attention; query head h reads kv head
+ *                 h / (Hq / Hkv).
+ *   ISK_KIND_MLA  absorbed multi-head latent attention: one shared latent
+ *                 row of head_dim_qk (576) values per token is the key, its
+ *                 first head_dim_v (512) values are the value.  With
+ *                 topk_width > 0 each row attends only the positions listed
+ *                 in its top-k index array (the sparse call of the page's
+ *                 section "Measurement": indices plus a per-row valid count).
+ *
+ * Conventions for every entry point:
+ *   - Return value: ISK_OK (0) or a negative isk_status.  Nothing throws or
+ *     aborts across the ABI; on failure isk_last_error() gives a message.
+ *   - Tensors are dense, row-major, and device pointers unless the name ends
+ *     in _host.  The caller owns all tensors and the workspace; the library
+ *     owns only plans.  bf16 means IEEE binary32 truncated to its top 16
+ *     bits (the usual bfloat16 layout).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     isk_attn_decode only enqueues work on it and returns.
+ */
+#ifndef ISK_H
+#define ISK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define ISK_API __attribute__((visibility("default")))
+#else
+#define ISK_API
+#endif
+
+typedef enum isk_status {
+  ISK_OK = 0,
+  ISK_ERR_INVALID_ARG = -1,   /* bad pointer, size, shape or enum value          */
+  ISK_ERR_UNSUPPORTED = -2,   /* valid request this build has no kernel for      */
+  ISK_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required      */
+  ISK_ERR_INDEX = -4,         /* check_inputs found a table/index entry invalid   */
+  ISK_ERR_HIP = -5            /* a HIP runtime call failed (message has detail)  */
+} isk_status;
+
+typedef enum isk_kind { ISK_KIND_GQA = 0, ISK_KIND_MLA = 1 } isk_kind;
+
+/* ISK_SPLIT_PER_ROW: split count ceil(units_b / split_tokens) from the row's
+ * own units only (tokens, or top-k slots for sparse rows); batch-invariant.
+ * ISK_SPLIT_BATCH_BALANCED: comparison mode reproducing the batch-wide
+ * scheduler that the FlashMLA issue page describes (section "Where it comes
+ * from"): a per-part block quota computed from the sum over the whole batch,
+ * then greedy packing that cuts rows at part boundaries.  Deterministic for
+ * a fixed batch, but a row's bits depend on its batchmates. */
+typedef enum isk_split_mode { ISK_SPLIT_PER_ROW = 0, ISK_SPLIT_BATCH_BALANCED = 1 } isk_split_mode;
+
+typedef enum isk_out_dtype { ISK_OUT_BF16 = 0, ISK_OUT_F32 = 1 } isk_out_dtype;
+
+typedef struct isk_desc {
+  int32_t kind;              /* isk_kind                                              */
+  int32_t num_q_heads;       /* Hq.  GQA: multiple of Hkv.  MLA: multiple of 16, <=128 */
+  int32_t num_kv_heads;      /* Hkv.  MLA: must be 1                                  */
+  int32_t head_dim_qk;       /* GQA: 64 or 128.  MLA: 576                             */
+  int32_t head_dim_v;        /* GQA: equal to head_dim_qk.  MLA: 512                  */
+  int32_t page_size;         /* tokens per KV page (GQA: multiple of 16, MLA: of 64)  */
+  int32_t num_pages;         /* pages in the pool; block-table entries must be below  */
+  int32_t max_pages_per_row; /* row stride of block_table                             */
+  int32_t topk_width;        /* 0: dense.  >0 (MLA only): row stride of topk_idx      */
+  int32_t split_mode;        /* isk_split_mode                                        */
+  int32_t split_tokens;      /* 0: library constant for the kind; else a multiple of
+                                the kind's tile (GQA 64, MLA 64)                      */
+  int32_t out_dtype;         /* isk_out_dtype                                         */
+  int32_t check_inputs;      /* 1: copy tables to the host and validate them first    */
+  float scale;               /* score scale, applied in fp32 after the dot product    */
+} isk_desc;
+
+typedef struct isk_plan isk_plan;   /* opaque, host-owned */
+
+typedef struct isk_plan_info {
+  int32_t batch;
+  int32_t split_tokens;      /* resolved split length in units (tokens or slots)     */
+  int32_t num_segments;      /* splits (one partial output each, or a direct write)  */
+  int32_t num_groups;        /* workgroup tasks the split kernel is launched with    */
+  int32_t num_partials;      /* partial (o, lse) slots in the workspace              */
+  int32_t reserved;
+  uint64_t workspace_bytes;  /* minimum workspace size for isk_attn_decode           */
+} isk_plan_info;
+
+/*
+ * isk_plan_create - plan the splits of one decode batch on the host.
+ *
+ * desc           problem description (copied; the caller may free it).
+ * batch          number of rows B (>= 1).
+ * lens_host      [B] host int32 KV lengths L_b >= 0, L_b <= max_pages_per_row
+ *                * page_size.  Must equal the device `lens` later passed to
+ *                isk_attn_decode.
+ * topk_len_host  [B] host int32 valid top-k counts for sparse MLA (clamped to
+ *                [0, topk_width]), NULL when dense.
+ * plan_out       receives the new plan.
+ *
+ * Per-row mode implements the per-row split rule requested in the FlashMLA
+ * issue page, section "Question".  Pure host work: no HIP call is made, so it
+ * may run on a machine without a GPU.  Errors: ISK_ERR_INVALID_ARG,
+ * ISK_ERR_UNSUPPORTED (no kernel for the shape).
+ */
+ISK_API int isk_plan_create(const isk_desc* desc, int32_t batch, const int32_t* lens_host,
+                    const int32_t* topk_len_host, isk_plan** plan_out);
+
+/*
+ * isk_plan_update - re-plan an existing plan in place for new lengths (the
+ * next decode step), keeping its descriptor.  Reuses the plan's buffers.
+ * Waits (host side) for the plan's previous work-list upload to finish before
+ * overwriting its pinned staging copy.  Same arguments and errors as create.
+ */
+ISK_API int isk_plan_update(isk_plan* plan, int32_t batch, const int32_t* lens_host,
+                    const int32_t* topk_len_host);
+
+/* isk_plan_destroy - free a plan (NULL is accepted).  Waits for the plan's
+ * last work-list upload first.  The caller must not destroy a plan while
+ * another thread uses it. */
+ISK_API int isk_plan_destroy(isk_plan* plan);
+
+/* isk_plan_query - sizes of a plan.  Host only. */
+ISK_API int isk_plan_query(const isk_plan* plan, isk_plan_info* info_out);
+
+/* isk_plan_workspace_bytes - minimum workspace bytes (0 if plan is NULL). */
+ISK_API size_t isk_plan_workspace_bytes(const isk_plan* plan);
+
+/*
+ * isk_plan_segments - host copy of the plan's split list, for inspection and
+ * tests.  Writes up to `capacity` records of 5 int32 each:
+ *   {row, begin, end, partial_slot, group}
+ * where [begin, end) is the split's range in the row's units (token
+ * positions, or top-k slots for sparse rows), partial_slot is the workspace
+ * slot the split writes (-1: the row has one split and writes the output
+ * directly), and group is the workgroup task that runs it.  Records are in
+ * launch order.  Returns the number of segments (or a negative status).
+ */
+ISK_API int isk_plan_segments(const isk_plan* plan, int32_t* records_out, int32_t capacity);
+
+/*
+ * isk_attn_decode - run split kernels and the fixed-order combine.
+ *
+ * plan        from isk_plan_create/update; not modified.
+ * q           [B, Hq, head_dim_qk] bf16.
+ * kv_pages    GQA: [num_pages, 2, Hkv, page_size, head_dim] bf16 (index 0 = K,
+ *             1 = V).  MLA: [num_pages, page_size, 576] bf16.
+ * block_table [B, max_pages_per_row] int32; entry j of row b is the page
+ *             holding the row's tokens [j*page_size, (j+1)*page_size).
+ * lens        [B] int32 device copy of lens_host.
+ * topk_idx    sparse MLA: [B, topk_width] int32 row-local token positions;
+ *             a slot below topk_len[b] whose value lies outside [0, L_b)
+ *             (e.g. -1) is skipped.  NULL when dense.
+ * topk_len    sparse MLA: [B] int32 device copy of topk_len_host.  NULL when
+ *             dense.
+ * out         [B, Hq, head_dim_v] bf16 or fp32 (desc.out_dtype); rows with
+ *             nothing to attend get 0.
+ * lse         [B, Hq] fp32 natural-log LSE of the scaled scores (-inf for
+ *             rows with nothing to attend).  May be NULL.
+ * workspace   device memory of at least isk_plan_workspace_bytes(plan) bytes,
+ *             256-byte aligned; holds the uploaded split list and the fp32
+ *             partials.  Must not be shared by calls in flight at the same time.
+ * stream      hipStream_t (as void*).
+ *
+ * Out-of-range block-table entries and top-k positions are masked in the
+ * kernels (never dereferenced); with desc.check_inputs = 1 they are instead
+ * reported as ISK_ERR_INDEX before any kernel runs (this synchronises the
+ * stream and copies the tables to the host).  Errors: ISK_ERR_INVALID_ARG,
+ * ISK_ERR_WORKSPACE, ISK_ERR_INDEX, ISK_ERR_HIP.
+ */
+ISK_API int isk_attn_decode(const isk_plan* plan, const void* q, const void* kv_pages,
+                    const int32_t* block_table, const int32_t* lens,
+                    const int32_t* topk_idx, const int32_t* topk_len,
+                    void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* isk_last_error - message for the last failing call on this thread
+ * ("" if none).  The pointer stays valid until the thread's next call. */
+ISK_API const char* isk_last_error(void);
+
+/* isk_numerics_id - the build's numerics identity: target architecture, the
+ * frozen split and tile constants and the kernel versions.  Output bits are
+ * claimed batch-invariant for a fixed value of this string (and GPU model). */
+ISK_API const char* isk_numerics_id(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISK_H */

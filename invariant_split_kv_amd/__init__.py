@@ -1,0 +1,204 @@
+"""Python binding of libisk, the batch-invariant split-KV decode-attention
+library for MI355X (gfx950).
+
+Argument marshalling only: every function here maps one-to-one onto an
+``isk_*`` entry point of include/isk.h and passes plain pointers and sizes.
+Device tensors may be given as torch tensors (their ``data_ptr()`` is passed)
+or as integer device addresses.  All computation runs in the HIP kernels of
+libisk.so; importing this package fails if the library has not been built
+(``python -m invariant_split_kv_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "IskError", "IskDesc", "IskPlanInfo", "KIND_GQA", "KIND_MLA", "SPLIT_PER_ROW",
+    "SPLIT_BATCH_BALANCED", "OUT_BF16", "OUT_F32", "LIB_PATH", "lib", "plan_create",
+    "plan_update", "plan_destroy", "plan_query", "plan_workspace_bytes", "plan_segments",
+    "attn_decode", "last_error", "numerics_id", "Plan",
+]
+
+KIND_GQA, KIND_MLA = 0, 1
+SPLIT_PER_ROW, SPLIT_BATCH_BALANCED = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+STATUS_NAMES = {0: "ISK_OK", -1: "ISK_ERR_INVALID_ARG", -2: "ISK_ERR_UNSUPPORTED",
+                -3: "ISK_ERR_WORKSPACE", -4: "ISK_ERR_INDEX", -5: "ISK_ERR_HIP"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libisk.so")
+
+
+class IskError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class IskDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_pages_per_row", ctypes.c_int32),
+                ("topk_width", ctypes.c_int32), ("split_mode", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("check_inputs", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class IskPlanInfo(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("split_tokens", ctypes.c_int32), ("num_segments", ctypes.c_int32),
+                ("num_groups", ctypes.c_int32), ("num_partials", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m invariant_split_kv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32P = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "isk_plan_create": (ctypes.c_int, [ctypes.POINTER(IskDesc), ctypes.c_int32, I32P, I32P, ctypes.POINTER(P)]),
+        "isk_plan_update": (ctypes.c_int, [P, ctypes.c_int32, I32P, I32P]),
+        "isk_plan_destroy": (ctypes.c_int, [P]),
+        "isk_plan_query": (ctypes.c_int, [P, ctypes.POINTER(IskPlanInfo)]),
+        "isk_plan_workspace_bytes": (ctypes.c_size_t, [P]),
+        "isk_plan_segments": (ctypes.c_int, [P, I32P, ctypes.c_int32]),
+        "isk_attn_decode": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "isk_last_error": (ctypes.c_char_p, []),
+        "isk_numerics_id": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise IskError(status, lib.isk_last_error().decode())
+
+
+def _i32_host(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr
+
+
+def _i32p(arr: Optional[np.ndarray]):
+    return None if arr is None else arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _ptr(x) -> Optional[int]:
+    """Device address of a torch tensor, an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def last_error() -> str:
+    return lib.isk_last_error().decode()
+
+
+def numerics_id() -> str:
+    return lib.isk_numerics_id().decode()
+
+
+def plan_create(desc: IskDesc, lens_host, topk_len_host=None) -> int:
+    lens = _i32_host(lens_host)
+    tl = _i32_host(topk_len_host)
+    out = ctypes.c_void_p()
+    _check(lib.isk_plan_create(ctypes.byref(desc), len(lens), _i32p(lens), _i32p(tl), ctypes.byref(out)))
+    return out.value
+
+
+def plan_update(plan: int, lens_host, topk_len_host=None) -> None:
+    lens = _i32_host(lens_host)
+    tl = _i32_host(topk_len_host)
+    _check(lib.isk_plan_update(plan, len(lens), _i32p(lens), _i32p(tl)))
+
+
+def plan_destroy(plan: int) -> None:
+    _check(lib.isk_plan_destroy(plan))
+
+
+def plan_query(plan: int) -> dict:
+    info = IskPlanInfo()
+    _check(lib.isk_plan_query(plan, ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in IskPlanInfo._fields_ if f != "reserved"}
+
+
+def plan_workspace_bytes(plan: int) -> int:
+    return int(lib.isk_plan_workspace_bytes(plan))
+
+
+def plan_segments(plan: int) -> np.ndarray:
+    """[n, 5] int32 records (row, begin, end, partial_slot, group), launch order."""
+    n = lib.isk_plan_segments(plan, None, 0)
+    if n < 0:
+        _check(n)
+    rec = np.zeros((max(n, 1), 5), dtype=np.int32)
+    got = lib.isk_plan_segments(plan, _i32p(rec), n)
+    if got < 0:
+        _check(got)
+    return rec[:n]
+
+
+def attn_decode(plan: int, q, kv_pages, block_table, lens, topk_idx, topk_len, out, lse, workspace,
+                workspace_bytes: int, stream=None) -> None:
+    """Enqueue one decode-attention call on `stream` (torch stream, raw
+    hipStream_t int, or None for torch's current stream)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(lib.isk_attn_decode(plan, _ptr(q), _ptr(kv_pages), _ptr(block_table), _ptr(lens), _ptr(topk_idx),
+                               _ptr(topk_len), _ptr(out), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                               stream))
+
+
+class Plan:
+    """Owning wrapper of an isk_plan handle (destroyed on close/garbage collection)."""
+
+    def __init__(self, desc: IskDesc, lens_host, topk_len_host=None):
+        self.desc = desc
+        self.handle = plan_create(desc, lens_host, topk_len_host)
+
+    def update(self, lens_host, topk_len_host=None) -> None:
+        plan_update(self.handle, lens_host, topk_len_host)
+
+    def info(self) -> dict:
+        return plan_query(self.handle)
+
+    @property
+    def workspace_bytes(self) -> int:
+        return plan_workspace_bytes(self.handle)
+
+    def segments(self) -> np.ndarray:
+        return plan_segments(self.handle)
+
+    def close(self) -> None:
+        if self.handle:
+            plan_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,69 @@
+"""Build libisk.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+
+Usage: python -m invariant_split_kv_amd.build   (or call build()).
+Always recompiles; objects go to _build/ at the repository root.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libisk.so")
+
+SOURCES = ["plan.cpp", "api.cpp", "gqa_split.hip", "mla_split.hip", "combine.hip"]
+ARCH = "gfx950"
+# Packed fp32 instructions stay disabled (the compiler would otherwise form
+# v_pk_* ops from scalar float code).
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function", "-fvisibility=hidden"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every source and link libisk.so; returns the library path."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+        if len(procs) >= jobs:
+            _wait(procs.pop(0), verbose)
+    while procs:
+        _wait(procs.pop(0), verbose)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _wait(item, verbose):
+    cmd, p = item
+    out, _ = p.communicate()
+    out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,315 @@
+// C ABI of libisk: argument checks, plan objects, per-call metadata upload and
+// kernel launches.  Every entry point returns an isk_status and records a
+// thread-local message on failure; nothing throws across the boundary.
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "isk_internal.hpp"
+
+using isk::MetaLayout;
+using isk::PlanData;
+
+namespace {
+
+thread_local std::string g_err;
+
+int set_err(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_err(hipError_t e, const char* what) {
+  std::ostringstream s;
+  s << what << ": " << hipGetErrorString(e);
+  return set_err(ISK_ERR_HIP, s.str());
+}
+
+// Pinned staging ring for the per-call metadata: a decode may be enqueued
+// while up to kRing earlier uploads of the same plan are still pending.
+constexpr int kRing = 4;
+
+}  // namespace
+
+struct isk_plan {
+  PlanData data;
+  MetaLayout layout{};
+  std::vector<unsigned char> meta_host;   // serialised metadata
+  void* staging[kRing] = {};
+  size_t staging_bytes[kRing] = {};
+  hipEvent_t staged[kRing] = {};
+  int ring_next = 0;
+};
+
+namespace {
+
+void serialise(isk_plan* p) {
+  p->layout = isk::meta_layout(p->data);
+  p->meta_host.assign(p->layout.bytes, 0);
+  std::memcpy(p->meta_host.data() + p->layout.segs_off, p->data.segs.data(), p->data.segs.size() * sizeof(isk::Seg));
+  std::memcpy(p->meta_host.data() + p->layout.groups_off, p->data.groups.data(), p->data.groups.size() * sizeof(int32_t));
+  std::memcpy(p->meta_host.data() + p->layout.rows_off, p->data.rows.data(), p->data.rows.size() * sizeof(isk::RowInfo));
+}
+
+void release_staging(isk_plan* p) {
+  for (int i = 0; i < kRing; ++i) {
+    if (p->staged[i] != nullptr) {
+      (void)hipEventSynchronize(p->staged[i]);
+      (void)hipEventDestroy(p->staged[i]);
+      p->staged[i] = nullptr;
+    }
+    if (p->staging[i] != nullptr) {
+      (void)hipHostFree(p->staging[i]);
+      p->staging[i] = nullptr;
+      p->staging_bytes[i] = 0;
+    }
+  }
+}
+
+// Audit of the tables against the plan (desc.check_inputs).  Copies the
+// device tables to the host (synchronising the stream).
+int audit_inputs(const isk_plan* p, const int32_t* block_table, const int32_t* lens, const int32_t* topk_idx,
+                 const int32_t* topk_len, hipStream_t stream) {
+  const isk_desc& d = p->data.desc;
+  const int B = p->data.batch;
+  std::vector<int32_t> h_lens(B), h_bt((size_t)B * d.max_pages_per_row), h_tl, h_idx;
+  hipError_t e = hipMemcpyAsync(h_lens.data(), lens, B * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h_bt.data(), block_table, h_bt.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  const bool sparse = d.topk_width > 0;
+  if (sparse && e == hipSuccess) {
+    h_tl.resize(B);
+    h_idx.resize((size_t)B * d.topk_width);
+    e = hipMemcpyAsync(h_tl.data(), topk_len, B * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(h_idx.data(), topk_idx, h_idx.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_err(e, "check_inputs: copying tables to the host");
+
+  auto page_ok = [&](int b, int pos) {
+    const int32_t pg = h_bt[(size_t)b * d.max_pages_per_row + pos / d.page_size];
+    return pg >= 0 && pg < d.num_pages;
+  };
+  for (int b = 0; b < B; ++b) {
+    const int32_t L = h_lens[b];
+    if (!sparse && L != p->data.units[b]) {
+      std::ostringstream s;
+      s << "check_inputs: lens[" << b << "] = " << L << " differs from the planned length " << p->data.units[b];
+      return set_err(ISK_ERR_INVALID_ARG, s.str());
+    }
+    if (L < 0 || (long long)L > (long long)d.max_pages_per_row * d.page_size) {
+      std::ostringstream s;
+      s << "check_inputs: lens[" << b << "] = " << L << " out of range";
+      return set_err(ISK_ERR_INDEX, s.str());
+    }
+    if (!sparse) {
+      for (int j = 0; j < L; j += d.page_size)
+        if (!page_ok(b, j)) {
+          std::ostringstream s;
+          s << "check_inputs: block_table[" << b << "][" << j / d.page_size << "] is not a page of the pool";
+          return set_err(ISK_ERR_INDEX, s.str());
+        }
+    } else {
+      const int32_t n = std::min(std::max(h_tl[b], 0), d.topk_width);
+      if (n != p->data.units[b]) {
+        std::ostringstream s;
+        s << "check_inputs: topk_len[" << b << "] differs from the planned count";
+        return set_err(ISK_ERR_INVALID_ARG, s.str());
+      }
+      for (int j = 0; j < n; ++j) {
+        const int32_t pos = h_idx[(size_t)b * d.topk_width + j];
+        if (pos < 0 || pos >= L) {
+          std::ostringstream s;
+          s << "check_inputs: topk_idx[" << b << "][" << j << "] = " << pos << " is not a position in [0, " << L
+            << ") although the slot is below topk_len";
+          return set_err(ISK_ERR_INDEX, s.str());
+        }
+        if (!page_ok(b, pos)) {
+          std::ostringstream s;
+          s << "check_inputs: the page of topk_idx[" << b << "][" << j << "] is not a page of the pool";
+          return set_err(ISK_ERR_INDEX, s.str());
+        }
+      }
+    }
+  }
+  return ISK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* isk_last_error(void) { return g_err.c_str(); }
+
+const char* isk_numerics_id(void) {
+  static const std::string id = [] {
+    std::ostringstream s;
+    s << "isk-1 arch=gfx950"
+      << " gqa_tile=" << isk::kGqaTile << " mla_tile=" << isk::kMlaTile
+      << " split_gqa=" << isk::kGqaSplitDefault << " split_mla=" << isk::kMlaSplitDefault
+      << " split_topk=" << isk::kSparseSplitDefault
+      << " gqa=vdot2-bf16/fp32-pv mla=mfma16x16x32-bf16/p-bf16/rescale-thr8 combine=fixed-order-fp32"
+      << " balanced=blk" << isk::kBalancedBlock << "-parts" << isk::kBalancedParts << "-ovh" << isk::kBalancedOverhead;
+    return s.str();
+  }();
+  return id.c_str();
+}
+
+int isk_plan_create(const isk_desc* desc, int32_t batch, const int32_t* lens_host, const int32_t* topk_len_host,
+                    isk_plan** plan_out) {
+  if (plan_out == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan_out is NULL");
+  *plan_out = nullptr;
+  if (desc == nullptr) return set_err(ISK_ERR_INVALID_ARG, "desc is NULL");
+  isk_plan* p = new (std::nothrow) isk_plan();
+  if (p == nullptr) return set_err(ISK_ERR_INVALID_ARG, "out of host memory");
+  int status = ISK_OK;
+  std::string msg = isk::plan_build(p->data, *desc, batch, lens_host, topk_len_host, &status);
+  if (status != ISK_OK) {
+    delete p;
+    return set_err(status, msg);
+  }
+  serialise(p);
+  *plan_out = p;
+  return ISK_OK;
+}
+
+int isk_plan_update(isk_plan* plan, int32_t batch, const int32_t* lens_host, const int32_t* topk_len_host) {
+  if (plan == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
+  PlanData fresh;
+  int status = ISK_OK;
+  std::string msg = isk::plan_build(fresh, plan->data.desc, batch, lens_host, topk_len_host, &status);
+  if (status != ISK_OK) return set_err(status, msg);
+  plan->data = std::move(fresh);
+  serialise(plan);
+  return ISK_OK;
+}
+
+int isk_plan_destroy(isk_plan* plan) {
+  if (plan == nullptr) return ISK_OK;
+  release_staging(plan);
+  delete plan;
+  return ISK_OK;
+}
+
+int isk_plan_query(const isk_plan* plan, isk_plan_info* info) {
+  if (plan == nullptr || info == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan or info_out is NULL");
+  info->batch = plan->data.batch;
+  info->split_tokens = plan->data.split_units;
+  info->num_segments = (int32_t)plan->data.segs.size();
+  info->num_groups = (int32_t)plan->data.groups.size() - 1;
+  info->num_partials = plan->data.n_partials;
+  info->reserved = 0;
+  info->workspace_bytes = plan->layout.total;
+  return ISK_OK;
+}
+
+size_t isk_plan_workspace_bytes(const isk_plan* plan) { return plan == nullptr ? 0 : plan->layout.total; }
+
+int isk_plan_segments(const isk_plan* plan, int32_t* records, int32_t capacity) {
+  if (plan == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
+  const int32_t n = (int32_t)plan->data.segs.size();
+  if (records != nullptr) {
+    for (int32_t i = 0; i < n && i < capacity; ++i) {
+      const isk::Seg& s = plan->data.segs[i];
+      int32_t* r = records + 5 * (size_t)i;
+      r[0] = s.row; r[1] = s.begin; r[2] = s.end; r[3] = s.part; r[4] = plan->data.seg_group[i];
+    }
+  }
+  return n;
+}
+
+int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages, const int32_t* block_table,
+                    const int32_t* lens, const int32_t* topk_idx, const int32_t* topk_len, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream_v) {
+  if (plan_c == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
+  isk_plan* plan = const_cast<isk_plan*>(plan_c);   // staging ring only; the plan itself is not changed
+  const PlanData& pd = plan->data;
+  const isk_desc& d = pd.desc;
+  const bool sparse = d.topk_width > 0;
+  hipStream_t stream = (hipStream_t)stream_v;
+  if (q == nullptr || kv_pages == nullptr || block_table == nullptr || lens == nullptr || out == nullptr)
+    return set_err(ISK_ERR_INVALID_ARG, "q, kv_pages, block_table, lens and out must be non-NULL");
+  if (sparse && (topk_idx == nullptr || topk_len == nullptr))
+    return set_err(ISK_ERR_INVALID_ARG, "sparse plan: topk_idx and topk_len must be non-NULL");
+  if (!sparse && (topk_idx != nullptr || topk_len != nullptr))
+    return set_err(ISK_ERR_INVALID_ARG, "dense plan: topk_idx and topk_len must be NULL");
+  if (workspace == nullptr || workspace_bytes < plan->layout.total) {
+    std::ostringstream s;
+    s << "workspace of " << workspace_bytes << " bytes is smaller than the " << plan->layout.total << " the plan needs";
+    return set_err(ISK_ERR_WORKSPACE, s.str());
+  }
+  if (((uintptr_t)workspace & 255u) != 0) return set_err(ISK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  auto aligned = [](const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; };
+  if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(out, 16) || !aligned(block_table, 4) || !aligned(lens, 4) ||
+      (lse != nullptr && !aligned(lse, 4)) || (sparse && !aligned(topk_idx, 4)))
+    return set_err(ISK_ERR_INVALID_ARG, "q, kv_pages and out must be 16-byte aligned, tables 4-byte aligned");
+
+  if (d.check_inputs) {
+    const int rc = audit_inputs(plan, block_table, lens, topk_idx, topk_len, stream);
+    if (rc != ISK_OK) return rc;
+  }
+
+  // Upload the metadata through a pinned staging slot.
+  const int slot = plan->ring_next;
+  plan->ring_next = (slot + 1) % kRing;
+  hipError_t e;
+  if (plan->staged[slot] != nullptr) {
+    e = hipEventSynchronize(plan->staged[slot]);
+    if (e != hipSuccess) return hip_err(e, "waiting for an earlier metadata upload");
+  } else {
+    e = hipEventCreateWithFlags(&plan->staged[slot], hipEventDisableTiming);
+    if (e != hipSuccess) return hip_err(e, "hipEventCreate");
+  }
+  const size_t mbytes = plan->layout.bytes;
+  if (plan->staging_bytes[slot] < mbytes) {
+    if (plan->staging[slot] != nullptr) (void)hipHostFree(plan->staging[slot]);
+    plan->staging[slot] = nullptr;
+    plan->staging_bytes[slot] = 0;
+    e = hipHostMalloc(&plan->staging[slot], mbytes, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_err(e, "hipHostMalloc (metadata staging)");
+    plan->staging_bytes[slot] = mbytes;
+  }
+  std::memcpy(plan->staging[slot], plan->meta_host.data(), mbytes);
+  unsigned char* ws = (unsigned char*)workspace;
+  e = hipMemcpyAsync(ws, plan->staging[slot], mbytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (metadata upload)");
+  e = hipEventRecord(plan->staged[slot], stream);
+  if (e != hipSuccess) return hip_err(e, "hipEventRecord");
+
+  const isk::Seg* segs = (const isk::Seg*)(ws + plan->layout.segs_off);
+  const int32_t* groups = (const int32_t*)(ws + plan->layout.groups_off);
+  const isk::RowInfo* rows = (const isk::RowInfo*)(ws + plan->layout.rows_off);
+  float* part_o = (float*)(ws + plan->layout.part_o_off);
+  float* part_lse = (float*)(ws + plan->layout.part_lse_off);
+  const int32_t n_groups = (int32_t)pd.groups.size() - 1;
+  const float scale_log2 = d.scale * isk::kLog2eHost;
+
+  if (d.kind == ISK_KIND_GQA) {
+    isk::GqaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, segs, groups, part_o, part_lse,
+                     out, lse, n_groups, d.num_q_heads, d.num_kv_heads, d.head_dim_qk, d.page_size, d.num_pages,
+                     d.max_pages_per_row, d.out_dtype == ISK_OUT_F32, scale_log2};
+    e = isk::launch_gqa_split(a, stream);
+    if (e != hipSuccess) return hip_err(e, "launching the GQA split kernel");
+  } else {
+    isk::MlaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, sparse ? topk_idx : nullptr,
+                     segs, groups, part_o, part_lse, out, lse, n_groups, d.num_q_heads, d.page_size, d.num_pages,
+                     d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2};
+    e = isk::launch_mla_split(a, stream);
+    if (e != hipSuccess) return hip_err(e, "launching the MLA split kernel");
+  }
+  if (pd.any_combine) {
+    isk::CombineLaunch c{rows, part_o, part_lse, out, lse, pd.batch, d.num_q_heads, d.head_dim_v,
+                         d.out_dtype == ISK_OUT_F32};
+    e = isk::launch_combine(c, stream);
+    if (e != hipSuccess) return hip_err(e, "launching the combine kernel");
+  }
+  return ISK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,276 @@
+// Dense grouped-query split kernel for gfx950.
+//
+// One workgroup runs the splits of one task for one kv head: for each split
+// ("segment") it computes softmax attention of the G query heads that share
+// that kv head over the segment's tokens, then writes the partial
+// (o_i, lse_i) of the split-KV scheme (FlashMLA issue page "Sparse MLA decode
+// is not batch-invariant ...", section "Where it comes from"), or the final
+// output when the row has a single split.
+//
+// The work per token is G*(2*D) multiply-adds against 4*D bytes of K and V,
+// about 4 FLOP per byte for G = 4, so the kernel is bound by HBM, not by the
+// matrix cores; it uses vector ALU arithmetic:
+//   * 64-token K and V tiles of the kv head are copied HBM -> LDS with 16-byte
+//     direct loads, double buffered.  Piece c (8 dims) of tile row t is stored
+//     at piece (c ^ (t & 7)) of that row, so that 8 lanes reading the same
+//     column of 8 consecutive rows hit distinct banks.
+//   * Scores: lane t owns token t of the tile and accumulates the dot product
+//     with packed bf16 pairs (v_dot2_f32_bf16, fp32 accumulate), in a fixed
+//     dimension order.
+//   * Softmax per head: wave-wide butterfly max, p = 2^(x - m) in fp32; each
+//     lane keeps a partial normaliser for its token slot, summed by a fixed
+//     butterfly at the end of the segment.
+//   * PV: lane l owns D/64 output dims and accumulates p_t * v_t[d] in fp32
+//     over the tile's tokens in order.
+// Heads: with G >= 4 each of the four waves owns G/4 heads; with G < 4 the
+// workgroup has G waves of one head each.
+
+#include "device.hpp"
+#include "isk_internal.hpp"
+
+namespace isk {
+namespace {
+
+constexpr int kTile = kGqaTile;   // 64 tokens per tile, one per lane
+
+template <int D>
+struct GqaShape {
+  static constexpr int kPieces = D / 8;                 // 16-byte pieces per row
+  static constexpr int kTileBytes = kTile * D * 2;      // one of K or V
+  static constexpr int kInstr = kTile * kPieces / 64;   // wave-wide 16B loads per tile
+  static constexpr int kDimsPerLane = D / 64;
+};
+
+template <int D>
+__device__ __forceinline__ uint64_t gqa_stage(const GqaLaunch& a, int b, int hk, int u0, int seg_end,
+                                              ISK_LDS unsigned char* kbuf, ISK_LDS unsigned char* vbuf,
+                                              int wave, int nw, int lane) {
+  using S = GqaShape<D>;
+  asm volatile("" : "+v"(lane));   // keep per-lane addresses out of the loop preheader
+  const int P = a.page_size;
+  // Token row `lane` of this tile: its pool offset (in elements) of K; V is
+  // Hkv*P*D elements further.
+  const int pos = u0 + lane;
+  bool ok = pos < seg_end;
+  const int pg = ok ? a.block_table[(size_t)b * a.max_pages + pos / P] : 0;
+  ok = ok && pg >= 0 && pg < a.num_pages;
+  const size_t my_off = ok ? ((((size_t)pg * 2) * a.hkv + hk) * P + pos % P) * (size_t)D : 0;
+  const uint64_t mask = __ballot(ok);
+  const size_t v_delta = (size_t)a.hkv * P * D;
+  const unsigned char* kv = (const unsigned char*)a.kv;
+  for (int i = wave; i < S::kInstr; i += nw) {
+    const int p = i * 64 + lane;
+    const int t = p / S::kPieces;
+    const int c = (p % S::kPieces) ^ (t & 7);
+    const bool valid = (mask >> t) & 1ull;
+    const size_t off = (size_t)__shfl((long long)my_off, t, 64);
+    if (valid) {
+      const unsigned char* src = kv + (off + (size_t)c * 8) * 2;
+      load_lds_16(src, kbuf + i * 1024);
+      load_lds_16(src + v_delta * 2, vbuf + i * 1024);
+    } else {
+      *(ISK_LDS f32x4*)(kbuf + p * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
+      *(ISK_LDS f32x4*)(vbuf + p * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  return mask;
+}
+
+template <int D, int HPW>
+__global__ void __launch_bounds__(256) gqa_split_kernel(GqaLaunch a) {
+  using S = GqaShape<D>;
+  constexpr int DPL = S::kDimsPerLane;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[4 * S::kTileBytes + 4 * HPW * kTile * 4];
+  ISK_LDS unsigned char* lds = (ISK_LDS unsigned char*)lds_raw;
+  ISK_LDS unsigned char* kbufs = lds;                               // [2][tile]
+  ISK_LDS unsigned char* vbufs = lds + 2 * S::kTileBytes;           // [2][tile]
+  ISK_LDS float* p_lds = (ISK_LDS float*)(lds + 4 * S::kTileBytes); // [wave][HPW][64]
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int g = a.hq / a.hkv;
+  const int hk = blockIdx.y;
+  const int task = blockIdx.x;
+  const int seg_first = a.groups[task], seg_last = a.groups[task + 1];
+  ISK_LDS float* my_p = p_lds + wave * HPW * kTile;
+
+  for (int si = seg_first; si < seg_last; ++si) {
+    const Seg sg = a.segs[si];
+    const int b = sg.row;
+    __syncthreads();   // LDS tiles of the previous segment are no longer read
+
+    // Query heads of this wave: hk*G + wave*HPW + hh.  q as packed bf16 pairs.
+    uint32_t qv[HPW][D / 2];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int head = hk * g + wave * HPW + hh;
+      const uint4* qrow = (const uint4*)(a.q + ((size_t)b * a.hq + head) * D);
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        const uint4 w = qrow[c];
+        qv[hh][4 * c + 0] = w.x; qv[hh][4 * c + 1] = w.y;
+        qv[hh][4 * c + 2] = w.z; qv[hh][4 * c + 3] = w.w;
+      }
+    }
+
+    float m_run[HPW], l_lane[HPW], acc[HPW][DPL];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      m_run[hh] = -INFINITY;
+      l_lane[hh] = 0.f;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) acc[hh][j] = 0.f;
+    }
+
+    const int n_tiles = (sg.end - sg.begin + kTile - 1) / kTile;
+    uint64_t mask_next = n_tiles > 0 ? gqa_stage<D>(a, b, hk, sg.begin, sg.end, kbufs, vbufs, wave, nw, lane) : 0ull;
+
+    for (int it = 0; it < n_tiles; ++it) {
+      wait_vmem_all();
+      __syncthreads();
+      const uint64_t mask = mask_next;
+      const int cur = it & 1;
+      ISK_LDS unsigned char* K = kbufs + cur * S::kTileBytes;
+      ISK_LDS unsigned char* V = vbufs + cur * S::kTileBytes;
+      if (it + 1 < n_tiles)
+        mask_next = gqa_stage<D>(a, b, hk, sg.begin + (it + 1) * kTile, sg.end, kbufs + (cur ^ 1) * S::kTileBytes,
+                                 vbufs + (cur ^ 1) * S::kTileBytes, wave, nw, lane);
+
+      // ---- scores: lane = token
+      float sc[HPW];
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) sc[hh] = 0.f;
+      {
+        const ISK_LDS unsigned char* krow = K + lane * (D * 2);
+#pragma unroll
+        for (int c = 0; c < S::kPieces; ++c) {
+          const u32x4 kp = *(const ISK_LDS u32x4*)(krow + ((c ^ (lane & 7)) * 16));
+          const uint32_t k0 = kp[0], k1 = kp[1], k2 = kp[2], k3 = kp[3];
+#pragma unroll
+          for (int hh = 0; hh < HPW; ++hh) {
+            float s = sc[hh];
+            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[hh][4 * c + 0]), as_bf16x2(k0), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[hh][4 * c + 1]), as_bf16x2(k1), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[hh][4 * c + 2]), as_bf16x2(k2), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[hh][4 * c + 3]), as_bf16x2(k3), s, false);
+            sc[hh] = s;
+          }
+        }
+      }
+
+      // ---- softmax per head (log2 domain)
+      const bool valid = (mask >> lane) & 1ull;
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const float x = valid ? sc[hh] * a.scale_log2 : -INFINITY;
+        float mx = x;
+#pragma unroll
+        for (int sh = 1; sh < 64; sh <<= 1) mx = wave_max_xor(mx, sh);
+        const float m_new = fmaxf(m_run[hh], mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[hh] - m_use);
+        m_run[hh] = m_new;
+        const float p = fast_exp2(x - m_use);
+        l_lane[hh] = l_lane[hh] * alpha + p;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[hh][j] *= alpha;
+        my_p[hh * kTile + lane] = p;
+      }
+      // p of this wave's heads is read back by the same wave only.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // ---- PV: lane owns dims [DPL*lane, DPL*lane + DPL)
+      {
+        const int vpiece = (DPL * lane) / 8;
+        const int vin = (DPL * lane * 2) % 16;
+#pragma unroll 4
+        for (int t4 = 0; t4 < kTile; t4 += 4) {
+          f32x4 pw[HPW];
+#pragma unroll
+          for (int hh = 0; hh < HPW; ++hh) pw[hh] = *(const ISK_LDS f32x4*)(my_p + hh * kTile + t4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int t = t4 + u;
+            const ISK_LDS unsigned char* vp = V + t * (D * 2) + ((vpiece ^ (t & 7)) * 16) + vin;
+            if constexpr (DPL == 2) {
+              const uint32_t w = *(const ISK_LDS uint32_t*)vp;
+              const float v0 = bf16_lo(w), v1 = bf16_hi(w);
+#pragma unroll
+              for (int hh = 0; hh < HPW; ++hh) {
+                acc[hh][0] = fmaf(pw[hh][u], v0, acc[hh][0]);
+                acc[hh][1] = fmaf(pw[hh][u], v1, acc[hh][1]);
+              }
+            } else {
+              const float v0 = __uint_as_float((uint32_t)(*(const ISK_LDS uint16_t*)vp) << 16);
+#pragma unroll
+              for (int hh = 0; hh < HPW; ++hh) acc[hh][0] = fmaf(pw[hh][u], v0, acc[hh][0]);
+            }
+          }
+        }
+      }
+    }
+
+    // ---- epilogue
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int head = hk * g + wave * HPW + hh;
+      float l_tot = l_lane[hh];
+#pragma unroll
+      for (int sh = 1; sh < 64; sh <<= 1) l_tot = wave_add_xor(l_tot, sh);
+      const bool empty = !(l_tot > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_tot;
+      const float lse_v = empty ? -INFINITY : (m_run[hh] + fast_log2(l_tot)) * kLn2;
+      float o[DPL];
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[j] = acc[hh][j] * inv;
+      if (sg.part >= 0) {
+        float* po = a.part_o + ((size_t)sg.part * a.hq + head) * D + DPL * lane;
+        if constexpr (DPL == 2) *(f32x2*)po = f32x2{o[0], o[1]};
+        else po[0] = o[0];
+        if (lane == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
+      } else {
+        const size_t ob = ((size_t)b * a.hq + head) * D + DPL * lane;
+        if (a.out_f32) {
+          float* op = (float*)a.out + ob;
+          if constexpr (DPL == 2) *(f32x2*)op = f32x2{o[0], o[1]};
+          else op[0] = o[0];
+        } else {
+          uint16_t* op = (uint16_t*)a.out + ob;
+          if constexpr (DPL == 2) {
+            *(uint32_t*)op = pack_bf16x2(o[0], o[1]);
+          } else {
+            op[0] = (uint16_t)(pack_bf16x2(o[0], 0.f) & 0xffffu);
+          }
+        }
+        if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const GqaLaunch& a, hipStream_t s) {
+  const int g = a.hq / a.hkv;
+  const dim3 grid(a.n_groups, a.hkv);
+  switch (g) {
+    case 1: hipLaunchKernelGGL((gqa_split_kernel<D, 1>), grid, dim3(64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gqa_split_kernel<D, 1>), grid, dim3(128), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gqa_split_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gqa_split_kernel<D, 2>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((gqa_split_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gqa_split(const GqaLaunch& a, hipStream_t s) {
+  if (a.n_groups == 0) return hipSuccess;
+  if (a.d == 128) return launch_d<128>(a, s);
+  if (a.d == 64) return launch_d<64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace isk

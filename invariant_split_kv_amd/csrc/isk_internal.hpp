@@ -1,0 +1,99 @@
+// Internal declarations shared by the host runtime (api.cpp, plan.cpp) and
+// the kernel launchers (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "isk.h"
+
+namespace isk {
+
+// Frozen numerics constants.  A row's split boundaries are multiples of the
+// split length, and tile boundaries inside a split are multiples of the tile,
+// so both are functions of the row's own length and these constants only.
+constexpr int kGqaTile = 64;          // tokens per GQA wave step
+constexpr int kMlaTile = 64;          // tokens per MLA LDS tile
+constexpr int kGqaSplitDefault = 512;
+constexpr int kMlaSplitDefault = 1024;
+constexpr int kSparseSplitDefault = 512;
+constexpr int kMlaDqk = 576;
+constexpr float kLog2eHost = 1.44269504088896340736f;   // log2(e), rounded to float
+constexpr int kMlaDv = 512;
+// Batch-balanced comparison mode: block granularity, parts and per-row
+// overhead charge of the batch-wide scheduler it reproduces.
+constexpr int kBalancedBlock = 64;
+constexpr int kBalancedParts = 256;
+constexpr int kBalancedOverhead = 1;
+
+// One split of one row: units [begin, end) of row `row`; `part` is the
+// workspace partial slot, or -1 when the row has a single split and writes
+// the final output directly.
+struct Seg {
+  int32_t row, begin, end, part;
+};
+
+struct RowInfo {
+  int32_t part_off;   // first partial slot of the row
+  int32_t n_parts;    // 0: empty row; 1: written directly; >1: combined
+};
+
+struct PlanData {
+  isk_desc desc{};
+  int32_t batch = 0;
+  int32_t split_units = 0;
+  std::vector<int32_t> units;       // per-row units (tokens or top-k slots)
+  std::vector<Seg> segs;            // launch order
+  std::vector<int32_t> seg_group;   // group of each segment (for inspection)
+  std::vector<int32_t> groups;      // CSR offsets into segs, size n_groups + 1
+  std::vector<RowInfo> rows;
+  int32_t n_partials = 0;
+  bool any_combine = false;         // some row has 0 or >1 splits
+};
+
+// Byte layout of the per-call metadata at the head of the workspace.
+struct MetaLayout {
+  size_t segs_off, groups_off, rows_off, bytes;        // meta block
+  size_t part_o_off, part_lse_off, total;               // whole workspace
+};
+MetaLayout meta_layout(const PlanData& p);
+
+// Planner (host only; no HIP calls).  Returns an empty string on success,
+// otherwise the error message; *status receives the isk_status.
+std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int32_t* lens_host,
+                       const int32_t* topk_len_host, int* status);
+
+// ---------------------------------------------------------------- launchers
+struct GqaLaunch {
+  const uint16_t* q; const uint16_t* kv;
+  const int32_t* block_table; const int32_t* lens;
+  const Seg* segs; const int32_t* groups;
+  float* part_o; float* part_lse; void* out; float* lse;
+  int32_t n_groups, hq, hkv, d, page_size, num_pages, max_pages, out_f32;
+  float scale_log2;
+};
+hipError_t launch_gqa_split(const GqaLaunch& a, hipStream_t s);
+
+struct MlaLaunch {
+  const uint16_t* q; const uint16_t* kv;
+  const int32_t* block_table; const int32_t* lens;
+  const int32_t* topk_idx;
+  const Seg* segs; const int32_t* groups;
+  float* part_o; float* part_lse; void* out; float* lse;
+  int32_t n_groups, hq, page_size, num_pages, max_pages, topk_width, out_f32;
+  float scale_log2;
+};
+hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s);
+
+struct CombineLaunch {
+  const RowInfo* rows; const float* part_o; const float* part_lse;
+  void* out; float* lse;
+  int32_t batch, hq, dv, out_f32;
+};
+hipError_t launch_combine(const CombineLaunch& a, hipStream_t s);
+
+}  // namespace isk

@@ -1,0 +1,192 @@
+// Host split planner (no HIP calls; usable without a GPU).
+//
+// Per-row mode follows the request on the FlashMLA issue page "Sparse MLA
+// decode is not batch-invariant ..." (section "Question"): a row's split
+// count comes only from its own length and fixed constants:
+//   n_b = ceil(U_b / S),  split i = [i*S, min((i+1)*S, U_b)),
+// where U_b is the row's length in tokens (dense) or its valid top-k count
+// (sparse) and S the frozen split length of the kind.  An exclusive scan over
+// rows assigns workspace slots to the partials; it decides where partials
+// live, never what is computed.  Splits are dispatched longest first, which
+// changes only which compute unit runs a split and when.
+//
+// Batch-balanced mode exists for comparison only.  It reproduces the
+// scheduler that page describes (same section: a block quota per part derived
+// from the total over the whole batch, then greedy packing that cuts rows at
+// part boundaries), so a row's splits depend on its batchmates.
+
+#include <algorithm>
+#include <cmath>
+#include <sstream>
+
+#include "isk_internal.hpp"
+
+namespace isk {
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+std::string fail(int* status, int code, const std::string& msg) {
+  *status = code;
+  return msg;
+}
+
+}  // namespace
+
+MetaLayout meta_layout(const PlanData& p) {
+  MetaLayout m{};
+  m.segs_off = 0;
+  m.groups_off = align256(m.segs_off + p.segs.size() * sizeof(Seg));
+  m.rows_off = align256(m.groups_off + p.groups.size() * sizeof(int32_t));
+  m.bytes = align256(m.rows_off + p.rows.size() * sizeof(RowInfo));
+  const int dv = p.desc.head_dim_v;
+  m.part_o_off = m.bytes;
+  m.part_lse_off = align256(m.part_o_off + (size_t)p.n_partials * p.desc.num_q_heads * dv * sizeof(float));
+  m.total = align256(m.part_lse_off + (size_t)p.n_partials * p.desc.num_q_heads * sizeof(float));
+  return m;
+}
+
+static std::string check_desc(const isk_desc& d, int* status) {
+  std::ostringstream e;
+  if (d.kind != ISK_KIND_GQA && d.kind != ISK_KIND_MLA) return fail(status, ISK_ERR_INVALID_ARG, "desc.kind must be ISK_KIND_GQA or ISK_KIND_MLA");
+  if (d.num_q_heads <= 0 || d.num_kv_heads <= 0) return fail(status, ISK_ERR_INVALID_ARG, "head counts must be positive");
+  if (d.page_size <= 0 || d.num_pages <= 0 || d.max_pages_per_row <= 0)
+    return fail(status, ISK_ERR_INVALID_ARG, "page_size, num_pages and max_pages_per_row must be positive");
+  if (d.split_mode != ISK_SPLIT_PER_ROW && d.split_mode != ISK_SPLIT_BATCH_BALANCED)
+    return fail(status, ISK_ERR_INVALID_ARG, "desc.split_mode is not a valid isk_split_mode");
+  if (d.out_dtype != ISK_OUT_BF16 && d.out_dtype != ISK_OUT_F32)
+    return fail(status, ISK_ERR_INVALID_ARG, "desc.out_dtype is not a valid isk_out_dtype");
+  if (d.split_tokens < 0 || d.split_tokens % 64 != 0)
+    return fail(status, ISK_ERR_INVALID_ARG, "desc.split_tokens must be 0 or a positive multiple of 64");
+  if (!std::isfinite(d.scale)) return fail(status, ISK_ERR_INVALID_ARG, "desc.scale must be finite");
+  if (d.topk_width < 0) return fail(status, ISK_ERR_INVALID_ARG, "desc.topk_width must be >= 0");
+  if (d.kind == ISK_KIND_GQA) {
+    if (d.num_q_heads % d.num_kv_heads != 0) return fail(status, ISK_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+    const int g = d.num_q_heads / d.num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+      return fail(status, ISK_ERR_UNSUPPORTED, "GQA group size Hq/Hkv must be 1, 2, 4, 8 or 16");
+    if (d.head_dim_qk != 64 && d.head_dim_qk != 128) return fail(status, ISK_ERR_UNSUPPORTED, "GQA head_dim_qk must be 64 or 128");
+    if (d.head_dim_v != d.head_dim_qk) return fail(status, ISK_ERR_INVALID_ARG, "GQA head_dim_v must equal head_dim_qk");
+    if (d.topk_width != 0) return fail(status, ISK_ERR_UNSUPPORTED, "top-k gather is supported for MLA only");
+  } else {
+    if (d.num_kv_heads != 1) return fail(status, ISK_ERR_INVALID_ARG, "MLA has one latent kv head (num_kv_heads = 1)");
+    if (d.head_dim_qk != kMlaDqk || d.head_dim_v != kMlaDv) return fail(status, ISK_ERR_UNSUPPORTED, "MLA needs head_dim_qk 576 and head_dim_v 512");
+    if (d.num_q_heads % 16 != 0 || (d.num_q_heads > 64 && d.num_q_heads % 64 != 0))
+      return fail(status, ISK_ERR_UNSUPPORTED, "MLA num_q_heads must be a multiple of 16 (and of 64 above 64)");
+    if (d.topk_width == 0 && d.page_size % 64 != 0) return fail(status, ISK_ERR_UNSUPPORTED, "dense MLA needs page_size a multiple of 64");
+  }
+  *status = ISK_OK;
+  return "";
+}
+
+std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int32_t* lens_host,
+                       const int32_t* topk_len_host, int* status) {
+  std::string err = check_desc(d, status);
+  if (*status != ISK_OK) return err;
+  if (batch <= 0) return fail(status, ISK_ERR_INVALID_ARG, "batch must be >= 1");
+  if (lens_host == nullptr) return fail(status, ISK_ERR_INVALID_ARG, "lens_host is NULL");
+  const bool sparse = d.topk_width > 0;
+  if (sparse && topk_len_host == nullptr) return fail(status, ISK_ERR_INVALID_ARG, "topk_len_host is NULL for a sparse plan");
+  if (!sparse && topk_len_host != nullptr) return fail(status, ISK_ERR_INVALID_ARG, "topk_len_host must be NULL for a dense plan");
+
+  const long long cap = (long long)d.max_pages_per_row * d.page_size;
+  std::vector<int32_t> units(batch);
+  for (int b = 0; b < batch; ++b) {
+    const int32_t L = lens_host[b];
+    if (L < 0 || L > cap) {
+      std::ostringstream e;
+      e << "lens_host[" << b << "] = " << L << " is outside [0, max_pages_per_row * page_size = " << cap << "]";
+      return fail(status, ISK_ERR_INVALID_ARG, e.str());
+    }
+    units[b] = sparse ? std::min(std::max(topk_len_host[b], 0), d.topk_width) : L;
+  }
+
+  int32_t S = d.split_tokens;
+  if (S == 0) S = d.kind == ISK_KIND_GQA ? kGqaSplitDefault : (sparse ? kSparseSplitDefault : kMlaSplitDefault);
+
+  p.desc = d;
+  p.batch = batch;
+  p.split_units = S;
+  p.units = units;
+  p.segs.clear();
+  p.seg_group.clear();
+  p.groups.clear();
+  p.rows.assign(batch, RowInfo{0, 0});
+  p.n_partials = 0;
+
+  std::vector<std::vector<Seg>> row_segs(batch);
+  std::vector<int32_t> seg_part_of;   // group index per segment (balanced)
+
+  if (d.split_mode == ISK_SPLIT_PER_ROW) {
+    for (int b = 0; b < batch; ++b) {
+      const int32_t U = units[b];
+      const int32_t n = (U + S - 1) / S;
+      for (int32_t i = 0; i < n; ++i) row_segs[b].push_back(Seg{b, i * S, std::min((i + 1) * S, U), 0});
+    }
+  } else {
+    // Batch-wide quota: total blocks plus a fixed overhead charge per row,
+    // divided over the parts; each part takes up to `payload` blocks, paying
+    // the overhead for every row piece it starts.
+    const int blk = kBalancedBlock;
+    long long total = 0;
+    for (int b = 0; b < batch; ++b) total += (units[b] + blk - 1) / blk + kBalancedOverhead;
+    const long long payload = (total + kBalancedParts - 1) / kBalancedParts + kBalancedOverhead;
+    int part = 0;
+    long long used = 0;
+    for (int b = 0; b < batch; ++b) {
+      const long long blocks = (units[b] + blk - 1) / blk;
+      long long pos = 0;
+      while (pos < blocks) {
+        const long long avail = payload - used - kBalancedOverhead;
+        if (avail <= 0) { ++part; used = 0; continue; }
+        const long long take = std::min(avail, blocks - pos);
+        Seg s{b, (int32_t)(pos * blk), (int32_t)std::min<long long>((pos + take) * blk, units[b]), 0};
+        row_segs[b].push_back(s);
+        seg_part_of.push_back(part);
+        used += take + kBalancedOverhead;
+        pos += take;
+        if (used >= payload) { ++part; used = 0; }
+      }
+    }
+  }
+
+  // Partial slots: rows in batch order, a row's splits in order.
+  for (int b = 0; b < batch; ++b) {
+    const int32_t n = (int32_t)row_segs[b].size();
+    p.rows[b] = RowInfo{p.n_partials, n};
+    if (n > 1) {
+      for (int32_t i = 0; i < n; ++i) row_segs[b][i].part = p.n_partials + i;
+      p.n_partials += n;
+    } else if (n == 1) {
+      row_segs[b][0].part = -1;
+    }
+  }
+  p.any_combine = false;
+  for (int b = 0; b < batch; ++b) p.any_combine |= p.rows[b].n_parts != 1;
+
+  if (d.split_mode == ISK_SPLIT_PER_ROW) {
+    // One split per workgroup task, longest first (ties: batch order, split order).
+    for (int b = 0; b < batch; ++b)
+      for (const Seg& s : row_segs[b]) p.segs.push_back(s);
+    std::stable_sort(p.segs.begin(), p.segs.end(),
+                     [](const Seg& x, const Seg& y) { return (x.end - x.begin) > (y.end - y.begin); });
+    p.groups.resize(p.segs.size() + 1);
+    for (size_t i = 0; i <= p.segs.size(); ++i) p.groups[i] = (int32_t)i;
+    p.seg_group.resize(p.segs.size());
+    for (size_t i = 0; i < p.segs.size(); ++i) p.seg_group[i] = (int32_t)i;
+  } else {
+    // One part per workgroup task; a part's pieces run in row order.
+    size_t k = 0;
+    for (int b = 0; b < batch; ++b)
+      for (const Seg& s : row_segs[b]) { p.segs.push_back(s); p.seg_group.push_back(seg_part_of[k++]); }
+    // seg order is already grouped by part (parts increase monotonically).
+    const int n_groups = p.seg_group.empty() ? 0 : p.seg_group.back() + 1;
+    p.groups.assign(n_groups + 1, 0);
+    for (int32_t g : p.seg_group) p.groups[g + 1]++;
+    for (int g = 0; g < n_groups; ++g) p.groups[g + 1] += p.groups[g];
+  }
+  *status = ISK_OK;
+  return "";
+}
+
+}  // namespace isk

@@ -144,9 +144,8 @@ def mla_sparse_decode(q, latent_rows, lens, topk_idx, topk_len, scale: float, dv
     q = np.asarray(q, dtype=np.float64)
     outs, lses = [], []
     for b in range(q.shape[0]):
-        c = np.asarray(latent_rows[b], dtype=np.float64)
         pos = sparse_positions(topk_idx[b], int(topk_len[b]), int(lens[b]))
-        g = c[pos]
+        g = np.asarray(np.asarray(latent_rows[b])[pos], dtype=np.float64)
         o, l = attend(q[b], g, g[:, :dv], scale)
         outs.append(o)
         lses.append(l)

@@ -1,0 +1,165 @@
+"""Parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Every configuration of the decode workloads runs at full size and is compared
+element by element with the oracle; edge cases cover empty and one-token
+rows, ragged tails at tile and split boundaries, garbage in unused cache
+slots, sparse masking, other head counts and dims, and the input audit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_split_kv_amd as isk
+from workloads import synth
+from workloads.device import DeviceCase
+
+from gpu_util import parity, reference
+
+pytestmark = pytest.mark.gpu
+
+GARBAGE = int(synth.bf16_bits(np.array([3.0e4], np.float32))[0])   # finite, large
+
+
+def run_case(case, **kw):
+    print(f"[case] {type(case).__name__} B={case.batch} lens[:8]={list(case.lens[:8])} kw={kw}", flush=True)
+    dc = DeviceCase(case, **kw)
+    dc.run()
+    out, lse, bits, lbits = dc.result()
+    dc.close()
+    return out, lse, bits, lbits
+
+
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_config1_gqa_tiny(out_f32):
+    case = synth.config1_gqa_tiny()
+    out, lse, _, _ = run_case(case, out_f32=out_f32)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, out_f32, f"config1 out_f32={out_f32}")
+
+
+def test_config2_gqa_llama8b_shape():
+    case = synth.config2_gqa()
+    out, lse, _, _ = run_case(case)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, "config2")
+
+
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_config3_mla(out_f32):
+    case = synth.config3_mla()
+    out, lse, _, _ = run_case(case, out_f32=out_f32)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, out_f32, f"config3 out_f32={out_f32}")
+
+
+def test_config4_sparse_mla():
+    case = synth.config4_sparse()
+    out, lse, _, _ = run_case(case)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, "config4")
+
+
+@pytest.mark.parametrize("mode", [isk.SPLIT_PER_ROW, isk.SPLIT_BATCH_BALANCED])
+def test_balanced_mode_parity(mode):
+    case = synth.config3_mla(batch=16)
+    out, lse, _, _ = run_case(case, split_mode=mode)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, f"config3 B=16 mode={mode}")
+
+
+# ---------------------------------------------------------------- edge cases
+
+EDGE_LENS = [0, 1, 2, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 2100]
+
+
+@pytest.mark.parametrize("g,d", [(4, 128), (1, 64), (2, 128), (8, 64), (16, 128)])
+def test_gqa_edges_and_group_sizes(g, d):
+    hkv = 2
+    case = synth.gqa_case(EDGE_LENS, g * hkv, hkv, d, 1.0 / math.sqrt(d), 16, structure_seed=30 + g)
+    out, lse, _, _ = run_case(case, fill=GARBAGE)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, f"gqa edges g={g} d={d}")
+
+
+@pytest.mark.parametrize("hq", [128, 64, 16])
+def test_mla_edges_and_head_counts(hq):
+    case = synth.mla_case(EDGE_LENS, hq, 1.0 / math.sqrt(192.0), 64, structure_seed=40 + hq)
+    out, lse, _, _ = run_case(case, fill=GARBAGE)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, f"mla edges hq={hq}")
+
+
+def test_mla_page_size_128_and_custom_split():
+    case = synth.mla_case([3000, 129, 5000, 64], 128, 0.07, 128, structure_seed=50, split_tokens=256)
+    out, lse, _, _ = run_case(case)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, "mla P=128 S=256")
+
+
+def test_sparse_edges():
+    W = 700
+    lens = [3000, 5, 800, 2000, 1, 0, 4096]
+    case = synth.mla_case(lens, 128, 1.0 / math.sqrt(192.0), 64, structure_seed=60, topk_width=W)
+    rows = case.rows
+    rng = np.random.default_rng(61)
+    rows[0].topk_idx[[3, 10, 200]] = -1                  # -1 inside topk_len: skipped
+    rows[2].topk_idx[[0, 1]] = [900, 100000]             # >= len: skipped
+    rows[3].topk_idx[5] = rows[3].topk_idx[6]            # duplicate position counts twice
+    rows[3].gathered[5] = rows[3].gathered[6]
+    rows[6].topk_len = 513                               # shorter than the row's entries
+    rows[6].topk_idx[513:] = rng.integers(0, 4096, W - 513)
+    out, lse, _, _ = run_case(case, fill=GARBAGE)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, "sparse edges")
+    assert np.all(out[5] == 0) and np.all(np.isneginf(lse[5]))
+
+
+def test_all_masked_sparse_row_gives_zero_and_neg_inf():
+    case = synth.mla_case([100, 50], 64, 0.1, 64, structure_seed=62, topk_width=128)
+    case.rows[0].topk_idx[:] = -1
+    out, lse, _, _ = run_case(case)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, "sparse all-masked")
+
+
+def test_check_inputs_reports_bad_tables():
+    case = synth.mla_case([300, 200], 64, 0.1, 64, structure_seed=63, topk_width=64)
+    case.rows[1].topk_idx[3] = 250                       # >= len inside topk_len
+    dc = DeviceCase(case, check_inputs=True)
+    with pytest.raises(isk.IskError) as e:
+        dc.run()
+    assert e.value.status == -4 and "topk_idx[1][3]" in e.value.message
+    dc.close()
+    # A block-table entry outside the pool, set on the device copy only (the
+    # pool itself is staged from the valid table).
+    dense = synth.mla_case([300, 200], 64, 0.1, 64, structure_seed=64)
+    dc = DeviceCase(dense, check_inputs=True)
+    dc.block_table[0, 2] = dense.paging.num_pages + 5
+    with pytest.raises(isk.IskError) as e:
+        dc.run()
+    assert e.value.status == -4 and "block_table[0][2]" in e.value.message
+    dc.close()
+    good = DeviceCase(synth.mla_case([300, 200], 64, 0.1, 64, structure_seed=65), check_inputs=True)
+    good.run()
+    good.close()
+
+
+def test_out_of_pool_page_is_masked_not_read():
+    """Without the audit, a block-table entry outside the pool masks its
+    tokens instead of being dereferenced."""
+    case = synth.mla_case([300, 200], 64, 0.1, 64, structure_seed=66)
+    dc = DeviceCase(case)
+    dc.block_table[0, 1] = case.paging.num_pages + 1000   # tokens 64..127 of row 0
+    dc.run()
+    out, lse, _, _ = dc.result()
+    dc.close()
+    keep = np.r_[0:64, 128:300]
+    row0 = synth.bf16_value(case.rows[0].latent)[keep]
+    q = synth.bf16_value(case.q_bits())
+    import oracle
+    ro0, rl0 = oracle.mla_decode(q[:1], [row0], case.scale)
+    parity(out[:1], lse[:1], ro0, rl0, False, "masked page")

@@ -229,13 +229,22 @@ class MlaCase:
     def topk_len(self) -> np.ndarray:
         return np.array([r.topk_len for r in self.rows], dtype=np.int32)
 
+    def placed_slots(self, b: int) -> np.ndarray:
+        """Slots of sparse row b whose position is attended: below topk_len and
+        inside [0, len).  Their gathered rows are what the row's cache holds at
+        those positions."""
+        r = self.rows[b]
+        n = min(max(int(r.topk_len), 0), len(r.topk_idx), len(r.gathered))
+        idx = r.topk_idx[:n]
+        return np.nonzero((idx >= 0) & (idx < int(self.lens[b])))[0]
+
     def fill_pool(self, flat_pool: np.ndarray) -> None:
         """Write every row's content into a flat [num_pages * P, 576] uint16 pool."""
         for b, r in enumerate(self.rows):
             if self.sparse:
-                n = r.topk_len
-                if n:
-                    flat_pool[self.paging.token_slots(b, r.topk_idx[:n])] = r.gathered
+                j = self.placed_slots(b)
+                if len(j):
+                    flat_pool[self.paging.token_slots(b, r.topk_idx[j])] = r.gathered[j]
             else:
                 L = int(self.lens[b])
                 if L:
@@ -254,8 +263,9 @@ class MlaCase:
             if self.sparse:
                 L = int(self.lens[b])
                 arr = np.zeros((L, MLA_DQK), np.float32)
-                if r.topk_len:
-                    arr[r.topk_idx[: r.topk_len]] = bf16_value(r.gathered)
+                j = self.placed_slots(b)
+                if len(j):
+                    arr[r.topk_idx[j]] = bf16_value(r.gathered[j])
                 yield arr
             else:
                 yield bf16_value(r.latent)
