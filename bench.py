@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of batch-invariant split-KV decode attention on one MI355X.
+
+Workload: absorbed-MLA decode, B=64 rows, 128 query heads over one shared
+576-wide latent KV (512 + 64 rope), value width 512, scale 1/sqrt(192),
+bf16 values N(0, 0.5^2), KV lengths lognormal (median 4096, sigma 1) clipped
+to [64, 32768], 64-token pages with a seeded permuted block table.  Inputs
+are synthetic and resident in HBM before timing starts.
+
+One step = the whole hot path: host re-planning of the per-row splits, the
+split-list upload, the split kernel and the fixed-order combine.  The timed
+region is exactly `--steps` steps after `--warmup` untimed ones, bracketed by
+device synchronisation.  Prints one JSON line (see the design doc for the fields).
+"""
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mla_split_b64_hbm_traffic.txt")
+SPLIT_KERNEL_SRC = os.path.join(ROOT, "invariant_split_kv_amd", "csrc", "mla_split.hip")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    return hashlib.sha256(open(SPLIT_KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        fields = dict(l.split(":", 1) for l in open(TRAFFIC_SUMMARY) if ":" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
+
+def copy_calibration():
+    """A plain device copy of 1 GiB, three times (reference for the byte counters)."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}), flush=True)
+METRIC = "decode-attn KV GB/s + % HBM roofline (MLA B=64); row batch-invariance pass rate"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.rt.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.rt.hipEventSynchronize(b) == 0
+        assert self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.rt.hipEventDestroy(ev)
+
+
+def timed_steps(dc, isk, torch, evs, steps, warmup, lens_host):
+    """Warm up, then time exactly `steps` steps; per-step split/combine
+    kernel times come from events recorded by the library's timing hook."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        dc.plan.update(lens_host)
+        dc.run(stream)
+    torch.cuda.synchronize()
+    marks = [(evs.create(), evs.create(), evs.create()) for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        isk.plan_set_timing_events(dc.plan.handle, *marks[i])
+        dc.plan.update(lens_host)
+        dc.run(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    isk.plan_set_timing_events(dc.plan.handle, None, None, None)
+    total_ms = t_start.elapsed_time(t_end)
+    split = [evs.elapsed_ms(a, b) for a, b, _ in marks]
+    comb = [evs.elapsed_ms(b, c) for _, b, c in marks]
+    for m in marks:
+        for e in m:
+            evs.destroy(e)
+    return total_ms, wall, split, comb
+
+
+def cold_steps(dc, torch, n):
+    """Per-call time with L2 and the 256 MB Infinity Cache flushed first."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    times = []
+    stream = torch.cuda.current_stream()
+    for _ in range(n):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dc.run(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del flush
+    return times
+
+
+def invariance_pass_rate(case, out_bits, lse_bits, mode, synth, DeviceCase, rows):
+    """Rows re-run alone in a freshly permuted page pool with a fresh plan:
+    bit equality of out (bf16) and lse (fp32) with the batched run."""
+    ok = 0
+    for b in rows:
+        one = synth.mla_case([case.lens[b]], case.hq, case.scale, 64, structure_seed=5000 + int(b), seeds=[0])
+        one.rows = [case.rows[b]]
+        d1 = DeviceCase(one, split_mode=mode)
+        d1.run()
+        _, _, sb, sl = d1.result()
+        d1.close()
+        ok += int(sb[0].tobytes() == out_bits[b].tobytes() and sl[0].tobytes() == lse_bits[b].tobytes())
+    return ok
+
+
+def cpu_baseline(case, seconds):
+    """The fp64 oracle on the host cores over a bounded sample of rows."""
+    import numpy as np
+    import oracle
+    from workloads import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    q = synth.bf16_value(case.q_bits())
+    lat = [synth.bf16_value(r.latent) for r in case.rows]
+    done_tokens, rows, passes = 0, 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:   # whole passes over the batch, row by row
+        for b in range(case.batch):
+            oracle.mla_decode(q[b:b + 1], [lat[b]], case.scale)
+            done_tokens += int(case.lens[b])
+            rows += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        passes += 1
+    dt = time.perf_counter() - t0
+    gbs = done_tokens * synth.MLA_DQK * 2 / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} rows ({done_tokens} KV tokens; {passes} pass(es) over the 64-row batch) of the "
+                      f"same workload, fp64 numpy oracle, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed region (for profiler runs); no balanced/cold/invariance/CPU legs")
+    ap.add_argument("--mode", choices=["per_row", "balanced"], default="per_row",
+                    help="split rule of the timed region (the headline line uses per_row)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy three times (byte-counter calibration run)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import invariant_split_kv_amd as isk
+    from workloads import synth
+    from workloads.device import DeviceCase, io_bytes, kv_bytes
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    mode = isk.SPLIT_PER_ROW if args.mode == "per_row" else isk.SPLIT_BATCH_BALANCED
+
+    log("generating the B=64 MLA batch")
+    case = synth.config3_mla()
+    lens_host = np.asarray(case.lens, dtype=np.int32)
+    dc = DeviceCase(case, split_mode=mode)
+    info = dc.plan.info()
+    kvb = kv_bytes(case)
+    iob = io_bytes(case)
+    q_bytes = case.batch * case.hq * synth.MLA_DQK * 2
+    evs = HipEvents()
+
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps (mode {args.mode})")
+    total_ms, wall, split, comb = timed_steps(dc, isk, torch, evs, args.steps, args.warmup, lens_host)
+    ms_step = total_ms / args.steps
+    split_ms = float(np.mean(split))
+    comb_ms = float(np.mean(comb))
+    gbs = kvb / (ms_step * 1e-3) / 1e9
+    achieved = (kvb + q_bytes) / (split_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; no dataset)",
+        "config": {
+            "workload": "absorbed MLA decode B=64, Hq=128, latent 576 (512+64), Dv=512, scale 1/sqrt(192), "
+                        "lens lognormal(median 4096, sigma 1) clipped [64,32768], 64-token pages, permuted table",
+            "batch": case.batch, "kv_tokens": int(lens_host.sum()), "split_mode": args.mode,
+            "split_tokens": info["split_tokens"], "splits": info["num_segments"],
+            "partials": info["num_partials"], "workgroups": info["num_groups"] * 2,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(),
+            "kernel": "mla_split_kernel<dense>",
+            "algorithmic_bytes_per_launch": kvb + q_bytes,
+            "avg_launch_ms": round(split_ms, 5),
+        },
+        "kv_bytes_per_step": kvb,
+        "pct_hbm_roofline": round(100.0 * (kvb + iob) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(case.batch / (ms_step * 1e-3), 1),
+        "kv_tokens_per_s": round(float(lens_host.sum()) / (ms_step * 1e-3), 1),
+        "combine_ms": round(comb_ms, 5),
+        "mfma_tflops_split": round(float(lens_host.sum()) * case.hq * (576 + 512) * 2 / (split_ms * 1e-3) / 1e12, 1),
+        "wall_s_timed_region": round(wall, 4),
+        "numerics_id": isk.numerics_id(),
+    }
+
+    if not args.no_extras:
+        torch.cuda.synchronize()
+        _, _, bits, lbits = dc.result()
+        log("invariance: every row re-run alone vs batched")
+        ok = invariance_pass_rate(case, bits, lbits, mode, synth, DeviceCase, range(case.batch))
+        res["invariance"] = {"pass": ok, "total": case.batch, "rate": round(ok / case.batch, 4),
+                             "check": "out bf16 bits + lse fp32 bits, solo (fresh pages, fresh plan) vs batched"}
+        log("cold-cache calls (1 GiB flush before each)")
+        cold = cold_steps(dc, torch, 10)
+        res["cold_ms_per_call"] = round(float(np.median(cold)), 5)
+        res["cold_kv_gbs"] = round(kvb / (np.median(cold) * 1e-3) / 1e9, 2)
+        if mode == isk.SPLIT_PER_ROW:
+            log("batch-balanced comparison mode on the same batch")
+            dcb = DeviceCase(case, split_mode=isk.SPLIT_BATCH_BALANCED, pool=dc.pool)
+            tb, _, sb, _ = timed_steps(dcb, isk, torch, evs, args.steps, args.warmup, lens_host)
+            _, _, bb, bl = dcb.result()
+            okb = invariance_pass_rate(case, bb, bl, isk.SPLIT_BATCH_BALANCED, synth, DeviceCase,
+                                       range(0, case.batch, 4))
+            res["balanced"] = {"ms_per_step": round(tb / args.steps, 5), "split_ms": round(float(np.mean(sb)), 5),
+                               "per_row_over_balanced": round(ms_step / (tb / args.steps), 4),
+                               "invariance_pass": okb, "invariance_total": len(range(0, case.batch, 4))}
+            dcb.close()
+        if not args.no_cpu_baseline:
+            log(f"CPU baseline: fp64 oracle for ~{args.cpu_seconds:.0f} s")
+            res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    dc.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -79,11 +79,12 @@ typedef enum isk_out_dtype { ISK_OUT_BF16 = 0, ISK_OUT_F32 = 1 } isk_out_dtype;
 
 typedef struct isk_desc {
   int32_t kind;              /* isk_kind                                              */
-  int32_t num_q_heads;       /* Hq.  GQA: multiple of Hkv.  MLA: multiple of 16, <=128 */
+  int32_t num_q_heads;       /* Hq.  GQA: Hkv * {1,2,4,8,16}.  MLA: multiple of 16,
+                                and of 64 above 64                                    */
   int32_t num_kv_heads;      /* Hkv.  MLA: must be 1                                  */
   int32_t head_dim_qk;       /* GQA: 64 or 128.  MLA: 576                             */
   int32_t head_dim_v;        /* GQA: equal to head_dim_qk.  MLA: 512                  */
-  int32_t page_size;         /* tokens per KV page (GQA: multiple of 16, MLA: of 64)  */
+  int32_t page_size;         /* tokens per KV page (dense MLA: a multiple of 64)      */
   int32_t num_pages;         /* pages in the pool; block-table entries must be below  */
   int32_t max_pages_per_row; /* row stride of block_table                             */
   int32_t topk_width;        /* 0: dense.  >0 (MLA only): row stride of topk_idx      */
@@ -129,16 +130,16 @@ ISK_API int isk_plan_create(const isk_desc* desc, int32_t batch, const int32_t* 
 
 /*
  * isk_plan_update - re-plan an existing plan in place for new lengths (the
- * next decode step), keeping its descriptor.  Reuses the plan's buffers.
- * Waits (host side) for the plan's previous work-list upload to finish before
- * overwriting its pinned staging copy.  Same arguments and errors as create.
+ * next decode step), keeping its descriptor and its pinned staging buffers.
+ * Host only.  Same arguments and errors as isk_plan_create.  Decode calls
+ * already enqueued keep the split list they uploaded.
  */
 ISK_API int isk_plan_update(isk_plan* plan, int32_t batch, const int32_t* lens_host,
                     const int32_t* topk_len_host);
 
-/* isk_plan_destroy - free a plan (NULL is accepted).  Waits for the plan's
- * last work-list upload first.  The caller must not destroy a plan while
- * another thread uses it. */
+/* isk_plan_destroy - free a plan (NULL is accepted).  Waits until the plan's
+ * pending split-list uploads have executed, then frees its pinned staging
+ * memory.  The caller must not destroy a plan while another thread uses it. */
 ISK_API int isk_plan_destroy(isk_plan* plan);
 
 /* isk_plan_query - sizes of a plan.  Host only. */
@@ -194,6 +195,18 @@ ISK_API int isk_attn_decode(const isk_plan* plan, const void* q, const void* kv_
                     const int32_t* topk_idx, const int32_t* topk_len,
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * isk_plan_set_timing_events - profiling hook.  Subsequent isk_attn_decode
+ * calls with this plan record `split_begin` on the call's stream right before
+ * the split kernel is launched, `split_end` right after it, and
+ * `combine_end` after the combine kernel (or right after split_end when no
+ * row needs combining).  Each argument is a hipEvent_t passed as void*; NULL
+ * disables that record.  Meant for timing the kernels with
+ * hipEventElapsedTime; the caller owns the events and may swap them between
+ * calls.  Host only; never fails for a non-NULL plan.
+ */
+ISK_API int isk_plan_set_timing_events(isk_plan* plan, void* split_begin, void* split_end, void* combine_end);
 
 /* isk_last_error - message for the last failing call on this thread
  * ("" if none).  The pointer stays valid until the thread's next call. */

@@ -6,7 +6,7 @@ Argument marshalling only: every function here maps one-to-one onto an
 Device tensors may be given as torch tensors (their ``data_ptr()`` is passed)
 or as integer device addresses.  All computation runs in the HIP kernels of
 libisk.so; importing this package fails if the library has not been built
-(``python -m invariant_split_kv_amd.build``).
+(``python invariant_split_kv_amd/build.py``).
 """
 
 from __future__ import annotations
@@ -21,6 +21,7 @@ __all__ = [
     "IskError", "IskDesc", "IskPlanInfo", "KIND_GQA", "KIND_MLA", "SPLIT_PER_ROW",
     "SPLIT_BATCH_BALANCED", "OUT_BF16", "OUT_F32", "LIB_PATH", "lib", "plan_create",
     "plan_update", "plan_destroy", "plan_query", "plan_workspace_bytes", "plan_segments",
+    "plan_set_timing_events",
     "attn_decode", "last_error", "numerics_id", "Plan",
 ]
 
@@ -56,7 +57,7 @@ class IskPlanInfo(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m invariant_split_kv_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python invariant_split_kv_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     P, I32P = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
     sig = {
@@ -67,6 +68,7 @@ def _load() -> ctypes.CDLL:
         "isk_plan_workspace_bytes": (ctypes.c_size_t, [P]),
         "isk_plan_segments": (ctypes.c_int, [P, I32P, ctypes.c_int32]),
         "isk_attn_decode": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "isk_plan_set_timing_events": (ctypes.c_int, [P, P, P, P]),
         "isk_last_error": (ctypes.c_char_p, []),
         "isk_numerics_id": (ctypes.c_char_p, []),
     }
@@ -150,6 +152,12 @@ def plan_segments(plan: int) -> np.ndarray:
     if got < 0:
         _check(got)
     return rec[:n]
+
+
+def plan_set_timing_events(plan: int, split_begin=None, split_end=None, combine_end=None) -> None:
+    """Profiling hook: hipEvent_t handles (ints) recorded around the split
+    kernel and after the combine of later attn_decode calls; None disables."""
+    _check(lib.isk_plan_set_timing_events(plan, split_begin, split_end, combine_end))
 
 
 def attn_decode(plan: int, q, kv_pages, block_table, lens, topk_idx, topk_len, out, lse, workspace,

@@ -1,6 +1,7 @@
 """Build libisk.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Usage: python -m invariant_split_kv_amd.build   (or call build()).
+Usage: python invariant_split_kv_amd/build.py [-v]   (or call build()).
+Run it by path: importing the package loads the library it builds.
 Always recompiles; objects go to _build/ at the repository root.
 """
 import os

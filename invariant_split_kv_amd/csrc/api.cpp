@@ -44,6 +44,7 @@ struct isk_plan {
   size_t staging_bytes[kRing] = {};
   hipEvent_t staged[kRing] = {};
   int ring_next = 0;
+  hipEvent_t t_split_begin = nullptr, t_split_end = nullptr, t_combine_end = nullptr;   // profiling hook
 };
 
 namespace {
@@ -154,7 +155,7 @@ const char* isk_numerics_id(void) {
       << " gqa_tile=" << isk::kGqaTile << " mla_tile=" << isk::kMlaTile
       << " split_gqa=" << isk::kGqaSplitDefault << " split_mla=" << isk::kMlaSplitDefault
       << " split_topk=" << isk::kSparseSplitDefault
-      << " gqa=vdot2-bf16/fp32-pv mla=mfma16x16x32-bf16/p-bf16/rescale-thr8 combine=fixed-order-fp32"
+      << " gqa=vdot2-bf16/fp32-pv mla=mfma16x16x32-bf16/p-hi+lo-bf16/rescale-thr8 combine=fixed-order-fp32"
       << " balanced=blk" << isk::kBalancedBlock << "-parts" << isk::kBalancedParts << "-ovh" << isk::kBalancedOverhead;
     return s.str();
   }();
@@ -290,6 +291,10 @@ int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages,
   const int32_t n_groups = (int32_t)pd.groups.size() - 1;
   const float scale_log2 = d.scale * isk::kLog2eHost;
 
+  if (plan->t_split_begin != nullptr) {
+    e = hipEventRecord(plan->t_split_begin, stream);
+    if (e != hipSuccess) return hip_err(e, "hipEventRecord (timing)");
+  }
   if (d.kind == ISK_KIND_GQA) {
     isk::GqaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, segs, groups, part_o, part_lse,
                      out, lse, n_groups, d.num_q_heads, d.num_kv_heads, d.head_dim_qk, d.page_size, d.num_pages,
@@ -303,12 +308,28 @@ int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages,
     e = isk::launch_mla_split(a, stream);
     if (e != hipSuccess) return hip_err(e, "launching the MLA split kernel");
   }
+  if (plan->t_split_end != nullptr) {
+    e = hipEventRecord(plan->t_split_end, stream);
+    if (e != hipSuccess) return hip_err(e, "hipEventRecord (timing)");
+  }
   if (pd.any_combine) {
     isk::CombineLaunch c{rows, part_o, part_lse, out, lse, pd.batch, d.num_q_heads, d.head_dim_v,
                          d.out_dtype == ISK_OUT_F32};
     e = isk::launch_combine(c, stream);
     if (e != hipSuccess) return hip_err(e, "launching the combine kernel");
   }
+  if (plan->t_combine_end != nullptr) {
+    e = hipEventRecord(plan->t_combine_end, stream);
+    if (e != hipSuccess) return hip_err(e, "hipEventRecord (timing)");
+  }
+  return ISK_OK;
+}
+
+int isk_plan_set_timing_events(isk_plan* plan, void* split_begin, void* split_end, void* combine_end) {
+  if (plan == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
+  plan->t_split_begin = (hipEvent_t)split_begin;
+  plan->t_split_end = (hipEvent_t)split_end;
+  plan->t_combine_end = (hipEvent_t)combine_end;
   return ISK_OK;
 }
 

@@ -12,8 +12,11 @@
 //   * The tile's latent rows (576 bf16 = 72 pieces of 16 B each) are copied
 //     straight from HBM into LDS with 16-byte global->LDS loads, double
 //     buffered: tile t+1 streams in while tile t is computed.  Piece c of
-//     tile row t sits at LDS piece (t*72 + (c ^ (t & 7))), an XOR swizzle that
-//     spreads the 16 rows read by one MFMA operand over distinct banks.
+//     tile row t sits at LDS piece (t*72 + (c ^ h(t))) with the XOR key
+//     h(t) = 4*((t >> 1) & 1) + ((t >> 3) & 3): the 16 rows one MFMA operand
+//     read touches (8 rows apart, see qk_token) get 8 distinct keys per row
+//     parity, so a 16-lane phase of that read hits 16 distinct 16-byte bank
+//     groups.
 //     Masked rows (past the split end, sparse slots that are -1 or out of
 //     range, pages outside the pool) are written as zeros instead of loaded.
 //   * Each wave owns 16 query heads and keeps their query slice in
@@ -52,6 +55,30 @@ __device__ __forceinline__ int qk_token(int tau, int m) {
   return 32 * (tau >> 1) + 8 * (m >> 2) + 4 * (tau & 1) + (m & 3);
 }
 
+// XOR key of tile row t (< 8, so c ^ key stays inside c's aligned block of 8
+// pieces and inside the 72-piece row).
+__device__ __forceinline__ int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 3) & 3); }
+
+// Staging offsets of a four-wave workgroup: wave w issues the 18 wave-wide
+// loads i = w + 4j of a tile; lane l of load i fills LDS piece slot
+// p = 64*i + l, i.e. tile row t = p / 72, latent piece (p % 72) ^ swz(t).
+// These byte offsets within the tile's source rows do not change from tile to
+// tile, so they are computed once.
+struct StageOffsets {
+  int off[kTileInstr / 4];
+  int row[kTileInstr / 4];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < kTileInstr / 4; ++j) {
+      const int p = (wave + 4 * j) * 64 + lane;
+      const int t = p / kPieces;
+      const int c = (p - t * kPieces) ^ swz(t);
+      off[j] = t * kRowBytes + c * 16;
+      row[j] = t;
+    }
+  }
+};
+
 template <bool kSparse>
 struct Stager {
   const unsigned char* kv;      // pool base (bytes)
@@ -61,10 +88,9 @@ struct Stager {
 
   // Issue the loads of tile `it` into `buf`; returns the tile's row-valid mask.
   __device__ __forceinline__ uint64_t operator()(int it, ISK_LDS unsigned char* buf, int wave, int nw,
-                                                 int lane) const {
-    // Recompute the per-lane addresses at every call instead of letting them
-    // be hoisted out of the tile loop, where they would hold ~50 registers
-    // that the MFMA operands need.
+                                                 int lane, const StageOffsets& so) const {
+    // Partial tiles and the sparse path recompute their per-lane addresses
+    // here rather than keep them live across the tile loop.
     asm volatile("" : "+v"(lane));
     const int u0 = seg_begin + it * kMlaTile;
     uint64_t mask;
@@ -88,11 +114,17 @@ struct Stager {
       mask = !page_ok ? 0ull : (nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull));
       if (page_ok)
         dense_base = kv + ((size_t)pg * page_size + (u0 % page_size)) * (size_t)kRowBytes;
+      if (nw == 4 && mask == ~0ull) {
+        // Full tile of a four-wave workgroup: precomputed offsets, no checks.
+#pragma unroll
+        for (int j = 0; j < kTileInstr / 4; ++j) load_lds_16(dense_base + so.off[j], buf + (wave + 4 * j) * 1024);
+        return mask;
+      }
     }
     for (int i = wave; i < kTileInstr; i += nw) {
       const int p = i * 64 + lane;             // LDS piece slot written by this lane
       const int t = p / kPieces;               // tile row
-      const int c = (p - t * kPieces) ^ (t & 7);   // latent piece stored there
+      const int c = (p - t * kPieces) ^ swz(t);    // latent piece stored there
       ISK_LDS unsigned char* chunk = buf + i * 1024;
       const bool valid = (mask >> t) & 1ull;
       const unsigned char* src;
@@ -147,26 +179,37 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
   const int seg_first = a.groups[g], seg_last = a.groups[g + 1];
   const unsigned char* kv = (const unsigned char*)a.kv;
 
-  // Per-lane LDS byte offsets of the MFMA operand reads (see the loops below).
-  const int k_lane_off = kRowBytes * (8 * (i16 >> 2) + (i16 & 3)) + 16 * (g16 ^ (i16 & 3));
-  int v_lane_off[2];
+  // Per-lane LDS byte offsets of the MFMA operand reads.  With the XOR key
+  // swz(), each operand address splits into a per-lane part (below, one per
+  // parity of the k-step or per dim tile modulo 4) and a compile-time part.
+  //  K operand, M-tile tau, k-step kk, lane (a = i16>>2, b = i16&3, g = g16):
+  //    row 32*(tau>>1) + 4*(tau&1) + 8a + b, piece 4kk + g, key 4*(b>>1) + a.
+  //  V^T operand, k-step kap, read r, dim tile nt, lane (ts = i16>>2, q = i16&3):
+  //    row 32*kap + 4r + 8*g16 + ts, piece 2nt + (q>>1), byte 8*(q&1), key 4*(ts>>1) + g16.
+  int k_lane_off[2], v_lane_off[4];
   {
-    const int tsub = i16 >> 2, phalf = (i16 & 3) >> 1, inner = (i16 & 1) * 8;
+    const int a4 = i16 >> 2, b4 = i16 & 3;
 #pragma unroll
     for (int par = 0; par < 2; ++par)
-      v_lane_off[par] = kRowBytes * (8 * g16 + tsub) + 16 * (2 * (par ^ (tsub >> 1)) + (phalf ^ (tsub & 1))) + inner;
+      k_lane_off[par] = kRowBytes * (8 * a4 + b4) + 64 * (par ^ (b4 >> 1)) + 16 * (g16 ^ a4);
+    const int ts = i16 >> 2, q = i16 & 3;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      v_lane_off[m] = kRowBytes * (8 * g16 + ts) + 64 * (((m >> 1) & 1) ^ (ts >> 1)) + 32 * ((m & 1) ^ (g16 >> 1)) +
+                      16 * ((q >> 1) ^ (g16 & 1)) + 8 * (q & 1);
   }
+  StageOffsets so;
+  if (nw == 4) so.init(wave, lane);
 
-  // Compile-time part of the operand addresses (tile row/piece arithmetic
-  // folded with the swizzle; the per-lane parts are the offsets above).
+  // Compile-time part of the operand addresses.
   auto k_tile_off = [](int tau, int kk) {
-    return kRowBytes * (32 * (tau >> 1) + 4 * (tau & 1)) + 128 * (kk >> 1) + 64 * ((kk ^ tau) & 1);
+    return kRowBytes * (32 * (tau >> 1) + 4 * (tau & 1)) + 128 * (kk >> 1);
   };
   auto v_read = [&](const ISK_LDS unsigned char* T, int j, s16x4* dst) {
     const int kap = j / kDvTiles, nt = j % kDvTiles;
-    const ISK_LDS unsigned char* vb = T + v_lane_off[nt & 1];
-    dst[0] = lds_read_tr16(vb + kRowBytes * 32 * kap + 16 * (8 * (nt >> 2) + 4 * ((nt >> 1) & 1)));
-    dst[1] = lds_read_tr16(vb + kRowBytes * (32 * kap + 4) + 16 * (8 * (nt >> 2) + 4 * (((nt >> 1) & 1) ^ 1)));
+    const ISK_LDS unsigned char* vb = T + v_lane_off[nt & 3];
+    dst[0] = lds_read_tr16(vb + kRowBytes * 32 * kap + 128 * (nt >> 2));
+    dst[1] = lds_read_tr16(vb + kRowBytes * (32 * kap + 4) + 128 * (nt >> 2));
   };
 
   for (int si = seg_first; si < seg_last; ++si) {
@@ -201,14 +244,14 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
     }
 
     const int n_tiles = (sg.end - sg.begin + kMlaTile - 1) / kMlaTile;
-    uint64_t mask_next = n_tiles > 0 ? stage(0, lds, wave, nw, lane) : 0ull;
+    uint64_t mask_next = n_tiles > 0 ? stage(0, lds, wave, nw, lane, so) : 0ull;
 
     for (int it = 0; it < n_tiles; ++it) {
       wait_vmem_all();
       __syncthreads();   // tile `it` has landed; tile it-1's buffer is free
       const uint64_t mask = mask_next;
       ISK_LDS unsigned char* T = lds + (it & 1) * kTileBytes;
-      if (it + 1 < n_tiles) mask_next = stage(it + 1, lds + ((it + 1) & 1) * kTileBytes, wave, nw, lane);
+      if (it + 1 < n_tiles) mask_next = stage(it + 1, lds + ((it + 1) & 1) * kTileBytes, wave, nw, lane, so);
 
       // ---- S^T = K * Q^T for 64 tokens x 16 heads per half (4 M-tiles)
       // Operand A of M-tile tau, k-step kk: lane (i16, g16) reads piece
@@ -223,17 +266,16 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
         // Software pipeline: the 4 operand reads of step kk+1 are issued before
         // the MFMAs of step kk; the scheduling fences keep the compiler from
         // hoisting further reads (which would cost registers, not time).
-        const ISK_LDS unsigned char* kb = T + k_lane_off;
         bf16x8 kf[2][4];
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau) kf[0][tau] = *(const ISK_LDS bf16x8*)(kb + k_tile_off(tau, 0));
+        for (int tau = 0; tau < 4; ++tau) kf[0][tau] = *(const ISK_LDS bf16x8*)(T + k_lane_off[0] + k_tile_off(tau, 0));
 #pragma unroll
         for (int kk = 0; kk < kKSteps; ++kk) {
           const int cur = kk & 1;
           if (kk + 1 < kKSteps) {
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau)
-              kf[cur ^ 1][tau] = *(const ISK_LDS bf16x8*)(kb + k_tile_off(tau, kk + 1));
+              kf[cur ^ 1][tau] = *(const ISK_LDS bf16x8*)(T + k_lane_off[(kk + 1) & 1] + k_tile_off(tau, kk + 1));
           }
 #pragma unroll
           for (int tau = 0; tau < 4; ++tau) {
@@ -316,8 +358,7 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
 
       // ---- O^T += V^T * P^T; V^T operand via transposing LDS reads.
       // For k-step kap and dim tile nt, lane (i16, g16) addresses 4 dims of
-      // tile rows 32*kap + 8*g16 + (i16 >> 2) (+4 for the second read); the
-      // swizzled address is v_lane_off[nt & 1] plus a compile-time offset.
+      // tile rows 32*kap + 8*g16 + (i16 >> 2) (+4 for the second read).
       {
         // 64 steps (kap, nt); the two transposing reads of step j + kVDepth
         // are issued before the MFMAs of step j.
