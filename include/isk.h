@@ -93,7 +93,7 @@ typedef struct isk_desc {
                                 the kind's tile (GQA 64, MLA 64)                      */
   int32_t out_dtype;         /* isk_out_dtype                                         */
   int32_t check_inputs;      /* 1: copy tables to the host and validate them first    */
-  float scale;               /* score scale, applied in fp32 after the dot product    */
+  float scale;               /* score scale (finite, > 0), applied in fp32 after the dot product */
 } isk_desc;
 
 typedef struct isk_plan isk_plan;   /* opaque, host-owned */

@@ -5,6 +5,7 @@ Run it by path: importing the package loads the library it builds.
 Always recompiles; objects go to _build/ at the repository root.
 """
 import os
+import re
 import subprocess
 import sys
 
@@ -15,12 +16,46 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libisk.so")
 
-SOURCES = ["plan.cpp", "api.cpp", "gqa_split.hip", "mla_split.hip", "combine.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "gqa_split.hip", "mla_split.hip", "mla_split_h32.hip", "combine.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions stay disabled (the compiler would otherwise form
 # v_pk_* ops from scalar float code).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function", "-fvisibility=hidden"]
+
+
+# Extra flags per source.  mla_split_h32.hip keeps its output block in AGPRs
+# that only its inline asm touches, so the compiler must not place MFMA
+# results or VGPR spills in AGPRs there.
+EXTRA_FLAGS = {
+    "mla_split_h32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-spill-vgpr-to-agpr=0"],
+}
+
+# Sources whose inline asm owns registers the compiler must never touch: all
+# AGPRs (the output accumulator) and v240..v255 (the LDS operand ring).
+ASM_OWNED = ["mla_split_h32.hip"]
+
+
+def check_register_ownership(asm_text: str) -> list:
+    """Instructions outside inline-asm blocks that name an AGPR or one of
+    v240..v255 (must be none)."""
+    bad, in_asm = [], False
+    agpr = re.compile(r"(?<![\w.])a(\d+|\[)")
+    ring = re.compile(r"(?<![\w.])v(24\d|25[0-5])\b")
+    rng = re.compile(r"v\[(\d+):(\d+)\]")
+    for n, line in enumerate(asm_text.splitlines(), 1):
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif s.startswith(";;#ASMEND"):
+            in_asm = False
+        elif not in_asm and s and not s.startswith((";", ".")) and not s.endswith(":"):
+            parts = s.split(";")[0].split(None, 1)
+            if len(parts) == 2:
+                ops = parts[1]
+                if agpr.search(ops) or ring.search(ops) or any(int(m.group(2)) >= 240 for m in rng.finditer(ops)):
+                    bad.append((n, s))
+    return bad
 
 
 def _run(cmd, verbose):
@@ -42,7 +77,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
@@ -50,6 +85,14 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             _wait(procs.pop(0), verbose)
     while procs:
         _wait(procs.pop(0), verbose)
+    for src in ASM_OWNED:
+        asm = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".device.s")
+        _run([hipcc, *FLAGS, *EXTRA_FLAGS.get(src, []), "--cuda-device-only", "-S", os.path.join(CSRC, src),
+              "-o", asm], verbose)
+        with open(asm) as f:
+            bad = check_register_ownership(f.read())
+        if bad:
+            raise RuntimeError(f"{src}: compiler-generated code uses registers owned by inline asm: {bad[:5]}")
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

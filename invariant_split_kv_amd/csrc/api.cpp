@@ -152,10 +152,12 @@ const char* isk_numerics_id(void) {
   static const std::string id = [] {
     std::ostringstream s;
     s << "isk-1 arch=gfx950"
-      << " gqa_tile=" << isk::kGqaTile << " mla_tile=" << isk::kMlaTile
+      << " gqa_tile=" << isk::kGqaTile
       << " split_gqa=" << isk::kGqaSplitDefault << " split_mla=" << isk::kMlaSplitDefault
       << " split_topk=" << isk::kSparseSplitDefault
-      << " gqa=vdot2-bf16/fp32-pv mla=mfma16x16x32-bf16/p-hi+lo-bf16/rescale-thr8 combine=fixed-order-fp32"
+      << " gqa=vdot2-bf16/fp32-pv"
+      << " mla(hq%128=0)=mfma32x32x16-bf16/tile32/p-hi+lo-bf16/rescale-thr8"
+      << " mla(other)=mfma16x16x32-bf16/tile64/p-hi+lo-bf16/rescale-thr8 combine=fixed-order-fp32"
       << " balanced=blk" << isk::kBalancedBlock << "-parts" << isk::kBalancedParts << "-ovh" << isk::kBalancedOverhead;
     return s.str();
   }();
@@ -305,7 +307,8 @@ int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages,
     isk::MlaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, sparse ? topk_idx : nullptr,
                      segs, groups, part_o, part_lse, out, lse, n_groups, d.num_q_heads, d.page_size, d.num_pages,
                      d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2};
-    e = isk::launch_mla_split(a, stream);
+    // 128-head blocks (32 heads per wave) when the head count allows it.
+    e = d.num_q_heads % 128 == 0 ? isk::launch_mla_split_h32(a, stream) : isk::launch_mla_split(a, stream);
     if (e != hipSuccess) return hip_err(e, "launching the MLA split kernel");
   }
   if (plan->t_split_end != nullptr) {

@@ -45,10 +45,8 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
       lse_out = m + fast_log2(ssum) * kLn2;
       const float* op = a.part_o + ((size_t)ri.part_off * a.hq + h) * a.dv + DPL * lane;
       const size_t stride = (size_t)a.hq * a.dv;
-      for (int i = 0; i < ri.n_parts; ++i) {
-        const float w = fast_exp2((lse_p[(size_t)i * a.hq] - m) * kLog2e) * inv;
+      auto load = [&](int i, float (&v)[DPL]) {
         const float* src = op + (size_t)i * stride;
-        float v[DPL];
         if constexpr (DPL % 4 == 0) {
 #pragma unroll
           for (int j = 0; j < DPL; j += 4) {
@@ -61,8 +59,24 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
         } else {
           v[0] = src[0];
         }
+      };
+      auto accumulate = [&](int i, const float (&v)[DPL]) {
+        const float w = fast_exp2((lse_p[(size_t)i * a.hq] - m) * kLog2e) * inv;
 #pragma unroll
         for (int j = 0; j < DPL; ++j) o[j] = fmaf(w, v[j], o[j]);
+      };
+      // Four partials' loads in flight at a time; the accumulation order is
+      // still i = 0, 1, 2, ... for every split count.
+      int i = 0;
+      for (; i + 4 <= ri.n_parts; i += 4) {
+        float v0[DPL], v1[DPL], v2[DPL], v3[DPL];
+        load(i, v0); load(i + 1, v1); load(i + 2, v2); load(i + 3, v3);
+        accumulate(i, v0); accumulate(i + 1, v1); accumulate(i + 2, v2); accumulate(i + 3, v3);
+      }
+      for (; i < ri.n_parts; ++i) {
+        float v0[DPL];
+        load(i, v0);
+        accumulate(i, v0);
       }
     }
   }

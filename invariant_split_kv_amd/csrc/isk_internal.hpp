@@ -17,7 +17,7 @@ namespace isk {
 // split length, and tile boundaries inside a split are multiples of the tile,
 // so both are functions of the row's own length and these constants only.
 constexpr int kGqaTile = 64;          // tokens per GQA wave step
-constexpr int kMlaTile = 64;          // tokens per MLA LDS tile
+constexpr int kMlaTile = 64;          // tokens per LDS tile of the 16-head MLA kernel
 constexpr int kGqaSplitDefault = 512;
 constexpr int kMlaSplitDefault = 1024;
 constexpr int kSparseSplitDefault = 512;
@@ -87,7 +87,8 @@ struct MlaLaunch {
   int32_t n_groups, hq, page_size, num_pages, max_pages, topk_width, out_f32;
   float scale_log2;
 };
-hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s);
+hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s);        // 16 heads per wave
+hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s);    // 32 heads per wave, hq % 128 == 0
 
 struct CombineLaunch {
   const RowInfo* rows; const float* part_o; const float* part_lse;

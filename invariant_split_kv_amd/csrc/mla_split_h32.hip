@@ -1,0 +1,665 @@
+// Absorbed-MLA split kernel for gfx950 with 32 query heads per wave (used
+// when the head count is a multiple of 128; dense and sparse top-k).
+//
+// Same job as the 16-head kernel in mla_split.hip: the split stage of the
+// split-KV scheme on the FlashMLA issue page "Sparse MLA decode is not
+// batch-invariant ..." (section "Where it comes from"), with split boundaries
+// from the host planner that depend only on the row's own length.  This
+// layout makes every 16-byte LDS operand read feed 32 heads instead of 16,
+// which halves the LDS traffic per MFMA:
+//   * One workgroup = four waves (one per SIMD) = 128 heads of one split, so
+//     a KV tile is copied into LDS once per split.  Wave w owns heads
+//     [32w, 32w + 32) of its head block and keeps their whole 576-dim query
+//     slice in VGPRs (36 MFMA B operands).
+//   * 32-token tiles (72 pieces of 16 B per token) are copied HBM -> LDS by
+//     16-byte direct loads, four tiles in flight.  Piece c of tile row t sits
+//     at LDS piece t*72 + (c ^ key(t)), key(t) = 4*((t>>1)&1) + ((t>>2)&3):
+//     the 16 rows of one K operand read and the 4-row x 32-byte blocks of a
+//     transposing V read land on distinct LDS banks.  Masked rows (past the
+//     split end, invalid sparse slots, pages outside the pool) are copied
+//     from a 16-byte zero block, so every tile issues the same number of
+//     loads and the tile waits can count them.
+//   * S^T (32 tokens x 32 heads) = K * Q^T with v_mfma_f32_32x32x16_bf16,
+//     fp32 accumulation, one chain over the 36 k-steps.  Lane (n, h) ends up
+//     with the 16 scores of head n for tokens 8*(e>>2) + 4h + (e&3).
+//   * Online softmax in the log2 domain, p = 2^(s*scale*log2(e) - m) with
+//     one fused multiply-add per score, and a lazily moved reference max
+//     (the accumulator is rescaled only when a head's max outgrows the
+//     reference by more than 2^8); p = 2^(x - m) is split into bf16 hi and lo
+//     parts and both multiply V, so the weights keep ~16 significant bits; the
+//     normaliser sums the fp32 p.
+//   * O^T (512 dims x 32 heads) += V^T * P^T.  The output block of a wave is
+//     256 fp32 values per lane and lives in AGPRs a0..a255 for the whole
+//     split, written only by the inline-asm MFMAs below (dim tile dt in
+//     a[16*dt .. 16*dt+15]); the compiler's own code uses VGPRs only (the
+//     file is built with MFMA results in VGPRs and no VGPR spills to AGPRs).
+//     V^T comes from the LDS tile through ds_read_b64_tr_b16.  Both products
+//     read their LDS operands through a fixed register ring (v240..v255)
+//     written and read only by inline asm, with explicit lgkmcnt waits.
+// Every reduction order above is fixed by the segment's own token range, so
+// the bits of a segment's result do not depend on anything else in the batch.
+
+#include <utility>
+
+#include "device.hpp"
+#include "isk_internal.hpp"
+
+namespace isk {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Read-only view of the block table: loads through the constant address
+// space become scalar loads (counted by lgkmcnt, not by the vector-memory
+// counter that the tile waits count).
+typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+
+constexpr int kTok = 32;                                   // tokens per LDS tile
+constexpr int kBufs = 4;                                   // LDS tile buffers (tiles in flight)
+constexpr int kWaves = 4;
+constexpr int kHeadsPerBlock = 32 * kWaves;                // 128
+constexpr int kPieces = kMlaDqk / 8;                       // 72 pieces of 16 B per latent row
+constexpr int kRowBytes = kMlaDqk * 2;                     // 1152
+constexpr int kTileBytes = kTok * kRowBytes;               // 36864
+constexpr int kLoadsPerWave = kTok * kPieces / 64 / kWaves;   // 9 wave-wide 16-byte loads per tile
+constexpr int kKSteps = kMlaDqk / 16;                      // 36
+constexpr int kKDepth = 4;                                 // K operand reads in flight (k-steps)
+constexpr int kDvTiles = kMlaDv / 32;                      // 16
+constexpr int kPvSteps = 2 * kDvTiles;                     // (k-step, dim tile) pairs per tile
+constexpr int kVDepth = 4;                                 // V operand reads in flight (PV steps)
+constexpr float kRescaleThreshold = 8.0f;                  // log2 units
+
+static_assert(kLoadsPerWave * 64 * kWaves == kTok * kPieces, "tile must split evenly over the waves");
+static_assert(2 * (kVDepth - 2) <= 15 && kKDepth - 1 <= 15 && kVDepth % 2 == 0, "lgkmcnt field");
+
+__device__ __forceinline__ int key(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
+
+// Source of the zero rows (masked tokens).
+__device__ __attribute__((aligned(16))) uint32_t g_zero_piece[4];
+
+// ---------------------------------------------------------------------------
+// Output block in fixed AGPRs.  Only these asm statements touch AGPRs.
+
+// Clobber list naming all 256 AGPRs (makes the kernel allocate them).
+#define ISK_A10(p) "a" #p "0", "a" #p "1", "a" #p "2", "a" #p "3", "a" #p "4", \
+                   "a" #p "5", "a" #p "6", "a" #p "7", "a" #p "8", "a" #p "9"
+#define ISK_ALL_AGPRS                                                                               \
+  ISK_A10(), ISK_A10(1), ISK_A10(2), ISK_A10(3), ISK_A10(4), ISK_A10(5), ISK_A10(6), ISK_A10(7),   \
+      ISK_A10(8), ISK_A10(9), ISK_A10(10), ISK_A10(11), ISK_A10(12), ISK_A10(13), ISK_A10(14),      \
+      ISK_A10(15), ISK_A10(16), ISK_A10(17), ISK_A10(18), ISK_A10(19), ISK_A10(20), ISK_A10(21),    \
+      ISK_A10(22), ISK_A10(23), ISK_A10(24), "a250", "a251", "a252", "a253", "a254", "a255"
+
+template <int DT>
+__device__ __forceinline__ void acc_zero_tile() {
+  asm volatile(
+      "v_accvgpr_write_b32 a[%0*16+0], 0\n\tv_accvgpr_write_b32 a[%0*16+1], 0\n\t"
+      "v_accvgpr_write_b32 a[%0*16+2], 0\n\tv_accvgpr_write_b32 a[%0*16+3], 0\n\t"
+      "v_accvgpr_write_b32 a[%0*16+4], 0\n\tv_accvgpr_write_b32 a[%0*16+5], 0\n\t"
+      "v_accvgpr_write_b32 a[%0*16+6], 0\n\tv_accvgpr_write_b32 a[%0*16+7], 0\n\t"
+      "v_accvgpr_write_b32 a[%0*16+8], 0\n\tv_accvgpr_write_b32 a[%0*16+9], 0\n\t"
+      "v_accvgpr_write_b32 a[%0*16+10], 0\n\tv_accvgpr_write_b32 a[%0*16+11], 0\n\t"
+      "v_accvgpr_write_b32 a[%0*16+12], 0\n\tv_accvgpr_write_b32 a[%0*16+13], 0\n\t"
+      "v_accvgpr_write_b32 a[%0*16+14], 0\n\tv_accvgpr_write_b32 a[%0*16+15], 0" ::"n"(DT));
+}
+
+template <int... DT>
+__device__ __forceinline__ void acc_zero_all(std::integer_sequence<int, DT...>) {
+  (acc_zero_tile<DT>(), ...);
+}
+
+__device__ __forceinline__ void acc_zero() {
+  asm volatile("" ::: ISK_ALL_AGPRS);
+  acc_zero_all(std::make_integer_sequence<int, kDvTiles>{});
+  // vector-ALU write of an AGPR -> MFMA srcC read
+  asm volatile("s_nop 4");
+}
+
+// acc[d0] += V(slot s0) * p_hi + V(s0) * p_lo and acc[d1] += V(s1) * p_hi +
+// V(s1) * p_lo, interleaved so that no MFMA waits on the one just issued.
+// The V^T operands sit in the fixed operand ring (see below).  The leading
+// s_nop covers a vector-ALU write of p_hi / p_lo right before the MFMA read.
+template <int D0, int D1, int S0, int S1>
+__device__ __forceinline__ void pv_pair(const bf16x8& p_hi, const bf16x8& p_lo) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[%2*16:%2*16+15], v[240+%4*4:243+%4*4], %0, a[%2*16:%2*16+15]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[%3*16:%3*16+15], v[240+%5*4:243+%5*4], %0, a[%3*16:%3*16+15]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[%2*16:%2*16+15], v[240+%4*4:243+%4*4], %1, a[%2*16:%2*16+15]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[%3*16:%3*16+15], v[240+%5*4:243+%5*4], %1, a[%3*16:%3*16+15]" ::"v"(p_hi),
+      "v"(p_lo), "n"(D0), "n"(D1), "n"(S0), "n"(S1));
+}
+
+#define ISK_SCALE4(o)                                                                       \
+  "v_accvgpr_read_b32 %0, a[%5*16+" #o "+0]\n\tv_accvgpr_read_b32 %1, a[%5*16+" #o "+1]\n\t"  \
+  "v_accvgpr_read_b32 %2, a[%5*16+" #o "+2]\n\tv_accvgpr_read_b32 %3, a[%5*16+" #o "+3]\n\t"  \
+  "v_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\t" \
+  "v_accvgpr_write_b32 a[%5*16+" #o "+0], %0\n\tv_accvgpr_write_b32 a[%5*16+" #o "+1], %1\n\t" \
+  "v_accvgpr_write_b32 a[%5*16+" #o "+2], %2\n\tv_accvgpr_write_b32 a[%5*16+" #o "+3], %3\n\t"
+
+// acc[dt] *= alpha (per lane).
+template <int DT>
+__device__ __forceinline__ void acc_scale(float alpha) {
+  float t0, t1, t2, t3;
+  asm volatile(ISK_SCALE4(0) ISK_SCALE4(4) ISK_SCALE4(8) ISK_SCALE4(12)
+               : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+               : "v"(alpha), "n"(DT));
+}
+
+template <int... DT>
+__device__ __forceinline__ void acc_scale_all(float alpha, std::integer_sequence<int, DT...>) {
+  (acc_scale<DT>(alpha), ...);
+}
+
+// Wait states between the last MFMA write of the accumulator and a
+// vector-ALU access of it (a 32x32x16 result needs fewer than 20).
+__device__ __forceinline__ void acc_settle() {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15");
+}
+
+template <int DT>
+__device__ __forceinline__ void acc_read(float (&o)[16]) {
+  asm volatile(
+      "v_accvgpr_read_b32 %0, a[%16*16+0]\n\tv_accvgpr_read_b32 %1, a[%16*16+1]\n\t"
+      "v_accvgpr_read_b32 %2, a[%16*16+2]\n\tv_accvgpr_read_b32 %3, a[%16*16+3]\n\t"
+      "v_accvgpr_read_b32 %4, a[%16*16+4]\n\tv_accvgpr_read_b32 %5, a[%16*16+5]\n\t"
+      "v_accvgpr_read_b32 %6, a[%16*16+6]\n\tv_accvgpr_read_b32 %7, a[%16*16+7]\n\t"
+      "v_accvgpr_read_b32 %8, a[%16*16+8]\n\tv_accvgpr_read_b32 %9, a[%16*16+9]\n\t"
+      "v_accvgpr_read_b32 %10, a[%16*16+10]\n\tv_accvgpr_read_b32 %11, a[%16*16+11]\n\t"
+      "v_accvgpr_read_b32 %12, a[%16*16+12]\n\tv_accvgpr_read_b32 %13, a[%16*16+13]\n\t"
+      "v_accvgpr_read_b32 %14, a[%16*16+14]\n\tv_accvgpr_read_b32 %15, a[%16*16+15]"
+      : "=v"(o[0]), "=v"(o[1]), "=v"(o[2]), "=v"(o[3]), "=v"(o[4]), "=v"(o[5]), "=v"(o[6]), "=v"(o[7]),
+        "=v"(o[8]), "=v"(o[9]), "=v"(o[10]), "=v"(o[11]), "=v"(o[12]), "=v"(o[13]), "=v"(o[14]), "=v"(o[15])
+      : "n"(DT));
+}
+
+// ---------------------------------------------------------------------------
+// Operand ring.  LDS reads in flight land in v240..v255 (four 4-register
+// slots) and the MFMAs read them there by name: the compiler never sees these
+// registers (the kernel caps its own allocation at 240 VGPRs), so it can
+// neither copy an operand before its wait nor reuse the register while the
+// read is outstanding.  S^T uses slots 0..kKDepth-1, O^T all four; the two
+// phases do not overlap.
+#define ISK_RING_VGPRS "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", \
+                       "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
+
+__device__ __forceinline__ void ring_claim() { asm volatile("" ::: ISK_RING_VGPRS); }
+
+// LDS reads complete in order, so waiting until at most N are outstanding
+// waits for every read issued before the last N.
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+
+// V^T operand reads.  Step st = (k-step j, dim tile dt): lane (n, h) needs
+// dims 32*dt + n of tile rows 16j + 4h + {0..3} and 16j + 8 + 4h + {0..3}.
+// With the transposing read, lane (i16, gp, h) addresses 4 dims of one row:
+// row 16j + 8u + 4h + (i16 >> 2), dims 32*dt + 16*gp + 4*(i16 & 3); its
+// per-lane byte offset is vaddr[2*(dt&1) + u], the rest is the immediate.
+template <int ST>
+__device__ __forceinline__ void v_issue(const uint32_t (&vaddr)[4]) {
+  constexpr int j = ST / kDvTiles, dt = ST % kDvTiles, m = 2 * (dt & 1), slot = ST % kVDepth;
+  constexpr int off0 = kRowBytes * 16 * j + 128 * (dt >> 1);
+  constexpr int off1 = kRowBytes * (16 * j + 8) + 128 * (dt >> 1);
+  asm volatile("ds_read_b64_tr_b16 v[240+%2*4:241+%2*4], %0 offset:%3\n\t"
+               "ds_read_b64_tr_b16 v[242+%2*4:243+%2*4], %1 offset:%4" ::"v"(vaddr[m]),
+               "v"(vaddr[m + 1]), "n"(slot), "n"(off0), "n"(off1));
+}
+
+// PV steps ST and ST+1 (dim tiles dt, dt+1 of one k-step); `hook` runs
+// after the pair's MFMAs are issued (it places the next tile's loads in the
+// MFMA stream).
+template <int ST, typename Hook>
+__device__ __forceinline__ void pv_do2(const uint32_t (&vaddr)[4], const bf16x8 (&pb)[2], const bf16x8 (&pl)[2],
+                                       Hook& hook) {
+  static_assert(ST % 2 == 0, "steps are taken in pairs");
+  constexpr int j = ST / kDvTiles, dt = ST % kDvTiles;
+  // reads issued after step ST+1's two: those of the later steps in flight
+  wait_lgkm<2 * ((ST + kVDepth < kPvSteps ? ST + kVDepth : kPvSteps) - ST - 2)>();
+  pv_pair<dt, dt + 1, ST % kVDepth, (ST + 1) % kVDepth>(pb[j], pl[j]);
+  if constexpr (ST + kVDepth < kPvSteps) v_issue<ST + kVDepth>(vaddr);
+  if constexpr (ST + 1 + kVDepth < kPvSteps) v_issue<ST + 1 + kVDepth>(vaddr);
+  __builtin_amdgcn_sched_barrier(0);
+  hook(std::integral_constant<int, ST / 2>{});
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int... ST>
+__device__ __forceinline__ void pv_issue_first(const uint32_t (&vaddr)[4], std::integer_sequence<int, ST...>) {
+  (v_issue<ST>(vaddr), ...);
+}
+
+template <typename Hook, int... PI>
+__device__ __forceinline__ void pv_all(const uint32_t (&vaddr)[4], const bf16x8 (&pb)[2], const bf16x8 (&pl)[2],
+                                       Hook& hook, std::integer_sequence<int, PI...>) {
+  (pv_do2<2 * PI>(vaddr, pb, pl, hook), ...);
+}
+
+// K operand reads of S^T (k-step kk): lane (n, h) reads piece 2*kk + h of
+// tile row n, at kaddr[kk & 3] + 128*(kk >> 2).
+template <int KK>
+__device__ __forceinline__ void k_issue(const uint32_t (&kaddr)[4]) {
+  asm volatile("ds_read_b128 v[240+%1*4:243+%1*4], %0 offset:%2" ::"v"(kaddr[KK & 3]), "n"(KK % kKDepth),
+               "n"(128 * (KK >> 2)));
+}
+
+// s += K-slot * q[kk] (S^T in VGPRs, fp32).  The first step starts from 0;
+// the last one is followed by the wait states a vector-ALU read of its result
+// needs, inside the same asm so nothing can be scheduled in between.
+template <int KK>
+__device__ __forceinline__ void qk_do(const uint32_t (&kaddr)[4], const bf16x8 (&qr)[kKSteps], f32x16& s) {
+  wait_lgkm<(KK + kKDepth < kKSteps ? KK + kKDepth : kKSteps) - KK - 1>();
+  if constexpr (KK == 0) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, v[240+%2*4:243+%2*4], %1, 0"
+                 : "=&v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
+  } else if constexpr (KK + 1 < kKSteps) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, v[240+%2*4:243+%2*4], %1, %0"
+                 : "+v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
+  } else {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, v[240+%2*4:243+%2*4], %1, %0\n\t"
+                 "s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15"
+                 : "+v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
+  }
+  if constexpr (KK + kKDepth < kKSteps) k_issue<KK + kKDepth>(kaddr);
+}
+
+template <int... KK>
+__device__ __forceinline__ void qk_issue_first(const uint32_t (&kaddr)[4], std::integer_sequence<int, KK...>) {
+  (k_issue<KK>(kaddr), ...);
+}
+
+template <int... KK>
+__device__ __forceinline__ void qk_all(const uint32_t (&kaddr)[4], const bf16x8 (&qr)[kKSteps], f32x16& s,
+                                       std::integer_sequence<int, KK...>) {
+  (qk_do<KK>(kaddr, qr, s), ...);
+}
+
+// vmcnt(n) with expcnt and lgkmcnt left at their maxima (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---------------------------------------------------------------------------
+// Tile staging: wave w issues the 9 wave-wide loads i = w + 4*jj; lane l of
+// load i fills LDS piece slot p = 64*i + l, i.e. tile row t = p / 72 and
+// latent piece (p % 72) ^ key(t).  Every tile costs exactly kLoadsPerWave
+// vector-memory instructions per wave (after any index loads), whatever the
+// mask, so "tile it has landed" is a fixed vmcnt.
+
+// Scalar plan of a dense tile: first pool row of the tile and row-valid mask.
+struct DenseTile {
+  const unsigned char* base;
+  uint32_t mask;
+};
+
+template <bool kSparse>
+struct Stager {
+  const unsigned char* kv;
+  const int32_t* bt_row;
+  const int32_t* idx_row;
+  int page_size, num_pages, len, seg_end;
+
+  // Dense: tiles start at multiples of 32 and pages hold a multiple of 64
+  // tokens, so a tile is one contiguous run of rows inside one page.
+  __device__ __forceinline__ DenseTile plan(int u0) const {
+    const int nvalid = min(kTok, seg_end - u0);
+    const int pg = ((const_i32p)bt_row)[u0 / page_size];
+    const bool page_ok = pg >= 0 && pg < num_pages;
+    DenseTile t;
+    t.mask = !page_ok ? 0u : (nvalid >= kTok ? ~0u : ((1u << nvalid) - 1u));
+    t.base = kv + ((size_t)(page_ok ? pg : 0) * page_size + (u0 % page_size)) * (size_t)kRowBytes;
+    return t;
+  }
+
+  // One of the 9 loads of a full dense tile, for the MFMA stream: pool
+  // address = SGPR base + 32-bit lane offset, LDS address in M0 from SGPRs,
+  // so no vector-ALU work.  The compiler's own value of M0 is saved and
+  // restored (M0 is read when the load issues).  Counted by vmcnt like the
+  // other tile loads.
+  __device__ __forceinline__ void issue_one(const DenseTile& t, uint32_t lds_sgpr, int jj,
+                                            const uint32_t (&so)[kLoadsPerWave]) const {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(so[jj]), "s"(t.base), "s"(lds_sgpr + (uint32_t)(kWaves * jj * 1024))
+        : "memory");
+  }
+
+  // All 9 loads of a dense tile with masked rows read from the zero block.
+  __device__ __forceinline__ void issue_masked(const DenseTile& t, ISK_LDS unsigned char* buf, int wave, int lane,
+                                               const uint32_t (&so)[kLoadsPerWave]) const {
+    const unsigned char* zero = (const unsigned char*)g_zero_piece;
+    int l = lane;
+    asm volatile("" : "+v"(l));   // recomputed per call, not kept live across the tile loop
+#pragma unroll
+    for (int jj = 0; jj < kLoadsPerWave; ++jj) {
+      const int i = wave + kWaves * jj;
+      const int tr = (i * 64 + l) / kPieces;
+      const unsigned char* src = ((t.mask >> tr) & 1u) ? t.base + (size_t)so[jj] : zero;
+      load_lds_16(src, buf + i * 1024);
+    }
+  }
+
+  // All 9 loads of a sparse tile (slots u0 .. u0+31 of the top-k list).
+  __device__ __forceinline__ uint32_t issue_sparse(int u0, ISK_LDS unsigned char* buf, int wave, int lane) const {
+    const unsigned char* zero = (const unsigned char*)g_zero_piece;
+    const int slot = u0 + (lane & 31);
+    bool ok = lane < 32 && slot < seg_end;
+    const int pos = ok ? idx_row[slot] : -1;
+    ok = ok && pos >= 0 && pos < len;
+    const int pg = ok ? bt_row[pos / page_size] : 0;
+    ok = ok && pg >= 0 && pg < num_pages;
+    const uint32_t my_row = ok ? (uint32_t)pg * (uint32_t)page_size + (uint32_t)(pos % page_size) : 0u;
+    const uint32_t mask = (uint32_t)__ballot(ok);
+    int l = lane;
+    asm volatile("" : "+v"(l));
+#pragma unroll
+    for (int jj = 0; jj < kLoadsPerWave; ++jj) {
+      const int i = wave + kWaves * jj;
+      const int p = i * 64 + l;
+      const int t = p / kPieces;
+      const int c = (p - t * kPieces) ^ key(t);
+      const uint32_t r = (uint32_t)__shfl((int)my_row, t, 64);
+      const unsigned char* src = ((mask >> t) & 1u) ? kv + (size_t)r * kRowBytes + c * 16 : zero;
+      load_lds_16(src, buf + i * 1024);
+    }
+    return mask;
+  }
+
+  // Whole tile at once; returns the row-valid mask.
+  __device__ __forceinline__ uint32_t operator()(int u0, ISK_LDS unsigned char* buf, int wave, int lane,
+                                                 const uint32_t (&so)[kLoadsPerWave]) const {
+    if constexpr (kSparse) {
+      return issue_sparse(u0, buf, wave, lane);
+    } else {
+      const DenseTile t = plan(u0);
+      if (t.mask == ~0u) {
+#pragma unroll
+        for (int jj = 0; jj < kLoadsPerWave; ++jj)
+          load_lds_16(t.base + (size_t)so[jj], buf + (wave + kWaves * jj) * 1024);
+      } else {
+        issue_masked(t, buf, wave, lane, so);
+      }
+      return t.mask;
+    }
+  }
+};
+
+template <bool kSparse>
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(240)))
+mla_split_h32_kernel(MlaLaunch a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kBufs * kTileBytes];
+  ISK_LDS unsigned char* tiles = (ISK_LDS unsigned char*)lds_raw;
+  const uint32_t tiles_u32 = (uint32_t)(uintptr_t)tiles;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n32 = lane & 31, hh = lane >> 5, i16 = lane & 15, gp = (lane >> 4) & 1;
+  // block id -> (task, head block): head blocks of one task sit 8 ids apart
+  // (same XCD under round-robin dealing of workgroups to the 8 XCDs).
+  const int n_hb = a.hq / kHeadsPerBlock;
+  const int bid = blockIdx.x;
+  const int g = (bid / (8 * n_hb)) * 8 + (bid & 7);
+  const int hb = (bid >> 3) % n_hb;
+  if (g >= a.n_groups) return;
+  ring_claim();
+  const int head = hb * kHeadsPerBlock + wave * 32 + n32;
+  const int seg_first = a.groups[g], seg_last = a.groups[g + 1];
+
+  // Per-lane LDS byte offsets of the operand reads (compile-time parts at the use).
+  //  K (A operand of S^T), k-step kk: tile row n32, piece 2*kk + hh
+  //    -> k_lane[kk & 3] + 128*(kk >> 2).
+  //  V^T (A operand of O^T): v_lane[2*(dt&1) + u], see v_issue.
+  // For m = 0..3 both offsets differ only in address bits 5-6 (the row
+  // offsets are multiples of 128 and a tile buffer starts at a multiple of
+  // 1024), so only m = 0 is kept: offset[m] = offset[0] ^ (32*m).
+  uint32_t k_lane0, v_lane0;
+  {
+    const int kh = key(n32);
+    k_lane0 = kRowBytes * n32 + 16 * (hh ^ kh);
+    const int hp = (i16 & 3) >> 1;
+    v_lane0 = kRowBytes * (4 * hh + (i16 >> 2)) + 64 * (i16 >> 3) + 32 * gp + 16 * (hp ^ hh) + 8 * (i16 & 1);
+  }
+  // Source offsets (within the tile's rows) of this lane's full-tile loads.
+  uint32_t so[kLoadsPerWave];
+#pragma unroll
+  for (int jj = 0; jj < kLoadsPerWave; ++jj) {
+    const int p = (wave + kWaves * jj) * 64 + lane;
+    const int t = p / kPieces;
+    so[jj] = (uint32_t)(t * kRowBytes + ((p - t * kPieces) ^ key(t)) * 16);
+  }
+
+  for (int si = seg_first; si < seg_last; ++si) {
+    const Seg sg = a.segs[si];
+    const int b = sg.row;
+    const Stager<kSparse> stage{(const unsigned char*)a.kv, a.block_table + (size_t)b * a.max_pages,
+                                kSparse ? a.topk_idx + (size_t)b * a.topk_width : nullptr,
+                                a.page_size, a.num_pages, a.lens[b], sg.end};
+
+    // Every wave is done reading the previous segment's tiles.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+
+    // Query slice: lane (n32, hh) holds q[head][16*kk + 8*hh + 0..7].
+    bf16x8 qr[kKSteps];
+    {
+      const bf16x8* qrow = (const bf16x8*)(a.q + ((size_t)b * a.hq + head) * kMlaDqk + 8 * hh);
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) qr[kk] = qrow[2 * kk];
+    }
+    // Wait for the query here, before any tile load is issued: the compiler
+    // cannot prove inside the tile loop that these loads have landed and
+    // would otherwise wait for every outstanding load at each tile.
+    wait_vmcnt<0>();
+
+    float m_ref = -INFINITY, l_run = 0.f;
+    acc_zero();
+
+    const int n_tiles = (sg.end - sg.begin + kTok - 1) / kTok;
+    // Prologue: tiles 0..kBufs-2 in flight; masks kept in a register ring.
+    uint32_t mk0 = 0, mk1 = 0, mk2 = 0;
+    if (n_tiles > 0) mk0 = stage(sg.begin, tiles, wave, lane, so);
+    if (n_tiles > 1) mk1 = stage(sg.begin + kTok, tiles + kTileBytes, wave, lane, so);
+    if (n_tiles > 2) mk2 = stage(sg.begin + 2 * kTok, tiles + 2 * kTileBytes, wave, lane, so);
+
+    for (int it = 0; it < n_tiles; ++it) {
+      // Tile `it` has landed once at most the loads of the tiles issued after
+      // it are outstanding; then every wave has finished tile it-1, whose
+      // buffer the next load reuses.
+      const int ahead = n_tiles - 1 - it;
+      if (ahead >= 2)
+        wait_vmcnt<2 * kLoadsPerWave>();
+      else if (ahead == 1)
+        wait_vmcnt<kLoadsPerWave>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      const uint32_t mask = mk0;
+      mk0 = mk1;
+      mk1 = mk2;
+      // Loads of tile it+3 (into the buffer tile it-1 used): a full dense
+      // tile's 9 loads are spread over the PV MFMA stream below, other tiles
+      // are issued here.
+      ISK_LDS unsigned char* nbuf = tiles + ((it + 3) & 3) * kTileBytes;
+      DenseTile nt{nullptr, 0u};
+      bool defer = false;
+      if (it + 3 < n_tiles) {
+        const int u0n = sg.begin + (it + 3) * kTok;
+        if constexpr (kSparse) {
+          mk2 = stage.issue_sparse(u0n, nbuf, wave, lane);
+        } else {
+          nt = stage.plan(u0n);
+          mk2 = nt.mask;
+          defer = nt.mask == ~0u;
+          if (!defer) stage.issue_masked(nt, nbuf, wave, lane, so);
+        }
+      }
+      const int buf = it & 3;
+      
+      // ---- S^T = K * Q^T (32 tokens x 32 heads), one accumulation chain
+      f32x16 s;
+      {
+        uint32_t kaddr[4];
+        kaddr[0] = tiles_u32 + buf * kTileBytes + k_lane0;
+#pragma unroll
+        for (int m = 1; m < 4; ++m) kaddr[m] = kaddr[0] ^ (32u * m);
+        __builtin_amdgcn_sched_barrier(0);
+        qk_issue_first(kaddr, std::make_integer_sequence<int, kKDepth>{});
+        qk_all(kaddr, qr, s, std::make_integer_sequence<int, kKSteps>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- online softmax; lane holds head n32, tokens 8*(e>>2) + 4*hh + (e&3)
+      if (mask != ~0u) {   // partial or masked tile (wave-uniform test)
+        const uint32_t mh = mask >> (4 * hh);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          s[e] = __builtin_amdgcn_ubfe(mh, 8 * (e >> 2) + (e & 3), 1) ? s[e] : -INFINITY;
+      }
+      // Max over the raw scores, then scaled: with scale > 0 (checked by the
+      // planner) this equals the max of the scaled scores, rounding included.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+      }
+      const float m_old = m_ref;
+      const bool move = mx > m_old + kRescaleThreshold || (m_old == -INFINITY && mx > -INFINITY);
+      const float m_new = move ? mx : m_old;
+      const float alpha = move ? fast_exp2(m_old - m_new) : 1.0f;   // m_old = -inf -> 0
+      const bool rescale = move && m_old != -INFINITY;             // acc is still 0 before the first move
+      m_ref = m_new;
+      const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+
+      bf16x8 pb[2], pl[2];
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[8 * j + 2 * q], a.scale_log2, -m_sub));
+          const float p1 = fast_exp2(__builtin_fmaf(s[8 * j + 2 * q + 1], a.scale_log2, -m_sub));
+          const bf16x2 hi = to_bf16x2(p0, p1);
+          const bf16x2 lo = to_bf16x2(p0 - (float)hi[0], p1 - (float)hi[1]);
+          pb[j][2 * q] = hi[0];
+          pb[j][2 * q + 1] = hi[1];
+          pl[j][2 * q] = lo[0];
+          pl[j][2 * q + 1] = lo[1];
+          psum += p0;
+          psum += p1;
+        }
+      }
+      l_run = l_run * alpha + psum;
+      if (__ballot(rescale) != 0ull) {
+        // Lanes that did not move have alpha == 1 exactly.
+        acc_settle();
+        acc_scale_all(alpha, std::make_integer_sequence<int, kDvTiles>{});
+        asm volatile("s_nop 4");
+      }
+
+      // ---- O^T += V^T * P^T over 2 k-steps x 16 dim tiles
+      uint32_t vaddr[4];
+      vaddr[0] = tiles_u32 + buf * kTileBytes + v_lane0;
+#pragma unroll
+      for (int m = 1; m < 4; ++m) vaddr[m] = vaddr[0] ^ (32u * m);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_issue_first(vaddr, std::make_integer_sequence<int, kVDepth>{});
+      if (defer) {
+        // LDS address of this wave's first load of tile it+3 (wave-uniform).
+        const uint32_t lds_sgpr = __builtin_amdgcn_readfirstlane(tiles_u32 + ((it + 3) & 3) * kTileBytes + wave * 1024);
+        auto dma = [&](auto pair) {
+          constexpr int jj = decltype(pair)::value;
+          if constexpr (jj < kLoadsPerWave) stage.issue_one(nt, lds_sgpr, jj, so);
+        };
+        pv_all(vaddr, pb, pl, dma, std::make_integer_sequence<int, kPvSteps / 2>{});
+      } else {
+        auto none = [](auto) {};
+        pv_all(vaddr, pb, pl, none, std::make_integer_sequence<int, kPvSteps / 2>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- epilogue: o = acc / l, lse = ln 2 * (m_ref + log2 l)
+    acc_settle();
+    float l_tot;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+      l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float lse_v = empty ? -INFINITY : (m_ref + fast_log2(l_tot)) * kLn2;
+    // lane holds O^T[32*dt + 8*q + 4*hh + e][head], e = 0..3, at acc[dt][4q + e]
+    float* of32 = nullptr;
+    uint16_t* obf = nullptr;
+    if (sg.part >= 0) {
+      of32 = a.part_o + ((size_t)sg.part * a.hq + head) * kMlaDv + 4 * hh;
+      if (hh == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
+    } else {
+      const size_t ob = ((size_t)b * a.hq + head) * kMlaDv + 4 * hh;
+      if (a.out_f32)
+        of32 = (float*)a.out + ob;
+      else
+        obf = (uint16_t*)a.out + ob;
+      if (a.lse != nullptr && hh == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
+    }
+    auto store_tile = [&](int dt, const float (&o)[16]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 r = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]} * inv;
+        if (of32 != nullptr) {
+          *(f32x4*)(of32 + 32 * dt + 8 * q) = r;
+        } else {
+          uint2 w;
+          w.x = pack_bf16x2(r[0], r[1]);
+          w.y = pack_bf16x2(r[2], r[3]);
+          *(uint2*)(obf + 32 * dt + 8 * q) = w;
+        }
+      }
+    };
+    {
+      float o[16];
+      acc_read<0>(o); store_tile(0, o);
+      acc_read<1>(o); store_tile(1, o);
+      acc_read<2>(o); store_tile(2, o);
+      acc_read<3>(o); store_tile(3, o);
+      acc_read<4>(o); store_tile(4, o);
+      acc_read<5>(o); store_tile(5, o);
+      acc_read<6>(o); store_tile(6, o);
+      acc_read<7>(o); store_tile(7, o);
+      acc_read<8>(o); store_tile(8, o);
+      acc_read<9>(o); store_tile(9, o);
+      acc_read<10>(o); store_tile(10, o);
+      acc_read<11>(o); store_tile(11, o);
+      acc_read<12>(o); store_tile(12, o);
+      acc_read<13>(o); store_tile(13, o);
+      acc_read<14>(o); store_tile(14, o);
+      acc_read<15>(o); store_tile(15, o);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s) {
+  if (a.n_groups == 0) return hipSuccess;
+  if (a.hq % kHeadsPerBlock != 0) return hipErrorInvalidValue;
+  const int n_hb = a.hq / kHeadsPerBlock;
+  const int n_blocks = ((a.n_groups + 7) / 8) * 8 * n_hb;
+  const dim3 grid(n_blocks), block(64 * kWaves);
+  if (a.topk_idx != nullptr)
+    hipLaunchKernelGGL(mla_split_h32_kernel<true>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(mla_split_h32_kernel<false>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace isk

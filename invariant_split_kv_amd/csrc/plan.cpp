@@ -58,7 +58,8 @@ static std::string check_desc(const isk_desc& d, int* status) {
     return fail(status, ISK_ERR_INVALID_ARG, "desc.out_dtype is not a valid isk_out_dtype");
   if (d.split_tokens < 0 || d.split_tokens % 64 != 0)
     return fail(status, ISK_ERR_INVALID_ARG, "desc.split_tokens must be 0 or a positive multiple of 64");
-  if (!std::isfinite(d.scale)) return fail(status, ISK_ERR_INVALID_ARG, "desc.scale must be finite");
+  if (!std::isfinite(d.scale) || !(d.scale > 0.f))
+    return fail(status, ISK_ERR_INVALID_ARG, "desc.scale must be finite and positive");
   if (d.topk_width < 0) return fail(status, ISK_ERR_INVALID_ARG, "desc.topk_width must be >= 0");
   if (d.kind == ISK_KIND_GQA) {
     if (d.num_q_heads % d.num_kv_heads != 0) return fail(status, ISK_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");

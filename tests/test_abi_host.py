@@ -62,6 +62,8 @@ def test_invalid_arguments_are_rejected_with_status_and_message():
         (mla_desc(page_size=16), [5], -2, "page_size"),
         (gqa_desc(topk_width=16), [5], -2, "MLA only"),
         (gqa_desc(scale=float("nan")), [5], -1, "finite"),
+        (gqa_desc(scale=0.0), [5], -1, "positive"),
+        (gqa_desc(scale=-0.1), [5], -1, "positive"),
     ]
     for desc, lens, status, text in cases:
         with pytest.raises(isk.IskError) as e:
