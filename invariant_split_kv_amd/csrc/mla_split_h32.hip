@@ -65,11 +65,10 @@ constexpr int kKSteps = kMlaDqk / 16;                      // 36
 constexpr int kKDepth = 4;                                 // K operand reads in flight (k-steps)
 constexpr int kDvTiles = kMlaDv / 32;                      // 16
 constexpr int kPvSteps = 2 * kDvTiles;                     // (k-step, dim tile) pairs per tile
-constexpr int kVDepth = 4;                                 // V operand reads in flight (PV steps)
 constexpr float kRescaleThreshold = 8.0f;                  // log2 units
 
 static_assert(kLoadsPerWave * 64 * kWaves == kTok * kPieces, "tile must split evenly over the waves");
-static_assert(2 * (kVDepth - 2) <= 15 && kKDepth - 1 <= 15 && kVDepth % 2 == 0, "lgkmcnt field");
+static_assert(kKDepth - 1 <= 15 && kKDepth <= 6, "lgkmcnt field / ring slots");
 
 __device__ __forceinline__ int key(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
 
@@ -111,21 +110,6 @@ __device__ __forceinline__ void acc_zero() {
   acc_zero_all(std::make_integer_sequence<int, kDvTiles>{});
   // vector-ALU write of an AGPR -> MFMA srcC read
   asm volatile("s_nop 4");
-}
-
-// acc[d0] += V(slot s0) * p_hi + V(s0) * p_lo and acc[d1] += V(s1) * p_hi +
-// V(s1) * p_lo, interleaved so that no MFMA waits on the one just issued.
-// The V^T operands sit in the fixed operand ring (see below).  The leading
-// s_nop covers a vector-ALU write of p_hi / p_lo right before the MFMA read.
-template <int D0, int D1, int S0, int S1>
-__device__ __forceinline__ void pv_pair(const bf16x8& p_hi, const bf16x8& p_lo) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 a[%2*16:%2*16+15], v[240+%4*4:243+%4*4], %0, a[%2*16:%2*16+15]\n\t"
-      "v_mfma_f32_32x32x16_bf16 a[%3*16:%3*16+15], v[240+%5*4:243+%5*4], %0, a[%3*16:%3*16+15]\n\t"
-      "v_mfma_f32_32x32x16_bf16 a[%2*16:%2*16+15], v[240+%4*4:243+%4*4], %1, a[%2*16:%2*16+15]\n\t"
-      "v_mfma_f32_32x32x16_bf16 a[%3*16:%3*16+15], v[240+%5*4:243+%5*4], %1, a[%3*16:%3*16+15]" ::"v"(p_hi),
-      "v"(p_lo), "n"(D0), "n"(D1), "n"(S0), "n"(S1));
 }
 
 #define ISK_SCALE4(o)                                                                       \
@@ -172,14 +156,16 @@ __device__ __forceinline__ void acc_read(float (&o)[16]) {
 }
 
 // ---------------------------------------------------------------------------
-// Operand ring.  LDS reads in flight land in v240..v255 (four 4-register
-// slots) and the MFMAs read them there by name: the compiler never sees these
-// registers (the kernel caps its own allocation at 240 VGPRs), so it can
-// neither copy an operand before its wait nor reuse the register while the
-// read is outstanding.  S^T uses slots 0..kKDepth-1, O^T all four; the two
-// phases do not overlap.
-#define ISK_RING_VGPRS "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", \
+// Operand ring.  LDS reads in flight land in v232..v255 (six 4-register
+// slots; slot i = v[232+4i .. 235+4i]) and the MFMAs read them there by name:
+// the compiler never sees these registers (the kernel caps its own
+// allocation at 232 VGPRs), so it can neither copy an operand before its wait
+// nor reuse the register while the read is outstanding.  S^T uses slots
+// 0..kKDepth-1, O^T all six; the two phases do not overlap.
+#define ISK_RING_VGPRS "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", \
+                       "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", \
                        "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
+constexpr int kRingSlots = 6;
 
 __device__ __forceinline__ void ring_claim() { asm volatile("" ::: ISK_RING_VGPRS); }
 
@@ -196,32 +182,95 @@ __device__ __forceinline__ void wait_lgkm() {
 // With the transposing read, lane (i16, gp, h) addresses 4 dims of one row:
 // row 16j + 8u + 4h + (i16 >> 2), dims 32*dt + 16*gp + 4*(i16 & 3); its
 // per-lane byte offset is vaddr[2*(dt&1) + u], the rest is the immediate.
+// Step st goes to ring slot st % 6; the reads of step st are issued while the
+// MFMAs of step st-4 run.
+template <int ST>
+struct VStep {
+  static constexpr int j = ST / kDvTiles, dt = ST % kDvTiles, slot = ST % kRingSlots;
+  static constexpr int off0 = kRowBytes * 16 * j + 128 * (dt >> 1);
+  static constexpr int off1 = kRowBytes * (16 * j + 8) + 128 * (dt >> 1);
+};
+
 template <int ST>
 __device__ __forceinline__ void v_issue(const uint32_t (&vaddr)[4]) {
-  constexpr int j = ST / kDvTiles, dt = ST % kDvTiles, m = 2 * (dt & 1), slot = ST % kVDepth;
-  constexpr int off0 = kRowBytes * 16 * j + 128 * (dt >> 1);
-  constexpr int off1 = kRowBytes * (16 * j + 8) + 128 * (dt >> 1);
-  asm volatile("ds_read_b64_tr_b16 v[240+%2*4:241+%2*4], %0 offset:%3\n\t"
-               "ds_read_b64_tr_b16 v[242+%2*4:243+%2*4], %1 offset:%4" ::"v"(vaddr[m]),
-               "v"(vaddr[m + 1]), "n"(slot), "n"(off0), "n"(off1));
+  using V = VStep<ST>;
+  constexpr int m = 2 * (V::dt & 1);
+  asm volatile("ds_read_b64_tr_b16 v[232+%2*4:233+%2*4], %0 offset:%3\n\t"
+               "ds_read_b64_tr_b16 v[234+%2*4:235+%2*4], %1 offset:%4" ::"v"(vaddr[m]),
+               "v"(vaddr[m + 1]), "n"(V::slot), "n"(V::off0), "n"(V::off1));
 }
 
-// PV steps ST and ST+1 (dim tiles dt, dt+1 of one k-step); `hook` runs
-// after the pair's MFMAs are issued (it places the next tile's loads in the
-// MFMA stream).
-template <int ST, typename Hook>
+// One PV step pair (steps ST, ST+1 = dim tiles dt, dt+1 of one k-step):
+//   acc[dt]   += V(ST)   * p_hi + V(ST)   * p_lo
+//   acc[dt+1] += V(ST+1) * p_hi + V(ST+1) * p_lo
+// as four MFMAs, hi and lo of one accumulator never back to back.  Between
+// them go the V^T reads of steps ST+4 and ST+5 (slots ST+4, ST+5 mod 6,
+// free since the previous pair) and, optionally, one 16-byte global->LDS load
+// of the next tile (pool offset `doff` from SGPR base `dbase`, LDS address
+// `dm0` in M0; the compiler's M0 is saved and restored, M0 being read when
+// the load issues).  Each MFMA thus shadows a few cheap issues instead of
+// all of them landing behind the last one.  The leading s_nop covers a
+// vector-ALU write of p_hi / p_lo right before the first MFMA.
+#define ISK_PV_MFMA(acc, slot, p) \
+  "v_mfma_f32_32x32x16_bf16 a[" acc "*16:" acc "*16+15], v[232+" slot "*4:235+" slot "*4], " p ", a[" acc "*16:" acc "*16+15]\n\t"
+#define ISK_PV_READS(slot, va, vb, oa, ob)                                    \
+  "ds_read_b64_tr_b16 v[232+" slot "*4:233+" slot "*4], " va " offset:" oa "\n\t" \
+  "ds_read_b64_tr_b16 v[234+" slot "*4:235+" slot "*4], " vb " offset:" ob "\n\t"
+#define ISK_PV_DMA "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %19\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %17, %18\n\ts_mov_b32 m0, %0\n\t"
+
+template <int ST, bool kReads, bool kDma>
+__device__ __forceinline__ void pv_pair(const bf16x8& p_hi, const bf16x8& p_lo, const uint32_t (&va)[4],
+                                        uint32_t doff, const unsigned char* dbase, uint32_t dm0) {
+  using A = VStep<ST>;
+  using B = VStep<ST + 1>;
+  using RA = VStep<(ST + 4 < kPvSteps ? ST + 4 : 0)>;
+  using RB = VStep<(ST + 5 < kPvSteps ? ST + 5 : 0)>;
+  uint32_t saved;
+#define ISK_PV_OPERANDS                                                                                   \
+  : "=&s"(saved)                                                                                          \
+  : "v"(p_hi), "v"(p_lo), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "n"(A::dt), "n"(B::dt),         \
+    "n"(A::slot), "n"(B::slot), "n"(RA::slot), "n"(RB::slot), "n"(RA::off0), "n"(RA::off1), "n"(RB::off0), \
+    "n"(RB::off1), "v"(doff), "s"(dbase), "s"(dm0)
+  if constexpr (kReads && kDma) {
+    asm volatile("s_nop 1\n\t" ISK_PV_MFMA("%7", "%9", "%1") ISK_PV_READS("%11", "%3", "%4", "%13", "%14")
+                 ISK_PV_MFMA("%8", "%10", "%1") ISK_PV_READS("%12", "%5", "%6", "%15", "%16")
+                 ISK_PV_MFMA("%7", "%9", "%2") ISK_PV_DMA ISK_PV_MFMA("%8", "%10", "%2") ISK_PV_OPERANDS);
+  } else if constexpr (kReads) {
+    asm volatile("s_nop 1\n\t" ISK_PV_MFMA("%7", "%9", "%1") ISK_PV_READS("%11", "%3", "%4", "%13", "%14")
+                 ISK_PV_MFMA("%8", "%10", "%1") ISK_PV_READS("%12", "%5", "%6", "%15", "%16")
+                 ISK_PV_MFMA("%7", "%9", "%2") ISK_PV_MFMA("%8", "%10", "%2") ISK_PV_OPERANDS);
+  } else if constexpr (kDma) {
+    asm volatile("s_nop 1\n\t" ISK_PV_MFMA("%7", "%9", "%1") ISK_PV_MFMA("%8", "%10", "%1")
+                 ISK_PV_MFMA("%7", "%9", "%2") ISK_PV_DMA ISK_PV_MFMA("%8", "%10", "%2") ISK_PV_OPERANDS);
+  } else {
+    asm volatile("s_nop 1\n\t" ISK_PV_MFMA("%7", "%9", "%1") ISK_PV_MFMA("%8", "%10", "%1")
+                 ISK_PV_MFMA("%7", "%9", "%2") ISK_PV_MFMA("%8", "%10", "%2") ISK_PV_OPERANDS);
+  }
+#undef ISK_PV_OPERANDS
+}
+
+// Next-tile loads placed in the PV stream (pairs 0..8, one load each) when
+// the next tile is a full dense tile.
+struct PvDma {
+  const unsigned char* base;
+  uint32_t m0;          // LDS address of this wave's load 0
+  uint32_t p16, keys;   // LoadOffsets fields
+};
+
+template <int PI, bool kDmaOn>
 __device__ __forceinline__ void pv_do2(const uint32_t (&vaddr)[4], const bf16x8 (&pb)[2], const bf16x8 (&pl)[2],
-                                       Hook& hook) {
-  static_assert(ST % 2 == 0, "steps are taken in pairs");
-  constexpr int j = ST / kDvTiles, dt = ST % kDvTiles;
-  // reads issued after step ST+1's two: those of the later steps in flight
-  wait_lgkm<2 * ((ST + kVDepth < kPvSteps ? ST + kVDepth : kPvSteps) - ST - 2)>();
-  pv_pair<dt, dt + 1, ST % kVDepth, (ST + 1) % kVDepth>(pb[j], pl[j]);
-  if constexpr (ST + kVDepth < kPvSteps) v_issue<ST + kVDepth>(vaddr);
-  if constexpr (ST + 1 + kVDepth < kPvSteps) v_issue<ST + 1 + kVDepth>(vaddr);
-  __builtin_amdgcn_sched_barrier(0);
-  hook(std::integral_constant<int, ST / 2>{});
-  __builtin_amdgcn_sched_barrier(0);
+                                       const PvDma& dma) {
+  constexpr int ST = 2 * PI;
+  constexpr int j = ST / kDvTiles;
+  constexpr bool reads = ST + 4 < kPvSteps;
+  // reads issued after step ST+1's two: steps ST+2, ST+3 (those that exist)
+  wait_lgkm<2 * ((ST + 3 < kPvSteps ? ST + 3 : kPvSteps - 1) - ST - 1)>();
+  if constexpr (kDmaOn && PI < kLoadsPerWave) {
+    const uint32_t off = (dma.p16 + 4096u * PI) ^ (__builtin_amdgcn_ubfe(dma.keys, 3 * PI, 3) << 4);
+    pv_pair<ST, reads, true>(pb[j], pl[j], vaddr, off, dma.base, dma.m0 + (uint32_t)(kWaves * 1024 * PI));
+  } else {
+    pv_pair<ST, reads, false>(pb[j], pl[j], vaddr, 0u, dma.base, dma.m0);
+  }
 }
 
 template <int... ST>
@@ -229,17 +278,17 @@ __device__ __forceinline__ void pv_issue_first(const uint32_t (&vaddr)[4], std::
   (v_issue<ST>(vaddr), ...);
 }
 
-template <typename Hook, int... PI>
+template <bool kDmaOn, int... PI>
 __device__ __forceinline__ void pv_all(const uint32_t (&vaddr)[4], const bf16x8 (&pb)[2], const bf16x8 (&pl)[2],
-                                       Hook& hook, std::integer_sequence<int, PI...>) {
-  (pv_do2<2 * PI>(vaddr, pb, pl, hook), ...);
+                                       const PvDma& dma, std::integer_sequence<int, PI...>) {
+  (pv_do2<PI, kDmaOn>(vaddr, pb, pl, dma), ...);
 }
 
 // K operand reads of S^T (k-step kk): lane (n, h) reads piece 2*kk + h of
 // tile row n, at kaddr[kk & 3] + 128*(kk >> 2).
 template <int KK>
 __device__ __forceinline__ void k_issue(const uint32_t (&kaddr)[4]) {
-  asm volatile("ds_read_b128 v[240+%1*4:243+%1*4], %0 offset:%2" ::"v"(kaddr[KK & 3]), "n"(KK % kKDepth),
+  asm volatile("ds_read_b128 v[232+%1*4:235+%1*4], %0 offset:%2" ::"v"(kaddr[KK & 3]), "n"(KK % kKDepth),
                "n"(128 * (KK >> 2)));
 }
 
@@ -250,13 +299,13 @@ template <int KK>
 __device__ __forceinline__ void qk_do(const uint32_t (&kaddr)[4], const bf16x8 (&qr)[kKSteps], f32x16& s) {
   wait_lgkm<(KK + kKDepth < kKSteps ? KK + kKDepth : kKSteps) - KK - 1>();
   if constexpr (KK == 0) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, v[240+%2*4:243+%2*4], %1, 0"
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, v[232+%2*4:235+%2*4], %1, 0"
                  : "=&v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
   } else if constexpr (KK + 1 < kKSteps) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, v[240+%2*4:243+%2*4], %1, %0"
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, v[232+%2*4:235+%2*4], %1, %0"
                  : "+v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
   } else {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, v[240+%2*4:243+%2*4], %1, %0\n\t"
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, v[232+%2*4:235+%2*4], %1, %0\n\t"
                  "s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15"
                  : "+v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
   }
@@ -294,6 +343,27 @@ struct DenseTile {
   uint32_t mask;
 };
 
+// Source offsets of a lane's tile loads.  Load jj of wave w fills LDS piece
+// slot p = p0 + 256*jj (p0 = 64*w + lane) with latent piece (p % 72) ^ key(t)
+// of tile row t = p / 72; since key(t) < 8 only flips bits of p % 72 inside
+// its aligned group of 8, the source byte offset within the tile's rows is
+// 16 * (p ^ key(t)).  The nine 3-bit keys are packed into one register.
+struct LoadOffsets {
+  uint32_t p16;    // 16 * p0
+  uint32_t keys;   // key of load jj in bits [3jj, 3jj + 3)
+  __device__ __forceinline__ void init(int wave, int lane) {
+    const int p0 = 64 * wave + lane;
+    p16 = 16u * (uint32_t)p0;
+    keys = 0u;
+#pragma unroll
+    for (int jj = 0; jj < kLoadsPerWave; ++jj) keys |= (uint32_t)key((p0 + 256 * jj) / kPieces) << (3 * jj);
+  }
+  // jj may be a run-time (wave-uniform) value.
+  __device__ __forceinline__ uint32_t operator()(int jj) const {
+    return (p16 + 4096u * (uint32_t)jj) ^ (__builtin_amdgcn_ubfe(keys, 3 * jj, 3) << 4);
+  }
+};
+
 template <bool kSparse>
 struct Stager {
   const unsigned char* kv;
@@ -302,39 +372,23 @@ struct Stager {
   int page_size, num_pages, len, seg_end;
 
   // Dense: tiles start at multiples of 32 and pages hold a multiple of 64
-  // tokens, so a tile is one contiguous run of rows inside one page.
-  __device__ __forceinline__ DenseTile plan(int u0) const {
+  // tokens, so a tile is one contiguous run of rows inside one page.  The
+  // block-table entries of the segment's first 64 pages sit in `pwin` (lane
+  // i holds entry pfirst + i); later pages are read from the table.
+  // (pi, off) = (u0 / page_size, u0 % page_size).
+  __device__ __forceinline__ DenseTile plan(int u0, int pi, int off, int pfirst, int pwin) const {
     const int nvalid = min(kTok, seg_end - u0);
-    const int pg = ((const_i32p)bt_row)[u0 / page_size];
+    const int pg = pi - pfirst < 64 ? __builtin_amdgcn_readlane(pwin, pi - pfirst) : ((const_i32p)bt_row)[pi];
     const bool page_ok = pg >= 0 && pg < num_pages;
     DenseTile t;
     t.mask = !page_ok ? 0u : (nvalid >= kTok ? ~0u : ((1u << nvalid) - 1u));
-    t.base = kv + ((size_t)(page_ok ? pg : 0) * page_size + (u0 % page_size)) * (size_t)kRowBytes;
+    t.base = kv + ((size_t)(page_ok ? pg : 0) * page_size + off) * (size_t)kRowBytes;
     return t;
-  }
-
-  // One of the 9 loads of a full dense tile, for the MFMA stream: pool
-  // address = SGPR base + 32-bit lane offset, LDS address in M0 from SGPRs,
-  // so no vector-ALU work.  The compiler's own value of M0 is saved and
-  // restored (M0 is read when the load issues).  Counted by vmcnt like the
-  // other tile loads.
-  __device__ __forceinline__ void issue_one(const DenseTile& t, uint32_t lds_sgpr, int jj,
-                                            const uint32_t (&so)[kLoadsPerWave]) const {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(so[jj]), "s"(t.base), "s"(lds_sgpr + (uint32_t)(kWaves * jj * 1024))
-        : "memory");
   }
 
   // All 9 loads of a dense tile with masked rows read from the zero block.
   __device__ __forceinline__ void issue_masked(const DenseTile& t, ISK_LDS unsigned char* buf, int wave, int lane,
-                                               const uint32_t (&so)[kLoadsPerWave]) const {
+                                               const LoadOffsets& so) const {
     const unsigned char* zero = (const unsigned char*)g_zero_piece;
     int l = lane;
     asm volatile("" : "+v"(l));   // recomputed per call, not kept live across the tile loop
@@ -342,7 +396,7 @@ struct Stager {
     for (int jj = 0; jj < kLoadsPerWave; ++jj) {
       const int i = wave + kWaves * jj;
       const int tr = (i * 64 + l) / kPieces;
-      const unsigned char* src = ((t.mask >> tr) & 1u) ? t.base + (size_t)so[jj] : zero;
+      const unsigned char* src = ((t.mask >> tr) & 1u) ? t.base + (size_t)so(jj) : zero;
       load_lds_16(src, buf + i * 1024);
     }
   }
@@ -375,15 +429,15 @@ struct Stager {
 
   // Whole tile at once; returns the row-valid mask.
   __device__ __forceinline__ uint32_t operator()(int u0, ISK_LDS unsigned char* buf, int wave, int lane,
-                                                 const uint32_t (&so)[kLoadsPerWave]) const {
+                                                 const LoadOffsets& so, int pfirst, int pwin) const {
     if constexpr (kSparse) {
       return issue_sparse(u0, buf, wave, lane);
     } else {
-      const DenseTile t = plan(u0);
+      const DenseTile t = plan(u0, u0 / page_size, u0 % page_size, pfirst, pwin);
       if (t.mask == ~0u) {
 #pragma unroll
         for (int jj = 0; jj < kLoadsPerWave; ++jj)
-          load_lds_16(t.base + (size_t)so[jj], buf + (wave + kWaves * jj) * 1024);
+          load_lds_16(t.base + (size_t)so(jj), buf + (wave + kWaves * jj) * 1024);
       } else {
         issue_masked(t, buf, wave, lane, so);
       }
@@ -393,7 +447,7 @@ struct Stager {
 };
 
 template <bool kSparse>
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(240)))
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(232)))
 mla_split_h32_kernel(MlaLaunch a) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kBufs * kTileBytes];
   ISK_LDS unsigned char* tiles = (ISK_LDS unsigned char*)lds_raw;
@@ -409,6 +463,8 @@ mla_split_h32_kernel(MlaLaunch a) {
   const int hb = (bid >> 3) % n_hb;
   if (g >= a.n_groups) return;
   ring_claim();
+  // Wave index as a wave-uniform (scalar) value for address arithmetic.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int head = hb * kHeadsPerBlock + wave * 32 + n32;
   const int seg_first = a.groups[g], seg_last = a.groups[g + 1];
 
@@ -427,13 +483,8 @@ mla_split_h32_kernel(MlaLaunch a) {
     v_lane0 = kRowBytes * (4 * hh + (i16 >> 2)) + 64 * (i16 >> 3) + 32 * gp + 16 * (hp ^ hh) + 8 * (i16 & 1);
   }
   // Source offsets (within the tile's rows) of this lane's full-tile loads.
-  uint32_t so[kLoadsPerWave];
-#pragma unroll
-  for (int jj = 0; jj < kLoadsPerWave; ++jj) {
-    const int p = (wave + kWaves * jj) * 64 + lane;
-    const int t = p / kPieces;
-    so[jj] = (uint32_t)(t * kRowBytes + ((p - t * kPieces) ^ key(t)) * 16);
-  }
+  LoadOffsets so;
+  so.init(wave_u, lane);
 
   for (int si = seg_first; si < seg_last; ++si) {
     const Seg sg = a.segs[si];
@@ -446,6 +497,14 @@ mla_split_h32_kernel(MlaLaunch a) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
 
+    // Block-table window of the segment (dense): lane i holds the entry of
+    // page pfirst + i (-1 past the row's pages).
+    const int pfirst = sg.begin / a.page_size;
+    int pwin = -1;
+    if constexpr (!kSparse) {
+      const int pl = pfirst + lane;
+      if ((long long)pl * a.page_size < (long long)sg.end) pwin = stage.bt_row[pl];
+    }
     // Query slice: lane (n32, hh) holds q[head][16*kk + 8*hh + 0..7].
     bf16x8 qr[kKSteps];
     {
@@ -453,20 +512,40 @@ mla_split_h32_kernel(MlaLaunch a) {
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) qr[kk] = qrow[2 * kk];
     }
-    // Wait for the query here, before any tile load is issued: the compiler
-    // cannot prove inside the tile loop that these loads have landed and
-    // would otherwise wait for every outstanding load at each tile.
-    wait_vmcnt<0>();
+    // The window has landed once only the query loads are younger.
+    wait_vmcnt<kKSteps>();
 
     float m_ref = -INFINITY, l_run = 0.f;
     acc_zero();
 
     const int n_tiles = (sg.end - sg.begin + kTok - 1) / kTok;
-    // Prologue: tiles 0..kBufs-2 in flight; masks kept in a register ring.
-    uint32_t mk0 = 0, mk1 = 0, mk2 = 0;
-    if (n_tiles > 0) mk0 = stage(sg.begin, tiles, wave, lane, so);
-    if (n_tiles > 1) mk1 = stage(sg.begin + kTok, tiles + kTileBytes, wave, lane, so);
-    if (n_tiles > 2) mk2 = stage(sg.begin + 2 * kTok, tiles + 2 * kTileBytes, wave, lane, so);
+    // Prologue: tiles 0..kBufs-2 in flight (loads for missing tiles come
+    // from the zero block into unused buffers, so the count is always 27);
+    // masks kept in a register ring.
+    uint32_t mk[3];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      ISK_LDS unsigned char* tb = tiles + t * kTileBytes;
+      if (t < n_tiles) {
+        mk[t] = stage(sg.begin + t * kTok, tb, wave_u, lane, so, pfirst, pwin);
+      } else {
+        mk[t] = 0u;
+        stage.issue_masked(DenseTile{(const unsigned char*)a.kv, 0u}, tb, wave_u, lane, so);
+      }
+    }
+    uint32_t mk0 = mk[0], mk1 = mk[1], mk2 = mk[2];
+    // Page and in-page offset of tile it+3, advanced by one tile per step.
+    int pn = (sg.begin + 3 * kTok) / a.page_size, on = (sg.begin + 3 * kTok) % a.page_size;
+    // The query has landed once only the 27 prologue loads are younger; the
+    // compiler cannot prove this inside the tile loop and would otherwise
+    // wait for every outstanding load at each tile.
+    wait_vmcnt<3 * kLoadsPerWave>();
+    // Pass the query through an empty asm: later uses read its outputs, so
+    // the compiler has no load of these registers left to wait for in the
+    // tile loop.
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; kk += 4)
+      asm volatile("" : "+v"(qr[kk]), "+v"(qr[kk + 1]), "+v"(qr[kk + 2]), "+v"(qr[kk + 3]));
 
     for (int it = 0; it < n_tiles; ++it) {
       // Tile `it` has landed once at most the loads of the tiles issued after
@@ -480,6 +559,9 @@ mla_split_h32_kernel(MlaLaunch a) {
       else
         wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
+      // Re-derive lane offsets inside the loop instead of keeping every
+      // derived value live across it.
+      asm volatile("" : "+v"(so.p16), "+v"(so.keys), "+v"(k_lane0), "+v"(v_lane0));
       const uint32_t mask = mk0;
       mk0 = mk1;
       mk1 = mk2;
@@ -492,12 +574,17 @@ mla_split_h32_kernel(MlaLaunch a) {
       if (it + 3 < n_tiles) {
         const int u0n = sg.begin + (it + 3) * kTok;
         if constexpr (kSparse) {
-          mk2 = stage.issue_sparse(u0n, nbuf, wave, lane);
+          mk2 = stage.issue_sparse(u0n, nbuf, wave_u, lane);
         } else {
-          nt = stage.plan(u0n);
+          nt = stage.plan(u0n, pn, on, pfirst, pwin);
+          on += kTok;
+          if (on >= a.page_size) {
+            on -= a.page_size;
+            ++pn;
+          }
           mk2 = nt.mask;
           defer = nt.mask == ~0u;
-          if (!defer) stage.issue_masked(nt, nbuf, wave, lane, so);
+          if (!defer) stage.issue_masked(nt, nbuf, wave_u, lane, so);
         }
       }
       const int buf = it & 3;
@@ -571,19 +658,13 @@ mla_split_h32_kernel(MlaLaunch a) {
 #pragma unroll
       for (int m = 1; m < 4; ++m) vaddr[m] = vaddr[0] ^ (32u * m);
       __builtin_amdgcn_sched_barrier(0);
-      pv_issue_first(vaddr, std::make_integer_sequence<int, kVDepth>{});
-      if (defer) {
-        // LDS address of this wave's first load of tile it+3 (wave-uniform).
-        const uint32_t lds_sgpr = __builtin_amdgcn_readfirstlane(tiles_u32 + ((it + 3) & 3) * kTileBytes + wave * 1024);
-        auto dma = [&](auto pair) {
-          constexpr int jj = decltype(pair)::value;
-          if constexpr (jj < kLoadsPerWave) stage.issue_one(nt, lds_sgpr, jj, so);
-        };
-        pv_all(vaddr, pb, pl, dma, std::make_integer_sequence<int, kPvSteps / 2>{});
-      } else {
-        auto none = [](auto) {};
-        pv_all(vaddr, pb, pl, none, std::make_integer_sequence<int, kPvSteps / 2>{});
-      }
+      pv_issue_first(vaddr, std::make_integer_sequence<int, 4>{});
+      // LDS address of this wave's first load of tile it+3 (wave-uniform).
+      const PvDma dma{nt.base, tiles_u32 + ((it + 3) & 3) * kTileBytes + wave_u * 1024, so.p16, so.keys};
+      if (defer)
+        pv_all<true>(vaddr, pb, pl, dma, std::make_integer_sequence<int, kPvSteps / 2>{});
+      else
+        pv_all<false>(vaddr, pb, pl, dma, std::make_integer_sequence<int, kPvSteps / 2>{});
       __builtin_amdgcn_sched_barrier(0);
     }
 
