@@ -295,8 +295,9 @@ __device__ __forceinline__ void k_issue(const uint32_t (&kaddr)[4]) {
 // s += K-slot * q[kk] (S^T in VGPRs, fp32).  The first step starts from 0;
 // the last one is followed by the wait states a vector-ALU read of its result
 // needs, inside the same asm so nothing can be scheduled in between.
-template <int KK>
-__device__ __forceinline__ void qk_do(const uint32_t (&kaddr)[4], const bf16x8 (&qr)[kKSteps], f32x16& s) {
+template <int KK, typename Hook>
+__device__ __forceinline__ void qk_do(const uint32_t (&kaddr)[4], const bf16x8 (&qr)[kKSteps], f32x16& s,
+                                      Hook& hook) {
   wait_lgkm<(KK + kKDepth < kKSteps ? KK + kKDepth : kKSteps) - KK - 1>();
   if constexpr (KK == 0) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, v[232+%2*4:235+%2*4], %1, 0"
@@ -310,6 +311,10 @@ __device__ __forceinline__ void qk_do(const uint32_t (&kaddr)[4], const bf16x8 (
                  : "+v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
   }
   if constexpr (KK + kKDepth < kKSteps) k_issue<KK + kKDepth>(kaddr);
+  // Independent vector-ALU work placed in this MFMA's shadow.
+  __builtin_amdgcn_sched_barrier(0);
+  hook(std::integral_constant<int, KK>{});
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int... KK>
@@ -317,10 +322,31 @@ __device__ __forceinline__ void qk_issue_first(const uint32_t (&kaddr)[4], std::
   (k_issue<KK>(kaddr), ...);
 }
 
-template <int... KK>
+template <typename Hook, int... KK>
 __device__ __forceinline__ void qk_all(const uint32_t (&kaddr)[4], const bf16x8 (&qr)[kKSteps], f32x16& s,
-                                       std::integer_sequence<int, KK...>) {
-  (qk_do<KK>(kaddr, qr, s), ...);
+                                       Hook& hook, std::integer_sequence<int, KK...>) {
+  (qk_do<KK>(kaddr, qr, s, hook), ...);
+}
+
+// S^T of one tile (buffer at LDS address `tile`), with `hook` run in the
+// MFMA shadows.
+template <typename Hook>
+__device__ __forceinline__ void qk_tile(uint32_t tile, uint32_t k_lane0, const bf16x8 (&qr)[kKSteps], f32x16& s,
+                                        Hook& hook) {
+  uint32_t kaddr[4];
+  kaddr[0] = tile + k_lane0;
+#pragma unroll
+  for (int m = 1; m < 4; ++m) kaddr[m] = kaddr[0] ^ (32u * m);
+  __builtin_amdgcn_sched_barrier(0);
+  qk_issue_first(kaddr, std::make_integer_sequence<int, kKDepth>{});
+  qk_all(kaddr, qr, s, hook, std::make_integer_sequence<int, kKSteps>{});
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The softmax slices of the last tile of a split, with no S^T to overlap.
+template <typename Hook, int... KK>
+__device__ __forceinline__ void softmax_only(Hook& hook, std::integer_sequence<int, KK...>) {
+  (hook(std::integral_constant<int, KK>{}), ...);
 }
 
 // vmcnt(n) with expcnt and lgkmcnt left at their maxima (gfx9 encoding).
@@ -547,14 +573,26 @@ mla_split_h32_kernel(MlaLaunch a) {
     for (int kk = 0; kk < kKSteps; kk += 4)
       asm volatile("" : "+v"(qr[kk]), "+v"(qr[kk + 1]), "+v"(qr[kk + 2]), "+v"(qr[kk + 3]));
 
+    // S^T of tile 0 (tiles 1 and 2 -- or their zero stand-ins -- are the
+    // 18 younger loads).
+    wait_vmcnt<2 * kLoadsPerWave>();
+    __builtin_amdgcn_s_barrier();
+    f32x16 s_cur;
+    {
+      auto none = [](auto) {};
+      qk_tile(tiles_u32, k_lane0, qr, s_cur, none);
+    }
+
+    // Tile loop, software-pipelined by one tile: step `it` computes S^T of
+    // tile it+1 and, in the shadows of those MFMAs, the softmax of tile it;
+    // then O^T += V^T P^T for tile it.  Buffers: it (PV), it+1 (S^T), it+2
+    // and it+3 (loads in flight).
     for (int it = 0; it < n_tiles; ++it) {
-      // Tile `it` has landed once at most the loads of the tiles issued after
-      // it are outstanding; then every wave has finished tile it-1, whose
-      // buffer the next load reuses.
-      const int ahead = n_tiles - 1 - it;
-      if (ahead >= 2)
-        wait_vmcnt<2 * kLoadsPerWave>();
-      else if (ahead == 1)
+      const bool has_next = it + 1 < n_tiles;
+      // Tile it+1 has landed once only the loads of tile it+2 (or of a zero
+      // stand-in of the prologue) are younger; after the barrier every wave
+      // is also done with tile it-1, whose buffer the loads of tile it+3 reuse.
+      if (it + 2 < max(n_tiles, 3))
         wait_vmcnt<kLoadsPerWave>();
       else
         wait_vmcnt<0>();
@@ -565,9 +603,8 @@ mla_split_h32_kernel(MlaLaunch a) {
       const uint32_t mask = mk0;
       mk0 = mk1;
       mk1 = mk2;
-      // Loads of tile it+3 (into the buffer tile it-1 used): a full dense
-      // tile's 9 loads are spread over the PV MFMA stream below, other tiles
-      // are issued here.
+      // Loads of tile it+3: a full dense tile's 9 loads are spread over the
+      // PV MFMA stream below, other tiles are issued here.
       ISK_LDS unsigned char* nbuf = tiles + ((it + 3) & 3) * kTileBytes;
       DenseTile nt{nullptr, 0u};
       bool defer = false;
@@ -588,63 +625,64 @@ mla_split_h32_kernel(MlaLaunch a) {
         }
       }
       const int buf = it & 3;
-      
-      // ---- S^T = K * Q^T (32 tokens x 32 heads), one accumulation chain
-      f32x16 s;
-      {
-        uint32_t kaddr[4];
-        kaddr[0] = tiles_u32 + buf * kTileBytes + k_lane0;
-#pragma unroll
-        for (int m = 1; m < 4; ++m) kaddr[m] = kaddr[0] ^ (32u * m);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_issue_first(kaddr, std::make_integer_sequence<int, kKDepth>{});
-        qk_all(kaddr, qr, s, std::make_integer_sequence<int, kKSteps>{});
-        __builtin_amdgcn_sched_barrier(0);
-      }
 
-      // ---- online softmax; lane holds head n32, tokens 8*(e>>2) + 4*hh + (e&3)
+      // ---- online softmax of tile it; lane holds head n32, tokens
+      // 8*(e>>2) + 4*hh + (e&3).  Masked scores become -inf first.
       if (mask != ~0u) {   // partial or masked tile (wave-uniform test)
         const uint32_t mh = mask >> (4 * hh);
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          s[e] = __builtin_amdgcn_ubfe(mh, 8 * (e >> 2) + (e & 3), 1) ? s[e] : -INFINITY;
+          s_cur[e] = __builtin_amdgcn_ubfe(mh, 8 * (e >> 2) + (e & 3), 1) ? s_cur[e] : -INFINITY;
       }
-      // Max over the raw scores, then scaled: with scale > 0 (checked by the
-      // planner) this equals the max of the scaled scores, rounding included.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
-      }
-      const float m_old = m_ref;
-      const bool move = mx > m_old + kRescaleThreshold || (m_old == -INFINITY && mx > -INFINITY);
-      const float m_new = move ? mx : m_old;
-      const float alpha = move ? fast_exp2(m_old - m_new) : 1.0f;   // m_old = -inf -> 0
-      const bool rescale = move && m_old != -INFINITY;             // acc is still 0 before the first move
-      m_ref = m_new;
-      const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-
+      float mx = -INFINITY, alpha = 1.f, m_sub = 0.f, psum = 0.f;
+      bool rescale = false;
       bf16x8 pb[2], pl[2];
-      float psum = 0.f;
+      // The softmax in slices, one per k-step of the next tile's S^T:
+      //  0..3   max over the raw scores (with scale > 0, checked by the
+      //         planner, the max of the scaled scores, rounding included)
+      //  4      lane-pair max, lazy reference move, alpha
+      //  5..20  p = 2^(s*scale - m), one score per slice
+      //  21..28 p -> bf16 hi + lo, one pair per slice; sum of the fp32 p
+      //  29     running normaliser
+      auto softmax = [&](auto kc) {
+        constexpr int KK = decltype(kc)::value;
+        if constexpr (KK < 4) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[8 * j + 2 * q], a.scale_log2, -m_sub));
-          const float p1 = fast_exp2(__builtin_fmaf(s[8 * j + 2 * q + 1], a.scale_log2, -m_sub));
+          for (int e = 4 * KK; e < 4 * KK + 4; ++e) mx = fmaxf(mx, s_cur[e]);
+        } else if constexpr (KK == 4) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+          const float m_old = m_ref;
+          const bool move = mx > m_old + kRescaleThreshold || (m_old == -INFINITY && mx > -INFINITY);
+          const float m_new = move ? mx : m_old;
+          alpha = move ? fast_exp2(m_old - m_new) : 1.0f;   // m_old = -inf -> 0
+          rescale = move && m_old != -INFINITY;             // acc is still 0 before the first move
+          m_ref = m_new;
+          m_sub = m_new == -INFINITY ? 0.f : m_new;
+        } else if constexpr (KK < 21) {
+          constexpr int e = KK - 5;
+          s_cur[e] = fast_exp2(__builtin_fmaf(s_cur[e], a.scale_log2, -m_sub));
+        } else if constexpr (KK < 29) {
+          constexpr int q = KK - 21, j = q >> 2, r = q & 3;
+          const float p0 = s_cur[2 * q], p1 = s_cur[2 * q + 1];
           const bf16x2 hi = to_bf16x2(p0, p1);
           const bf16x2 lo = to_bf16x2(p0 - (float)hi[0], p1 - (float)hi[1]);
-          pb[j][2 * q] = hi[0];
-          pb[j][2 * q + 1] = hi[1];
-          pl[j][2 * q] = lo[0];
-          pl[j][2 * q + 1] = lo[1];
+          pb[j][2 * r] = hi[0];
+          pb[j][2 * r + 1] = hi[1];
+          pl[j][2 * r] = lo[0];
+          pl[j][2 * r + 1] = lo[1];
           psum += p0;
           psum += p1;
+        } else if constexpr (KK == 29) {
+          l_run = l_run * alpha + psum;
         }
+      };
+      f32x16 s_next;
+      if (has_next) {
+        qk_tile(tiles_u32 + ((it + 1) & 3) * kTileBytes, k_lane0, qr, s_next, softmax);
+      } else {
+        softmax_only(softmax, std::make_integer_sequence<int, kKSteps>{});
       }
-      l_run = l_run * alpha + psum;
       if (__ballot(rescale) != 0ull) {
         // Lanes that did not move have alpha == 1 exactly.
         acc_settle();
@@ -666,6 +704,7 @@ mla_split_h32_kernel(MlaLaunch a) {
       else
         pv_all<false>(vaddr, pb, pl, dma, std::make_integer_sequence<int, kPvSteps / 2>{});
       __builtin_amdgcn_sched_barrier(0);
+      s_cur = s_next;
     }
 
     // ---- epilogue: o = acc / l, lse = ln 2 * (m_ref + log2 l)
