@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mla_split_b64_hbm_traffic.txt")
-SPLIT_KERNEL_SRC = os.path.join(ROOT, "invariant_split_kv_amd", "csrc", "mla_split.hip")
+SPLIT_KERNEL_SRC = os.path.join(ROOT, "invariant_split_kv_amd", "csrc", "mla_split_h32.hip")
 
 
 def kernel_source_hash() -> str:
@@ -252,7 +252,7 @@ def main():
                         "lens lognormal(median 4096, sigma 1) clipped [64,32768], 64-token pages, permuted table",
             "batch": case.batch, "kv_tokens": int(lens_host.sum()), "split_mode": args.mode,
             "split_tokens": info["split_tokens"], "splits": info["num_segments"],
-            "partials": info["num_partials"], "workgroups": info["num_groups"] * 2,
+            "partials": info["num_partials"], "workgroups": info["num_groups"],
         },
         "roofline": {
             "bound": "hbm",
@@ -261,7 +261,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
-            "kernel": "mla_split_kernel<dense>",
+            "kernel": "mla_split_h32_kernel<dense>",
             "algorithmic_bytes_per_launch": kvb + q_bytes,
             "avg_launch_ms": round(split_ms, 5),
         },

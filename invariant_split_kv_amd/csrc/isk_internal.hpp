@@ -19,7 +19,7 @@ namespace isk {
 constexpr int kGqaTile = 64;          // tokens per GQA wave step
 constexpr int kMlaTile = 64;          // tokens per LDS tile of the 16-head MLA kernel
 constexpr int kGqaSplitDefault = 512;
-constexpr int kMlaSplitDefault = 1024;
+constexpr int kMlaSplitDefault = 1536;
 constexpr int kSparseSplitDefault = 512;
 constexpr int kMlaDqk = 576;
 constexpr float kLog2eHost = 1.44269504088896340736f;   // log2(e), rounded to float
