@@ -99,6 +99,46 @@ def test_mla_page_size_128_and_custom_split():
     parity(out, lse, ro, rl, False, "mla P=128 S=256")
 
 
+def _grow_rope_scores(case, growth):
+    """Scale the 64 rope dims of each cached token by growth(t / L): the
+    scores climb (or jump) across the row while the values (the first 512
+    dims) keep their N(0, 0.5^2) range, so the tolerance stays tight."""
+    for b, r in enumerate(case.rows):
+        L = int(case.lens[b])
+        if L == 0:
+            continue
+        g = np.asarray(growth(np.arange(L) / max(L - 1, 1)), np.float32)[:, None]
+        rope = synth.bf16_value(r.latent[:, 512:]) * g
+        r.latent[:, 512:] = synth.bf16_bits(rope)
+    return case
+
+
+@pytest.mark.parametrize("hq", [128, 64])
+@pytest.mark.parametrize("shape", ["ramp", "jump"])
+def test_mla_running_max_moves_rescale_accumulator(hq, shape):
+    """Rows whose scores grow far past the lazy-rescale threshold (2^8 in
+    the exponent) several times per split, so the accumulator rescale runs;
+    the normal workloads' flat scores never trigger it."""
+    growth = (lambda x: 1.0 + 200.0 * x) if shape == "ramp" else (lambda x: np.where(x < 0.6, 1.0, 150.0))
+    case = _grow_rope_scores(synth.mla_case([3000, 5000, 700, 64, 1537], hq, 1.0 / math.sqrt(192.0), 64,
+                                            structure_seed=70 + hq), growth)
+    for out_f32 in (False, True):
+        out, lse, _, _ = run_case(case, out_f32=out_f32)
+        ro, rl = reference(case)
+        parity(out, lse, ro, rl, out_f32, f"mla rescale {shape} hq={hq} f32={out_f32}")
+
+
+@pytest.mark.parametrize("hq", [128, 64])
+def test_mla_split_longer_than_the_page_window(hq):
+    """Splits of 8192 tokens over 64-token pages span 128 pages: tiles past
+    the first 64 pages of a split read the block table directly."""
+    case = synth.mla_case([9000, 20000, 8192], hq, 1.0 / math.sqrt(192.0), 64, structure_seed=80 + hq,
+                          split_tokens=8192)
+    out, lse, _, _ = run_case(case, fill=GARBAGE)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, f"mla S=8192 hq={hq}")
+
+
 def test_sparse_edges():
     W = 700
     lens = [3000, 5, 800, 2000, 1, 0, 4096]
