@@ -166,7 +166,11 @@ ISK_API int isk_plan_segments(const isk_plan* plan, int32_t* records_out, int32_
  * plan        from isk_plan_create/update; not modified.
  * q           [B, Hq, head_dim_qk] bf16.
  * kv_pages    GQA: [num_pages, 2, Hkv, page_size, head_dim] bf16 (index 0 = K,
- *             1 = V).  MLA: [num_pages, page_size, 576] bf16.
+ *             1 = V).  MLA: [num_pages, page_size, 576] bf16.  With Hq a
+ *             multiple of 128 the MLA kernel multiplies P by V in fp16: the
+ *             first 512 latent values (V) are exact there when their magnitude
+ *             lies in [2^-14, 65504]; larger ones are clamped to 65504 and
+ *             smaller ones rounded toward zero to fp16 subnormals.
  * block_table [B, max_pages_per_row] int32; entry j of row b is the page
  *             holding the row's tokens [j*page_size, (j+1)*page_size).
  * lens        [B] int32 device copy of lens_host.

@@ -156,7 +156,7 @@ const char* isk_numerics_id(void) {
       << " split_gqa=" << isk::kGqaSplitDefault << " split_mla=" << isk::kMlaSplitDefault
       << " split_topk=" << isk::kSparseSplitDefault
       << " gqa=vdot2-bf16/fp32-pv"
-      << " mla(hq%128=0)=mfma32x32x16-bf16/tile32/p-hi+lo-bf16/rescale-thr8"
+      << " mla(hq%128=0)=qk:mfma32x32x16-bf16/pv:mfma32x32x16-f16(p-fp16-rne-x2^7,v-bf16-to-fp16-rtz)/tile32/rescale-thr8"
       << " mla(other)=mfma16x16x32-bf16/tile64/p-hi+lo-bf16/rescale-thr8 combine=fixed-order-fp32"
       << " balanced=blk" << isk::kBalancedBlock << "-parts" << isk::kBalancedParts << "-ovh" << isk::kBalancedOverhead;
     return s.str();

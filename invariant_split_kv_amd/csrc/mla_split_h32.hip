@@ -12,7 +12,9 @@
 //     [32w, 32w + 32) of its head block and keeps their whole 576-dim query
 //     slice in VGPRs (36 MFMA B operands).
 //   * 32-token tiles (72 pieces of 16 B per token) are copied HBM -> LDS by
-//     16-byte direct loads, four tiles in flight.  Piece c of tile row t sits
+//     16-byte direct loads into three row buffers (tile i converted, tile
+//     i+1 read by S^T, tile i+2 in flight; tile i+3's loads start once tile
+//     i is converted).  Piece c of tile row t sits
 //     at LDS piece t*72 + (c ^ key(t)), key(t) = 4*((t>>1)&1) + ((t>>2)&3):
 //     the 16 rows of one K operand read and the 4-row x 32-byte blocks of a
 //     transposing V read land on distinct LDS banks.  Masked rows (past the
@@ -22,20 +24,24 @@
 //   * S^T (32 tokens x 32 heads) = K * Q^T with v_mfma_f32_32x32x16_bf16,
 //     fp32 accumulation, one chain over the 36 k-steps.  Lane (n, h) ends up
 //     with the 16 scores of head n for tokens 8*(e>>2) + 4h + (e&3).
-//   * Online softmax in the log2 domain, p = 2^(s*scale*log2(e) - m) with
-//     one fused multiply-add per score, and a lazily moved reference max
-//     (the accumulator is rescaled only when a head's max outgrows the
-//     reference by more than 2^8); p = 2^(x - m) is split into bf16 hi and lo
-//     parts and both multiply V, so the weights keep ~16 significant bits; the
-//     normaliser sums the fp32 p.
-//   * O^T (512 dims x 32 heads) += V^T * P^T.  The output block of a wave is
-//     256 fp32 values per lane and lives in AGPRs a0..a255 for the whole
-//     split, written only by the inline-asm MFMAs below (dim tile dt in
-//     a[16*dt .. 16*dt+15]); the compiler's own code uses VGPRs only (the
-//     file is built with MFMA results in VGPRs and no VGPR spills to AGPRs).
-//     V^T comes from the LDS tile through ds_read_b64_tr_b16.  Both products
-//     read their LDS operands through a fixed register ring (v240..v255)
-//     written and read only by inline asm, with explicit lgkmcnt waits.
+//   * Online softmax in the log2 domain, p = 2^(s*scale*log2(e) - m + 7)
+//     with one fused multiply-add per score, and a lazily moved reference
+//     max (the accumulator is rescaled only when a head's max outgrows the
+//     reference by more than 2^8).  p is rounded to fp16 for the PV product
+//     (the 2^7 factor keeps p within fp16's normal range; it cancels in o =
+//     acc / l and is taken out of the LSE); the normaliser sums the fp32 p.
+//   * O^T (512 dims x 32 heads) += V^T * P^T with v_mfma_f32_32x32x16_f16.
+//     Once per tile and workgroup the V part of the tile is converted to an
+//     fp16 V^T buffer in LDS (each wave a quarter of the dims, in the
+//     shadows of the S^T MFMAs of the next tile); PV reads it back with one
+//     16-byte read per MFMA.  The output block of a wave is 256 fp32 values
+//     per lane and lives in AGPRs a0..a255 for the whole split, written only
+//     by the inline-asm MFMAs below (dim tile dt in a[16*dt .. 16*dt+15]);
+//     the compiler's own code uses VGPRs only (the file is built with MFMA
+//     results in VGPRs and no VGPR spills to AGPRs).  The LDS operands of
+//     both products and of the conversion pass through a fixed register ring
+//     (v232..v255) written and read only by inline asm, with explicit lgkmcnt
+//     waits.
 // Every reduction order above is fixed by the segment's own token range, so
 // the bits of a segment's result do not depend on anything else in the batch.
 
@@ -48,13 +54,14 @@ namespace isk {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // Read-only view of the block table: loads through the constant address
 // space become scalar loads (counted by lgkmcnt, not by the vector-memory
 // counter that the tile waits count).
 typedef const __attribute__((address_space(4))) int32_t* const_i32p;
 
 constexpr int kTok = 32;                                   // tokens per LDS tile
-constexpr int kBufs = 4;                                   // LDS tile buffers (tiles in flight)
+constexpr int kBufs = 3;                                   // LDS row-tile buffers
 constexpr int kWaves = 4;
 constexpr int kHeadsPerBlock = 32 * kWaves;                // 128
 constexpr int kPieces = kMlaDqk / 8;                       // 72 pieces of 16 B per latent row
@@ -66,6 +73,9 @@ constexpr int kKDepth = 4;                                 // K operand reads in
 constexpr int kDvTiles = kMlaDv / 32;                      // 16
 constexpr int kPvSteps = 2 * kDvTiles;                     // (k-step, dim tile) pairs per tile
 constexpr float kRescaleThreshold = 8.0f;                  // log2 units
+// p is computed as 2^(x - m + kPShift): at most 2^(8 + 7), well inside fp16,
+// and fp16 subnormals only start 2^21 below the reference max.
+constexpr float kPShift = 7.0f;
 
 static_assert(kLoadsPerWave * 64 * kWaves == kTok * kPieces, "tile must split evenly over the waves");
 static_assert(kKDepth - 1 <= 15 && kKDepth <= 6, "lgkmcnt field / ring slots");
@@ -134,9 +144,11 @@ __device__ __forceinline__ void acc_scale_all(float alpha, std::integer_sequence
 }
 
 // Wait states between the last MFMA write of the accumulator and a
-// vector-ALU access of it (a 32x32x16 result needs fewer than 20).
+// vector-ALU access of it: 16 (the compiler puts 12 after a 32x32x16 MFMA
+// of its own before a vector-ALU read or write of the result).  With one
+// wave per SIMD every wait state costs four cycles, so no more are used.
 __device__ __forceinline__ void acc_settle() {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15");
+  asm volatile("s_nop 7\n\ts_nop 7");
 }
 
 template <int DT>
@@ -161,11 +173,13 @@ __device__ __forceinline__ void acc_read(float (&o)[16]) {
 // the compiler never sees these registers (the kernel caps its own
 // allocation at 232 VGPRs), so it can neither copy an operand before its wait
 // nor reuse the register while the read is outstanding.  S^T uses slots
-// 0..kKDepth-1, O^T all six; the two phases do not overlap.
+// 0..kKDepth-1 and the V conversion slots 4 and 5; O^T uses all six; the two
+// phases do not overlap.
 #define ISK_RING_VGPRS "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", \
                        "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", \
                        "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
 constexpr int kRingSlots = 6;
+static_assert(kKDepth <= 4, "S^T reads may only use ring slots 0..3");
 
 __device__ __forceinline__ void ring_claim() { asm volatile("" ::: ISK_RING_VGPRS); }
 
@@ -177,79 +191,132 @@ __device__ __forceinline__ void wait_lgkm() {
   asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
 }
 
-// V^T operand reads.  Step st = (k-step j, dim tile dt): lane (n, h) needs
-// dims 32*dt + n of tile rows 16j + 4h + {0..3} and 16j + 8 + 4h + {0..3}.
-// With the transposing read, lane (i16, gp, h) addresses 4 dims of one row:
-// row 16j + 8u + 4h + (i16 >> 2), dims 32*dt + 16*gp + 4*(i16 & 3); its
-// per-lane byte offset is vaddr[2*(dt&1) + u], the rest is the immediate.
-// Step st goes to ring slot st % 6; the reads of step st are issued while the
-// MFMAs of step st-4 run.
+// ---------------------------------------------------------------------------
+// V^T in fp16.  PV needs V^T fragments: for k-step j (tokens 16j .. 16j+15)
+// and dim tile dt, lane (n, h) holds dim 32*dt + n of the eight tokens
+// 16j + 8*(e>>2) + 4h + (e&3), e = 0..7, in that order (the order of P^T in
+// the B operand).  Each tile's V part is converted once per workgroup into
+// a separate buffer of 512 rows x 64 B (one row per dim, four 16-byte chunks
+// c = 2j + h per row), chunk c of dim d stored at d*64 + 16*(c ^ ((d>>2)&3)):
+// the 16 lanes of a quarter-wave then hit distinct bank groups both when a
+// fragment is written and when PV reads it back with one ds_read_b128.
+//
+// Conversion of fragment (dt, j) from the bf16 row tile: two transposing
+// reads give lane (i16, gp, h) four dims' worth of rows 16j + 8u + 4h +
+// (i16 >> 2), dims 32*dt + 16*gp + 4*(i16 & 3); the lane's byte offset is
+// vaddr[2*(dt&1) + u], the rest is the immediate.  The four dwords (two bf16
+// each) are converted to fp16 pairs in place and written out as one chunk.
+// bf16 values with magnitude in [2^-14, 65504] are exact in fp16; the
+// round-toward-zero conversion keeps larger ones finite (clamped to 65504)
+// and truncates smaller ones to fp16 subnormals.
+constexpr int kVtBytes = kMlaDv * 64;
+
+template <int DT, int J>
+struct VFrag {
+  static constexpr int off0 = kRowBytes * 16 * J + 128 * (DT >> 1);
+  static constexpr int off1 = kRowBytes * (16 * J + 8) + 128 * (DT >> 1);
+  static constexpr int m = 2 * (DT & 1);
+};
+
+// Wave w converts dim tiles 4w .. 4w+3: fragment f = (d = f >> 1, j = f & 1)
+// is dim tile 4w + d.  The wave's dim offset is folded into the base
+// addresses (cvaddr: +256*w in the row tile, wvt: +8192*w in V^T).
+template <int F>
+__device__ __forceinline__ void cv_issue(const uint32_t (&cvaddr)[4]) {
+  using V = VFrag<(F >> 1), (F & 1)>;
+  asm volatile("ds_read_b64_tr_b16 v[232+%2*4:233+%2*4], %0 offset:%3\n\t"
+               "ds_read_b64_tr_b16 v[234+%2*4:235+%2*4], %1 offset:%4" ::"v"(cvaddr[V::m]),
+               "v"(cvaddr[V::m + 1]), "n"(4 + (F & 1)), "n"(V::off0), "n"(V::off1));
+}
+
+#define ISK_CV_DWORD(i)                                                                           \
+  "v_lshlrev_b32 %0, 16, v[232+%2*4+" #i "]\n\tv_and_b32 %1, 0xffff0000, v[232+%2*4+" #i "]\n\t" \
+  "v_cvt_pkrtz_f16_f32 v[232+%2*4+" #i "], %0, %1\n\t"
+
+// The reads of fragment F must have completed (counted by the caller's waits).
+template <int F>
+__device__ __forceinline__ void cv_store(uint32_t wvt0, uint32_t wvt1) {
+  float t0, t1;
+  asm volatile(ISK_CV_DWORD(0) ISK_CV_DWORD(1) ISK_CV_DWORD(2) ISK_CV_DWORD(3)
+               "ds_write_b128 %3, v[232+%2*4:235+%2*4] offset:%4"
+               : "=&v"(t0), "=&v"(t1)
+               : "n"(4 + (F & 1)), "v"((F & 1) ? wvt1 : wvt0), "n"(2048 * (F >> 1)));
+}
+
+// Conversion schedule inside the S^T stream of the next tile: fragments 0
+// and 1 are read before the first S^T read, fragment f is converted and
+// stored in the hook after S^T step kCvAt[f], followed by the reads of
+// fragment f+2 (same ring slot).  A read issued in hook h is complete once
+// the MFMA of step h+5 has waited, so kCvAt[f+2] >= kCvAt[f] + 5.
+constexpr int kCvAt[8] = {0, 1, 5, 6, 10, 11, 15, 16};
+constexpr int cv_frag_at(int kk) {
+  for (int f = 0; f < 8; ++f)
+    if (kCvAt[f] == kk) return f;
+  return -1;
+}
+// LDS operations a hook issues besides the S^T reads.
+constexpr int cv_ops(int kk) { return cv_frag_at(kk) < 0 ? 0 : cv_frag_at(kk) < 6 ? 3 : 1; }
+
+// ---------------------------------------------------------------------------
+// PV.  Step st = (k-step j = st / 16, dim tile dt = st % 16) reads its V^T
+// fragment into ring slot st % 6 (one ds_read_b128 at pvaddr[j] + 2048*dt);
+// the read is issued right after the MFMA of step st-5.
+constexpr int kVAhead = 5;   // V^T reads in flight, in steps
+static_assert(kVAhead < kRingSlots, "a step's slot must not be refilled before its MFMA");
+
 template <int ST>
 struct VStep {
   static constexpr int j = ST / kDvTiles, dt = ST % kDvTiles, slot = ST % kRingSlots;
-  static constexpr int off0 = kRowBytes * 16 * j + 128 * (dt >> 1);
-  static constexpr int off1 = kRowBytes * (16 * j + 8) + 128 * (dt >> 1);
 };
 
 template <int ST>
-__device__ __forceinline__ void v_issue(const uint32_t (&vaddr)[4]) {
+__device__ __forceinline__ void v_issue(const uint32_t (&pvaddr)[2]) {
   using V = VStep<ST>;
-  constexpr int m = 2 * (V::dt & 1);
-  asm volatile("ds_read_b64_tr_b16 v[232+%2*4:233+%2*4], %0 offset:%3\n\t"
-               "ds_read_b64_tr_b16 v[234+%2*4:235+%2*4], %1 offset:%4" ::"v"(vaddr[m]),
-               "v"(vaddr[m + 1]), "n"(V::slot), "n"(V::off0), "n"(V::off1));
+  asm volatile("ds_read_b128 v[232+%1*4:235+%1*4], %0 offset:%2" ::"v"(pvaddr[V::j]), "n"(V::slot),
+               "n"(2048 * V::dt));
 }
 
-// One PV step pair (steps ST, ST+1 = dim tiles dt, dt+1 of one k-step):
-//   acc[dt]   += V(ST)   * p_hi + V(ST)   * p_lo
-//   acc[dt+1] += V(ST+1) * p_hi + V(ST+1) * p_lo
-// as four MFMAs, hi and lo of one accumulator never back to back.  Between
-// them go the V^T reads of steps ST+4 and ST+5 (slots ST+4, ST+5 mod 6,
-// free since the previous pair) and, optionally, one 16-byte global->LDS load
-// of the next tile (pool offset `doff` from SGPR base `dbase`, LDS address
-// `dm0` in M0; the compiler's M0 is saved and restored, M0 being read when
-// the load issues).  Each MFMA thus shadows a few cheap issues instead of
-// all of them landing behind the last one.  The leading s_nop covers a
-// vector-ALU write of p_hi / p_lo right before the first MFMA.
-#define ISK_PV_MFMA(acc, slot, p) \
-  "v_mfma_f32_32x32x16_bf16 a[" acc "*16:" acc "*16+15], v[232+" slot "*4:235+" slot "*4], " p ", a[" acc "*16:" acc "*16+15]\n\t"
-#define ISK_PV_READS(slot, va, vb, oa, ob)                                    \
-  "ds_read_b64_tr_b16 v[232+" slot "*4:233+" slot "*4], " va " offset:" oa "\n\t" \
-  "ds_read_b64_tr_b16 v[234+" slot "*4:235+" slot "*4], " vb " offset:" ob "\n\t"
-#define ISK_PV_DMA "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %19\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %17, %18\n\ts_mov_b32 m0, %0\n\t"
+// One PV step: acc[dt] += V^T(step ST) * P^T(k-step j), fp16 operands, fp32
+// accumulation.  After the MFMA go the V^T read of step ST+5 and,
+// optionally, one 16-byte global->LDS load of a later tile (pool offset
+// `doff` from SGPR base `dbase`, LDS address `dm0` in M0; the compiler's M0
+// is saved and restored, M0 being read when the load issues).  The leading
+// s_nop at the first step of each k-step covers a vector-ALU write of the P
+// operand right before it.
+#define ISK_PV_MFMA16 "v_mfma_f32_32x32x16_f16 a[%3*16:%3*16+15], v[232+%4*4:235+%4*4], %1, a[%3*16:%3*16+15]\n\t"
+#define ISK_PV_READ16 "ds_read_b128 v[232+%5*4:235+%5*4], %2 offset:%6\n\t"
+#define ISK_PV_DMA16 "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %9\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %8\n\ts_mov_b32 m0, %0\n\t"
 
 template <int ST, bool kReads, bool kDma>
-__device__ __forceinline__ void pv_pair(const bf16x8& p_hi, const bf16x8& p_lo, const uint32_t (&va)[4],
-                                        uint32_t doff, const unsigned char* dbase, uint32_t dm0) {
+__device__ __forceinline__ void pv_step(const f16x8& p, const uint32_t (&pvaddr)[2], uint32_t doff,
+                                        const unsigned char* dbase, uint32_t dm0) {
   using A = VStep<ST>;
-  using B = VStep<ST + 1>;
-  using RA = VStep<(ST + 4 < kPvSteps ? ST + 4 : 0)>;
-  using RB = VStep<(ST + 5 < kPvSteps ? ST + 5 : 0)>;
+  using R = VStep<(ST + kVAhead < kPvSteps ? ST + kVAhead : 0)>;
+  constexpr bool lead = A::dt == 0;
   uint32_t saved;
-#define ISK_PV_OPERANDS                                                                                   \
-  : "=&s"(saved)                                                                                          \
-  : "v"(p_hi), "v"(p_lo), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "n"(A::dt), "n"(B::dt),         \
-    "n"(A::slot), "n"(B::slot), "n"(RA::slot), "n"(RB::slot), "n"(RA::off0), "n"(RA::off1), "n"(RB::off0), \
-    "n"(RB::off1), "v"(doff), "s"(dbase), "s"(dm0)
-  if constexpr (kReads && kDma) {
-    asm volatile("s_nop 1\n\t" ISK_PV_MFMA("%7", "%9", "%1") ISK_PV_READS("%11", "%3", "%4", "%13", "%14")
-                 ISK_PV_MFMA("%8", "%10", "%1") ISK_PV_READS("%12", "%5", "%6", "%15", "%16")
-                 ISK_PV_MFMA("%7", "%9", "%2") ISK_PV_DMA ISK_PV_MFMA("%8", "%10", "%2") ISK_PV_OPERANDS);
+#define ISK_PV16_OPERANDS                                                                          \
+  : "=&s"(saved)                                                                                   \
+  : "v"(p), "v"(pvaddr[R::j]), "n"(A::dt), "n"(A::slot), "n"(R::slot), "n"(2048 * R::dt), "v"(doff), \
+    "s"(dbase), "s"(dm0)
+  if constexpr (lead && kReads && kDma) {
+    asm volatile("s_nop 1\n\t" ISK_PV_MFMA16 ISK_PV_READ16 ISK_PV_DMA16 ISK_PV16_OPERANDS);
+  } else if constexpr (lead && kReads) {
+    asm volatile("s_nop 1\n\t" ISK_PV_MFMA16 ISK_PV_READ16 ISK_PV16_OPERANDS);
+  } else if constexpr (lead) {
+    asm volatile("s_nop 1\n\t" ISK_PV_MFMA16 ISK_PV16_OPERANDS);
+  } else if constexpr (kReads && kDma) {
+    asm volatile(ISK_PV_MFMA16 ISK_PV_READ16 ISK_PV_DMA16 ISK_PV16_OPERANDS);
   } else if constexpr (kReads) {
-    asm volatile("s_nop 1\n\t" ISK_PV_MFMA("%7", "%9", "%1") ISK_PV_READS("%11", "%3", "%4", "%13", "%14")
-                 ISK_PV_MFMA("%8", "%10", "%1") ISK_PV_READS("%12", "%5", "%6", "%15", "%16")
-                 ISK_PV_MFMA("%7", "%9", "%2") ISK_PV_MFMA("%8", "%10", "%2") ISK_PV_OPERANDS);
+    asm volatile(ISK_PV_MFMA16 ISK_PV_READ16 ISK_PV16_OPERANDS);
   } else if constexpr (kDma) {
-    asm volatile("s_nop 1\n\t" ISK_PV_MFMA("%7", "%9", "%1") ISK_PV_MFMA("%8", "%10", "%1")
-                 ISK_PV_MFMA("%7", "%9", "%2") ISK_PV_DMA ISK_PV_MFMA("%8", "%10", "%2") ISK_PV_OPERANDS);
+    asm volatile(ISK_PV_MFMA16 ISK_PV_DMA16 ISK_PV16_OPERANDS);
   } else {
-    asm volatile("s_nop 1\n\t" ISK_PV_MFMA("%7", "%9", "%1") ISK_PV_MFMA("%8", "%10", "%1")
-                 ISK_PV_MFMA("%7", "%9", "%2") ISK_PV_MFMA("%8", "%10", "%2") ISK_PV_OPERANDS);
+    asm volatile(ISK_PV_MFMA16 ISK_PV16_OPERANDS);
   }
-#undef ISK_PV_OPERANDS
+#undef ISK_PV16_OPERANDS
 }
 
-// Next-tile loads placed in the PV stream (pairs 0..8, one load each) when
+// Next-tile loads placed in the PV stream (one at each odd step 1..17) when
 // the next tile is a full dense tile.
 struct PvDma {
   const unsigned char* base;
@@ -257,31 +324,32 @@ struct PvDma {
   uint32_t p16, keys;   // LoadOffsets fields
 };
 
-template <int PI, bool kDmaOn>
-__device__ __forceinline__ void pv_do2(const uint32_t (&vaddr)[4], const bf16x8 (&pb)[2], const bf16x8 (&pl)[2],
-                                       const PvDma& dma) {
-  constexpr int ST = 2 * PI;
+template <int ST, bool kDmaOn>
+__device__ __forceinline__ void pv_do(const uint32_t (&pvaddr)[2], const f16x8 (&ph)[2], const PvDma& dma) {
   constexpr int j = ST / kDvTiles;
-  constexpr bool reads = ST + 4 < kPvSteps;
-  // reads issued after step ST+1's two: steps ST+2, ST+3 (those that exist)
-  wait_lgkm<2 * ((ST + 3 < kPvSteps ? ST + 3 : kPvSteps - 1) - ST - 1)>();
-  if constexpr (kDmaOn && PI < kLoadsPerWave) {
+  constexpr bool reads = ST + kVAhead < kPvSteps;
+  constexpr int PI = ST >> 1;
+  constexpr bool dma_here = (ST & 1) != 0 && PI < kLoadsPerWave;
+  // The read of step ST is done once only those of steps ST+1 .. ST+4 (the
+  // ones issued so far) are younger.
+  wait_lgkm<(ST + kVAhead - 1 < kPvSteps ? ST + kVAhead - 1 : kPvSteps - 1) - ST>();
+  if constexpr (kDmaOn && dma_here) {
     const uint32_t off = (dma.p16 + 4096u * PI) ^ (__builtin_amdgcn_ubfe(dma.keys, 3 * PI, 3) << 4);
-    pv_pair<ST, reads, true>(pb[j], pl[j], vaddr, off, dma.base, dma.m0 + (uint32_t)(kWaves * 1024 * PI));
+    pv_step<ST, reads, true>(ph[j], pvaddr, off, dma.base, dma.m0 + (uint32_t)(kWaves * 1024 * PI));
   } else {
-    pv_pair<ST, reads, false>(pb[j], pl[j], vaddr, 0u, dma.base, dma.m0);
+    pv_step<ST, reads, false>(ph[j], pvaddr, 0u, dma.base, dma.m0);
   }
 }
 
 template <int... ST>
-__device__ __forceinline__ void pv_issue_first(const uint32_t (&vaddr)[4], std::integer_sequence<int, ST...>) {
-  (v_issue<ST>(vaddr), ...);
+__device__ __forceinline__ void pv_issue_first(const uint32_t (&pvaddr)[2], std::integer_sequence<int, ST...>) {
+  (v_issue<ST>(pvaddr), ...);
 }
 
-template <bool kDmaOn, int... PI>
-__device__ __forceinline__ void pv_all(const uint32_t (&vaddr)[4], const bf16x8 (&pb)[2], const bf16x8 (&pl)[2],
-                                       const PvDma& dma, std::integer_sequence<int, PI...>) {
-  (pv_do2<PI, kDmaOn>(vaddr, pb, pl, dma), ...);
+template <bool kDmaOn, int... ST>
+__device__ __forceinline__ void pv_all(const uint32_t (&pvaddr)[2], const f16x8 (&ph)[2], const PvDma& dma,
+                                       std::integer_sequence<int, ST...>) {
+  (pv_do<ST, kDmaOn>(pvaddr, ph, dma), ...);
 }
 
 // K operand reads of S^T (k-step kk): lane (n, h) reads piece 2*kk + h of
@@ -292,13 +360,26 @@ __device__ __forceinline__ void k_issue(const uint32_t (&kaddr)[4]) {
                "n"(128 * (KK >> 2)));
 }
 
+// LDS operations younger than the S^T read of step KK when its MFMA waits:
+// the S^T reads issued after it and, with the conversion on, whatever the
+// hooks of steps KK-4 .. KK-1 issued (the read of step KK goes out right
+// before hook KK-4).
+template <bool kConv>
+constexpr int qk_younger(int kk) {
+  int n = (kk + kKDepth < kKSteps ? kk + kKDepth : kKSteps) - kk - 1;
+  if (kConv)
+    for (int h = kk - kKDepth; h < kk; ++h) n += h >= 0 ? cv_ops(h) : 0;
+  return n;
+}
+
 // s += K-slot * q[kk] (S^T in VGPRs, fp32).  The first step starts from 0;
 // the last one is followed by the wait states a vector-ALU read of its result
 // needs, inside the same asm so nothing can be scheduled in between.
-template <int KK, typename Hook>
+template <int KK, bool kConv, typename Hook>
 __device__ __forceinline__ void qk_do(const uint32_t (&kaddr)[4], const bf16x8 (&qr)[kKSteps], f32x16& s,
                                       Hook& hook) {
-  wait_lgkm<(KK + kKDepth < kKSteps ? KK + kKDepth : kKSteps) - KK - 1>();
+  static_assert(qk_younger<kConv>(KK) <= 15, "lgkmcnt field");
+  wait_lgkm<qk_younger<kConv>(KK)>();
   if constexpr (KK == 0) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, v[232+%2*4:235+%2*4], %1, 0"
                  : "=&v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
@@ -307,7 +388,7 @@ __device__ __forceinline__ void qk_do(const uint32_t (&kaddr)[4], const bf16x8 (
                  : "+v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
   } else {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, v[232+%2*4:235+%2*4], %1, %0\n\t"
-                 "s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15"
+                 "s_nop 7\n\ts_nop 7"
                  : "+v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
   }
   if constexpr (KK + kKDepth < kKSteps) k_issue<KK + kKDepth>(kaddr);
@@ -322,15 +403,16 @@ __device__ __forceinline__ void qk_issue_first(const uint32_t (&kaddr)[4], std::
   (k_issue<KK>(kaddr), ...);
 }
 
-template <typename Hook, int... KK>
+template <bool kConv, typename Hook, int... KK>
 __device__ __forceinline__ void qk_all(const uint32_t (&kaddr)[4], const bf16x8 (&qr)[kKSteps], f32x16& s,
                                        Hook& hook, std::integer_sequence<int, KK...>) {
-  (qk_do<KK>(kaddr, qr, s, hook), ...);
+  (qk_do<KK, kConv>(kaddr, qr, s, hook), ...);
 }
 
 // S^T of one tile (buffer at LDS address `tile`), with `hook` run in the
-// MFMA shadows.
-template <typename Hook>
+// MFMA shadows (kConv: the hook also issues the V conversion's LDS
+// operations, and the reads of fragments 0 and 1 were issued just before).
+template <bool kConv, typename Hook>
 __device__ __forceinline__ void qk_tile(uint32_t tile, uint32_t k_lane0, const bf16x8 (&qr)[kKSteps], f32x16& s,
                                         Hook& hook) {
   uint32_t kaddr[4];
@@ -339,7 +421,7 @@ __device__ __forceinline__ void qk_tile(uint32_t tile, uint32_t k_lane0, const b
   for (int m = 1; m < 4; ++m) kaddr[m] = kaddr[0] ^ (32u * m);
   __builtin_amdgcn_sched_barrier(0);
   qk_issue_first(kaddr, std::make_integer_sequence<int, kKDepth>{});
-  qk_all(kaddr, qr, s, hook, std::make_integer_sequence<int, kKSteps>{});
+  qk_all<kConv>(kaddr, qr, s, hook, std::make_integer_sequence<int, kKSteps>{});
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -475,9 +557,10 @@ struct Stager {
 template <bool kSparse>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(232)))
 mla_split_h32_kernel(MlaLaunch a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kBufs * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kBufs * kTileBytes + kVtBytes];
   ISK_LDS unsigned char* tiles = (ISK_LDS unsigned char*)lds_raw;
   const uint32_t tiles_u32 = (uint32_t)(uintptr_t)tiles;
+  const uint32_t vt_u32 = tiles_u32 + kBufs * kTileBytes;   // fp16 V^T of the current tile
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n32 = lane & 31, hh = lane >> 5, i16 = lane & 15, gp = (lane >> 4) & 1;
@@ -497,16 +580,20 @@ mla_split_h32_kernel(MlaLaunch a) {
   // Per-lane LDS byte offsets of the operand reads (compile-time parts at the use).
   //  K (A operand of S^T), k-step kk: tile row n32, piece 2*kk + hh
   //    -> k_lane[kk & 3] + 128*(kk >> 2).
-  //  V^T (A operand of O^T): v_lane[2*(dt&1) + u], see v_issue.
+  //  bf16 V^T fragment reads of the conversion: v_lane[2*(dt&1) + u], see
+  //    cv_issue.
   // For m = 0..3 both offsets differ only in address bits 5-6 (the row
   // offsets are multiples of 128 and a tile buffer starts at a multiple of
   // 1024), so only m = 0 is kept: offset[m] = offset[0] ^ (32*m).
-  uint32_t k_lane0, v_lane0;
+  //  fp16 V^T chunk (conversion store, PV read), k-step j:
+  //    vt_lane0 ^ (32*j) + 2048*dt.
+  uint32_t k_lane0, v_lane0, vt_lane0;
   {
     const int kh = key(n32);
     k_lane0 = kRowBytes * n32 + 16 * (hh ^ kh);
     const int hp = (i16 & 3) >> 1;
     v_lane0 = kRowBytes * (4 * hh + (i16 >> 2)) + 64 * (i16 >> 3) + 32 * gp + 16 * (hp ^ hh) + 8 * (i16 & 1);
+    vt_lane0 = 64 * n32 + 16 * (hh ^ ((n32 >> 2) & 3));
   }
   // Source offsets (within the tile's rows) of this lane's full-tile loads.
   LoadOffsets so;
@@ -545,7 +632,7 @@ mla_split_h32_kernel(MlaLaunch a) {
     acc_zero();
 
     const int n_tiles = (sg.end - sg.begin + kTok - 1) / kTok;
-    // Prologue: tiles 0..kBufs-2 in flight (loads for missing tiles come
+    // Prologue: tiles 0..2 in flight (loads for missing tiles come
     // from the zero block into unused buffers, so the count is always 27);
     // masks kept in a register ring.
     uint32_t mk[3];
@@ -580,40 +667,43 @@ mla_split_h32_kernel(MlaLaunch a) {
     f32x16 s_cur;
     {
       auto none = [](auto) {};
-      qk_tile(tiles_u32, k_lane0, qr, s_cur, none);
+      qk_tile<false>(tiles_u32, k_lane0, qr, s_cur, none);
     }
 
     // Tile loop, software-pipelined by one tile: step `it` computes S^T of
-    // tile it+1 and, in the shadows of those MFMAs, the softmax of tile it;
-    // then O^T += V^T P^T for tile it.  Buffers: it (PV), it+1 (S^T), it+2
-    // and it+3 (loads in flight).
+    // tile it+1 and, in the shadows of those MFMAs, the softmax of tile it
+    // and the fp16 V^T of tile it; then O^T += V^T P^T for tile it.  Row
+    // buffers: it (V^T source), it+1 (S^T), it+2 (loads in flight); once
+    // tile it is converted its buffer takes the loads of tile it+3.
+    int buf = 0;   // it % kBufs
     for (int it = 0; it < n_tiles; ++it) {
       const bool has_next = it + 1 < n_tiles;
       // Tile it+1 has landed once only the loads of tile it+2 (or of a zero
       // stand-in of the prologue) are younger; after the barrier every wave
-      // is also done with tile it-1, whose buffer the loads of tile it+3 reuse.
+      // is also done with the V^T buffer (PV of tile it-1).
       if (it + 2 < max(n_tiles, 3))
         wait_vmcnt<kLoadsPerWave>();
       else
         wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
+      const int buf1 = buf == kBufs - 1 ? 0 : buf + 1;   // (it + 1) % kBufs
       // Re-derive lane offsets inside the loop instead of keeping every
       // derived value live across it.
-      asm volatile("" : "+v"(so.p16), "+v"(so.keys), "+v"(k_lane0), "+v"(v_lane0));
+      asm volatile("" : "+v"(so.p16), "+v"(so.keys), "+v"(k_lane0), "+v"(v_lane0), "+v"(vt_lane0));
       const uint32_t mask = mk0;
       mk0 = mk1;
       mk1 = mk2;
-      // Loads of tile it+3: a full dense tile's 9 loads are spread over the
-      // PV MFMA stream below, other tiles are issued here.
-      ISK_LDS unsigned char* nbuf = tiles + ((it + 3) & 3) * kTileBytes;
+      // Plan of tile it+3, whose loads go into buffer `buf` once tile it is
+      // converted (after the second barrier below): a full dense tile's 9
+      // loads are spread over the PV MFMA stream, other tiles are issued
+      // right after that barrier.
+      ISK_LDS unsigned char* nbuf = tiles + buf * kTileBytes;
       DenseTile nt{nullptr, 0u};
       bool defer = false;
-      if (it + 3 < n_tiles) {
-        const int u0n = sg.begin + (it + 3) * kTok;
-        if constexpr (kSparse) {
-          mk2 = stage.issue_sparse(u0n, nbuf, wave_u, lane);
-        } else {
-          nt = stage.plan(u0n, pn, on, pfirst, pwin);
+      const bool load_next = it + 3 < n_tiles;
+      if (load_next) {
+        if constexpr (!kSparse) {
+          nt = stage.plan(sg.begin + (it + 3) * kTok, pn, on, pfirst, pwin);
           on += kTok;
           if (on >= a.page_size) {
             on -= a.page_size;
@@ -621,10 +711,8 @@ mla_split_h32_kernel(MlaLaunch a) {
           }
           mk2 = nt.mask;
           defer = nt.mask == ~0u;
-          if (!defer) stage.issue_masked(nt, nbuf, wave_u, lane, so);
         }
       }
-      const int buf = it & 3;
 
       // ---- online softmax of tile it; lane holds head n32, tokens
       // 8*(e>>2) + 4*hh + (e&3).  Masked scores become -inf first.
@@ -636,13 +724,13 @@ mla_split_h32_kernel(MlaLaunch a) {
       }
       float mx = -INFINITY, alpha = 1.f, m_sub = 0.f, psum = 0.f;
       bool rescale = false;
-      bf16x8 pb[2], pl[2];
+      f16x8 ph[2];
       // The softmax in slices, one per k-step of the next tile's S^T:
       //  0..3   max over the raw scores (with scale > 0, checked by the
       //         planner, the max of the scaled scores, rounding included)
       //  4      lane-pair max, lazy reference move, alpha
       //  5..20  p = 2^(s*scale - m), one score per slice
-      //  21..28 p -> bf16 hi + lo, one pair per slice; sum of the fp32 p
+      //  21..28 p -> fp16, one pair per slice; sum of the fp32 p
       //  29     running normaliser
       auto softmax = [&](auto kc) {
         constexpr int KK = decltype(kc)::value;
@@ -658,30 +746,52 @@ mla_split_h32_kernel(MlaLaunch a) {
           alpha = move ? fast_exp2(m_old - m_new) : 1.0f;   // m_old = -inf -> 0
           rescale = move && m_old != -INFINITY;             // acc is still 0 before the first move
           m_ref = m_new;
-          m_sub = m_new == -INFINITY ? 0.f : m_new;
+          m_sub = m_new == -INFINITY ? 0.f : m_new - kPShift;
         } else if constexpr (KK < 21) {
           constexpr int e = KK - 5;
           s_cur[e] = fast_exp2(__builtin_fmaf(s_cur[e], a.scale_log2, -m_sub));
         } else if constexpr (KK < 29) {
           constexpr int q = KK - 21, j = q >> 2, r = q & 3;
           const float p0 = s_cur[2 * q], p1 = s_cur[2 * q + 1];
-          const bf16x2 hi = to_bf16x2(p0, p1);
-          const bf16x2 lo = to_bf16x2(p0 - (float)hi[0], p1 - (float)hi[1]);
-          pb[j][2 * r] = hi[0];
-          pb[j][2 * r + 1] = hi[1];
-          pl[j][2 * r] = lo[0];
-          pl[j][2 * r + 1] = lo[1];
+          ph[j][2 * r] = (_Float16)p0;
+          ph[j][2 * r + 1] = (_Float16)p1;
           psum += p0;
           psum += p1;
         } else if constexpr (KK == 29) {
           l_run = l_run * alpha + psum;
         }
       };
+      // fp16 V^T of tile it: this wave's dim tiles 4w .. 4w+3.
+      uint32_t cvaddr[4];
+      cvaddr[0] = tiles_u32 + buf * kTileBytes + 256u * wave_u + v_lane0;
+#pragma unroll
+      for (int m = 1; m < 4; ++m) cvaddr[m] = cvaddr[0] ^ (32u * m);
+      const uint32_t wvt0 = vt_u32 + 8192u * wave_u + vt_lane0, wvt1 = wvt0 ^ 32u;
+      auto step_hook = [&](auto kc) {
+        softmax(kc);
+        constexpr int KK = decltype(kc)::value;
+        constexpr int f = cv_frag_at(KK);
+        if constexpr (f >= 0) {
+          cv_store<f>(wvt0, wvt1);
+          if constexpr (f + 2 < 8) cv_issue<f + 2>(cvaddr);
+        }
+      };
       f32x16 s_next;
       if (has_next) {
-        qk_tile(tiles_u32 + ((it + 1) & 3) * kTileBytes, k_lane0, qr, s_next, softmax);
+        __builtin_amdgcn_sched_barrier(0);
+        cv_issue<0>(cvaddr);
+        cv_issue<1>(cvaddr);
+        qk_tile<true>(tiles_u32 + buf1 * kTileBytes, k_lane0, qr, s_next, step_hook);
       } else {
         softmax_only(softmax, std::make_integer_sequence<int, kKSteps>{});
+        cv_issue<0>(cvaddr); wait_lgkm<0>(); cv_store<0>(wvt0, wvt1);
+        cv_issue<1>(cvaddr); wait_lgkm<0>(); cv_store<1>(wvt0, wvt1);
+        cv_issue<2>(cvaddr); wait_lgkm<0>(); cv_store<2>(wvt0, wvt1);
+        cv_issue<3>(cvaddr); wait_lgkm<0>(); cv_store<3>(wvt0, wvt1);
+        cv_issue<4>(cvaddr); wait_lgkm<0>(); cv_store<4>(wvt0, wvt1);
+        cv_issue<5>(cvaddr); wait_lgkm<0>(); cv_store<5>(wvt0, wvt1);
+        cv_issue<6>(cvaddr); wait_lgkm<0>(); cv_store<6>(wvt0, wvt1);
+        cv_issue<7>(cvaddr); wait_lgkm<0>(); cv_store<7>(wvt0, wvt1);
       }
       if (__ballot(rescale) != 0ull) {
         // Lanes that did not move have alpha == 1 exactly.
@@ -689,25 +799,35 @@ mla_split_h32_kernel(MlaLaunch a) {
         acc_scale_all(alpha, std::make_integer_sequence<int, kDvTiles>{});
         asm volatile("s_nop 4");
       }
+      // Every wave's share of the fp16 V^T is written, and every wave is
+      // done reading row buffer `buf`.
+      wait_lgkm<0>();
+      __builtin_amdgcn_s_barrier();
+      if (load_next) {
+        if constexpr (kSparse)
+          mk2 = stage.issue_sparse(sg.begin + (it + 3) * kTok, nbuf, wave_u, lane);
+        else if (!defer)
+          stage.issue_masked(nt, nbuf, wave_u, lane, so);
+      }
 
       // ---- O^T += V^T * P^T over 2 k-steps x 16 dim tiles
-      uint32_t vaddr[4];
-      vaddr[0] = tiles_u32 + buf * kTileBytes + v_lane0;
-#pragma unroll
-      for (int m = 1; m < 4; ++m) vaddr[m] = vaddr[0] ^ (32u * m);
+      uint32_t pvaddr[2];
+      pvaddr[0] = vt_u32 + vt_lane0;
+      pvaddr[1] = pvaddr[0] ^ 32u;
       __builtin_amdgcn_sched_barrier(0);
-      pv_issue_first(vaddr, std::make_integer_sequence<int, 4>{});
+      pv_issue_first(pvaddr, std::make_integer_sequence<int, kVAhead>{});
       // LDS address of this wave's first load of tile it+3 (wave-uniform).
-      const PvDma dma{nt.base, tiles_u32 + ((it + 3) & 3) * kTileBytes + wave_u * 1024, so.p16, so.keys};
+      const PvDma dma{nt.base, tiles_u32 + buf * kTileBytes + wave_u * 1024, so.p16, so.keys};
       if (defer)
-        pv_all<true>(vaddr, pb, pl, dma, std::make_integer_sequence<int, kPvSteps / 2>{});
+        pv_all<true>(pvaddr, ph, dma, std::make_integer_sequence<int, kPvSteps>{});
       else
-        pv_all<false>(vaddr, pb, pl, dma, std::make_integer_sequence<int, kPvSteps / 2>{});
+        pv_all<false>(pvaddr, ph, dma, std::make_integer_sequence<int, kPvSteps>{});
       __builtin_amdgcn_sched_barrier(0);
       s_cur = s_next;
+      buf = buf1;
     }
 
-    // ---- epilogue: o = acc / l, lse = ln 2 * (m_ref + log2 l)
+    // ---- epilogue: o = acc / l, lse = ln 2 * (m_ref - kPShift + log2 l)
     acc_settle();
     float l_tot;
     {
@@ -716,20 +836,24 @@ mla_split_h32_kernel(MlaLaunch a) {
     }
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : 1.f / l_tot;
-    const float lse_v = empty ? -INFINITY : (m_ref + fast_log2(l_tot)) * kLn2;
+    const float lse_v = empty ? -INFINITY : (m_ref - kPShift + fast_log2(l_tot)) * kLn2;
     // lane holds O^T[32*dt + 8*q + 4*hh + e][head], e = 0..3, at acc[dt][4q + e]
+    // (head re-read here so that its address arithmetic is not hoisted out
+    // of the segment loop and kept live across it).
+    int head_e = head;
+    asm volatile("" : "+v"(head_e));
     float* of32 = nullptr;
     uint16_t* obf = nullptr;
     if (sg.part >= 0) {
-      of32 = a.part_o + ((size_t)sg.part * a.hq + head) * kMlaDv + 4 * hh;
-      if (hh == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
+      of32 = a.part_o + ((size_t)sg.part * a.hq + head_e) * kMlaDv + 4 * hh;
+      if (hh == 0) a.part_lse[(size_t)sg.part * a.hq + head_e] = lse_v;
     } else {
-      const size_t ob = ((size_t)b * a.hq + head) * kMlaDv + 4 * hh;
+      const size_t ob = ((size_t)b * a.hq + head_e) * kMlaDv + 4 * hh;
       if (a.out_f32)
         of32 = (float*)a.out + ob;
       else
         obf = (uint16_t*)a.out + ob;
-      if (a.lse != nullptr && hh == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
+      if (a.lse != nullptr && hh == 0) a.lse[(size_t)b * a.hq + head_e] = lse_v;
     }
     auto store_tile = [&](int dt, const float (&o)[16]) {
 #pragma unroll
