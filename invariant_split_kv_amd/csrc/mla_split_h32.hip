@@ -4,17 +4,14 @@
 // Same job as the 16-head kernel in mla_split.hip: the split stage of the
 // split-KV scheme on the FlashMLA issue page "Sparse MLA decode is not
 // batch-invariant ..." (section "Where it comes from"), with split boundaries
-// from the host planner that depend only on the row's own length.  This
-// layout makes every 16-byte LDS operand read feed 32 heads instead of 16,
-// which halves the LDS traffic per MFMA:
+// from the host planner that depend only on the row's own length.
 //   * One workgroup = four waves (one per SIMD) = 128 heads of one split, so
-//     a KV tile is copied into LDS once per split.  Wave w owns heads
-//     [32w, 32w + 32) of its head block and keeps their whole 576-dim query
-//     slice in VGPRs (36 MFMA B operands).
+//     a KV tile is copied into LDS once per split.  For S^T, wave w owns
+//     heads [32w, 32w + 32) and keeps their whole 576-dim query slice in
+//     VGPRs (36 MFMA B operands); for PV it owns dims [128w, 128w + 128) of
+//     all 128 heads.
 //   * 32-token tiles (72 pieces of 16 B per token) are copied HBM -> LDS by
-//     16-byte direct loads into three row buffers (tile i converted, tile
-//     i+1 read by S^T, tile i+2 in flight; tile i+3's loads start once tile
-//     i is converted).  Piece c of tile row t sits
+//     16-byte direct loads, four tiles in flight.  Piece c of tile row t sits
 //     at LDS piece t*72 + (c ^ key(t)), key(t) = 4*((t>>1)&1) + ((t>>2)&3):
 //     the 16 rows of one K operand read and the 4-row x 32-byte blocks of a
 //     transposing V read land on distinct LDS banks.  Masked rows (past the
@@ -30,16 +27,15 @@
 //     reference by more than 2^8).  p is rounded to fp16 for the PV product
 //     (the 2^7 factor keeps p within fp16's normal range; it cancels in o =
 //     acc / l and is taken out of the LSE); the normaliser sums the fp32 p.
-//   * O^T (512 dims x 32 heads) += V^T * P^T with v_mfma_f32_32x32x16_f16.
-//     Once per tile and workgroup the V part of the tile is converted to an
-//     fp16 V^T buffer in LDS (each wave a quarter of the dims, in the
-//     shadows of the S^T MFMAs of the next tile); PV reads it back with one
-//     16-byte read per MFMA.  The output block of a wave is 256 fp32 values
-//     per lane and lives in AGPRs a0..a255 for the whole split, written only
-//     by the inline-asm MFMAs below (dim tile dt in a[16*dt .. 16*dt+15]);
-//     the compiler's own code uses VGPRs only (the file is built with MFMA
-//     results in VGPRs and no VGPR spills to AGPRs).  The LDS operands of
-//     both products and of the conversion pass through a fixed register ring
+//     Each wave's P and alphas go through LDS to the waves holding the dims.
+//   * O^T (128 dims x 128 heads per wave) += V^T * P^T with
+//     v_mfma_f32_32x32x16_f16.  Each wave converts the V^T fragments of its
+//     own dims from bf16 to fp16 in registers, once per tile, in the shadows
+//     of its MFMAs.  The output block of a wave is 256 fp32 values per lane
+//     and lives in AGPRs a0..a255 for the whole split, written only by the
+//     inline-asm MFMAs below; the compiler's own code uses VGPRs only (the
+//     file is built with MFMA results in VGPRs and no VGPR spills to AGPRs).
+//     The LDS operands of both products pass through a fixed register ring
 //     (v232..v255) written and read only by inline asm, with explicit lgkmcnt
 //     waits.
 // Every reduction order above is fixed by the segment's own token range, so
@@ -61,7 +57,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef const __attribute__((address_space(4))) int32_t* const_i32p;
 
 constexpr int kTok = 32;                                   // tokens per LDS tile
-constexpr int kBufs = 3;                                   // LDS row-tile buffers
+constexpr int kBufs = 4;                                   // LDS tile buffers (tiles in flight)
 constexpr int kWaves = 4;
 constexpr int kHeadsPerBlock = 32 * kWaves;                // 128
 constexpr int kPieces = kMlaDqk / 8;                       // 72 pieces of 16 B per latent row
@@ -138,9 +134,10 @@ __device__ __forceinline__ void acc_scale(float alpha) {
                : "v"(alpha), "n"(DT));
 }
 
-template <int... DT>
-__device__ __forceinline__ void acc_scale_all(float alpha, std::integer_sequence<int, DT...>) {
-  (acc_scale<DT>(alpha), ...);
+// acc[T] *= al[T & 3] (head tile ht = T & 3).
+template <int... T>
+__device__ __forceinline__ void acc_scale_heads(const float (&al)[4], std::integer_sequence<int, T...>) {
+  (acc_scale<T>(al[T & 3]), ...);
 }
 
 // Wait states between the last MFMA write of the accumulator and a
@@ -173,8 +170,8 @@ __device__ __forceinline__ void acc_read(float (&o)[16]) {
 // the compiler never sees these registers (the kernel caps its own
 // allocation at 232 VGPRs), so it can neither copy an operand before its wait
 // nor reuse the register while the read is outstanding.  S^T uses slots
-// 0..kKDepth-1 and the V conversion slots 4 and 5; O^T uses all six; the two
-// phases do not overlap.
+// 0..kKDepth-1 and, from hook 30 on, slots 4 and 5 for the first V^T
+// fragments; PV uses slots 0..2 for P and 3..5 for V^T.
 #define ISK_RING_VGPRS "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", \
                        "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", \
                        "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
@@ -192,128 +189,118 @@ __device__ __forceinline__ void wait_lgkm() {
 }
 
 // ---------------------------------------------------------------------------
-// V^T in fp16.  PV needs V^T fragments: for k-step j (tokens 16j .. 16j+15)
-// and dim tile dt, lane (n, h) holds dim 32*dt + n of the eight tokens
-// 16j + 8*(e>>2) + 4h + (e&3), e = 0..7, in that order (the order of P^T in
-// the B operand).  Each tile's V part is converted once per workgroup into
-// a separate buffer of 512 rows x 64 B (one row per dim, four 16-byte chunks
-// c = 2j + h per row), chunk c of dim d stored at d*64 + 16*(c ^ ((d>>2)&3)):
-// the 16 lanes of a quarter-wave then hit distinct bank groups both when a
-// fragment is written and when PV reads it back with one ds_read_b128.
-//
-// Conversion of fragment (dt, j) from the bf16 row tile: two transposing
-// reads give lane (i16, gp, h) four dims' worth of rows 16j + 8u + 4h +
-// (i16 >> 2), dims 32*dt + 16*gp + 4*(i16 & 3); the lane's byte offset is
-// vaddr[2*(dt&1) + u], the rest is the immediate.  The four dwords (two bf16
-// each) are converted to fp16 pairs in place and written out as one chunk.
-// bf16 values with magnitude in [2^-14, 65504] are exact in fp16; the
-// round-toward-zero conversion keeps larger ones finite (clamped to 65504)
-// and truncates smaller ones to fp16 subnormals.
-constexpr int kVtBytes = kMlaDv * 64;
+// PV, split by dims.  Wave w computes O^T for dims [128w, 128w + 128) of all
+// 128 heads of the block.  Accumulator tile T = 4*dt + ht (dt = local dim
+// tile 0..3, ht = head tile 0..3) holds, for lane (n, h), O^T[128w + 32dt +
+// 8q + 4h + e][32ht + n] at a[16T + 4q + e].  Step s = 8*dt + 4*j + ht:
+//   acc[T] += V^T(dim tile 4w + dt, k-step j) * P^T(k-step j, head tile ht),
+// v_mfma_f32_32x32x16_f16.  Lane (n, h) of either operand covers the eight
+// tokens 16j + 8*(e>>2) + 4h + (e&3), e = 0..7, the order in which the
+// softmax holds them.
+//  * P^T(j, ht) is the fp16 P that wave ht computed for its own heads; it is
+//    exchanged through LDS as pl[ht][j][lane] (16 bytes), written and read
+//    back by the same lane index, so a wave-wide access is one contiguous
+//    KiB.  P reads go to ring slot s % 3, three steps ahead of their MFMA.
+//  * V^T fragment vf = 2*dt + j comes from the bf16 row tile by two
+//    transposing reads: lane (i16, gp, h) gets four dims' worth of rows
+//    16j + 8u + 4h + (i16 >> 2), dims 32*dt' + 16*gp + 4*(i16 & 3) (dt' the
+//    tile's global dim tile), at vaddr[2*(dt'&1) + u] plus an immediate.
+//    The four dwords (two bf16 each) are converted to fp16 pairs in place,
+//    so each wave converts only the V it multiplies, once per tile.  bf16
+//    values with magnitude in [2^-14, 65504] are exact in fp16; the
+//    round-toward-zero conversion keeps larger ones finite (clamped to
+//    65504) and truncates smaller ones to fp16 subnormals.  Fragment vf
+//    lives in ring slot 5 - vf % 3.  Fragments 0 and 1 are read and
+//    converted in the S^T stream; fragment vf >= 2 is read after step
+//    4vf - 8 and converted one dword per step after steps 4vf-4 .. 4vf-1,
+//    three vector-ALU instructions in each MFMA's shadow.
+constexpr int kPBytes = kWaves * 2 * 1024;   // pl[4][2][64] x 16 B
+constexpr int kXBytes = 32 * 16;             // per-head floats [n][ht]: alpha, later l
 
-template <int DT, int J>
+template <int VF>
 struct VFrag {
-  static constexpr int off0 = kRowBytes * 16 * J + 128 * (DT >> 1);
-  static constexpr int off1 = kRowBytes * (16 * J + 8) + 128 * (DT >> 1);
-  static constexpr int m = 2 * (DT & 1);
+  static constexpr int dt = VF >> 1, j = VF & 1, slot = 5 - VF % 3;
+  static constexpr int off0 = kRowBytes * 16 * j + 128 * (dt >> 1);
+  static constexpr int off1 = kRowBytes * (16 * j + 8) + 128 * (dt >> 1);
+  static constexpr int m = 2 * (dt & 1);
 };
 
-// Wave w converts dim tiles 4w .. 4w+3: fragment f = (d = f >> 1, j = f & 1)
-// is dim tile 4w + d.  The wave's dim offset is folded into the base
-// addresses (cvaddr: +256*w in the row tile, wvt: +8192*w in V^T).
-template <int F>
-__device__ __forceinline__ void cv_issue(const uint32_t (&cvaddr)[4]) {
-  using V = VFrag<(F >> 1), (F & 1)>;
+// LDS operations of one tile's PV stream, in issue order: the alpha read and
+// the P reads of steps 0..2 before step 0; after the MFMA of step s the P
+// read of step s+3 and, every fourth step, the two reads of fragment s/4+2.
+constexpr int pv_ops_in_step(int s) { return (s + 3 < kPvSteps ? 1 : 0) + (s % 4 == 0 && s / 4 + 2 < 8 ? 2 : 0); }
+constexpr int pv_issued_before(int s) {   // operations issued before the MFMA of step s
+  int n = 4;
+  for (int u = 0; u < s; ++u) n += pv_ops_in_step(u);
+  return n;
+}
+constexpr int pv_idx_p(int t) { return t < 3 ? 1 + t : pv_issued_before(t - 3); }
+constexpr int pv_idx_v(int vf) {   // index of the second read of fragment vf >= 2
+  return pv_issued_before(4 * vf - 8) + (4 * vf - 8 + 3 < kPvSteps ? 1 : 0) + 1;
+}
+// Younger operations than the P read of step s when its MFMA waits.
+constexpr int pv_wait_p(int s) { return pv_issued_before(s) - pv_idx_p(s) - 1; }
+// Younger operations than fragment vf's reads when its conversion starts,
+// after the operations of step 4vf - 4.
+constexpr int pv_wait_v(int vf) { return pv_issued_before(4 * vf - 3) - pv_idx_v(vf) - 1; }
+
+template <int VF>
+__device__ __forceinline__ void v_issue(const uint32_t (&vaddr)[4]) {
+  using V = VFrag<VF>;
   asm volatile("ds_read_b64_tr_b16 v[232+%2*4:233+%2*4], %0 offset:%3\n\t"
-               "ds_read_b64_tr_b16 v[234+%2*4:235+%2*4], %1 offset:%4" ::"v"(cvaddr[V::m]),
-               "v"(cvaddr[V::m + 1]), "n"(4 + (F & 1)), "n"(V::off0), "n"(V::off1));
+               "ds_read_b64_tr_b16 v[234+%2*4:235+%2*4], %1 offset:%4" ::"v"(vaddr[V::m]),
+               "v"(vaddr[V::m + 1]), "n"(V::slot), "n"(V::off0), "n"(V::off1));
 }
 
 #define ISK_CV_DWORD(i)                                                                           \
   "v_lshlrev_b32 %0, 16, v[232+%2*4+" #i "]\n\tv_and_b32 %1, 0xffff0000, v[232+%2*4+" #i "]\n\t" \
   "v_cvt_pkrtz_f16_f32 v[232+%2*4+" #i "], %0, %1\n\t"
 
-// The reads of fragment F must have completed (counted by the caller's waits).
-template <int F>
-__device__ __forceinline__ void cv_store(uint32_t wvt0, uint32_t wvt1) {
+// Dword I of fragment VF to fp16.  Dword 0 first waits until at most N LDS
+// operations are outstanding (N < 0: no wait; N must cover only operations
+// younger than the fragment's reads); dword 3 ends with the wait states an
+// MFMA reading the converted registers right after needs.
+template <int VF, int I, int N>
+__device__ __forceinline__ void v_convert_dword() {
+  static_assert(N <= 15, "lgkmcnt field");
   float t0, t1;
-  asm volatile(ISK_CV_DWORD(0) ISK_CV_DWORD(1) ISK_CV_DWORD(2) ISK_CV_DWORD(3)
-               "ds_write_b128 %3, v[232+%2*4:235+%2*4] offset:%4"
-               : "=&v"(t0), "=&v"(t1)
-               : "n"(4 + (F & 1)), "v"((F & 1) ? wvt1 : wvt0), "n"(2048 * (F >> 1)));
+  if constexpr (N >= 0)
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\t" ISK_CV_DWORD(%4)
+                 : "=&v"(t0), "=&v"(t1) : "n"(VFrag<VF>::slot), "n"(N), "n"(I));
+  else if constexpr (I == 3)
+    asm volatile(ISK_CV_DWORD(%4) "s_nop 1"
+                 : "=&v"(t0), "=&v"(t1) : "n"(VFrag<VF>::slot), "n"(N), "n"(I));
+  else
+    asm volatile(ISK_CV_DWORD(%4)
+                 : "=&v"(t0), "=&v"(t1) : "n"(VFrag<VF>::slot), "n"(N), "n"(I));
 }
 
-// Conversion schedule inside the S^T stream of the next tile: fragments 0
-// and 1 are read before the first S^T read, fragment f is converted and
-// stored in the hook after S^T step kCvAt[f], followed by the reads of
-// fragment f+2 (same ring slot).  A read issued in hook h is complete once
-// the MFMA of step h+5 has waited, so kCvAt[f+2] >= kCvAt[f] + 5.
-constexpr int kCvAt[8] = {0, 1, 5, 6, 10, 11, 15, 16};
-constexpr int cv_frag_at(int kk) {
-  for (int f = 0; f < 8; ++f)
-    if (kCvAt[f] == kk) return f;
-  return -1;
-}
-// LDS operations a hook issues besides the S^T reads.
-constexpr int cv_ops(int kk) { return cv_frag_at(kk) < 0 ? 0 : cv_frag_at(kk) < 6 ? 3 : 1; }
-
-// ---------------------------------------------------------------------------
-// PV.  Step st = (k-step j = st / 16, dim tile dt = st % 16) reads its V^T
-// fragment into ring slot st % 6 (one ds_read_b128 at pvaddr[j] + 2048*dt);
-// the read is issued right after the MFMA of step st-5.
-constexpr int kVAhead = 5;   // V^T reads in flight, in steps
-static_assert(kVAhead < kRingSlots, "a step's slot must not be refilled before its MFMA");
-
-template <int ST>
-struct VStep {
-  static constexpr int j = ST / kDvTiles, dt = ST % kDvTiles, slot = ST % kRingSlots;
-};
-
-template <int ST>
-__device__ __forceinline__ void v_issue(const uint32_t (&pvaddr)[2]) {
-  using V = VStep<ST>;
-  asm volatile("ds_read_b128 v[232+%1*4:235+%1*4], %0 offset:%2" ::"v"(pvaddr[V::j]), "n"(V::slot),
-               "n"(2048 * V::dt));
+template <int S>
+__device__ __forceinline__ void p_issue(uint32_t paddr) {
+  constexpr int j = (S >> 2) & 1, ht = S & 3;
+  asm volatile("ds_read_b128 v[232+%1*4:235+%1*4], %0 offset:%2" ::"v"(paddr), "n"(S % 3), "n"(2048 * ht + 1024 * j));
 }
 
-// One PV step: acc[dt] += V^T(step ST) * P^T(k-step j), fp16 operands, fp32
-// accumulation.  After the MFMA go the V^T read of step ST+5 and,
-// optionally, one 16-byte global->LDS load of a later tile (pool offset
-// `doff` from SGPR base `dbase`, LDS address `dm0` in M0; the compiler's M0
-// is saved and restored, M0 being read when the load issues).  The leading
-// s_nop at the first step of each k-step covers a vector-ALU write of the P
-// operand right before it.
-#define ISK_PV_MFMA16 "v_mfma_f32_32x32x16_f16 a[%3*16:%3*16+15], v[232+%4*4:235+%4*4], %1, a[%3*16:%3*16+15]\n\t"
-#define ISK_PV_READ16 "ds_read_b128 v[232+%5*4:235+%5*4], %2 offset:%6\n\t"
-#define ISK_PV_DMA16 "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %9\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %8\n\ts_mov_b32 m0, %0\n\t"
+// One PV step: the MFMA of step S, then the P read of step S+3 and, every
+// fourth step, the reads of fragment S/4+2; optionally one 16-byte
+// global->LDS load of a later tile (pool offset `doff` from SGPR base
+// `dbase`, LDS address `dm0` in M0; the compiler's M0 is saved and
+// restored, M0 being read when the load issues).
+#define ISK_PV_MFMA "v_mfma_f32_32x32x16_f16 a[%2*16:%2*16+15], v[232+%3*4:235+%3*4], v[232+%4*4:235+%4*4], a[%2*16:%2*16+15]\n\t"
+#define ISK_PV_DMA "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %6\n\ts_mov_b32 m0, %0\n\t"
 
-template <int ST, bool kReads, bool kDma>
-__device__ __forceinline__ void pv_step(const f16x8& p, const uint32_t (&pvaddr)[2], uint32_t doff,
-                                        const unsigned char* dbase, uint32_t dm0) {
-  using A = VStep<ST>;
-  using R = VStep<(ST + kVAhead < kPvSteps ? ST + kVAhead : 0)>;
-  constexpr bool lead = A::dt == 0;
+template <int S, bool kDma>
+__device__ __forceinline__ void pv_step(uint32_t doff, const unsigned char* dbase, uint32_t dm0) {
+  constexpr int dt = S >> 3, ht = S & 3, vf = S >> 2;
   uint32_t saved;
-#define ISK_PV16_OPERANDS                                                                          \
-  : "=&s"(saved)                                                                                   \
-  : "v"(p), "v"(pvaddr[R::j]), "n"(A::dt), "n"(A::slot), "n"(R::slot), "n"(2048 * R::dt), "v"(doff), \
-    "s"(dbase), "s"(dm0)
-  if constexpr (lead && kReads && kDma) {
-    asm volatile("s_nop 1\n\t" ISK_PV_MFMA16 ISK_PV_READ16 ISK_PV_DMA16 ISK_PV16_OPERANDS);
-  } else if constexpr (lead && kReads) {
-    asm volatile("s_nop 1\n\t" ISK_PV_MFMA16 ISK_PV_READ16 ISK_PV16_OPERANDS);
-  } else if constexpr (lead) {
-    asm volatile("s_nop 1\n\t" ISK_PV_MFMA16 ISK_PV16_OPERANDS);
-  } else if constexpr (kReads && kDma) {
-    asm volatile(ISK_PV_MFMA16 ISK_PV_READ16 ISK_PV_DMA16 ISK_PV16_OPERANDS);
-  } else if constexpr (kReads) {
-    asm volatile(ISK_PV_MFMA16 ISK_PV_READ16 ISK_PV16_OPERANDS);
-  } else if constexpr (kDma) {
-    asm volatile(ISK_PV_MFMA16 ISK_PV_DMA16 ISK_PV16_OPERANDS);
-  } else {
-    asm volatile(ISK_PV_MFMA16 ISK_PV16_OPERANDS);
-  }
-#undef ISK_PV16_OPERANDS
+#define ISK_PV_OPERANDS                                                                                 \
+  : "=&s"(saved)                                                                                        \
+  : "n"(0), "n"(4 * dt + ht), "n"(VFrag<vf>::slot), "n"(S % 3), "v"(doff), "s"(dbase), "s"(dm0)
+  if constexpr (kDma)
+    asm volatile(ISK_PV_MFMA ISK_PV_DMA ISK_PV_OPERANDS);
+  else
+    asm volatile(ISK_PV_MFMA ISK_PV_OPERANDS);
+#undef ISK_PV_OPERANDS
 }
 
 // Next-tile loads placed in the PV stream (one at each odd step 1..17) when
@@ -324,33 +311,36 @@ struct PvDma {
   uint32_t p16, keys;   // LoadOffsets fields
 };
 
-template <int ST, bool kDmaOn>
-__device__ __forceinline__ void pv_do(const uint32_t (&pvaddr)[2], const f16x8 (&ph)[2], const PvDma& dma) {
-  constexpr int j = ST / kDvTiles;
-  constexpr bool reads = ST + kVAhead < kPvSteps;
-  constexpr int PI = ST >> 1;
-  constexpr bool dma_here = (ST & 1) != 0 && PI < kLoadsPerWave;
-  // The read of step ST is done once only those of steps ST+1 .. ST+4 (the
-  // ones issued so far) are younger.
-  wait_lgkm<(ST + kVAhead - 1 < kPvSteps ? ST + kVAhead - 1 : kPvSteps - 1) - ST>();
+template <int S, bool kDmaOn>
+__device__ __forceinline__ void pv_do(const uint32_t (&vaddr)[4], uint32_t paddr, const PvDma& dma) {
+  constexpr int PI = S >> 1;
+  constexpr bool dma_here = (S & 1) != 0 && PI < kLoadsPerWave;
+  static_assert(pv_wait_p(S) >= 0 && pv_wait_p(S) <= 15, "lgkmcnt field");
+  wait_lgkm<pv_wait_p(S)>();
   if constexpr (kDmaOn && dma_here) {
     const uint32_t off = (dma.p16 + 4096u * PI) ^ (__builtin_amdgcn_ubfe(dma.keys, 3 * PI, 3) << 4);
-    pv_step<ST, reads, true>(ph[j], pvaddr, off, dma.base, dma.m0 + (uint32_t)(kWaves * 1024 * PI));
+    pv_step<S, true>(off, dma.base, dma.m0 + (uint32_t)(kWaves * 1024 * PI));
   } else {
-    pv_step<ST, reads, false>(ph[j], pvaddr, 0u, dma.base, dma.m0);
+    pv_step<S, false>(0u, dma.base, dma.m0);
   }
+  if constexpr (S + 3 < kPvSteps) p_issue<S + 3>(paddr);
+  if constexpr (S % 4 == 0 && S / 4 + 2 < 8) v_issue<S / 4 + 2>(vaddr);
+  constexpr int cvf = S / 4 + 1, ci = S % 4;   // fragment converted in steps 4cvf-4 .. 4cvf-1
+  if constexpr (cvf >= 2 && cvf < 8) v_convert_dword<cvf, ci, ci == 0 ? pv_wait_v(cvf) : -1>();
 }
 
-template <int... ST>
-__device__ __forceinline__ void pv_issue_first(const uint32_t (&pvaddr)[2], std::integer_sequence<int, ST...>) {
-  (v_issue<ST>(pvaddr), ...);
+template <bool kDmaOn, int... S>
+__device__ __forceinline__ void pv_all(const uint32_t (&vaddr)[4], uint32_t paddr, const PvDma& dma,
+                                       std::integer_sequence<int, S...>) {
+  (pv_do<S, kDmaOn>(vaddr, paddr, dma), ...);
 }
 
-template <bool kDmaOn, int... ST>
-__device__ __forceinline__ void pv_all(const uint32_t (&pvaddr)[2], const f16x8 (&ph)[2], const PvDma& dma,
-                                       std::integer_sequence<int, ST...>) {
-  (pv_do<ST, kDmaOn>(pvaddr, ph, dma), ...);
-}
+// ---------------------------------------------------------------------------
+// LDS operations the softmax hooks put into the S^T stream of the next tile:
+// hook 4 writes this lane's alpha, hooks 12 and 13 read V^T fragments 0 and
+// 1 of the current tile, hook 29 writes the lane's two P fragments.  Hooks
+// 30..33 convert fragment 0 and hooks 32..35 fragment 1, a dword each.
+constexpr int hook_ops(int kk) { return kk == 4 ? 1 : kk == 12 || kk == 13 || kk == 29 ? 2 : 0; }
 
 // K operand reads of S^T (k-step kk): lane (n, h) reads piece 2*kk + h of
 // tile row n, at kaddr[kk & 3] + 128*(kk >> 2).
@@ -368,7 +358,7 @@ template <bool kConv>
 constexpr int qk_younger(int kk) {
   int n = (kk + kKDepth < kKSteps ? kk + kKDepth : kKSteps) - kk - 1;
   if (kConv)
-    for (int h = kk - kKDepth; h < kk; ++h) n += h >= 0 ? cv_ops(h) : 0;
+    for (int h = kk - kKDepth; h < kk; ++h) n += h >= 0 ? hook_ops(h) : 0;
   return n;
 }
 
@@ -410,8 +400,8 @@ __device__ __forceinline__ void qk_all(const uint32_t (&kaddr)[4], const bf16x8 
 }
 
 // S^T of one tile (buffer at LDS address `tile`), with `hook` run in the
-// MFMA shadows (kConv: the hook also issues the V conversion's LDS
-// operations, and the reads of fragments 0 and 1 were issued just before).
+// MFMA shadows (kConv: the hook also issues the LDS operations counted by
+// hook_ops).
 template <bool kConv, typename Hook>
 __device__ __forceinline__ void qk_tile(uint32_t tile, uint32_t k_lane0, const bf16x8 (&qr)[kKSteps], f32x16& s,
                                         Hook& hook) {
@@ -557,10 +547,11 @@ struct Stager {
 template <bool kSparse>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(232)))
 mla_split_h32_kernel(MlaLaunch a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kBufs * kTileBytes + kVtBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kBufs * kTileBytes + kPBytes + kXBytes];
   ISK_LDS unsigned char* tiles = (ISK_LDS unsigned char*)lds_raw;
   const uint32_t tiles_u32 = (uint32_t)(uintptr_t)tiles;
-  const uint32_t vt_u32 = tiles_u32 + kBufs * kTileBytes;   // fp16 V^T of the current tile
+  const uint32_t pl_u32 = tiles_u32 + kBufs * kTileBytes;   // fp16 P of the current tile, all heads
+  const uint32_t x_u32 = pl_u32 + kPBytes;                  // per-head alpha (per tile) or l (epilogue)
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n32 = lane & 31, hh = lane >> 5, i16 = lane & 15, gp = (lane >> 4) & 1;
@@ -580,20 +571,16 @@ mla_split_h32_kernel(MlaLaunch a) {
   // Per-lane LDS byte offsets of the operand reads (compile-time parts at the use).
   //  K (A operand of S^T), k-step kk: tile row n32, piece 2*kk + hh
   //    -> k_lane[kk & 3] + 128*(kk >> 2).
-  //  bf16 V^T fragment reads of the conversion: v_lane[2*(dt&1) + u], see
-  //    cv_issue.
+  //  V^T fragment (transposing reads): v_lane[2*(dt&1) + u], see VFrag.
   // For m = 0..3 both offsets differ only in address bits 5-6 (the row
   // offsets are multiples of 128 and a tile buffer starts at a multiple of
   // 1024), so only m = 0 is kept: offset[m] = offset[0] ^ (32*m).
-  //  fp16 V^T chunk (conversion store, PV read), k-step j:
-  //    vt_lane0 ^ (32*j) + 2048*dt.
-  uint32_t k_lane0, v_lane0, vt_lane0;
+  uint32_t k_lane0, v_lane0;
   {
     const int kh = key(n32);
     k_lane0 = kRowBytes * n32 + 16 * (hh ^ kh);
     const int hp = (i16 & 3) >> 1;
     v_lane0 = kRowBytes * (4 * hh + (i16 >> 2)) + 64 * (i16 >> 3) + 32 * gp + 16 * (hp ^ hh) + 8 * (i16 & 1);
-    vt_lane0 = 64 * n32 + 16 * (hh ^ ((n32 >> 2) & 3));
   }
   // Source offsets (within the tile's rows) of this lane's full-tile loads.
   LoadOffsets so;
@@ -671,39 +658,40 @@ mla_split_h32_kernel(MlaLaunch a) {
     }
 
     // Tile loop, software-pipelined by one tile: step `it` computes S^T of
-    // tile it+1 and, in the shadows of those MFMAs, the softmax of tile it
-    // and the fp16 V^T of tile it; then O^T += V^T P^T for tile it.  Row
-    // buffers: it (V^T source), it+1 (S^T), it+2 (loads in flight); once
-    // tile it is converted its buffer takes the loads of tile it+3.
-    int buf = 0;   // it % kBufs
+    // tile it+1 and, in the shadows of those MFMAs, the softmax of tile it,
+    // whose P (fp16) and alpha go to LDS for the other waves; after a barrier
+    // every wave adds V^T * P^T of tile it for its 128 dims and all heads.
+    // Buffers: it (PV), it+1 (S^T), it+2 and it+3 (loads in flight).
+    const uint32_t pw = pl_u32 + 2048u * wave_u + 16u * lane;   // this lane's P fragments
+    const uint32_t xw = x_u32 + 16u * n32 + 4u * wave_u;        // this head's alpha / l slot
     for (int it = 0; it < n_tiles; ++it) {
       const bool has_next = it + 1 < n_tiles;
       // Tile it+1 has landed once only the loads of tile it+2 (or of a zero
       // stand-in of the prologue) are younger; after the barrier every wave
-      // is also done with the V^T buffer (PV of tile it-1).
+      // is also done with tile it-1, whose buffer the loads of tile it+3
+      // reuse, and with the P and alpha of tile it-1.
       if (it + 2 < max(n_tiles, 3))
         wait_vmcnt<kLoadsPerWave>();
       else
         wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      const int buf1 = buf == kBufs - 1 ? 0 : buf + 1;   // (it + 1) % kBufs
       // Re-derive lane offsets inside the loop instead of keeping every
       // derived value live across it.
-      asm volatile("" : "+v"(so.p16), "+v"(so.keys), "+v"(k_lane0), "+v"(v_lane0), "+v"(vt_lane0));
+      asm volatile("" : "+v"(so.p16), "+v"(so.keys), "+v"(k_lane0), "+v"(v_lane0));
       const uint32_t mask = mk0;
       mk0 = mk1;
       mk1 = mk2;
-      // Plan of tile it+3, whose loads go into buffer `buf` once tile it is
-      // converted (after the second barrier below): a full dense tile's 9
-      // loads are spread over the PV MFMA stream, other tiles are issued
-      // right after that barrier.
-      ISK_LDS unsigned char* nbuf = tiles + buf * kTileBytes;
+      // Loads of tile it+3: a full dense tile's 9 loads are spread over the
+      // PV MFMA stream below, other tiles are issued here.
+      ISK_LDS unsigned char* nbuf = tiles + ((it + 3) & 3) * kTileBytes;
       DenseTile nt{nullptr, 0u};
       bool defer = false;
-      const bool load_next = it + 3 < n_tiles;
-      if (load_next) {
-        if constexpr (!kSparse) {
-          nt = stage.plan(sg.begin + (it + 3) * kTok, pn, on, pfirst, pwin);
+      if (it + 3 < n_tiles) {
+        const int u0n = sg.begin + (it + 3) * kTok;
+        if constexpr (kSparse) {
+          mk2 = stage.issue_sparse(u0n, nbuf, wave_u, lane);
+        } else {
+          nt = stage.plan(u0n, pn, on, pfirst, pwin);
           on += kTok;
           if (on >= a.page_size) {
             on -= a.page_size;
@@ -711,8 +699,10 @@ mla_split_h32_kernel(MlaLaunch a) {
           }
           mk2 = nt.mask;
           defer = nt.mask == ~0u;
+          if (!defer) stage.issue_masked(nt, nbuf, wave_u, lane, so);
         }
       }
+      const int buf = it & 3;
 
       // ---- online softmax of tile it; lane holds head n32, tokens
       // 8*(e>>2) + 4*hh + (e&3).  Masked scores become -inf first.
@@ -723,15 +713,21 @@ mla_split_h32_kernel(MlaLaunch a) {
           s_cur[e] = __builtin_amdgcn_ubfe(mh, 8 * (e >> 2) + (e & 3), 1) ? s_cur[e] : -INFINITY;
       }
       float mx = -INFINITY, alpha = 1.f, m_sub = 0.f, psum = 0.f;
-      bool rescale = false;
       f16x8 ph[2];
+      // V^T fragments of tile it for this wave's dims (dim tiles 4w ..).
+      uint32_t vaddr[4];
+      vaddr[0] = tiles_u32 + buf * kTileBytes + 256u * wave_u + v_lane0;
+#pragma unroll
+      for (int m = 1; m < 4; ++m) vaddr[m] = vaddr[0] ^ (32u * m);
       // The softmax in slices, one per k-step of the next tile's S^T:
       //  0..3   max over the raw scores (with scale > 0, checked by the
       //         planner, the max of the scaled scores, rounding included)
-      //  4      lane-pair max, lazy reference move, alpha
-      //  5..20  p = 2^(s*scale - m), one score per slice
+      //  4      lane-pair max, lazy reference move, alpha (to LDS)
+      //  5..20  p = 2^(s*scale - m + 7), one score per slice
+      //  12, 13 reads of V^T fragments 0 and 1
       //  21..28 p -> fp16, one pair per slice; sum of the fp32 p
-      //  29     running normaliser
+      //  29     running normaliser; P to LDS
+      //  30..35 conversion of fragments 0 (30..33) and 1 (32..35)
       auto softmax = [&](auto kc) {
         constexpr int KK = decltype(kc)::value;
         if constexpr (KK < 4) {
@@ -743,10 +739,12 @@ mla_split_h32_kernel(MlaLaunch a) {
           const float m_old = m_ref;
           const bool move = mx > m_old + kRescaleThreshold || (m_old == -INFINITY && mx > -INFINITY);
           const float m_new = move ? mx : m_old;
-          alpha = move ? fast_exp2(m_old - m_new) : 1.0f;   // m_old = -inf -> 0
-          rescale = move && m_old != -INFINITY;             // acc is still 0 before the first move
+          // acc is still 0 before the first move: no rescale then.
+          alpha = move && m_old != -INFINITY ? fast_exp2(m_old - m_new) : 1.0f;
           m_ref = m_new;
           m_sub = m_new == -INFINITY ? 0.f : m_new - kPShift;
+          // Both lanes of a head write the same value.
+          asm volatile("ds_write_b32 %0, %1" ::"v"(xw), "v"(alpha));
         } else if constexpr (KK < 21) {
           constexpr int e = KK - 5;
           s_cur[e] = fast_exp2(__builtin_fmaf(s_cur[e], a.scale_log2, -m_sub));
@@ -759,113 +757,118 @@ mla_split_h32_kernel(MlaLaunch a) {
           psum += p1;
         } else if constexpr (KK == 29) {
           l_run = l_run * alpha + psum;
+          asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024" ::"v"(pw), "v"(ph[0]), "v"(ph[1]));
         }
-      };
-      // fp16 V^T of tile it: this wave's dim tiles 4w .. 4w+3.
-      uint32_t cvaddr[4];
-      cvaddr[0] = tiles_u32 + buf * kTileBytes + 256u * wave_u + v_lane0;
-#pragma unroll
-      for (int m = 1; m < 4; ++m) cvaddr[m] = cvaddr[0] ^ (32u * m);
-      const uint32_t wvt0 = vt_u32 + 8192u * wave_u + vt_lane0, wvt1 = wvt0 ^ 32u;
-      auto step_hook = [&](auto kc) {
-        softmax(kc);
-        constexpr int KK = decltype(kc)::value;
-        constexpr int f = cv_frag_at(KK);
-        if constexpr (f >= 0) {
-          cv_store<f>(wvt0, wvt1);
-          if constexpr (f + 2 < 8) cv_issue<f + 2>(cvaddr);
-        }
+        if constexpr (KK == 12) v_issue<0>(vaddr);
+        if constexpr (KK == 13) v_issue<1>(vaddr);
+        // The reads of hooks 12 and 13 are complete once the MFMA of step 18
+        // has waited; without an S^T stream (last tile) hook 30 waits itself.
+        if constexpr (KK == 30)
+          if (!has_next) wait_lgkm<0>();
+        if constexpr (KK >= 30 && KK <= 33) v_convert_dword<0, KK - 30, -1>();
+        if constexpr (KK >= 32 && KK <= 35) v_convert_dword<1, KK - 32, -1>();
       };
       f32x16 s_next;
-      if (has_next) {
-        __builtin_amdgcn_sched_barrier(0);
-        cv_issue<0>(cvaddr);
-        cv_issue<1>(cvaddr);
-        qk_tile<true>(tiles_u32 + buf1 * kTileBytes, k_lane0, qr, s_next, step_hook);
-      } else {
+      if (has_next)
+        qk_tile<true>(tiles_u32 + ((it + 1) & 3) * kTileBytes, k_lane0, qr, s_next, softmax);
+      else
         softmax_only(softmax, std::make_integer_sequence<int, kKSteps>{});
-        cv_issue<0>(cvaddr); wait_lgkm<0>(); cv_store<0>(wvt0, wvt1);
-        cv_issue<1>(cvaddr); wait_lgkm<0>(); cv_store<1>(wvt0, wvt1);
-        cv_issue<2>(cvaddr); wait_lgkm<0>(); cv_store<2>(wvt0, wvt1);
-        cv_issue<3>(cvaddr); wait_lgkm<0>(); cv_store<3>(wvt0, wvt1);
-        cv_issue<4>(cvaddr); wait_lgkm<0>(); cv_store<4>(wvt0, wvt1);
-        cv_issue<5>(cvaddr); wait_lgkm<0>(); cv_store<5>(wvt0, wvt1);
-        cv_issue<6>(cvaddr); wait_lgkm<0>(); cv_store<6>(wvt0, wvt1);
-        cv_issue<7>(cvaddr); wait_lgkm<0>(); cv_store<7>(wvt0, wvt1);
-      }
-      if (__ballot(rescale) != 0ull) {
-        // Lanes that did not move have alpha == 1 exactly.
-        acc_settle();
-        acc_scale_all(alpha, std::make_integer_sequence<int, kDvTiles>{});
-        asm volatile("s_nop 4");
-      }
-      // Every wave's share of the fp16 V^T is written, and every wave is
-      // done reading row buffer `buf`.
+      // Every wave's P and alpha of tile it are in LDS.
       wait_lgkm<0>();
       __builtin_amdgcn_s_barrier();
-      if (load_next) {
-        if constexpr (kSparse)
-          mk2 = stage.issue_sparse(sg.begin + (it + 3) * kTok, nbuf, wave_u, lane);
-        else if (!defer)
-          stage.issue_masked(nt, nbuf, wave_u, lane, so);
-      }
 
-      // ---- O^T += V^T * P^T over 2 k-steps x 16 dim tiles
-      uint32_t pvaddr[2];
-      pvaddr[0] = vt_u32 + vt_lane0;
-      pvaddr[1] = pvaddr[0] ^ 32u;
+      // ---- O^T += V^T * P^T for this wave's dims and all heads.  The alpha
+      // of the four heads this lane accumulates comes first; the accumulator
+      // is rescaled when any of them moved (lanes that did not move have
+      // alpha == 1 exactly).
+      const uint32_t pr = pl_u32 + 16u * lane;
+      float al[4];
       __builtin_amdgcn_sched_barrier(0);
-      pv_issue_first(pvaddr, std::make_integer_sequence<int, kVAhead>{});
+      // The alphas land in ring slot 3 (V^T fragment 2 is read into it only
+      // after the first MFMA), the first P reads in slots 0..2.
+      static_assert(VFrag<2>::slot == 3, "alpha slot");
+      asm volatile("ds_read_b128 v[244:247], %0" ::"v"(x_u32 + 16u * n32));
+      p_issue<0>(pr);
+      p_issue<1>(pr);
+      p_issue<2>(pr);
+      asm volatile("s_waitcnt lgkmcnt(3)\n\tv_mov_b32 %0, v244\n\tv_mov_b32 %1, v245\n\tv_mov_b32 %2, v246\n\tv_mov_b32 %3, v247"
+                   : "=v"(al[0]), "=v"(al[1]), "=v"(al[2]), "=v"(al[3]));
+      __builtin_amdgcn_sched_barrier(0);
+      if (__ballot(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) != 0ull) {
+        acc_settle();
+        acc_scale_heads(al, std::make_integer_sequence<int, 16>{});
+        asm volatile("s_nop 4");
+      }
       // LDS address of this wave's first load of tile it+3 (wave-uniform).
-      const PvDma dma{nt.base, tiles_u32 + buf * kTileBytes + wave_u * 1024, so.p16, so.keys};
+      const PvDma dma{nt.base, tiles_u32 + ((it + 3) & 3) * kTileBytes + wave_u * 1024, so.p16, so.keys};
+      __builtin_amdgcn_sched_barrier(0);
       if (defer)
-        pv_all<true>(pvaddr, ph, dma, std::make_integer_sequence<int, kPvSteps>{});
+        pv_all<true>(vaddr, pr, dma, std::make_integer_sequence<int, kPvSteps>{});
       else
-        pv_all<false>(pvaddr, ph, dma, std::make_integer_sequence<int, kPvSteps>{});
+        pv_all<false>(vaddr, pr, dma, std::make_integer_sequence<int, kPvSteps>{});
       __builtin_amdgcn_sched_barrier(0);
       s_cur = s_next;
-      buf = buf1;
     }
 
-    // ---- epilogue: o = acc / l, lse = ln 2 * (m_ref - kPShift + log2 l)
-    acc_settle();
+    // ---- epilogue: o = acc / l, lse = ln 2 * (m_ref - kPShift + log2 l).
+    // Each head's l goes through LDS to the waves holding its dims.
     float l_tot;
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
       l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
     const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : 1.f / l_tot;
     const float lse_v = empty ? -INFINITY : (m_ref - kPShift + fast_log2(l_tot)) * kLn2;
-    // lane holds O^T[32*dt + 8*q + 4*hh + e][head], e = 0..3, at acc[dt][4q + e]
-    // (head re-read here so that its address arithmetic is not hoisted out
-    // of the segment loop and kept live across it).
+    __builtin_amdgcn_s_barrier();   // every wave is done with the last alphas
+    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(xw), "v"(l_tot) : "memory");
+    __builtin_amdgcn_s_barrier();
+    float inv[4];
+    {
+      float l4[4];
+      asm volatile("ds_read_b128 v[232:235], %4\n\ts_waitcnt lgkmcnt(0)\n\tv_mov_b32 %0, v232\n\tv_mov_b32 %1, v233\n\t"
+                   "v_mov_b32 %2, v234\n\tv_mov_b32 %3, v235"
+                   : "=v"(l4[0]), "=v"(l4[1]), "=v"(l4[2]), "=v"(l4[3])
+                   : "v"(x_u32 + 16u * n32));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) inv[t] = l4[t] > 0.f ? 1.f / l4[t] : 0.f;
+    }
+    acc_settle();
+    // lane holds O^T[128w + 32*dt + 8*q + 4*hh + e][32*ht + n32] at
+    // acc[4*dt + ht][4q + e] (row and wave re-read here so that their address
+    // arithmetic is not hoisted out of the segment loop and kept live
+    // across it).
     int head_e = head;
     asm volatile("" : "+v"(head_e));
     float* of32 = nullptr;
     uint16_t* obf = nullptr;
-    if (sg.part >= 0) {
-      of32 = a.part_o + ((size_t)sg.part * a.hq + head_e) * kMlaDv + 4 * hh;
-      if (hh == 0) a.part_lse[(size_t)sg.part * a.hq + head_e] = lse_v;
-    } else {
-      const size_t ob = ((size_t)b * a.hq + head_e) * kMlaDv + 4 * hh;
-      if (a.out_f32)
-        of32 = (float*)a.out + ob;
-      else
-        obf = (uint16_t*)a.out + ob;
-      if (a.lse != nullptr && hh == 0) a.lse[(size_t)b * a.hq + head_e] = lse_v;
+    {
+      const size_t hb0 = (size_t)(hb * kHeadsPerBlock + n32);   // head of tile ht = 0
+      const size_t base = (sg.part >= 0 ? (size_t)sg.part : (size_t)b) * a.hq + hb0;
+      const size_t eo = base * kMlaDv + 128 * (size_t)wave_u + 4 * hh;
+      if (sg.part >= 0) {
+        of32 = a.part_o + eo;
+        if (hh == 0) a.part_lse[(size_t)sg.part * a.hq + head_e] = lse_v;
+      } else {
+        if (a.out_f32)
+          of32 = (float*)a.out + eo;
+        else
+          obf = (uint16_t*)a.out + eo;
+        if (a.lse != nullptr && hh == 0) a.lse[(size_t)b * a.hq + head_e] = lse_v;
+      }
     }
-    auto store_tile = [&](int dt, const float (&o)[16]) {
+    auto store_tile = [&](int t, const float (&o)[16]) {
+      const int dt = t >> 2, ht = t & 3;
+      const size_t off = (size_t)ht * 32 * kMlaDv + 32 * dt;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4 r = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]} * inv;
+        const f32x4 r = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]} * inv[ht];
         if (of32 != nullptr) {
-          *(f32x4*)(of32 + 32 * dt + 8 * q) = r;
+          *(f32x4*)(of32 + off + 8 * q) = r;
         } else {
           uint2 w;
           w.x = pack_bf16x2(r[0], r[1]);
           w.y = pack_bf16x2(r[2], r[3]);
-          *(uint2*)(obf + 32 * dt + 8 * q) = w;
+          *(uint2*)(obf + off + 8 * q) = w;
         }
       }
     };
