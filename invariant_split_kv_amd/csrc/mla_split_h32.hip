@@ -51,10 +51,6 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-// Read-only view of the block table: loads through the constant address
-// space become scalar loads (counted by lgkmcnt, not by the vector-memory
-// counter that the tile waits count).
-typedef const __attribute__((address_space(4))) int32_t* const_i32p;
 
 constexpr int kTok = 32;                                   // tokens per LDS tile
 constexpr int kBufs = 4;                                   // LDS tile buffers (tiles in flight)
@@ -471,12 +467,12 @@ struct Stager {
 
   // Dense: tiles start at multiples of 32 and pages hold a multiple of 64
   // tokens, so a tile is one contiguous run of rows inside one page.  The
-  // block-table entries of the segment's first 64 pages sit in `pwin` (lane
-  // i holds entry pfirst + i); later pages are read from the table.
+  // block-table entries of pages pbase .. pbase+63 sit in `pwin` (lane i
+  // holds entry pbase + i); the caller keeps pi - pbase in [0, 64).
   // (pi, off) = (u0 / page_size, u0 % page_size).
-  __device__ __forceinline__ DenseTile plan(int u0, int pi, int off, int pfirst, int pwin) const {
+  __device__ __forceinline__ DenseTile plan(int u0, int pi, int off, int pbase, int pwin) const {
     const int nvalid = min(kTok, seg_end - u0);
-    const int pg = pi - pfirst < 64 ? __builtin_amdgcn_readlane(pwin, pi - pfirst) : ((const_i32p)bt_row)[pi];
+    const int pg = __builtin_amdgcn_readlane(pwin, pi - pbase);
     const bool page_ok = pg >= 0 && pg < num_pages;
     DenseTile t;
     t.mask = !page_ok ? 0u : (nvalid >= kTok ? ~0u : ((1u << nvalid) - 1u));
@@ -527,11 +523,11 @@ struct Stager {
 
   // Whole tile at once; returns the row-valid mask.
   __device__ __forceinline__ uint32_t operator()(int u0, ISK_LDS unsigned char* buf, int wave, int lane,
-                                                 const LoadOffsets& so, int pfirst, int pwin) const {
+                                                 const LoadOffsets& so, int pbase, int pwin) const {
     if constexpr (kSparse) {
       return issue_sparse(u0, buf, wave, lane);
     } else {
-      const DenseTile t = plan(u0, u0 / page_size, u0 % page_size, pfirst, pwin);
+      const DenseTile t = plan(u0, u0 / page_size, u0 % page_size, pbase, pwin);
       if (t.mask == ~0u) {
 #pragma unroll
         for (int jj = 0; jj < kLoadsPerWave; ++jj)
@@ -598,13 +594,15 @@ mla_split_h32_kernel(MlaLaunch a) {
     __builtin_amdgcn_s_barrier();
 
     // Block-table window of the segment (dense): lane i holds the entry of
-    // page pfirst + i (-1 past the row's pages).
-    const int pfirst = sg.begin / a.page_size;
+    // page pbase + i (-1 past the segment's pages); moved on by 64 pages
+    // when the next tile to plan leaves it.
+    int pbase = sg.begin / a.page_size;
     int pwin = -1;
-    if constexpr (!kSparse) {
-      const int pl = pfirst + lane;
-      if ((long long)pl * a.page_size < (long long)sg.end) pwin = stage.bt_row[pl];
-    }
+    auto load_window = [&]() {
+      const int pl = pbase + lane;
+      pwin = (long long)pl * a.page_size < (long long)sg.end ? stage.bt_row[pl] : -1;
+    };
+    if constexpr (!kSparse) load_window();
     // Query slice: lane (n32, hh) holds q[head][16*kk + 8*hh + 0..7].
     bf16x8 qr[kKSteps];
     {
@@ -627,7 +625,7 @@ mla_split_h32_kernel(MlaLaunch a) {
     for (int t = 0; t < 3; ++t) {
       ISK_LDS unsigned char* tb = tiles + t * kTileBytes;
       if (t < n_tiles) {
-        mk[t] = stage(sg.begin + t * kTok, tb, wave_u, lane, so, pfirst, pwin);
+        mk[t] = stage(sg.begin + t * kTok, tb, wave_u, lane, so, pbase, pwin);
       } else {
         mk[t] = 0u;
         stage.issue_masked(DenseTile{(const unsigned char*)a.kv, 0u}, tb, wave_u, lane, so);
@@ -681,8 +679,9 @@ mla_split_h32_kernel(MlaLaunch a) {
       const uint32_t mask = mk0;
       mk0 = mk1;
       mk1 = mk2;
-      // Loads of tile it+3: a full dense tile's 9 loads are spread over the
-      // PV MFMA stream below, other tiles are issued here.
+      // Loads of tile it+3 (buffer free since the barrier): a full dense
+      // tile's 9 loads are spread over the PV MFMA stream below, other tiles
+      // are issued here.
       ISK_LDS unsigned char* nbuf = tiles + ((it + 3) & 3) * kTileBytes;
       DenseTile nt{nullptr, 0u};
       bool defer = false;
@@ -691,7 +690,15 @@ mla_split_h32_kernel(MlaLaunch a) {
         if constexpr (kSparse) {
           mk2 = stage.issue_sparse(u0n, nbuf, wave_u, lane);
         } else {
-          nt = stage.plan(u0n, pn, on, pfirst, pwin);
+          if (pn - pbase >= 64) {   // every 64 pages: the next window
+            pbase = pn;
+            load_window();
+            // Waited for here, so that no other path into the plan below
+            // carries a wait for it (the compiler would otherwise wait for
+            // every outstanding tile load at each step).
+            asm volatile("" ::"v"(pwin));
+          }
+          nt = stage.plan(u0n, pn, on, pbase, pwin);
           on += kTok;
           if (on >= a.page_size) {
             on -= a.page_size;
