@@ -10,9 +10,13 @@
 // count (no per-count code variants, no atomics):
 //   m = max_i lse_i;  e_i = 2^((lse_i - m) * log2 e);  S = sum_i e_i;
 //   lse = m + ln S;   out = sum_i (e_i / S) * o_i   (fp32 FMA chain, i ascending)
-// One wave handles one (row, head); lane l owns Dv/64 consecutive dims.
+// One wave handles one (row, head); lane l owns Dv/64 consecutive dims.  The
+// LSEs are loaded lane-parallel and the partials four at a time, so a row
+// costs a few memory round trips instead of one per split.
 // Rows with one split were written by the split kernel and are skipped; rows
 // with none get out = 0 and lse = -inf.
+
+#include <utility>
 
 #include "device.hpp"
 #include "isk_internal.hpp"
@@ -20,6 +24,26 @@
 namespace isk {
 namespace {
 
+template <int DPL>
+__device__ __forceinline__ void load_part(const float* src, float (&v)[DPL]) {
+  if constexpr (DPL % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < DPL; j += 4) {
+      const f32x4 x = *(const f32x4*)(src + j);
+      v[j] = x[0]; v[j + 1] = x[1]; v[j + 2] = x[2]; v[j + 3] = x[3];
+    }
+  } else if constexpr (DPL == 2) {
+    const f32x2 x = *(const f32x2*)src;
+    v[0] = x[0]; v[1] = x[1];
+  } else {
+    v[0] = src[0];
+  }
+}
+
+// The partials' LSEs are loaded lane-parallel (lane l of chunk c holds split
+// 64c + l); the sum of the weights and the output FMA chain still run over
+// the splits one at a time in ascending order (v_readlane of the lane that
+// holds split i), so every value is the one the sequential definition gives.
 template <int DPL>
 __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
   const int lane = threadIdx.x & 63;
@@ -36,47 +60,56 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
 
   if (ri.n_parts > 1) {
     const float* lse_p = a.part_lse + (size_t)ri.part_off * a.hq + h;
+    const int n = ri.n_parts;
+    // m = max_i lse_i (exact, any order).
     float m = -INFINITY;
-    for (int i = 0; i < ri.n_parts; ++i) m = fmaxf(m, lse_p[(size_t)i * a.hq]);
+    for (int c = 0; c < n; c += 64) {
+      const float x = c + lane < n ? lse_p[(size_t)(c + lane) * a.hq] : -INFINITY;
+      float w = x;
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) w = fmaxf(w, __shfl_xor(w, d, 64));
+      m = fmaxf(m, w);
+    }
     if (m != -INFINITY) {
+      // S = sum_i 2^((lse_i - m) log2 e), i ascending.
       float ssum = 0.f;
-      for (int i = 0; i < ri.n_parts; ++i) ssum += fast_exp2((lse_p[(size_t)i * a.hq] - m) * kLog2e);
+      for (int c = 0; c < n; c += 64) {
+        const float x = c + lane < n ? lse_p[(size_t)(c + lane) * a.hq] : -INFINITY;
+        const float e = fast_exp2((x - m) * kLog2e);
+        const int cn = min(64, n - c);
+        for (int i = 0; i < cn; ++i) ssum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), i));
+      }
       const float inv = 1.f / ssum;
       lse_out = m + fast_log2(ssum) * kLn2;
       const float* op = a.part_o + ((size_t)ri.part_off * a.hq + h) * a.dv + DPL * lane;
       const size_t stride = (size_t)a.hq * a.dv;
-      auto load = [&](int i, float (&v)[DPL]) {
-        const float* src = op + (size_t)i * stride;
-        if constexpr (DPL % 4 == 0) {
+      // out = sum_i (e_i / S) o_i, an FMA chain with i ascending; the
+      // partials' loads go out four at a time.
+      for (int c = 0; c < n; c += 64) {
+        const float x = c + lane < n ? lse_p[(size_t)(c + lane) * a.hq] : -INFINITY;
+        const float wl = fast_exp2((x - m) * kLog2e) * inv;
+        const int cn = min(64, n - c);
+        // Loads of a group go out together, then its FMAs in order.
+        auto group = [&](int i0, auto kn) {
+          constexpr int K = decltype(kn)::value;
+          float v[K][DPL];
 #pragma unroll
-          for (int j = 0; j < DPL; j += 4) {
-            const f32x4 x = *(const f32x4*)(src + j);
-            v[j] = x[0]; v[j + 1] = x[1]; v[j + 2] = x[2]; v[j + 3] = x[3];
+          for (int k = 0; k < K; ++k) load_part<DPL>(op + (size_t)(c + i0 + k) * stride, v[k]);
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i0 + k));
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) o[j] = fmaf(w, v[k][j], o[j]);
           }
-        } else if constexpr (DPL == 2) {
-          const f32x2 x = *(const f32x2*)src;
-          v[0] = x[0]; v[1] = x[1];
-        } else {
-          v[0] = src[0];
+        };
+        int i = 0;
+        for (; i + 4 <= cn; i += 4) group(i, std::integral_constant<int, 4>{});
+        switch (cn - i) {
+          case 3: group(i, std::integral_constant<int, 3>{}); break;
+          case 2: group(i, std::integral_constant<int, 2>{}); break;
+          case 1: group(i, std::integral_constant<int, 1>{}); break;
+          default: break;
         }
-      };
-      auto accumulate = [&](int i, const float (&v)[DPL]) {
-        const float w = fast_exp2((lse_p[(size_t)i * a.hq] - m) * kLog2e) * inv;
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) o[j] = fmaf(w, v[j], o[j]);
-      };
-      // Four partials' loads in flight at a time; the accumulation order is
-      // still i = 0, 1, 2, ... for every split count.
-      int i = 0;
-      for (; i + 4 <= ri.n_parts; i += 4) {
-        float v0[DPL], v1[DPL], v2[DPL], v3[DPL];
-        load(i, v0); load(i + 1, v1); load(i + 2, v2); load(i + 3, v3);
-        accumulate(i, v0); accumulate(i + 1, v1); accumulate(i + 2, v2); accumulate(i + 3, v3);
-      }
-      for (; i < ri.n_parts; ++i) {
-        float v0[DPL];
-        load(i, v0);
-        accumulate(i, v0);
       }
     }
   }
