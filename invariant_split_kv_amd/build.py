@@ -34,16 +34,17 @@ EXTRA_FLAGS = {
 }
 
 # Sources whose inline asm owns registers the compiler must never touch: all
-# AGPRs (the output accumulator) and v232..v255 (the LDS operand ring).
+# AGPRs (the output accumulator), v231 (an asm scratch register) and
+# v232..v255 (the LDS operand ring).
 ASM_OWNED = ["mla_split_h32.hip"]
 
 
 def check_register_ownership(asm_text: str) -> list:
     """Instructions outside inline-asm blocks that name an AGPR or one of
-    v232..v255 (must be none)."""
+    v231..v255 (must be none)."""
     bad, in_asm = [], False
     agpr = re.compile(r"(?<![\w.])a(\d+|\[)")
-    ring = re.compile(r"(?<![\w.])v(23[2-9]|24\d|25[0-5])\b")
+    ring = re.compile(r"(?<![\w.])v(23[1-9]|24\d|25[0-5])\b")
     rng = re.compile(r"v\[(\d+):(\d+)\]")
     for n, line in enumerate(asm_text.splitlines(), 1):
         s = line.strip()
@@ -55,7 +56,7 @@ def check_register_ownership(asm_text: str) -> list:
             parts = s.split(";")[0].split(None, 1)
             if len(parts) == 2:
                 ops = parts[1]
-                if agpr.search(ops) or ring.search(ops) or any(int(m.group(2)) >= 232 for m in rng.finditer(ops)):
+                if agpr.search(ops) or ring.search(ops) or any(int(m.group(2)) >= 231 for m in rng.finditer(ops)):
                     bad.append((n, s))
     return bad
 

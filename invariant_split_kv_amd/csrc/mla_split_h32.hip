@@ -37,7 +37,7 @@
 //     file is built with MFMA results in VGPRs and no VGPR spills to AGPRs).
 //     The LDS operands of both products pass through a fixed register ring
 //     (v232..v255) written and read only by inline asm, with explicit lgkmcnt
-//     waits.
+//     waits; v231 is the inline asm's own scratch register.
 // Every reduction order above is fixed by the segment's own token range, so
 // the bits of a segment's result do not depend on anything else in the batch.
 
@@ -164,8 +164,11 @@ __device__ __forceinline__ void acc_read(float (&o)[16]) {
 // Operand ring.  LDS reads in flight land in v232..v255 (six 4-register
 // slots; slot i = v[232+4i .. 235+4i]) and the MFMAs read them there by name:
 // the compiler never sees these registers (the kernel caps its own
-// allocation at 232 VGPRs), so it can neither copy an operand before its wait
-// nor reuse the register while the read is outstanding.  S^T uses slots
+// allocation at 231 VGPRs), so it can neither copy an operand before its wait
+// nor reuse the register while the read is outstanding.  v231, also outside
+// the compiler's allocation, is scratch for single asm statements: no
+// compiler-visible temporaries pass between consecutive statements, which
+// would make the compiler put a wait state between them.  S^T uses slots
 // 0..kKDepth-1 and, from hook 30 on, slots 4 and 5 for the first V^T
 // fragments; PV uses slots 0..2 for P and 3..5 for V^T.
 #define ISK_RING_VGPRS "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", \
@@ -248,27 +251,28 @@ __device__ __forceinline__ void v_issue(const uint32_t (&vaddr)[4]) {
                "v"(vaddr[V::m + 1]), "n"(V::slot), "n"(V::off0), "n"(V::off1));
 }
 
-#define ISK_CV_DWORD(i)                                                                           \
-  "v_lshlrev_b32 %0, 16, v[232+%2*4+" #i "]\n\tv_and_b32 %1, 0xffff0000, v[232+%2*4+" #i "]\n\t" \
-  "v_cvt_pkrtz_f16_f32 v[232+%2*4+" #i "], %0, %1\n\t"
+// bf16 pair -> fp16 pair in place: the high value as fp32 goes to the
+// scratch register v231, the low one is shifted up in place.
+#define ISK_CV_DWORD(i)                                                                       \
+  "v_and_b32 v231, 0xffff0000, v[232+%0*4+" #i "]\n\t"                                       \
+  "v_lshlrev_b32 v[232+%0*4+" #i "], 16, v[232+%0*4+" #i "]\n\t"                             \
+  "v_cvt_pkrtz_f16_f32 v[232+%0*4+" #i "], v[232+%0*4+" #i "], v231\n\t"
 
 // Dword I of fragment VF to fp16.  Dword 0 first waits until at most N LDS
 // operations are outstanding (N < 0: no wait; N must cover only operations
-// younger than the fragment's reads); dword 3 ends with the wait states an
-// MFMA reading the converted registers right after needs.
-template <int VF, int I, int N>
+// younger than the fragment's reads).  With kNext, dword 3 is followed by
+// the MFMA of the next PV step, which reads the fragment: a vector-ALU write
+// must be two wait states ahead of an MFMA read of the register, and that
+// step's lgkmcnt wait is the second.
+template <int VF, int I, int N, bool kNext = false>
 __device__ __forceinline__ void v_convert_dword() {
   static_assert(N <= 15, "lgkmcnt field");
-  float t0, t1;
   if constexpr (N >= 0)
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\t" ISK_CV_DWORD(%4)
-                 : "=&v"(t0), "=&v"(t1) : "n"(VFrag<VF>::slot), "n"(N), "n"(I));
-  else if constexpr (I == 3)
-    asm volatile(ISK_CV_DWORD(%4) "s_nop 1"
-                 : "=&v"(t0), "=&v"(t1) : "n"(VFrag<VF>::slot), "n"(N), "n"(I));
+    asm volatile("s_waitcnt lgkmcnt(%1)\n\t" ISK_CV_DWORD(%2) ::"n"(VFrag<VF>::slot), "n"(N), "n"(I));
+  else if constexpr (I == 3 && kNext)
+    asm volatile(ISK_CV_DWORD(%2) "s_nop 0" ::"n"(VFrag<VF>::slot), "n"(N), "n"(I));
   else
-    asm volatile(ISK_CV_DWORD(%4)
-                 : "=&v"(t0), "=&v"(t1) : "n"(VFrag<VF>::slot), "n"(N), "n"(I));
+    asm volatile(ISK_CV_DWORD(%2) ::"n"(VFrag<VF>::slot), "n"(N), "n"(I));
 }
 
 template <int S>
@@ -278,34 +282,61 @@ __device__ __forceinline__ void p_issue(uint32_t paddr) {
 }
 
 // One PV step: the MFMA of step S, then the P read of step S+3 and, every
-// fourth step, the reads of fragment S/4+2; optionally one 16-byte
-// global->LDS load of a later tile (pool offset `doff` from SGPR base
-// `dbase`, LDS address `dm0` in M0; the compiler's M0 is saved and
-// restored, M0 being read when the load issues).
-#define ISK_PV_MFMA "v_mfma_f32_32x32x16_f16 a[%2*16:%2*16+15], v[232+%3*4:235+%3*4], v[232+%4*4:235+%4*4], a[%2*16:%2*16+15]\n\t"
-#define ISK_PV_DMA "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %6\n\ts_mov_b32 m0, %0\n\t"
+// fourth step, the reads of fragment S/4+2; at odd steps 1..17, when the
+// next tile is a full dense tile, also load S/2 of that tile (16 bytes per
+// lane from `base`, into LDS at the wave's M0 base + 4096 * load).
+#define ISK_PV_MFMA "v_mfma_f32_32x32x16_f16 a[%[T]*16:%[T]*16+15], v[232+%[VS]*4:235+%[VS]*4], v[232+%[PS]*4:235+%[PS]*4], a[%[T]*16:%[T]*16+15]\n\t"
 
-template <int S, bool kDma>
-__device__ __forceinline__ void pv_step(uint32_t doff, const unsigned char* dbase, uint32_t dm0) {
+template <int S>
+__device__ __forceinline__ void pv_step() {
   constexpr int dt = S >> 3, ht = S & 3, vf = S >> 2;
-  uint32_t saved;
-#define ISK_PV_OPERANDS                                                                                 \
-  : "=&s"(saved)                                                                                        \
-  : "n"(0), "n"(4 * dt + ht), "n"(VFrag<vf>::slot), "n"(S % 3), "v"(doff), "s"(dbase), "s"(dm0)
-  if constexpr (kDma)
-    asm volatile(ISK_PV_MFMA ISK_PV_DMA ISK_PV_OPERANDS);
-  else
-    asm volatile(ISK_PV_MFMA ISK_PV_OPERANDS);
-#undef ISK_PV_OPERANDS
+  asm volatile(ISK_PV_MFMA ::[T] "n"(4 * dt + ht), [VS] "n"(VFrag<vf>::slot), [PS] "n"(S % 3));
 }
 
-// Next-tile loads placed in the PV stream (one at each odd step 1..17) when
-// the next tile is a full dense tile.
+// Next-tile loads placed in the PV stream.  The stream sets M0 freely: the
+// caller saves the compiler's M0 before the stream and restores it after.
 struct PvDma {
   const unsigned char* base;
   uint32_t m0;          // LDS address of this wave's load 0
   uint32_t p16, keys;   // LoadOffsets fields
 };
+
+// MFMA of step S and load PI.  The lane's source offset
+// (p16 ^ (key_PI << 4)) + 4096*PI (key_PI in bits [3PI, 3PI+3) of `keys`;
+// p16 < 4096, so this equals (p16 + 4096*PI) ^ (key_PI << 4)) is formed in
+// the scratch register v231 after the M0 write, so that its vector-ALU
+// instructions also cover the wait state the load needs after that write.
+template <int S, int PI>
+__device__ __forceinline__ void pv_step_dma(const PvDma& d) {
+  constexpr int dt = S >> 3, ht = S & 3, vf = S >> 2;
+  constexpr int sh = 3 * PI - 4;   // right shift taking key_PI to bits 4..6
+#define ISK_PV_DMA_OPS                                                                                   \
+  ::[T] "n"(4 * dt + ht), [VS] "n"(VFrag<vf>::slot), [PS] "n"(S % 3),                                  \
+    [m0] "s"(d.m0 + (uint32_t)(kWaves * 1024 * PI)), [pio] "n"(4096 * PI), [sh] "n"(sh < 0 ? -sh : sh),  \
+    [p16] "v"(d.p16), [keys] "v"(d.keys), [msk] "s"(0x70u), [base] "s"(d.base)
+  // bitop3 0x6c: (src0 & src2) ^ src1.
+  if constexpr (PI == 0)
+    asm volatile(ISK_PV_MFMA
+                 "s_mov_b32 m0, %[m0]\n\t"
+                 "v_lshlrev_b32 v231, %[sh], %[keys]\n\t"
+                 "v_bitop3_b32 v231, v231, %[p16], %[msk] bitop3:0x6c\n\t"
+                 "global_load_lds_dwordx4 v231, %[base]" ISK_PV_DMA_OPS);
+  else if constexpr (sh < 0)
+    asm volatile(ISK_PV_MFMA
+                 "s_mov_b32 m0, %[m0]\n\t"
+                 "v_lshlrev_b32 v231, %[sh], %[keys]\n\t"
+                 "v_bitop3_b32 v231, v231, %[p16], %[msk] bitop3:0x6c\n\t"
+                 "v_add_u32 v231, %[pio], v231\n\t"
+                 "global_load_lds_dwordx4 v231, %[base]" ISK_PV_DMA_OPS);
+  else
+    asm volatile(ISK_PV_MFMA
+                 "s_mov_b32 m0, %[m0]\n\t"
+                 "v_lshrrev_b32 v231, %[sh], %[keys]\n\t"
+                 "v_bitop3_b32 v231, v231, %[p16], %[msk] bitop3:0x6c\n\t"
+                 "v_add_u32 v231, %[pio], v231\n\t"
+                 "global_load_lds_dwordx4 v231, %[base]" ISK_PV_DMA_OPS);
+#undef ISK_PV_DMA_OPS
+}
 
 template <int S, bool kDmaOn>
 __device__ __forceinline__ void pv_do(const uint32_t (&vaddr)[4], uint32_t paddr, const PvDma& dma) {
@@ -313,22 +344,23 @@ __device__ __forceinline__ void pv_do(const uint32_t (&vaddr)[4], uint32_t paddr
   constexpr bool dma_here = (S & 1) != 0 && PI < kLoadsPerWave;
   static_assert(pv_wait_p(S) >= 0 && pv_wait_p(S) <= 15, "lgkmcnt field");
   wait_lgkm<pv_wait_p(S)>();
-  if constexpr (kDmaOn && dma_here) {
-    const uint32_t off = (dma.p16 + 4096u * PI) ^ (__builtin_amdgcn_ubfe(dma.keys, 3 * PI, 3) << 4);
-    pv_step<S, true>(off, dma.base, dma.m0 + (uint32_t)(kWaves * 1024 * PI));
-  } else {
-    pv_step<S, false>(0u, dma.base, dma.m0);
-  }
+  if constexpr (kDmaOn && dma_here)
+    pv_step_dma<S, PI>(dma);
+  else
+    pv_step<S>();
   if constexpr (S + 3 < kPvSteps) p_issue<S + 3>(paddr);
   if constexpr (S % 4 == 0 && S / 4 + 2 < 8) v_issue<S / 4 + 2>(vaddr);
   constexpr int cvf = S / 4 + 1, ci = S % 4;   // fragment converted in steps 4cvf-4 .. 4cvf-1
-  if constexpr (cvf >= 2 && cvf < 8) v_convert_dword<cvf, ci, ci == 0 ? pv_wait_v(cvf) : -1>();
+  if constexpr (cvf >= 2 && cvf < 8) v_convert_dword<cvf, ci, ci == 0 ? pv_wait_v(cvf) : -1, true>();
 }
 
 template <bool kDmaOn, int... S>
 __device__ __forceinline__ void pv_all(const uint32_t (&vaddr)[4], uint32_t paddr, const PvDma& dma,
                                        std::integer_sequence<int, S...>) {
+  uint32_t saved_m0;
+  if constexpr (kDmaOn) asm volatile("s_mov_b32 %0, m0" : "=s"(saved_m0));
   (pv_do<S, kDmaOn>(vaddr, paddr, dma), ...);
+  if constexpr (kDmaOn) asm volatile("s_mov_b32 m0, %0" ::"s"(saved_m0));
 }
 
 // ---------------------------------------------------------------------------
@@ -541,7 +573,7 @@ struct Stager {
 };
 
 template <bool kSparse>
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(232)))
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(231)))
 mla_split_h32_kernel(MlaLaunch a) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kBufs * kTileBytes + kPBytes + kXBytes];
   ISK_LDS unsigned char* tiles = (ISK_LDS unsigned char*)lds_raw;
