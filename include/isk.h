@@ -86,6 +86,7 @@ typedef struct isk_desc {
   int32_t head_dim_v;        /* GQA: equal to head_dim_qk.  MLA: 512                  */
   int32_t page_size;         /* tokens per KV page (dense MLA: a multiple of 64)      */
   int32_t num_pages;         /* pages in the pool; block-table entries must be below  */
+                             /* it.  MLA: num_pages * page_size below 2^31            */
   int32_t max_pages_per_row; /* row stride of block_table                             */
   int32_t topk_width;        /* 0: dense.  >0 (MLA only): row stride of topk_idx      */
   int32_t split_mode;        /* isk_split_mode                                        */

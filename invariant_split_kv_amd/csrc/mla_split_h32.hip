@@ -390,9 +390,12 @@ constexpr int qk_younger(int kk) {
   return n;
 }
 
-// s += K-slot * q[kk] (S^T in VGPRs, fp32).  The first step starts from 0;
-// the last one is followed by the wait states a vector-ALU read of its result
-// needs, inside the same asm so nothing can be scheduled in between.
+// s += K-slot * q[kk] (S^T in VGPRs, fp32).  The first step starts from 0.
+// Without kConv (the S^T of a segment's first tile) the last step is followed
+// by the wait states a vector-ALU read of its result needs, inside the same
+// asm so nothing can be scheduled in between.  In the tile loop (kConv) the
+// result is first read in the next loop step, after the whole PV stream, so
+// no wait states are added there.
 template <int KK, bool kConv, typename Hook>
 __device__ __forceinline__ void qk_do(const uint32_t (&kaddr)[4], const bf16x8 (&qr)[kKSteps], f32x16& s,
                                       Hook& hook) {
@@ -402,6 +405,9 @@ __device__ __forceinline__ void qk_do(const uint32_t (&kaddr)[4], const bf16x8 (
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, v[232+%2*4:235+%2*4], %1, 0"
                  : "=&v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
   } else if constexpr (KK + 1 < kKSteps) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, v[232+%2*4:235+%2*4], %1, %0"
+                 : "+v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
+  } else if constexpr (kConv) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, v[232+%2*4:235+%2*4], %1, %0"
                  : "+v"(s) : "v"(qr[KK]), "n"(KK % kKDepth));
   } else {
@@ -711,36 +717,31 @@ mla_split_h32_kernel(MlaLaunch a) {
       const uint32_t mask = mk0;
       mk0 = mk1;
       mk1 = mk2;
-      // Loads of tile it+3 (buffer free since the barrier): a full dense
-      // tile's 9 loads are spread over the PV MFMA stream below, other tiles
-      // are issued here.
+      // Loads of tile it+3 (buffer free since the barrier).  Sparse tiles
+      // are issued here.  A dense tile is planned in the hooks of S^T steps
+      // 6..11 below (scalar work in MFMA shadows); a full one's 9 loads are
+      // then spread over the PV MFMA stream, a partial or masked one's are
+      // issued right after the S^T stream.
       ISK_LDS unsigned char* nbuf = tiles + ((it + 3) & 3) * kTileBytes;
-      DenseTile nt{nullptr, 0u};
-      bool defer = false;
-      if (it + 3 < n_tiles) {
-        const int u0n = sg.begin + (it + 3) * kTok;
+      const bool stage_on = it + 3 < n_tiles;
+      const int u0n = sg.begin + (it + 3) * kTok;
+      if (stage_on) {
         if constexpr (kSparse) {
           mk2 = stage.issue_sparse(u0n, nbuf, wave_u, lane);
-        } else {
-          if (pn - pbase >= 64) {   // every 64 pages: the next window
-            pbase = pn;
-            load_window();
-            // Waited for here, so that no other path into the plan below
-            // carries a wait for it (the compiler would otherwise wait for
-            // every outstanding tile load at each step).
-            asm volatile("" ::"v"(pwin));
-          }
-          nt = stage.plan(u0n, pn, on, pbase, pwin);
-          on += kTok;
-          if (on >= a.page_size) {
-            on -= a.page_size;
-            ++pn;
-          }
-          mk2 = nt.mask;
-          defer = nt.mask == ~0u;
-          if (!defer) stage.issue_masked(nt, nbuf, wave_u, lane, so);
+        } else if (pn - pbase >= 64) {   // every 64 pages: the next window
+          pbase = pn;
+          load_window();
+          // Waited for here, so that no other path into the plan below
+          // carries a wait for it (the compiler would otherwise wait for
+          // every outstanding tile load at each step).
+          asm volatile("" ::"v"(pwin));
         }
       }
+      // Dense plan of tile it+3 (page entry, row mask, first pool row); the
+      // page cursor (pn, on) advances by one tile every step.
+      int pg_n = 0, row_n = 0;
+      uint32_t mask_n = 0u;
+      const unsigned char* base_n = nullptr;
       const int buf = it & 3;
 
       // ---- online softmax of tile it; lane holds head n32, tokens
@@ -763,6 +764,7 @@ mla_split_h32_kernel(MlaLaunch a) {
       //         planner, the max of the scaled scores, rounding included)
       //  4      lane-pair max, lazy reference move, alpha (to LDS)
       //  5..20  p = 2^(s*scale - m + 7), one score per slice
+      //  6..11  (dense) scalar plan of tile it+3
       //  12, 13 reads of V^T fragments 0 and 1
       //  21..28 p -> fp16, one pair per slice; sum of the fp32 p
       //  29     running normaliser; P to LDS
@@ -798,6 +800,34 @@ mla_split_h32_kernel(MlaLaunch a) {
           l_run = l_run * alpha + psum;
           asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024" ::"v"(pw), "v"(ph[0]), "v"(ph[1]));
         }
+        if constexpr (!kSparse) {
+          // Each piece is pinned to its hook by an empty asm use of its result.
+          if constexpr (KK == 6) {
+            pg_n = __builtin_amdgcn_readlane(pwin, pn - pbase);
+            asm volatile("" ::"s"(pg_n));
+          } else if constexpr (KK == 7) {
+            // page entry outside the pool: the whole tile is masked
+            pg_n = pg_n >= 0 && pg_n < a.num_pages ? pg_n : -1;
+            asm volatile("" ::"s"(pg_n));
+          } else if constexpr (KK == 8) {
+            const int nvalid = min(kTok, sg.end - u0n);
+            mask_n = pg_n < 0 ? 0u : (nvalid >= kTok ? ~0u : ((1u << nvalid) - 1u));
+            asm volatile("" ::"s"(mask_n));
+          } else if constexpr (KK == 9) {
+            row_n = max(pg_n, 0) * a.page_size + on;
+            asm volatile("" ::"s"(row_n));
+          } else if constexpr (KK == 10) {
+            base_n = (const unsigned char*)a.kv + (size_t)(uint32_t)row_n * kRowBytes;
+            asm volatile("" ::"s"(base_n));
+          } else if constexpr (KK == 11) {
+            on += kTok;
+            if (on >= a.page_size) {
+              on -= a.page_size;
+              ++pn;
+            }
+            asm volatile("" ::"s"(on), "s"(pn));
+          }
+        }
         if constexpr (KK == 12) v_issue<0>(vaddr);
         if constexpr (KK == 13) v_issue<1>(vaddr);
         // The reads of hooks 12 and 13 are complete once the MFMA of step 18
@@ -812,6 +842,14 @@ mla_split_h32_kernel(MlaLaunch a) {
         qk_tile<true>(tiles_u32 + ((it + 1) & 3) * kTileBytes, k_lane0, qr, s_next, softmax);
       else
         softmax_only(softmax, std::make_integer_sequence<int, kKSteps>{});
+      bool defer = false;
+      if constexpr (!kSparse) {
+        if (stage_on) {
+          mk2 = mask_n;
+          defer = mask_n == ~0u;
+          if (!defer) stage.issue_masked(DenseTile{base_n, mask_n}, nbuf, wave_u, lane, so);
+        }
+      }
       // Every wave's P and alpha of tile it are in LDS.
       wait_lgkm<0>();
       __builtin_amdgcn_s_barrier();
@@ -839,7 +877,7 @@ mla_split_h32_kernel(MlaLaunch a) {
         asm volatile("s_nop 4");
       }
       // LDS address of this wave's first load of tile it+3 (wave-uniform).
-      const PvDma dma{nt.base, tiles_u32 + ((it + 3) & 3) * kTileBytes + wave_u * 1024, so.p16, so.keys};
+      const PvDma dma{base_n, tiles_u32 + ((it + 3) & 3) * kTileBytes + wave_u * 1024, so.p16, so.keys};
       __builtin_amdgcn_sched_barrier(0);
       if (defer)
         pv_all<true>(vaddr, pr, dma, std::make_integer_sequence<int, kPvSteps>{});

@@ -75,6 +75,9 @@ static std::string check_desc(const isk_desc& d, int* status) {
     if (d.num_q_heads % 16 != 0 || (d.num_q_heads > 64 && d.num_q_heads % 64 != 0))
       return fail(status, ISK_ERR_UNSUPPORTED, "MLA num_q_heads must be a multiple of 16 (and of 64 above 64)");
     if (d.topk_width == 0 && d.page_size % 64 != 0) return fail(status, ISK_ERR_UNSUPPORTED, "dense MLA needs page_size a multiple of 64");
+    // The MLA kernels index pool rows (token slots) with 32-bit arithmetic.
+    if ((long long)d.num_pages * d.page_size > 0x7fffffffLL)
+      return fail(status, ISK_ERR_UNSUPPORTED, "MLA pools are limited to 2^31 - 1 token rows (num_pages * page_size)");
   }
   *status = ISK_OK;
   return "";
