@@ -61,10 +61,14 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
   if (ri.n_parts > 1) {
     const float* lse_p = a.part_lse + (size_t)ri.part_off * a.hq + h;
     const int n = ri.n_parts;
+    // The LSEs of chunk c (splits 64c .. 64c+63, lane-parallel); with at most
+    // 64 splits (every row up to 98304 tokens) the one chunk is loaded once.
+    const float x0 = lane < n ? lse_p[(size_t)lane * a.hq] : -INFINITY;
+    auto lse_chunk = [&](int c) { return c == 0 ? x0 : (c + lane < n ? lse_p[(size_t)(c + lane) * a.hq] : -INFINITY); };
     // m = max_i lse_i (exact, any order).
     float m = -INFINITY;
     for (int c = 0; c < n; c += 64) {
-      const float x = c + lane < n ? lse_p[(size_t)(c + lane) * a.hq] : -INFINITY;
+      const float x = lse_chunk(c);
       float w = x;
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) w = fmaxf(w, __shfl_xor(w, d, 64));
@@ -74,7 +78,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
       // S = sum_i 2^((lse_i - m) log2 e), i ascending.
       float ssum = 0.f;
       for (int c = 0; c < n; c += 64) {
-        const float x = c + lane < n ? lse_p[(size_t)(c + lane) * a.hq] : -INFINITY;
+        const float x = lse_chunk(c);
         const float e = fast_exp2((x - m) * kLog2e);
         const int cn = min(64, n - c);
         for (int i = 0; i < cn; ++i) ssum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), i));
@@ -86,7 +90,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
       // out = sum_i (e_i / S) o_i, an FMA chain with i ascending; the
       // partials' loads go out four at a time.
       for (int c = 0; c < n; c += 64) {
-        const float x = c + lane < n ? lse_p[(size_t)(c + lane) * a.hq] : -INFINITY;
+        const float x = lse_chunk(c);
         const float wl = fast_exp2((x - m) * kLog2e) * inv;
         const int cn = min(64, n - c);
         // Loads of a group go out together, then its FMAs in order.
