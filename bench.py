@@ -10,7 +10,12 @@ are synthetic and resident in HBM before timing starts.
 One step = the whole hot path: host re-planning of the per-row splits, the
 split-list upload, the split kernel and the fixed-order combine.  The timed
 region is exactly `--steps` steps after `--warmup` untimed ones, bracketed by
-device synchronisation.  Prints one JSON line (see the design doc for the fields).
+device synchronisation, with nothing else recorded on the stream (per-step
+timing events would add their own gaps to the step).  The split kernel's
+duration for the roofline comes from a second pass of `--steps` steps right
+after it, in which the library records HIP events around each launch on the
+same stream.  Prints one JSON line: the metric, the roofline of the split
+kernel and the CPU oracle baseline.
 """
 
 import argparse
@@ -90,28 +95,32 @@ class HipEvents:
         self.rt.hipEventDestroy(ev)
 
 
-def timed_steps(dc, isk, torch, evs, steps, warmup, lens_host):
-    """Warm up, then time exactly `steps` steps; per-step split/combine
-    kernel times come from events recorded by the library's timing hook."""
+def timed_steps(dc, isk, torch, evs, steps, warmup, lens_host, instrument):
+    """Warm up, then time exactly `steps` steps.  With `instrument`, the
+    library's timing hook records HIP events around every split and combine
+    launch and their per-step durations are returned too (None otherwise)."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         dc.plan.update(lens_host)
         dc.run(stream)
     torch.cuda.synchronize()
-    marks = [(evs.create(), evs.create(), evs.create()) for _ in range(steps)]
+    marks = [(evs.create(), evs.create(), evs.create()) for _ in range(steps)] if instrument else None
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(steps):
-        isk.plan_set_timing_events(dc.plan.handle, *marks[i])
+        if instrument:
+            isk.plan_set_timing_events(dc.plan.handle, *marks[i])
         dc.plan.update(lens_host)
         dc.run(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    isk.plan_set_timing_events(dc.plan.handle, None, None, None)
     total_ms = t_start.elapsed_time(t_end)
+    if not instrument:
+        return total_ms, wall, None, None
+    isk.plan_set_timing_events(dc.plan.handle, None, None, None)
     split = [evs.elapsed_ms(a, b) for a, b, _ in marks]
     comb = [evs.elapsed_ms(b, c) for _, b, c in marks]
     for m in marks:
@@ -184,8 +193,9 @@ def cpu_baseline(case, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # The shader clock takes on the order of a hundred steps to settle.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -227,7 +237,9 @@ def main():
     evs = HipEvents()
 
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps (mode {args.mode})")
-    total_ms, wall, split, comb = timed_steps(dc, isk, torch, evs, args.steps, args.warmup, lens_host)
+    total_ms, wall, _, _ = timed_steps(dc, isk, torch, evs, args.steps, args.warmup, lens_host, False)
+    log(f"kernel durations: {args.steps} more steps with HIP events around each launch")
+    inst_ms, _, split, comb = timed_steps(dc, isk, torch, evs, args.steps, 0, lens_host, True)
     ms_step = total_ms / args.steps
     split_ms = float(np.mean(split))
     comb_ms = float(np.mean(comb))
@@ -272,6 +284,7 @@ def main():
         "combine_ms": round(comb_ms, 5),
         "mfma_tflops_split": round(float(lens_host.sum()) * case.hq * (576 + 512) * 2 / (split_ms * 1e-3) / 1e12, 1),
         "wall_s_timed_region": round(wall, 4),
+        "ms_per_step_with_kernel_events": round(inst_ms / args.steps, 5),
         "numerics_id": isk.numerics_id(),
     }
 
@@ -289,7 +302,8 @@ def main():
         if mode == isk.SPLIT_PER_ROW:
             log("batch-balanced comparison mode on the same batch")
             dcb = DeviceCase(case, split_mode=isk.SPLIT_BATCH_BALANCED, pool=dc.pool)
-            tb, _, sb, _ = timed_steps(dcb, isk, torch, evs, args.steps, args.warmup, lens_host)
+            tb, _, _, _ = timed_steps(dcb, isk, torch, evs, args.steps, args.warmup, lens_host, False)
+            _, _, sb, _ = timed_steps(dcb, isk, torch, evs, args.steps, 0, lens_host, True)
             _, _, bb, bl = dcb.result()
             okb = invariance_pass_rate(case, bb, bl, isk.SPLIT_BATCH_BALANCED, synth, DeviceCase,
                                        range(0, case.batch, 4))

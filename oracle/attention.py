@@ -24,7 +24,7 @@ with no splitting, tiling or reordering:
   approximated, so the oracle has no notion of splits at all except
   :func:`merge`, which states the partial-merge rule itself.
 
-Readings of points the pages leave open (each is listed in the design doc too):
+Readings of points the pages leave open:
 
 * The log-sum-exp is the natural log of the sum of exp of the *scaled*
   scores.
