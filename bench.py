@@ -241,6 +241,12 @@ def main():
     log(f"kernel durations: {args.steps} more steps with HIP events around each launch")
     inst_ms, _, split, comb = timed_steps(dc, isk, torch, evs, args.steps, 0, lens_host, True)
     ms_step = total_ms / args.steps
+    # Host cost of re-planning the batch (part of every step above).
+    plan_us = []
+    for _ in range(200):
+        t0 = time.perf_counter()
+        dc.plan.update(lens_host)
+        plan_us.append((time.perf_counter() - t0) * 1e6)
     split_ms = float(np.mean(split))
     comb_ms = float(np.mean(comb))
     gbs = kvb / (ms_step * 1e-3) / 1e9
@@ -282,6 +288,7 @@ def main():
         "tokens_per_s": round(case.batch / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(lens_host.sum()) / (ms_step * 1e-3), 1),
         "combine_ms": round(comb_ms, 5),
+        "host_plan_us": round(float(np.median(plan_us)), 1),
         "mfma_tflops_split": round(float(lens_host.sum()) * case.hq * (576 + 512) * 2 / (split_ms * 1e-3) / 1e12, 1),
         "wall_s_timed_region": round(wall, 4),
         "ms_per_step_with_kernel_events": round(inst_ms / args.steps, 5),
@@ -296,7 +303,7 @@ def main():
         res["invariance"] = {"pass": ok, "total": case.batch, "rate": round(ok / case.batch, 4),
                              "check": "out bf16 bits + lse fp32 bits, solo (fresh pages, fresh plan) vs batched"}
         log("cold-cache calls (1 GiB flush before each)")
-        cold = cold_steps(dc, torch, 10)
+        cold = cold_steps(dc, torch, 50)
         res["cold_ms_per_call"] = round(float(np.median(cold)), 5)
         res["cold_kv_gbs"] = round(kvb / (np.median(cold) * 1e-3) / 1e9, 2)
         if mode == isk.SPLIT_PER_ROW:

@@ -202,6 +202,30 @@ ISK_API int isk_attn_decode(const isk_plan* plan, const void* q, const void* kv_
                     void* stream);
 
 /*
+ * isk_attn_decode_oneshot - plan, allocate the workspace and decode in one
+ * call, for callers that decode a batch once (the signature the pages give
+ * for the decode entry: q, KV pages, block table, lengths and optional top-k
+ * indices in, out and lse out; FlashMLA issue "Sparse MLA decode is not
+ * batch-invariant ...", section "Where it comes from").
+ *
+ * desc, batch, lens_host, topk_len_host: as for isk_plan_create (host).
+ * q .. lse, stream: as for isk_attn_decode.
+ *
+ * The workspace comes from hipMallocAsync on `stream` and is released with
+ * hipFreeAsync on the same stream after the kernels, so the call allocates
+ * stream-ordered device memory (unlike isk_attn_decode).  The plan is built
+ * and destroyed inside the call; the call returns once the split list has
+ * been uploaded, with the kernels still in flight on `stream`.  Output bits
+ * equal those of isk_plan_create + isk_attn_decode on the same inputs.
+ * Errors: those of isk_plan_create and isk_attn_decode; ISK_ERR_HIP when the
+ * stream-ordered allocation fails.
+ */
+ISK_API int isk_attn_decode_oneshot(const isk_desc* desc, int32_t batch, const int32_t* lens_host,
+                            const int32_t* topk_len_host, const void* q, const void* kv_pages,
+                            const int32_t* block_table, const int32_t* lens, const int32_t* topk_idx,
+                            const int32_t* topk_len, void* out, float* lse, void* stream);
+
+/*
  * isk_plan_set_timing_events - profiling hook.  Subsequent isk_attn_decode
  * calls with this plan record `split_begin` on the call's stream right before
  * the split kernel is launched, `split_end` right after it, and

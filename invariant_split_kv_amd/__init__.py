@@ -22,7 +22,7 @@ __all__ = [
     "SPLIT_BATCH_BALANCED", "OUT_BF16", "OUT_F32", "LIB_PATH", "lib", "plan_create",
     "plan_update", "plan_destroy", "plan_query", "plan_workspace_bytes", "plan_segments",
     "plan_set_timing_events",
-    "attn_decode", "last_error", "numerics_id", "Plan",
+    "attn_decode", "attn_decode_oneshot", "last_error", "numerics_id", "Plan",
 ]
 
 KIND_GQA, KIND_MLA = 0, 1
@@ -68,6 +68,8 @@ def _load() -> ctypes.CDLL:
         "isk_plan_workspace_bytes": (ctypes.c_size_t, [P]),
         "isk_plan_segments": (ctypes.c_int, [P, I32P, ctypes.c_int32]),
         "isk_attn_decode": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "isk_attn_decode_oneshot": (ctypes.c_int, [ctypes.POINTER(IskDesc), ctypes.c_int32, I32P, I32P,
+                                                    P, P, P, P, P, P, P, P, P]),
         "isk_plan_set_timing_events": (ctypes.c_int, [P, P, P, P]),
         "isk_last_error": (ctypes.c_char_p, []),
         "isk_numerics_id": (ctypes.c_char_p, []),
@@ -172,6 +174,21 @@ def attn_decode(plan: int, q, kv_pages, block_table, lens, topk_idx, topk_len, o
     _check(lib.isk_attn_decode(plan, _ptr(q), _ptr(kv_pages), _ptr(block_table), _ptr(lens), _ptr(topk_idx),
                                _ptr(topk_len), _ptr(out), _ptr(lse), _ptr(workspace), int(workspace_bytes),
                                stream))
+
+
+def attn_decode_oneshot(desc: IskDesc, lens_host, topk_len_host, q, kv_pages, block_table, lens, topk_idx,
+                        topk_len, out, lse, stream=None) -> None:
+    """Plan, allocate the workspace on `stream` and decode in one call."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    lh = _i32_host(lens_host)
+    th = _i32_host(topk_len_host)
+    _check(lib.isk_attn_decode_oneshot(ctypes.byref(desc), len(lh), _i32p(lh), _i32p(th), _ptr(q), _ptr(kv_pages),
+                                       _ptr(block_table), _ptr(lens), _ptr(topk_idx), _ptr(topk_len), _ptr(out),
+                                       _ptr(lse), stream))
 
 
 class Plan:

@@ -227,6 +227,28 @@ int isk_plan_segments(const isk_plan* plan, int32_t* records, int32_t capacity) 
   return n;
 }
 
+namespace {
+
+// Pointer checks of a decode call (everything but the workspace).
+int check_decode_args(const isk_desc& d, const void* q, const void* kv_pages, const int32_t* block_table,
+                      const int32_t* lens, const int32_t* topk_idx, const int32_t* topk_len, const void* out,
+                      const float* lse) {
+  const bool sparse = d.topk_width > 0;
+  if (q == nullptr || kv_pages == nullptr || block_table == nullptr || lens == nullptr || out == nullptr)
+    return set_err(ISK_ERR_INVALID_ARG, "q, kv_pages, block_table, lens and out must be non-NULL");
+  if (sparse && (topk_idx == nullptr || topk_len == nullptr))
+    return set_err(ISK_ERR_INVALID_ARG, "sparse plan: topk_idx and topk_len must be non-NULL");
+  if (!sparse && (topk_idx != nullptr || topk_len != nullptr))
+    return set_err(ISK_ERR_INVALID_ARG, "dense plan: topk_idx and topk_len must be NULL");
+  auto aligned = [](const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; };
+  if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(out, 16) || !aligned(block_table, 4) || !aligned(lens, 4) ||
+      (lse != nullptr && !aligned(lse, 4)) || (sparse && !aligned(topk_idx, 4)))
+    return set_err(ISK_ERR_INVALID_ARG, "q, kv_pages and out must be 16-byte aligned, tables 4-byte aligned");
+  return ISK_OK;
+}
+
+}  // namespace
+
 int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages, const int32_t* block_table,
                     const int32_t* lens, const int32_t* topk_idx, const int32_t* topk_len, void* out, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream_v) {
@@ -236,22 +258,16 @@ int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages,
   const isk_desc& d = pd.desc;
   const bool sparse = d.topk_width > 0;
   hipStream_t stream = (hipStream_t)stream_v;
-  if (q == nullptr || kv_pages == nullptr || block_table == nullptr || lens == nullptr || out == nullptr)
-    return set_err(ISK_ERR_INVALID_ARG, "q, kv_pages, block_table, lens and out must be non-NULL");
-  if (sparse && (topk_idx == nullptr || topk_len == nullptr))
-    return set_err(ISK_ERR_INVALID_ARG, "sparse plan: topk_idx and topk_len must be non-NULL");
-  if (!sparse && (topk_idx != nullptr || topk_len != nullptr))
-    return set_err(ISK_ERR_INVALID_ARG, "dense plan: topk_idx and topk_len must be NULL");
+  {
+    const int rc = check_decode_args(d, q, kv_pages, block_table, lens, topk_idx, topk_len, out, lse);
+    if (rc != ISK_OK) return rc;
+  }
   if (workspace == nullptr || workspace_bytes < plan->layout.total) {
     std::ostringstream s;
     s << "workspace of " << workspace_bytes << " bytes is smaller than the " << plan->layout.total << " the plan needs";
     return set_err(ISK_ERR_WORKSPACE, s.str());
   }
   if (((uintptr_t)workspace & 255u) != 0) return set_err(ISK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  auto aligned = [](const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; };
-  if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(out, 16) || !aligned(block_table, 4) || !aligned(lens, 4) ||
-      (lse != nullptr && !aligned(lse, 4)) || (sparse && !aligned(topk_idx, 4)))
-    return set_err(ISK_ERR_INVALID_ARG, "q, kv_pages and out must be 16-byte aligned, tables 4-byte aligned");
 
   if (d.check_inputs) {
     const int rc = audit_inputs(plan, block_table, lens, topk_idx, topk_len, stream);
@@ -325,6 +341,43 @@ int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages,
     e = hipEventRecord(plan->t_combine_end, stream);
     if (e != hipSuccess) return hip_err(e, "hipEventRecord (timing)");
   }
+  return ISK_OK;
+}
+
+int isk_attn_decode_oneshot(const isk_desc* desc, int32_t batch, const int32_t* lens_host,
+                            const int32_t* topk_len_host, const void* q, const void* kv_pages,
+                            const int32_t* block_table, const int32_t* lens, const int32_t* topk_idx,
+                            const int32_t* topk_len, void* out, float* lse, void* stream_v) {
+  isk_plan* plan = nullptr;
+  int rc = isk_plan_create(desc, batch, lens_host, topk_len_host, &plan);
+  if (rc != ISK_OK) return rc;
+  rc = check_decode_args(*desc, q, kv_pages, block_table, lens, topk_idx, topk_len, out, lse);
+  if (rc != ISK_OK) {
+    const std::string msg = isk_last_error();
+    (void)isk_plan_destroy(plan);
+    return set_err(rc, msg);
+  }
+  hipStream_t stream = (hipStream_t)stream_v;
+  const size_t bytes = plan->layout.total;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, stream);
+  if (e != hipSuccess) {
+    (void)isk_plan_destroy(plan);
+    return hip_err(e, "hipMallocAsync (workspace)");
+  }
+  if (((uintptr_t)ws & 255u) != 0) {
+    (void)hipFreeAsync(ws, stream);
+    (void)isk_plan_destroy(plan);
+    return set_err(ISK_ERR_WORKSPACE, "hipMallocAsync returned a workspace that is not 256-byte aligned");
+  }
+  rc = isk_attn_decode(plan, q, kv_pages, block_table, lens, topk_idx, topk_len, out, lse, ws, bytes, stream_v);
+  const std::string msg = rc != ISK_OK ? std::string(isk_last_error()) : std::string();
+  e = hipFreeAsync(ws, stream);
+  // Waits until the split-list upload has executed (the kernels read the
+  // device copy in the workspace, not the plan's staging memory).
+  (void)isk_plan_destroy(plan);
+  if (rc != ISK_OK) return set_err(rc, msg);
+  if (e != hipSuccess) return hip_err(e, "hipFreeAsync (workspace)");
   return ISK_OK;
 }
 

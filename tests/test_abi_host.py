@@ -42,7 +42,7 @@ def segments(desc, lens, topk=None):
 def test_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "isk.h")).read()
     declared = set(re.findall(r"ISK_API\s+[\w\s\*]+?\b(isk_\w+)\s*\(", header))
-    assert len(declared) == 10
+    assert len(declared) == 11
     for name in declared:
         assert hasattr(isk.lib, name), name
     assert "gfx950" in isk.numerics_id()
@@ -94,6 +94,14 @@ def test_decode_argument_errors_without_launch():
         with pytest.raises(isk.IskError) as e:   # misaligned workspace
             isk.attn_decode(p.handle, 256, 256, 256, 256, None, None, 256, 256, 260, ws, stream=0)
         assert e.value.status == -3
+    # The one-shot entry checks its arguments before allocating anything.
+    with pytest.raises(isk.IskError) as e:
+        isk.attn_decode_oneshot(desc, [100, 7], None, None, 256, 256, 256, 256, None, 256, 256, stream=0)
+    assert e.value.status == -1 and "non-NULL" in e.value.message
+    with pytest.raises(isk.IskError) as e:
+        isk.attn_decode_oneshot(gqa_desc(num_q_heads=30), [5], None, 256, 256, 256, 256, None, None, 256, 256,
+                                stream=0)
+    assert e.value.status == -1 and "multiple" in e.value.message
 
 
 def _check_tiling(segs, info, units, split):

@@ -203,3 +203,31 @@ def test_out_of_pool_page_is_masked_not_read():
     import oracle
     ro0, rl0 = oracle.mla_decode(q[:1], [row0], case.scale)
     parity(out[:1], lse[:1], ro0, rl0, False, "masked page")
+
+
+@pytest.mark.parametrize("kind", ["gqa", "mla", "sparse"])
+def test_oneshot_entry_matches_planned_call(kind):
+    """isk_attn_decode_oneshot (plan + stream-ordered workspace + decode in one
+    call) gives the bits of the plan-based call and passes parity itself."""
+    if kind == "gqa":
+        case = synth.config1_gqa_tiny()
+    elif kind == "mla":
+        case = synth.mla_case([1, 100, 1537, 3100], 128, 1 / math.sqrt(192.0), 64, structure_seed=71)
+    else:
+        case = synth.mla_case([300, 2500, 64], 128, 1 / math.sqrt(192.0), 64, structure_seed=72,
+                              topk_width=1024)
+    print(f"[oneshot] {kind} B={case.batch} lens={list(case.lens)}", flush=True)
+    dc = DeviceCase(case)
+    dc.run()
+    _, _, bits, lbits = dc.result()
+    out2 = torch.empty_like(dc.out)
+    lse2 = torch.empty_like(dc.lse)
+    isk.attn_decode_oneshot(dc.desc, dc.lens_host, dc.topk_len_host, dc.q, dc.pool, dc.block_table, dc.lens,
+                            dc.topk_idx, dc.topk_len, out2, lse2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.view(torch.int16).cpu().numpy(), bits)
+    assert np.array_equal(lse2.view(torch.int32).cpu().numpy(), lbits)
+    ro, rl = reference(case)
+    parity(out2.float().cpu().numpy().astype(np.float64), lse2.cpu().numpy().astype(np.float64), ro, rl, False,
+           f"oneshot {kind}")
+    dc.close()
