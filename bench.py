@@ -129,6 +129,49 @@ def timed_steps(dc, isk, torch, evs, steps, warmup, lens_host, instrument):
     return total_ms, wall, split, comb
 
 
+def per_row_vs_balanced_sizes(isk, synth, torch, np, sizes=(1, 2, 8, 32, 128), calls=50):
+    """Per-row over balanced call time on the invariance-stress batches (probe
+    row of 16384 tokens among batchmates of 1..131072 tokens, composition 0),
+    one batch per size.  Values are drawn on the GPU (N(0, 0.5^2), bf16); only
+    the timing is used."""
+    res = {}
+    stream = torch.cuda.current_stream()
+    for B in sizes:
+        lens, _, _ = synth.config5_composition(B, 0)
+        lens = np.asarray(lens, dtype=np.int32)
+        paging = synth.make_paging(lens, 64, np.random.default_rng([B, 77]))
+        g = torch.Generator(device="cuda").manual_seed(B)
+        pool = (torch.randn((paging.num_pages, 64, synth.MLA_DQK), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+        q = (torch.randn((B, 128, synth.MLA_DQK), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+        bt = torch.from_numpy(paging.block_table).cuda()
+        lens_d = torch.from_numpy(lens).cuda()
+        out = torch.empty((B, 128, synth.MLA_DV), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, 128), dtype=torch.float32, device="cuda")
+        ms = {}
+        for name, mode in (("per_row", isk.SPLIT_PER_ROW), ("balanced", isk.SPLIT_BATCH_BALANCED)):
+            desc = isk.IskDesc(isk.KIND_MLA, 128, 1, synth.MLA_DQK, synth.MLA_DV, 64, paging.num_pages,
+                               paging.max_pages_per_row, 0, mode, 0, isk.OUT_BF16, 0, 1.0 / math.sqrt(192.0))
+            with isk.Plan(desc, lens) as plan:
+                ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+                call = lambda: isk.attn_decode(plan.handle, q, pool, bt, lens_d, None, None, out, lse, ws,
+                                               ws.numel(), stream)
+                for _ in range(20):
+                    call()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(calls):
+                    call()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ms[name] = a.elapsed_time(b) / calls
+        res[str(B)] = {"kv_tokens": int(lens.sum()), "per_row_ms": round(ms["per_row"], 5),
+                       "balanced_ms": round(ms["balanced"], 5),
+                       "per_row_over_balanced": round(ms["per_row"] / ms["balanced"], 4)}
+        del pool, q
+        torch.cuda.empty_cache()
+    return res
+
+
 def cold_steps(dc, torch, n):
     """Per-call time with L2 and the 256 MB Infinity Cache flushed first."""
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -318,6 +361,8 @@ def main():
                                "per_row_over_balanced": round(ms_step / (tb / args.steps), 4),
                                "invariance_pass": okb, "invariance_total": len(range(0, case.batch, 4))}
             dcb.close()
+            log("per-row vs balanced at batch sizes 1, 2, 8, 32, 128 (invariance-stress lengths)")
+            res["per_row_over_balanced_by_batch"] = per_row_vs_balanced_sizes(isk, synth, torch, np)
         if not args.no_cpu_baseline:
             log(f"CPU baseline: fp64 oracle for ~{args.cpu_seconds:.0f} s")
             res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
