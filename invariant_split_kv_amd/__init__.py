@@ -58,6 +58,14 @@ class IskPlanInfo(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python invariant_split_kv_amd/build.py`")
+    # One HIP runtime per process: torch ships its own libamdhip64 (same
+    # soname), and the device memory handed to libisk comes from it.  Loading
+    # torch first makes libisk bind to that runtime instead of pulling in a
+    # second copy from /opt/rocm, which on some hosts sees no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     P, I32P = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
     sig = {
