@@ -227,13 +227,16 @@ ISK_API int isk_attn_decode_oneshot(const isk_desc* desc, int32_t batch, const i
 
 /*
  * isk_plan_set_timing_events - profiling hook.  Subsequent isk_attn_decode
- * calls with this plan record `split_begin` on the call's stream right before
- * the split kernel is launched, `split_end` right after it, and
- * `combine_end` after the combine kernel (or right after split_end when no
- * row needs combining).  Each argument is a hipEvent_t passed as void*; NULL
- * disables that record.  Meant for timing the kernels with
- * hipEventElapsedTime; the caller owns the events and may swap them between
- * calls.  Host only; never fails for a non-NULL plan.
+ * calls with this plan launch the split kernel through hipExtLaunchKernel
+ * with `split_begin` and `split_end` as its start and stop events, so they
+ * carry the split kernel's own start and end times, and record
+ * `combine_end` on the call's stream after the combine kernel (or right
+ * after the split kernel when no row needs combining).  Each argument is a
+ * hipEvent_t passed as void*; NULL disables that event (with both split
+ * events NULL the split kernel is launched the ordinary way).  Meant for
+ * timing the kernels with hipEventElapsedTime; the caller owns the events
+ * and may swap them between calls.  Host only; never fails for a non-NULL
+ * plan.
  */
 ISK_API int isk_plan_set_timing_events(isk_plan* plan, void* split_begin, void* split_end, void* combine_end);
 

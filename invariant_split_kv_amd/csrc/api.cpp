@@ -309,27 +309,22 @@ int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages,
   const int32_t n_groups = (int32_t)pd.groups.size() - 1;
   const float scale_log2 = d.scale * isk::kLog2eHost;
 
-  if (plan->t_split_begin != nullptr) {
-    e = hipEventRecord(plan->t_split_begin, stream);
-    if (e != hipSuccess) return hip_err(e, "hipEventRecord (timing)");
-  }
+  isk::LaunchEvents ev;
+  ev.begin = plan->t_split_begin;
+  ev.end = plan->t_split_end;
   if (d.kind == ISK_KIND_GQA) {
     isk::GqaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, segs, groups, part_o, part_lse,
                      out, lse, n_groups, d.num_q_heads, d.num_kv_heads, d.head_dim_qk, d.page_size, d.num_pages,
                      d.max_pages_per_row, d.out_dtype == ISK_OUT_F32, scale_log2};
-    e = isk::launch_gqa_split(a, stream);
+    e = isk::launch_gqa_split(a, stream, ev);
     if (e != hipSuccess) return hip_err(e, "launching the GQA split kernel");
   } else {
     isk::MlaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, sparse ? topk_idx : nullptr,
                      segs, groups, part_o, part_lse, out, lse, n_groups, d.num_q_heads, d.page_size, d.num_pages,
                      d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2};
     // 128-head blocks (32 heads per wave) when the head count allows it.
-    e = d.num_q_heads % 128 == 0 ? isk::launch_mla_split_h32(a, stream) : isk::launch_mla_split(a, stream);
+    e = d.num_q_heads % 128 == 0 ? isk::launch_mla_split_h32(a, stream, ev) : isk::launch_mla_split(a, stream, ev);
     if (e != hipSuccess) return hip_err(e, "launching the MLA split kernel");
-  }
-  if (plan->t_split_end != nullptr) {
-    e = hipEventRecord(plan->t_split_end, stream);
-    if (e != hipSuccess) return hip_err(e, "hipEventRecord (timing)");
   }
   if (pd.any_combine) {
     isk::CombineLaunch c{rows, part_o, part_lse, out, lse, pd.batch, d.num_q_heads, d.head_dim_v,

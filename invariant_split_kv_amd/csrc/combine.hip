@@ -11,8 +11,8 @@
 //   m = max_i lse_i;  e_i = 2^((lse_i - m) * log2 e);  S = sum_i e_i;
 //   lse = m + ln S;   out = sum_i (e_i / S) * o_i   (fp32 FMA chain, i ascending)
 // One wave handles one (row, head); lane l owns Dv/64 consecutive dims.  The
-// LSEs are loaded lane-parallel and the partials four at a time, so a row
-// costs a few memory round trips instead of one per split.
+// LSEs are loaded lane-parallel and the partials up to eight at a time, so a
+// row costs a few memory round trips instead of one per split.
 // Rows with one split were written by the split kernel and are skipped; rows
 // with none get out = 0 and lse = -inf.
 
@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
       const float* op = a.part_o + ((size_t)ri.part_off * a.hq + h) * a.dv + DPL * lane;
       const size_t stride = (size_t)a.hq * a.dv;
       // out = sum_i (e_i / S) o_i, an FMA chain with i ascending; the
-      // partials' loads go out four at a time.
+      // partials' loads go out eight (then four, then the rest) at a time.
       for (int c = 0; c < n; c += 64) {
         const float x = lse_chunk(c);
         const float wl = fast_exp2((x - m) * kLog2e) * inv;
@@ -107,7 +107,11 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
           }
         };
         int i = 0;
-        for (; i + 4 <= cn; i += 4) group(i, std::integral_constant<int, 4>{});
+        for (; i + 8 <= cn; i += 8) group(i, std::integral_constant<int, 8>{});
+        if (i + 4 <= cn) {
+          group(i, std::integral_constant<int, 4>{});
+          i += 4;
+        }
         switch (cn - i) {
           case 3: group(i, std::integral_constant<int, 3>{}); break;
           case 2: group(i, std::integral_constant<int, 2>{}); break;

@@ -250,26 +250,25 @@ __global__ void __launch_bounds__(256) gqa_split_kernel(GqaLaunch a) {
 }
 
 template <int D>
-hipError_t launch_d(const GqaLaunch& a, hipStream_t s) {
+hipError_t launch_d(const GqaLaunch& a, hipStream_t s, const LaunchEvents& ev) {
   const int g = a.hq / a.hkv;
   const dim3 grid(a.n_groups, a.hkv);
   switch (g) {
-    case 1: hipLaunchKernelGGL((gqa_split_kernel<D, 1>), grid, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gqa_split_kernel<D, 1>), grid, dim3(128), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gqa_split_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((gqa_split_kernel<D, 2>), grid, dim3(256), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((gqa_split_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
+    case 1: return launch_one(gqa_split_kernel<D, 1>, grid, dim3(64), s, a, ev);
+    case 2: return launch_one(gqa_split_kernel<D, 1>, grid, dim3(128), s, a, ev);
+    case 4: return launch_one(gqa_split_kernel<D, 1>, grid, dim3(256), s, a, ev);
+    case 8: return launch_one(gqa_split_kernel<D, 2>, grid, dim3(256), s, a, ev);
+    case 16: return launch_one(gqa_split_kernel<D, 4>, grid, dim3(256), s, a, ev);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gqa_split(const GqaLaunch& a, hipStream_t s) {
+hipError_t launch_gqa_split(const GqaLaunch& a, hipStream_t s, const LaunchEvents& ev) {
   if (a.n_groups == 0) return hipSuccess;
-  if (a.d == 128) return launch_d<128>(a, s);
-  if (a.d == 64) return launch_d<64>(a, s);
+  if (a.d == 128) return launch_d<128>(a, s, ev);
+  if (a.d == 64) return launch_d<64>(a, s, ev);
   return hipErrorInvalidValue;
 }
 

@@ -2,6 +2,7 @@
 // the kernel launchers (*.hip).  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -68,6 +69,26 @@ std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int3
                        const int32_t* topk_len_host, int* status);
 
 // ---------------------------------------------------------------- launchers
+// Optional profiling events of a split-kernel launch.  When set, the kernel
+// goes through hipExtLaunchKernel, which stamps the events with the kernel's
+// own start and end (not the time the stream reached a marker).
+struct LaunchEvents {
+  hipEvent_t begin = nullptr, end = nullptr;
+};
+
+// Launch a kernel whose only argument is the struct `a`.
+template <typename Arg>
+inline hipError_t launch_one(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t s, const Arg& a,
+                             const LaunchEvents& ev) {
+  if (ev.begin == nullptr && ev.end == nullptr) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+    return hipGetLastError();
+  }
+  Arg copy = a;
+  void* args[] = {&copy};
+  return hipExtLaunchKernel((const void*)kernel, grid, block, args, 0, s, ev.begin, ev.end, 0);
+}
+
 struct GqaLaunch {
   const uint16_t* q; const uint16_t* kv;
   const int32_t* block_table; const int32_t* lens;
@@ -76,7 +97,7 @@ struct GqaLaunch {
   int32_t n_groups, hq, hkv, d, page_size, num_pages, max_pages, out_f32;
   float scale_log2;
 };
-hipError_t launch_gqa_split(const GqaLaunch& a, hipStream_t s);
+hipError_t launch_gqa_split(const GqaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});
 
 struct MlaLaunch {
   const uint16_t* q; const uint16_t* kv;
@@ -87,8 +108,8 @@ struct MlaLaunch {
   int32_t n_groups, hq, page_size, num_pages, max_pages, topk_width, out_f32;
   float scale_log2;
 };
-hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s);        // 16 heads per wave
-hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s);    // 32 heads per wave, hq % 128 == 0
+hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});       // 16 heads per wave
+hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});   // 32 heads per wave, hq % 128 == 0
 
 struct CombineLaunch {
   const RowInfo* rows; const float* part_o; const float* part_lse;

@@ -421,7 +421,7 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
 
 }  // namespace
 
-hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s) {
+hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev) {
   if (a.n_groups == 0) return hipSuccess;
   // Heads per workgroup: all of them up to 64, else 64 (hq % 64 == 0 is
   // checked by the planner).
@@ -429,11 +429,8 @@ hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s) {
   const int n_hb = a.hq / hw;
   const int n_blocks = ((a.n_groups + 7) / 8) * 8 * n_hb;
   const dim3 grid(n_blocks), block(hw * 4);
-  if (a.topk_idx != nullptr)
-    hipLaunchKernelGGL(mla_split_kernel<true>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(mla_split_kernel<false>, grid, block, 0, s, a);
-  return hipGetLastError();
+  if (a.topk_idx != nullptr) return launch_one(mla_split_kernel<true>, grid, block, s, a, ev);
+  return launch_one(mla_split_kernel<false>, grid, block, s, a, ev);
 }
 
 }  // namespace isk

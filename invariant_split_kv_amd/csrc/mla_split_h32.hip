@@ -973,17 +973,14 @@ mla_split_h32_kernel(MlaLaunch a) {
 
 }  // namespace
 
-hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s) {
+hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev) {
   if (a.n_groups == 0) return hipSuccess;
   if (a.hq % kHeadsPerBlock != 0) return hipErrorInvalidValue;
   const int n_hb = a.hq / kHeadsPerBlock;
   const int n_blocks = ((a.n_groups + 7) / 8) * 8 * n_hb;
   const dim3 grid(n_blocks), block(64 * kWaves);
-  if (a.topk_idx != nullptr)
-    hipLaunchKernelGGL(mla_split_h32_kernel<true>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(mla_split_h32_kernel<false>, grid, block, 0, s, a);
-  return hipGetLastError();
+  if (a.topk_idx != nullptr) return launch_one(mla_split_h32_kernel<true>, grid, block, s, a, ev);
+  return launch_one(mla_split_h32_kernel<false>, grid, block, s, a, ev);
 }
 
 }  // namespace isk
