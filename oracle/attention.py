@@ -38,6 +38,13 @@ Readings of points the pages leave open:
   ``-1`` or any other out-of-range value is skipped.  Duplicated positions
   count once per occurrence.
 * An empty key set gives ``out = 0`` and ``lse = -inf``.
+* Extra KV source (same page, sections "Measurement" and "Environment": the
+  sparse call also takes ``extra_indices_in_kvcache`` / ``extra_topk_length``
+  into a second cache, ``extra_k_cache``).  The pages name these arguments
+  without defining them; the reading taken here is the plainest one: a row
+  attends, with one softmax, the multiset union of its main gathered set
+  (positions in its main cache) and its extra gathered set (positions in its
+  extra cache, validated against the extra cache's own length).
 
 All inputs are taken as given numbers (the exact bf16 values, widened to
 float64); all arithmetic is float64.
@@ -52,6 +59,7 @@ __all__ = [
     "gqa_decode",
     "mla_decode",
     "mla_sparse_decode",
+    "mla_sparse_extra_decode",
     "sparse_positions",
     "merge",
     "merge_many",
@@ -146,6 +154,32 @@ def mla_sparse_decode(q, latent_rows, lens, topk_idx, topk_len, scale: float, dv
     for b in range(q.shape[0]):
         pos = sparse_positions(topk_idx[b], int(topk_len[b]), int(lens[b]))
         g = np.asarray(np.asarray(latent_rows[b])[pos], dtype=np.float64)
+        o, l = attend(q[b], g, g[:, :dv], scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+def mla_sparse_extra_decode(q, latent_rows, lens, topk_idx, topk_len,
+                            extra_rows, extra_lens, extra_idx, extra_topk_len, scale: float, dv: int = 512):
+    """Sparse absorbed-MLA decode over two gathered key sets per row.
+
+    Row b attends the latent rows of its main cache at
+    ``sparse_positions(topk_idx[b], topk_len[b], lens[b])`` together with
+    the latent rows of its extra cache at
+    ``sparse_positions(extra_idx[b], extra_topk_len[b], extra_lens[b])``,
+    all in one softmax (keys are the whole latent rows, values their first
+    ``dv`` entries).  Either set may be empty.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    outs, lses = [], []
+    for b in range(q.shape[0]):
+        pos = sparse_positions(topk_idx[b], int(topk_len[b]), int(lens[b]))
+        xpos = sparse_positions(extra_idx[b], int(extra_topk_len[b]), int(extra_lens[b]))
+        width = q.shape[2]
+        main = np.asarray(latent_rows[b], dtype=np.float64).reshape(-1, width)[pos]
+        extra = np.asarray(extra_rows[b], dtype=np.float64).reshape(-1, width)[xpos]
+        g = np.concatenate([main, extra], axis=0)        # main set first, then the extra set
         o, l = attend(q[b], g, g[:, :dv], scale)
         outs.append(o)
         lses.append(l)

@@ -379,3 +379,125 @@ def test_planted_mistakes_are_caught(monkeypatch, kind):
 
 def test_planted_head_mapping_mistake_is_caught(monkeypatch):
     assert not _pins_pass(monkeypatch, attend_ok, gqa_map=_gqa_wrong_head_map)
+
+
+# ----------------------------------------------------------------------------
+# Extra KV source: one softmax over the main and the extra gathered sets
+# ----------------------------------------------------------------------------
+
+def _extra_inputs(seed, hq=3, dqk=7, dv=4, L=11, LX=9, W=6, WX=5):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, hq, dqk))
+    c = rng.standard_normal((L, dqk))
+    cx = rng.standard_normal((LX, dqk))
+    idx = rng.permutation(L)[:W].astype(np.int32)[None]
+    xidx = rng.permutation(LX)[:WX].astype(np.int32)[None]
+    return q, c, cx, idx, xidx, dv
+
+
+def test_extra_source_matches_brute_force_over_the_union():
+    q, c, cx, idx, xidx, dv = _extra_inputs(21)
+    # main: slots 0..3 used, slot 1 made -1 (skipped); extra: slots 0..2, one out of range
+    idx = idx.copy(); idx[0, 1] = -1
+    xidx = xidx.copy(); xidx[0, 2] = 9                      # == extra length: masked
+    out, lse = oracle.mla_sparse_extra_decode(q, [c], [11], idx, [4], [cx], [9], xidx, [3], 0.37, dv=dv)
+    keys = np.concatenate([c[[idx[0, 0], idx[0, 2], idx[0, 3]]], cx[[xidx[0, 0], xidx[0, 1]]]])
+    bo, bl = brute_force(q[0], keys, keys[:, :dv], 0.37)
+    assert rel_close(out[0], bo, 1e-12)[0] and rel_close(lse[0], bl, 1e-12)[0]
+
+
+def test_extra_source_reduces_to_plain_sparse_when_either_set_is_empty():
+    q, c, cx, idx, xidx, dv = _extra_inputs(22)
+    so, sl = oracle.mla_sparse_decode(q, [c], [11], idx, [6], 0.5, dv=dv)
+    eo, el = oracle.mla_sparse_extra_decode(q, [c], [11], idx, [6], [cx], [9], xidx, [0], 0.5, dv=dv)
+    assert np.array_equal(so, eo) and np.array_equal(sl, el)
+    xo, xl = oracle.mla_sparse_decode(q, [cx], [9], xidx, [5], 0.5, dv=dv)
+    eo, el = oracle.mla_sparse_extra_decode(q, [c], [11], idx, [0], [cx], [9], xidx, [5], 0.5, dv=dv)
+    assert np.array_equal(xo, eo) and np.array_equal(xl, el)
+    eo, el = oracle.mla_sparse_extra_decode(q, [c], [11], idx, [0], [cx], [9], xidx, [0], 0.5, dv=dv)
+    assert np.all(eo == 0.0) and np.all(np.isneginf(el))
+
+
+def test_extra_source_is_the_merge_of_the_two_sets():
+    q, c, cx, idx, xidx, dv = _extra_inputs(23)
+    a = oracle.mla_sparse_decode(q, [c], [11], idx, [6], 0.45, dv=dv)
+    x = oracle.mla_sparse_decode(q, [cx], [9], xidx, [5], 0.45, dv=dv)
+    mo, ml = oracle.merge(a, x)
+    eo, el = oracle.mla_sparse_extra_decode(q, [c], [11], idx, [6], [cx], [9], xidx, [5], 0.45, dv=dv)
+    assert rel_close(eo, mo, 1e-12)[0] and rel_close(el, ml, 1e-12)[0]
+
+
+def test_extra_source_with_full_permutations_equals_dense_over_both_caches():
+    rng = np.random.default_rng(24)
+    L, LX, hq, dqk, dv = 30, 17, 4, 10, 6
+    q = rng.standard_normal((1, hq, dqk))
+    c = rng.standard_normal((L, dqk))
+    cx = rng.standard_normal((LX, dqk))
+    idx = rng.permutation(L).astype(np.int32)[None]
+    xidx = rng.permutation(LX).astype(np.int32)[None]
+    eo, el = oracle.mla_sparse_extra_decode(q, [c], [L], idx, [L], [cx], [LX], xidx, [LX], 0.3, dv=dv)
+    do, dl = oracle.mla_decode(q, [np.concatenate([c, cx])], 0.3, dv=dv)
+    assert np.allclose(eo, do, atol=1e-13) and np.allclose(el, dl, atol=1e-13)
+
+
+def test_extra_positions_are_checked_against_the_extra_length():
+    # an extra position valid for the main cache (len 11) but not for the
+    # extra cache (len 4) must be skipped
+    q, c, cx, idx, xidx, dv = _extra_inputs(25, LX=9)
+    xidx = np.array([[2, 7, 3, -1, 0]], dtype=np.int32)
+    eo, el = oracle.mla_sparse_extra_decode(q, [c], [11], idx, [2], [cx], [4], xidx, [5], 0.6, dv=dv)
+    keys = np.concatenate([c[idx[0, :2]], cx[[2, 3, 0]]])
+    ro, rl = oracle.attend(q[0], keys, keys[:, :dv], 0.6)
+    assert np.allclose(eo[0], ro, atol=1e-14) and np.allclose(el[0], rl, atol=1e-14)
+
+
+def _extra_mutant(kind):
+    def impl(q, rows, lens, idx, tl, xrows, xlens, xidx, xtl, scale, dv=512):
+        q = np.asarray(q, np.float64)
+        outs, lses = [], []
+        for b in range(q.shape[0]):
+            pos = oracle.sparse_positions(idx[b], int(tl[b]), int(lens[b]))
+            xl = int(lens[b]) if kind == "main_len_for_extra" else int(xlens[b])
+            xpos = oracle.sparse_positions(xidx[b], int(xtl[b]), xl)
+            main = np.asarray(rows[b], np.float64)[pos]
+            src = rows[b] if kind == "extra_from_main_cache" else xrows[b]
+            xpos = xpos[xpos < len(src)]
+            extra = np.asarray(src, np.float64)[xpos].reshape(-1, q.shape[2])
+            if kind == "drop_extra":
+                extra = extra[:0]
+            if kind == "equal_weights" and len(main) and len(extra):
+                oa_, la_ = oracle.attend(q[b], main, main[:, :dv], scale)
+                ox_, lx_ = oracle.attend(q[b], extra, extra[:, :dv], scale)
+                o, l = 0.5 * (oa_ + ox_), np.logaddexp(la_, lx_)
+            else:
+                g = np.concatenate([main.reshape(-1, q.shape[2]), extra])
+                o, l = oracle.attend(q[b], g, g[:, :dv], scale)
+            outs.append(o)
+            lses.append(l)
+        return np.stack(outs), np.stack(lses)
+    return impl
+
+
+_EXTRA_PINS = [test_extra_source_matches_brute_force_over_the_union,
+               test_extra_source_reduces_to_plain_sparse_when_either_set_is_empty,
+               test_extra_source_is_the_merge_of_the_two_sets,
+               test_extra_source_with_full_permutations_equals_dense_over_both_caches,
+               test_extra_positions_are_checked_against_the_extra_length]
+
+
+@pytest.mark.parametrize("kind", ["drop_extra", "main_len_for_extra", "extra_from_main_cache", "equal_weights"])
+def test_planted_extra_source_mistakes_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(oracle, "mla_sparse_extra_decode", _extra_mutant(kind))
+    failed = 0
+    for pin in _EXTRA_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, f"no pin rejects the planted mistake {kind}"
+
+
+def test_extra_pins_accept_a_faithful_restatement(monkeypatch):
+    monkeypatch.setattr(oracle, "mla_sparse_extra_decode", _extra_mutant("none"))
+    for pin in _EXTRA_PINS:
+        pin()
