@@ -226,6 +226,71 @@ ISK_API int isk_attn_decode_oneshot(const isk_desc* desc, int32_t batch, const i
                             const int32_t* topk_len, void* out, float* lse, void* stream);
 
 /*
+ * Extra KV source of sparse MLA decode.  The sparse FlashMLA call on the
+ * FlashMLA issue page "Sparse MLA decode is not batch-invariant ..." also
+ * takes extra_indices_in_kvcache / extra_topk_length into a second cache,
+ * extra_k_cache (sections "Measurement" and "Environment").  The page names
+ * these arguments without defining them; this library reads them as a second
+ * gathered key set per row, from its own paged latent cache, attended in the
+ * same softmax as the main set: row b attends the valid main positions and
+ * the valid extra positions (each checked against its own cache length).
+ * The extra set's splits follow the main set's in the row's fixed combine
+ * order and are cut by the same per-row rule (the extra top-k count and the
+ * sparse split length only), so the output bits stay batch-invariant.
+ */
+typedef struct isk_extra_desc {
+  int32_t page_size;          /* tokens per page of the extra pool (>= 1)          */
+  int32_t num_pages;          /* pages in the extra pool                             */
+  int32_t max_pages_per_row;  /* columns of the extra block table                    */
+  int32_t topk_width;         /* columns of the extra index array (>= 1)             */
+} isk_extra_desc;
+
+typedef struct isk_extra_kv {  /* device pointers, owned by the caller */
+  const void* kv_pages;          /* [num_pages, page_size, 576] bf16                  */
+  const int32_t* block_table;    /* [B, max_pages_per_row] int32                      */
+  const int32_t* lens;           /* [B] int32 extra cache length of each row          */
+  const int32_t* topk_idx;       /* [B, topk_width] int32 row-local positions         */
+  const int32_t* topk_len;       /* [B] int32 device copy of extra_topk_len_host      */
+} isk_extra_kv;
+
+/*
+ * isk_plan_create_extra - plan a sparse MLA batch with an extra KV source.
+ *
+ * desc                 as for isk_plan_create; must be ISK_KIND_MLA with
+ *                      topk_width > 0 and split_mode ISK_SPLIT_PER_ROW.
+ * extra                the extra source's shape (copied).
+ * lens_host,
+ * topk_len_host        as for isk_plan_create (main set).
+ * extra_topk_len_host  [B] host int32 valid extra top-k counts (clamped to
+ *                      [0, extra->topk_width]).
+ *
+ * Row b gets ceil(topk_len_b / S) main splits followed by
+ * ceil(extra_topk_len_b / S) extra splits, S the sparse split length; in
+ * isk_plan_segments records an extra split's range is reported shifted by
+ * desc->topk_width (slot j of the extra set is unit topk_width + j).  Plans
+ * with an extra source are used with isk_attn_decode_extra only and are not
+ * re-planned by isk_plan_update (create a new plan).  Host only.  Errors:
+ * ISK_ERR_INVALID_ARG, ISK_ERR_UNSUPPORTED.
+ */
+ISK_API int isk_plan_create_extra(const isk_desc* desc, const isk_extra_desc* extra, int32_t batch,
+                                  const int32_t* lens_host, const int32_t* topk_len_host,
+                                  const int32_t* extra_topk_len_host, isk_plan** plan_out);
+
+/*
+ * isk_attn_decode_extra - isk_attn_decode for a plan from
+ * isk_plan_create_extra: the same arguments plus `extra`, a host struct of
+ * the extra source's device tensors (all non-NULL).  Extra positions outside
+ * [0, extra lens[b]) and extra block-table entries outside the extra pool
+ * are masked; with desc.check_inputs = 1 they are reported as ISK_ERR_INDEX
+ * instead.  Errors: those of isk_attn_decode.
+ */
+ISK_API int isk_attn_decode_extra(const isk_plan* plan, const void* q, const void* kv_pages,
+                                  const int32_t* block_table, const int32_t* lens,
+                                  const int32_t* topk_idx, const int32_t* topk_len,
+                                  const isk_extra_kv* extra, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * isk_plan_set_timing_events - profiling hook.  Subsequent isk_attn_decode
  * calls with this plan launch the split kernel through hipExtLaunchKernel
  * with `split_begin` and `split_end` as its start and stop events, so they

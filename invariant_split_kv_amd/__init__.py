@@ -18,11 +18,11 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "IskError", "IskDesc", "IskPlanInfo", "KIND_GQA", "KIND_MLA", "SPLIT_PER_ROW",
+    "IskError", "IskDesc", "IskExtraDesc", "IskExtraKv", "IskPlanInfo", "KIND_GQA", "KIND_MLA", "SPLIT_PER_ROW",
     "SPLIT_BATCH_BALANCED", "OUT_BF16", "OUT_F32", "LIB_PATH", "lib", "plan_create",
     "plan_update", "plan_destroy", "plan_query", "plan_workspace_bytes", "plan_segments",
-    "plan_set_timing_events",
-    "attn_decode", "attn_decode_oneshot", "last_error", "numerics_id", "Plan",
+    "plan_set_timing_events", "plan_create_extra",
+    "attn_decode", "attn_decode_extra", "attn_decode_oneshot", "last_error", "numerics_id", "Plan",
 ]
 
 KIND_GQA, KIND_MLA = 0, 1
@@ -47,6 +47,16 @@ class IskDesc(ctypes.Structure):
                 ("num_pages", ctypes.c_int32), ("max_pages_per_row", ctypes.c_int32),
                 ("topk_width", ctypes.c_int32), ("split_mode", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("check_inputs", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class IskExtraDesc(ctypes.Structure):
+    _fields_ = [("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages_per_row", ctypes.c_int32), ("topk_width", ctypes.c_int32)]
+
+
+class IskExtraKv(ctypes.Structure):
+    _fields_ = [("kv_pages", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("lens", ctypes.c_void_p),
+                ("topk_idx", ctypes.c_void_p), ("topk_len", ctypes.c_void_p)]
 
 
 class IskPlanInfo(ctypes.Structure):
@@ -79,6 +89,10 @@ def _load() -> ctypes.CDLL:
         "isk_attn_decode_oneshot": (ctypes.c_int, [ctypes.POINTER(IskDesc), ctypes.c_int32, I32P, I32P,
                                                     P, P, P, P, P, P, P, P, P]),
         "isk_plan_set_timing_events": (ctypes.c_int, [P, P, P, P]),
+        "isk_plan_create_extra": (ctypes.c_int, [ctypes.POINTER(IskDesc), ctypes.POINTER(IskExtraDesc), ctypes.c_int32,
+                                                  I32P, I32P, I32P, ctypes.POINTER(P)]),
+        "isk_attn_decode_extra": (ctypes.c_int, [P, P, P, P, P, P, P, ctypes.POINTER(IskExtraKv), P, P, P,
+                                                  ctypes.c_size_t, P]),
         "isk_last_error": (ctypes.c_char_p, []),
         "isk_numerics_id": (ctypes.c_char_p, []),
     }
@@ -129,6 +143,16 @@ def plan_create(desc: IskDesc, lens_host, topk_len_host=None) -> int:
     tl = _i32_host(topk_len_host)
     out = ctypes.c_void_p()
     _check(lib.isk_plan_create(ctypes.byref(desc), len(lens), _i32p(lens), _i32p(tl), ctypes.byref(out)))
+    return out.value
+
+
+def plan_create_extra(desc: IskDesc, extra: IskExtraDesc, lens_host, topk_len_host, extra_topk_len_host) -> int:
+    lens = _i32_host(lens_host)
+    tl = _i32_host(topk_len_host)
+    xtl = _i32_host(extra_topk_len_host)
+    out = ctypes.c_void_p()
+    _check(lib.isk_plan_create_extra(ctypes.byref(desc), ctypes.byref(extra), len(lens), _i32p(lens), _i32p(tl),
+                                     _i32p(xtl), ctypes.byref(out)))
     return out.value
 
 
@@ -184,6 +208,22 @@ def attn_decode(plan: int, q, kv_pages, block_table, lens, topk_idx, topk_len, o
                                stream))
 
 
+def attn_decode_extra(plan: int, q, kv_pages, block_table, lens, topk_idx, topk_len, extra_kv_pages,
+                      extra_block_table, extra_lens, extra_topk_idx, extra_topk_len, out, lse, workspace,
+                      workspace_bytes: int, stream=None) -> None:
+    """attn_decode for a plan with an extra KV source (plan_create_extra)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    x = IskExtraKv(_ptr(extra_kv_pages), _ptr(extra_block_table), _ptr(extra_lens), _ptr(extra_topk_idx),
+                   _ptr(extra_topk_len))
+    _check(lib.isk_attn_decode_extra(plan, _ptr(q), _ptr(kv_pages), _ptr(block_table), _ptr(lens), _ptr(topk_idx),
+                                     _ptr(topk_len), ctypes.byref(x), _ptr(out), _ptr(lse), _ptr(workspace),
+                                     int(workspace_bytes), stream))
+
+
 def attn_decode_oneshot(desc: IskDesc, lens_host, topk_len_host, q, kv_pages, block_table, lens, topk_idx,
                         topk_len, out, lse, stream=None) -> None:
     """Plan, allocate the workspace on `stream` and decode in one call."""
@@ -202,9 +242,14 @@ def attn_decode_oneshot(desc: IskDesc, lens_host, topk_len_host, q, kv_pages, bl
 class Plan:
     """Owning wrapper of an isk_plan handle (destroyed on close/garbage collection)."""
 
-    def __init__(self, desc: IskDesc, lens_host, topk_len_host=None):
+    def __init__(self, desc: IskDesc, lens_host, topk_len_host=None, extra: Optional[IskExtraDesc] = None,
+                 extra_topk_len_host=None):
         self.desc = desc
-        self.handle = plan_create(desc, lens_host, topk_len_host)
+        self.extra = extra
+        if extra is None:
+            self.handle = plan_create(desc, lens_host, topk_len_host)
+        else:
+            self.handle = plan_create_extra(desc, extra, lens_host, topk_len_host, extra_topk_len_host)
 
     def update(self, lens_host, topk_len_host=None) -> None:
         plan_update(self.handle, lens_host, topk_len_host)

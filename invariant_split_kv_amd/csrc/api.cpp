@@ -74,8 +74,10 @@ void release_staging(isk_plan* p) {
 
 // Audit of the tables against the plan (desc.check_inputs).  Copies the
 // device tables to the host (synchronising the stream).
+int audit_extra(const isk_plan* p, const isk_extra_kv& x, hipStream_t stream);
+
 int audit_inputs(const isk_plan* p, const int32_t* block_table, const int32_t* lens, const int32_t* topk_idx,
-                 const int32_t* topk_len, hipStream_t stream) {
+                 const int32_t* topk_len, const isk_extra_kv* extra, hipStream_t stream) {
   const isk_desc& d = p->data.desc;
   const int B = p->data.batch;
   std::vector<int32_t> h_lens(B), h_bt((size_t)B * d.max_pages_per_row), h_tl, h_idx;
@@ -139,6 +141,51 @@ int audit_inputs(const isk_plan* p, const int32_t* block_table, const int32_t* l
       }
     }
   }
+  return extra != nullptr ? audit_extra(p, *extra, stream) : ISK_OK;
+}
+
+// The same audit for the extra KV source.
+int audit_extra(const isk_plan* p, const isk_extra_kv& x, hipStream_t stream) {
+  const isk_extra_desc& d = p->data.extra;
+  const int B = p->data.batch;
+  std::vector<int32_t> h_lens(B), h_bt((size_t)B * d.max_pages_per_row), h_tl(B), h_idx((size_t)B * d.topk_width);
+  hipError_t e = hipMemcpyAsync(h_lens.data(), x.lens, B * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h_bt.data(), x.block_table, h_bt.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(h_tl.data(), x.topk_len, B * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h_idx.data(), x.topk_idx, h_idx.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_err(e, "check_inputs: copying the extra tables to the host");
+  for (int b = 0; b < B; ++b) {
+    const int32_t L = h_lens[b];
+    if (L < 0 || (long long)L > (long long)d.max_pages_per_row * d.page_size) {
+      std::ostringstream s;
+      s << "check_inputs: extra lens[" << b << "] = " << L << " out of range";
+      return set_err(ISK_ERR_INDEX, s.str());
+    }
+    const int32_t n = std::min(std::max(h_tl[b], 0), d.topk_width);
+    if (n != p->data.extra_units[b]) {
+      std::ostringstream s;
+      s << "check_inputs: extra topk_len[" << b << "] differs from the planned count";
+      return set_err(ISK_ERR_INVALID_ARG, s.str());
+    }
+    for (int j = 0; j < n; ++j) {
+      const int32_t pos = h_idx[(size_t)b * d.topk_width + j];
+      if (pos < 0 || pos >= L) {
+        std::ostringstream s;
+        s << "check_inputs: extra topk_idx[" << b << "][" << j << "] = " << pos << " is not a position in [0, " << L
+          << ") although the slot is below the extra topk_len";
+        return set_err(ISK_ERR_INDEX, s.str());
+      }
+      const int32_t pg = h_bt[(size_t)b * d.max_pages_per_row + pos / d.page_size];
+      if (pg < 0 || pg >= d.num_pages) {
+        std::ostringstream s;
+        s << "check_inputs: the page of extra topk_idx[" << b << "][" << j << "] is not a page of the extra pool";
+        return set_err(ISK_ERR_INDEX, s.str());
+      }
+    }
+  }
   return ISK_OK;
 }
 
@@ -182,8 +229,29 @@ int isk_plan_create(const isk_desc* desc, int32_t batch, const int32_t* lens_hos
   return ISK_OK;
 }
 
+int isk_plan_create_extra(const isk_desc* desc, const isk_extra_desc* extra, int32_t batch, const int32_t* lens_host,
+                          const int32_t* topk_len_host, const int32_t* extra_topk_len_host, isk_plan** plan_out) {
+  if (plan_out == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan_out is NULL");
+  *plan_out = nullptr;
+  if (desc == nullptr || extra == nullptr) return set_err(ISK_ERR_INVALID_ARG, "desc or extra is NULL");
+  isk_plan* p = new (std::nothrow) isk_plan();
+  if (p == nullptr) return set_err(ISK_ERR_INVALID_ARG, "out of host memory");
+  int status = ISK_OK;
+  std::string msg =
+      isk::plan_build(p->data, *desc, batch, lens_host, topk_len_host, &status, extra, extra_topk_len_host);
+  if (status != ISK_OK) {
+    delete p;
+    return set_err(status, msg);
+  }
+  serialise(p);
+  *plan_out = p;
+  return ISK_OK;
+}
+
 int isk_plan_update(isk_plan* plan, int32_t batch, const int32_t* lens_host, const int32_t* topk_len_host) {
   if (plan == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->data.has_extra)
+    return set_err(ISK_ERR_INVALID_ARG, "a plan with an extra KV source is re-planned with isk_plan_create_extra");
   PlanData fresh;
   int status = ISK_OK;
   std::string msg = isk::plan_build(fresh, plan->data.desc, batch, lens_host, topk_len_host, &status);
@@ -249,9 +317,10 @@ int check_decode_args(const isk_desc& d, const void* q, const void* kv_pages, co
 
 }  // namespace
 
-int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages, const int32_t* block_table,
-                    const int32_t* lens, const int32_t* topk_idx, const int32_t* topk_len, void* out, float* lse,
-                    void* workspace, size_t workspace_bytes, void* stream_v) {
+static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pages, const int32_t* block_table,
+                       const int32_t* lens, const int32_t* topk_idx, const int32_t* topk_len,
+                       const isk_extra_kv* extra, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream_v) {
   if (plan_c == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
   isk_plan* plan = const_cast<isk_plan*>(plan_c);   // staging ring only; the plan itself is not changed
   const PlanData& pd = plan->data;
@@ -262,6 +331,18 @@ int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages,
     const int rc = check_decode_args(d, q, kv_pages, block_table, lens, topk_idx, topk_len, out, lse);
     if (rc != ISK_OK) return rc;
   }
+  if (pd.has_extra && extra == nullptr)
+    return set_err(ISK_ERR_INVALID_ARG, "the plan has an extra KV source: call isk_attn_decode_extra");
+  if (!pd.has_extra && extra != nullptr)
+    return set_err(ISK_ERR_INVALID_ARG, "the plan has no extra KV source (create it with isk_plan_create_extra)");
+  if (extra != nullptr) {
+    if (extra->kv_pages == nullptr || extra->block_table == nullptr || extra->lens == nullptr ||
+        extra->topk_idx == nullptr || extra->topk_len == nullptr)
+      return set_err(ISK_ERR_INVALID_ARG, "every pointer of the extra KV source must be non-NULL");
+    if ((uintptr_t)extra->kv_pages % 16 != 0 || (uintptr_t)extra->block_table % 4 != 0 ||
+        (uintptr_t)extra->lens % 4 != 0 || (uintptr_t)extra->topk_idx % 4 != 0 || (uintptr_t)extra->topk_len % 4 != 0)
+      return set_err(ISK_ERR_INVALID_ARG, "extra kv_pages must be 16-byte aligned, extra tables 4-byte aligned");
+  }
   if (workspace == nullptr || workspace_bytes < plan->layout.total) {
     std::ostringstream s;
     s << "workspace of " << workspace_bytes << " bytes is smaller than the " << plan->layout.total << " the plan needs";
@@ -270,7 +351,7 @@ int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages,
   if (((uintptr_t)workspace & 255u) != 0) return set_err(ISK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
   if (d.check_inputs) {
-    const int rc = audit_inputs(plan, block_table, lens, topk_idx, topk_len, stream);
+    const int rc = audit_inputs(plan, block_table, lens, topk_idx, topk_len, extra, stream);
     if (rc != ISK_OK) return rc;
   }
 
@@ -321,7 +402,18 @@ int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages,
   } else {
     isk::MlaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, sparse ? topk_idx : nullptr,
                      segs, groups, part_o, part_lse, out, lse, n_groups, d.num_q_heads, d.page_size, d.num_pages,
-                     d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2};
+                     d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2,
+                     nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0};
+    if (extra != nullptr) {
+      a.xkv = (const uint16_t*)extra->kv_pages;
+      a.xblock_table = extra->block_table;
+      a.xlens = extra->lens;
+      a.xtopk_idx = extra->topk_idx;
+      a.xpage_size = pd.extra.page_size;
+      a.xnum_pages = pd.extra.num_pages;
+      a.xmax_pages = pd.extra.max_pages_per_row;
+      a.xtopk_width = pd.extra.topk_width;
+    }
     // 128-head blocks (32 heads per wave) when the head count allows it.
     e = d.num_q_heads % 128 == 0 ? isk::launch_mla_split_h32(a, stream, ev) : isk::launch_mla_split(a, stream, ev);
     if (e != hipSuccess) return hip_err(e, "launching the MLA split kernel");
@@ -337,6 +429,22 @@ int isk_attn_decode(const isk_plan* plan_c, const void* q, const void* kv_pages,
     if (e != hipSuccess) return hip_err(e, "hipEventRecord (timing)");
   }
   return ISK_OK;
+}
+
+int isk_attn_decode(const isk_plan* plan, const void* q, const void* kv_pages, const int32_t* block_table,
+                    const int32_t* lens, const int32_t* topk_idx, const int32_t* topk_len, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(plan, q, kv_pages, block_table, lens, topk_idx, topk_len, nullptr, out, lse, workspace,
+                     workspace_bytes, stream);
+}
+
+int isk_attn_decode_extra(const isk_plan* plan, const void* q, const void* kv_pages, const int32_t* block_table,
+                          const int32_t* lens, const int32_t* topk_idx, const int32_t* topk_len,
+                          const isk_extra_kv* extra, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (extra == nullptr) return set_err(ISK_ERR_INVALID_ARG, "extra is NULL");
+  return decode_impl(plan, q, kv_pages, block_table, lens, topk_idx, topk_len, extra, out, lse, workspace,
+                     workspace_bytes, stream);
 }
 
 int isk_attn_decode_oneshot(const isk_desc* desc, int32_t batch, const int32_t* lens_host,

@@ -54,6 +54,11 @@ struct PlanData {
   std::vector<RowInfo> rows;
   int32_t n_partials = 0;
   bool any_combine = false;         // some row has 0 or >1 splits
+  // Extra KV source (sparse MLA): its segments cover units
+  // [desc.topk_width + j0, desc.topk_width + j1) of the row.
+  bool has_extra = false;
+  isk_extra_desc extra{};
+  std::vector<int32_t> extra_units; // per-row valid extra top-k counts
 };
 
 // Byte layout of the per-call metadata at the head of the workspace.
@@ -65,8 +70,11 @@ MetaLayout meta_layout(const PlanData& p);
 
 // Planner (host only; no HIP calls).  Returns an empty string on success,
 // otherwise the error message; *status receives the isk_status.
+// With `extra` non-NULL the plan also covers an extra KV source
+// (extra_topk_len_host gives its per-row valid counts).
 std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int32_t* lens_host,
-                       const int32_t* topk_len_host, int* status);
+                       const int32_t* topk_len_host, int* status, const isk_extra_desc* extra = nullptr,
+                       const int32_t* extra_topk_len_host = nullptr);
 
 // ---------------------------------------------------------------- launchers
 // Optional profiling events of a split-kernel launch.  When set, the kernel
@@ -107,6 +115,11 @@ struct MlaLaunch {
   float* part_o; float* part_lse; void* out; float* lse;
   int32_t n_groups, hq, page_size, num_pages, max_pages, topk_width, out_f32;
   float scale_log2;
+  // Extra KV source (sparse only; xtopk_idx NULL when absent).  A segment
+  // whose begin is >= topk_width gathers from it, at extra slots
+  // [begin - topk_width, end - topk_width).
+  const uint16_t* xkv; const int32_t* xblock_table; const int32_t* xlens; const int32_t* xtopk_idx;
+  int32_t xpage_size, xnum_pages, xmax_pages, xtopk_width;
 };
 hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});       // 16 heads per wave
 hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});   // 32 heads per wave, hq % 128 == 0

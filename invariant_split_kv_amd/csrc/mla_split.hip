@@ -213,12 +213,24 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
   };
 
   for (int si = seg_first; si < seg_last; ++si) {
-    const Seg sg = a.segs[si];
+    Seg sg = a.segs[si];
     const int b = sg.row;
-    const int len = a.lens[b];
-    Stager<kSparse> stage{kv, a.block_table + (size_t)b * a.max_pages,
-                          kSparse ? a.topk_idx + (size_t)b * a.topk_width : nullptr,
-                          a.page_size, a.num_pages, len, sg.begin, sg.end};
+    // A sparse segment past the main index width gathers from the extra KV
+    // source, at its slots [begin - topk_width, end - topk_width).  The
+    // extra lengths are device-only, so positions past the extra block
+    // table's capacity are masked here.
+    const bool from_extra = kSparse && sg.begin >= a.topk_width;
+    if (from_extra) {
+      sg.begin -= a.topk_width;
+      sg.end -= a.topk_width;
+    }
+    Stager<kSparse> stage =
+        from_extra ? Stager<kSparse>{(const unsigned char*)a.xkv, a.xblock_table + (size_t)b * a.xmax_pages,
+                                     a.xtopk_idx + (size_t)b * a.xtopk_width, a.xpage_size, a.xnum_pages,
+                                     min(a.xlens[b], a.xmax_pages * a.xpage_size), sg.begin, sg.end}
+                   : Stager<kSparse>{kv, a.block_table + (size_t)b * a.max_pages,
+                                     kSparse ? a.topk_idx + (size_t)b * a.topk_width : nullptr, a.page_size,
+                                     a.num_pages, a.lens[b], sg.begin, sg.end};
 
     __syncthreads();   // every wave is done with the LDS tiles of the previous segment
 

@@ -621,11 +621,24 @@ mla_split_h32_kernel(MlaLaunch a) {
   so.init(wave_u, lane);
 
   for (int si = seg_first; si < seg_last; ++si) {
-    const Seg sg = a.segs[si];
+    Seg sg = a.segs[si];
     const int b = sg.row;
-    const Stager<kSparse> stage{(const unsigned char*)a.kv, a.block_table + (size_t)b * a.max_pages,
-                                kSparse ? a.topk_idx + (size_t)b * a.topk_width : nullptr,
-                                a.page_size, a.num_pages, a.lens[b], sg.end};
+    // A sparse segment past the main index width gathers from the extra KV
+    // source, at its slots [begin - topk_width, end - topk_width).  The
+    // extra lengths are device-only, so positions past the extra block
+    // table's capacity are masked here.
+    const bool from_extra = kSparse && sg.begin >= a.topk_width;
+    if (from_extra) {
+      sg.begin -= a.topk_width;
+      sg.end -= a.topk_width;
+    }
+    const Stager<kSparse> stage =
+        from_extra ? Stager<kSparse>{(const unsigned char*)a.xkv, a.xblock_table + (size_t)b * a.xmax_pages,
+                                     a.xtopk_idx + (size_t)b * a.xtopk_width, a.xpage_size, a.xnum_pages,
+                                     min(a.xlens[b], a.xmax_pages * a.xpage_size), sg.end}
+                   : Stager<kSparse>{(const unsigned char*)a.kv, a.block_table + (size_t)b * a.max_pages,
+                                     kSparse ? a.topk_idx + (size_t)b * a.topk_width : nullptr, a.page_size,
+                                     a.num_pages, a.lens[b], sg.end};
 
     // Every wave is done reading the previous segment's tiles.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

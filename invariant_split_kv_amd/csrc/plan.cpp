@@ -8,7 +8,9 @@
 // (sparse) and S the frozen split length of the kind.  An exclusive scan over
 // rows assigns workspace slots to the partials; it decides where partials
 // live, never what is computed.  Splits are dispatched longest first, which
-// changes only which compute unit runs a split and when.
+// changes only which compute unit runs a split and when.  A sparse row with
+// an extra KV source gets the same rule applied to its extra top-k count;
+// those splits follow the main set's in the row's partial order.
 //
 // Batch-balanced mode exists for comparison only.  It reproduces the
 // scheduler that page describes (same section: a block quota per part derived
@@ -84,9 +86,26 @@ static std::string check_desc(const isk_desc& d, int* status) {
 }
 
 std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int32_t* lens_host,
-                       const int32_t* topk_len_host, int* status) {
+                       const int32_t* topk_len_host, int* status, const isk_extra_desc* extra,
+                       const int32_t* extra_topk_len_host) {
   std::string err = check_desc(d, status);
   if (*status != ISK_OK) return err;
+  if (extra != nullptr) {
+    if (d.kind != ISK_KIND_MLA || d.topk_width <= 0)
+      return fail(status, ISK_ERR_UNSUPPORTED, "an extra KV source needs a sparse MLA descriptor (topk_width > 0)");
+    if (d.split_mode != ISK_SPLIT_PER_ROW)
+      return fail(status, ISK_ERR_UNSUPPORTED, "an extra KV source is planned in per-row split mode only");
+    if (extra->page_size <= 0 || extra->num_pages <= 0 || extra->max_pages_per_row <= 0 || extra->topk_width <= 0)
+      return fail(status, ISK_ERR_INVALID_ARG,
+                  "extra page_size, num_pages, max_pages_per_row and topk_width must be positive");
+    if ((long long)extra->num_pages * extra->page_size > 0x7fffffffLL)
+      return fail(status, ISK_ERR_UNSUPPORTED, "extra pools are limited to 2^31 - 1 token rows");
+    if ((long long)extra->max_pages_per_row * extra->page_size > 0x7fffffffLL)
+      return fail(status, ISK_ERR_UNSUPPORTED, "extra max_pages_per_row * page_size must fit in int32");
+    if ((long long)d.topk_width + extra->topk_width > 0x7fffffffLL)
+      return fail(status, ISK_ERR_UNSUPPORTED, "topk_width + extra topk_width must fit in int32");
+    if (extra_topk_len_host == nullptr) return fail(status, ISK_ERR_INVALID_ARG, "extra_topk_len_host is NULL");
+  }
   if (batch <= 0) return fail(status, ISK_ERR_INVALID_ARG, "batch must be >= 1");
   if (lens_host == nullptr) return fail(status, ISK_ERR_INVALID_ARG, "lens_host is NULL");
   const bool sparse = d.topk_width > 0;
@@ -117,6 +136,11 @@ std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int3
   p.groups.clear();
   p.rows.assign(batch, RowInfo{0, 0});
   p.n_partials = 0;
+  p.has_extra = extra != nullptr;
+  p.extra = extra != nullptr ? *extra : isk_extra_desc{};
+  p.extra_units.assign(extra != nullptr ? batch : 0, 0);
+  for (int b = 0; b < (int)p.extra_units.size(); ++b)
+    p.extra_units[b] = std::min(std::max(extra_topk_len_host[b], 0), extra->topk_width);
 
   std::vector<std::vector<Seg>> row_segs(batch);
   std::vector<int32_t> seg_part_of;   // group index per segment (balanced)
@@ -126,6 +150,13 @@ std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int3
       const int32_t U = units[b];
       const int32_t n = (U + S - 1) / S;
       for (int32_t i = 0; i < n; ++i) row_segs[b].push_back(Seg{b, i * S, std::min((i + 1) * S, U), 0});
+      if (p.has_extra) {
+        // The extra set's splits follow the main set's, by the same rule;
+        // their units are offset by the main index width.
+        const int32_t W = d.topk_width, X = p.extra_units[b];
+        const int32_t nx = (X + S - 1) / S;
+        for (int32_t i = 0; i < nx; ++i) row_segs[b].push_back(Seg{b, W + i * S, W + std::min((i + 1) * S, X), 0});
+      }
     }
   } else {
     // Batch-wide quota: total blocks plus a fixed overhead charge per row,

@@ -36,6 +36,11 @@ def reference(case):
         ks = [synth.bf16_value(r.k) for r in case.rows]
         vs = [synth.bf16_value(r.v) for r in case.rows]
         return oracle.gqa_decode(q, ks, vs, case.scale)
+    if case.sparse and case.extra is not None:
+        x = case.extra
+        return oracle.mla_sparse_extra_decode(q, list(case.logical_rows()), case.lens, case.topk_idx(),
+                                              case.topk_len(), list(x.logical_rows()), x.lens, x.topk_idx(),
+                                              x.topk_len(), case.scale, dv=synth.MLA_DV)
     if case.sparse:
         return oracle.mla_sparse_decode(q, list(case.logical_rows()), case.lens, case.topk_idx(),
                                         case.topk_len(), case.scale, dv=synth.MLA_DV)

@@ -42,7 +42,7 @@ def segments(desc, lens, topk=None):
 def test_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "isk.h")).read()
     declared = set(re.findall(r"ISK_API\s+[\w\s\*]+?\b(isk_\w+)\s*\(", header))
-    assert len(declared) == 11
+    assert len(declared) == 13
     for name in declared:
         assert hasattr(isk.lib, name), name
     assert "gfx950" in isk.numerics_id()
@@ -195,3 +195,92 @@ def test_workspace_size_covers_partials():
         assert p.workspace_bytes == info["workspace_bytes"]
         p.update([100, 100])
         assert p.info()["num_partials"] == 0 and p.info()["batch"] == 2
+
+
+# ----------------------------------------------------------------------------
+# Extra KV source (sparse MLA): planner and argument checks
+# ----------------------------------------------------------------------------
+
+def xdesc(**kw):
+    d = dict(page_size=64, num_pages=4096, max_pages_per_row=256, topk_width=1024)
+    d.update(kw)
+    return isk.IskExtraDesc(**d)
+
+
+def extra_segments(lens, tl, xtl, width=2048, xwidth=1024, split=0):
+    with isk.Plan(mla_desc(topk_width=width, split_tokens=split), lens, tl, extra=xdesc(topk_width=xwidth),
+                  extra_topk_len_host=xtl) as p:
+        return p.segments(), p.info()
+
+
+def test_extra_source_splits_follow_the_main_splits_per_row():
+    W, S = 2048, 512
+    segs, info = extra_segments([5000, 100, 9000], [2048, 0, 700], [900, 1024, 0])
+    by_row = {}
+    for r in segs:
+        by_row.setdefault(int(r[0]), []).append(r)
+    for b, (n_main, xtl) in enumerate([(4, 900), (0, 1024), (2, 0)]):
+        rs = sorted(by_row.get(b, []), key=lambda r: r[3] if r[3] >= 0 else 0)
+        main = [r for r in rs if r[1] < W]
+        extra = [r for r in rs if r[1] >= W]
+        assert len(main) == n_main
+        assert [(int(r[1]) - W, int(r[2]) - W) for r in sorted(extra, key=lambda r: r[1])] == \
+            [(i * S, min((i + 1) * S, xtl)) for i in range(-(-xtl // S))]
+        # partial slots: the row's main splits first, then its extra splits
+        if len(rs) > 1:
+            slots = [int(r[3]) for r in sorted(main, key=lambda r: r[1])] + \
+                    [int(r[3]) for r in sorted(extra, key=lambda r: r[1])]
+            assert slots == list(range(slots[0], slots[0] + len(slots)))
+    assert info["num_segments"] == 4 + 0 + 2 + 2 + 2 + 0
+
+
+@settings(max_examples=40, deadline=None)
+@given(xtl=st.lists(st.integers(-3, 1300), min_size=1, max_size=8), seed=st.integers(0, 2 ** 31 - 1))
+def test_extra_splits_of_a_row_do_not_depend_on_batchmates(xtl, seed):
+    rng = np.random.default_rng(seed)
+    B = len(xtl)
+    lens = rng.integers(1, 70000, B)
+    tl = rng.integers(0, 2049, B)
+    segs, _ = extra_segments(lens, tl, xtl)
+    for b in range(B):
+        solo, _ = extra_segments([lens[b]], [tl[b]], [xtl[b]])
+        mine = sorted((int(r[1]), int(r[2])) for r in segs if r[0] == b)
+        assert mine == sorted((int(r[1]), int(r[2])) for r in solo)
+
+
+def test_extra_source_arguments_are_checked():
+    bad = [
+        (dict(), dict(page_size=0), -1, "positive"),
+        (dict(), dict(topk_width=0), -1, "positive"),
+        (dict(), dict(num_pages=2 ** 26, page_size=64), -2, "2^31"),
+        (dict(topk_width=0), dict(), -2, "sparse MLA"),
+        (dict(split_mode=isk.SPLIT_BATCH_BALANCED), dict(), -2, "per-row"),
+    ]
+    for dkw, xkw, status, text in bad:
+        with pytest.raises(isk.IskError) as e:
+            isk.plan_create_extra(mla_desc(**{"topk_width": 2048, **dkw}), xdesc(**xkw), [100], [10], [5])
+        assert e.value.status == status and text in e.value.message, (e.value.status, e.value.message)
+    with pytest.raises(isk.IskError) as e:
+        isk.plan_create_extra(mla_desc(topk_width=2048), xdesc(), [100], [10], None)
+    assert e.value.status == -1 and "extra_topk_len_host" in e.value.message
+    # an extra plan is not re-planned in place
+    with isk.Plan(mla_desc(topk_width=2048), [100], [10], extra=xdesc(), extra_topk_len_host=[5]) as p:
+        with pytest.raises(isk.IskError) as e:
+            p.update([200], [20])
+        assert e.value.status == -1 and "isk_plan_create_extra" in e.value.message
+
+
+def test_decode_entry_points_match_the_plan_kind():
+    # Mismatches are rejected before any device work (fake, aligned addresses).
+    A = 1 << 20
+    with isk.Plan(mla_desc(topk_width=2048), [100], [10], extra=xdesc(), extra_topk_len_host=[5]) as p:
+        with pytest.raises(isk.IskError) as e:
+            isk.attn_decode(p.handle, A, A, A, A, A, A, A, A, A, p.workspace_bytes, 0)
+        assert "isk_attn_decode_extra" in e.value.message
+        with pytest.raises(isk.IskError) as e:
+            isk.attn_decode_extra(p.handle, A, A, A, A, A, A, A, None, A, A, A, A, A, A, p.workspace_bytes, 0)
+        assert e.value.status == -1 and "non-NULL" in e.value.message
+    with isk.Plan(mla_desc(topk_width=2048), [100], [10]) as p:
+        with pytest.raises(isk.IskError) as e:
+            isk.attn_decode_extra(p.handle, A, A, A, A, A, A, A, A, A, A, A, A, A, A, p.workspace_bytes, 0)
+        assert "no extra KV source" in e.value.message

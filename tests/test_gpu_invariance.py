@@ -47,6 +47,11 @@ def solo_case(case, b, structure_seed):
     one = synth.mla_case([case.lens[b]], case.hq, case.scale, case.paging.page_size, structure_seed,
                          topk_width=case.topk_width, split_tokens=case.split_tokens, seeds=[0])
     one.rows = [case.rows[b]]
+    if case.extra is not None:
+        x = case.extra
+        one.extra = synth.mla_case([x.lens[b]], case.hq, case.scale, x.paging.page_size, structure_seed + 1,
+                                   topk_width=x.topk_width, split_tokens=case.split_tokens, seeds=[0])
+        one.extra.rows = [x.rows[b]]
     return one
 
 
@@ -82,10 +87,11 @@ def test_cold_and_warm_cache_give_the_same_bits():
     assert np.array_equal(warm_b, warm2_b)
 
 
-@pytest.mark.parametrize("which", ["config1", "config2", "config3", "config4"])
+@pytest.mark.parametrize("which", ["config1", "config2", "config3", "config4", "config4_extra"])
 def test_every_row_solo_equals_batched(which):
     case = {"config1": synth.config1_gqa_tiny, "config2": synth.config2_gqa,
-            "config3": synth.config3_mla, "config4": synth.config4_sparse}[which]()
+            "config3": synth.config3_mla, "config4": synth.config4_sparse,
+            "config4_extra": synth.config4_sparse_extra}[which]()
     _, _, bits, lbits = run_bits(case)
     mism = []
     for b in range(case.batch):

@@ -231,3 +231,59 @@ def test_oneshot_entry_matches_planned_call(kind):
     parity(out2.float().cpu().numpy().astype(np.float64), lse2.cpu().numpy().astype(np.float64), ro, rl, False,
            f"oneshot {kind}")
     dc.close()
+
+
+# ----------------------------------------------------------------------------
+# Extra KV source (a second gathered set per row, from its own cache)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_sparse_extra_source(out_f32):
+    case = synth.config4_sparse_extra()
+    out, lse, _, _ = run_case(case, out_f32=out_f32)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, out_f32, f"sparse + extra out_f32={out_f32}")
+
+
+def test_sparse_extra_source_edges():
+    """Either set empty, both empty, masked extra slots, an extra set of three
+    splits, a smaller extra page size, garbage in unused slots."""
+    lens = [3000, 900, 50, 4000, 2500, 6000]
+    xlens = [400, 2000, 0, 9, 1500, 3000]
+    XW = 1100
+    case = synth.mla_extra_case(lens, xlens, 128, 1.0 / math.sqrt(192.0), 64, structure_seed=70,
+                                topk_width=700, extra_width=XW, extra_page_size=16)
+    rows, xrows = case.rows, case.extra.rows
+    xrows[0].topk_len = 0                                # extra set empty
+    rows[1].topk_len = 0                                 # main set empty
+    rows[2].topk_len = 0                                 # both empty (extra len 0)
+    xrows[4].topk_idx[[0, 7, 300]] = -1                  # -1 inside the extra topk_len
+    xrows[4].topk_idx[[1, 2]] = [1500, 99999]            # >= extra len: skipped
+    xrows[5].topk_len = 1100                             # three extra splits of 512
+    out, lse, _, _ = run_case(case, fill=GARBAGE)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, "sparse + extra edges")
+    assert np.all(out[2] == 0) and np.all(np.isneginf(lse[2]))
+
+
+def test_sparse_extra_source_audit():
+    case = synth.mla_extra_case([300, 200], [100, 50], 64, 0.1, 64, structure_seed=71, topk_width=64,
+                                extra_width=32)
+    case.extra.rows[1].topk_idx[4] = 60                  # >= extra len 50 inside the extra topk_len
+    dc = DeviceCase(case, check_inputs=True)
+    with pytest.raises(isk.IskError) as e:
+        dc.run()
+    assert e.value.status == -4 and "extra topk_idx[1][4]" in e.value.message
+    dc.close()
+    good = DeviceCase(synth.mla_extra_case([300, 200], [100, 50], 64, 0.1, 64, structure_seed=72, topk_width=64,
+                                           extra_width=32), check_inputs=True)
+    good.run()
+    good.close()
+
+
+def test_sparse_extra_source_16_head_kernel():
+    case = synth.mla_extra_case([3000, 700, 5000], [900, 30, 2000], 64, 1.0 / math.sqrt(192.0), 64,
+                                structure_seed=73, topk_width=600, extra_width=700)
+    out, lse, _, _ = run_case(case)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, "sparse + extra, 64 heads")

@@ -86,7 +86,21 @@ class DeviceCase:
         self.topk_len_host = case.topk_len() if sparse else None
         self.topk_idx = torch.from_numpy(case.topk_idx()).to(device) if sparse else None
         self.topk_len = torch.from_numpy(self.topk_len_host).to(device) if sparse else None
-        self.plan = isk.Plan(self.desc, self.lens_host, self.topk_len_host)
+        self.extra = getattr(case, "extra", None)
+        if self.extra is not None:
+            x = self.extra
+            self.x_pool = device_pool(x, device, fill)
+            self.x_block_table = torch.from_numpy(x.paging.block_table).to(device)
+            self.x_lens = torch.from_numpy(np.asarray(x.lens, dtype=np.int32)).to(device)
+            self.x_topk_idx = torch.from_numpy(x.topk_idx()).to(device)
+            self.x_topk_len_host = x.topk_len()
+            self.x_topk_len = torch.from_numpy(self.x_topk_len_host).to(device)
+            xdesc = isk.IskExtraDesc(x.paging.page_size, x.paging.num_pages, x.paging.max_pages_per_row,
+                                     x.topk_width)
+            self.plan = isk.Plan(self.desc, self.lens_host, self.topk_len_host, extra=xdesc,
+                                 extra_topk_len_host=self.x_topk_len_host)
+        else:
+            self.plan = isk.Plan(self.desc, self.lens_host, self.topk_len_host)
         dv = self.desc.head_dim_v
         self.out = torch.empty((case.batch, case.hq, dv), dtype=torch.float32 if out_f32 else torch.bfloat16,
                                device=device)
@@ -95,6 +109,11 @@ class DeviceCase:
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
 
     def run(self, stream=None) -> None:
+        if self.extra is not None:
+            isk.attn_decode_extra(self.plan.handle, self.q, self.pool, self.block_table, self.lens, self.topk_idx,
+                                  self.topk_len, self.x_pool, self.x_block_table, self.x_lens, self.x_topk_idx,
+                                  self.x_topk_len, self.out, self.lse, self.workspace, self.ws_bytes, stream)
+            return
         isk.attn_decode(self.plan.handle, self.q, self.pool, self.block_table, self.lens, self.topk_idx,
                         self.topk_len, self.out, self.lse, self.workspace, self.ws_bytes, stream)
 
@@ -117,7 +136,10 @@ def kv_bytes(case) -> int:
     if isinstance(case, synth.GqaCase):
         return int(np.sum(case.lens)) * case.hkv * case.d * 2 * 2
     if case.sparse:
-        return int(np.sum(case.topk_len())) * synth.MLA_DQK * 2
+        n = int(np.sum(case.topk_len()))
+        if getattr(case, "extra", None) is not None:
+            n += int(np.sum(case.extra.topk_len()))
+        return n * synth.MLA_DQK * 2
     return int(np.sum(case.lens)) * synth.MLA_DQK * 2
 
 
@@ -132,4 +154,8 @@ def io_bytes(case) -> int:
     b += pages * 4 + case.batch * 4
     if isinstance(case, synth.MlaCase) and case.sparse:
         b += int(np.sum(case.topk_len())) * 4 + case.batch * 4
+    if getattr(case, "extra", None) is not None:
+        x = case.extra
+        b += sum(math.ceil(int(L) / x.paging.page_size) for L in x.lens) * 4 + x.batch * 4
+        b += int(np.sum(x.topk_len())) * 4 + x.batch * 4
     return b

@@ -211,6 +211,9 @@ class MlaCase:
     paging: Paging
     topk_width: int = 0         # 0 = dense
     split_tokens: int = 0
+    # sparse only: a second gathered set per row from its own cache (the
+    # extra KV source); a sparse case of the same batch whose q is unused
+    extra: Optional["MlaCase"] = None
 
     @property
     def batch(self) -> int:
@@ -300,6 +303,26 @@ def mla_case(lens, hq, scale, page_size, structure_seed, std=0.5, topk_width=0, 
     return MlaCase(rows, lens, hq, scale, paging, topk_width, split_tokens)
 
 
+EXTRA_SEED_OFFSET = 1 << 40   # extra-set row seed = main row seed + this
+
+
+def mla_extra_case(lens, extra_lens, hq, scale, page_size, structure_seed, topk_width, extra_width,
+                   extra_page_size=None, std=0.5, topk=None, extra_topk=None, split_tokens=0,
+                   seeds: Optional[Sequence[int]] = None) -> MlaCase:
+    """Sparse MLA case with an extra KV source: each row also attends
+    ``min(extra_topk, extra_len)`` positions of its own extra cache.  The
+    extra set of a row is drawn from the row's seed plus EXTRA_SEED_OFFSET,
+    so it too does not depend on the batch."""
+    lens = np.asarray(lens, dtype=np.int32)
+    seeds = [row_seed(structure_seed, b) for b in range(len(lens))] if seeds is None else list(seeds)
+    case = mla_case(lens, hq, scale, page_size, structure_seed, std=std, topk_width=topk_width, topk=topk,
+                    split_tokens=split_tokens, seeds=seeds)
+    case.extra = mla_case(extra_lens, hq, scale, page_size if extra_page_size is None else extra_page_size,
+                          structure_seed + 7919, std=std, topk_width=extra_width, topk=extra_topk,
+                          split_tokens=split_tokens, seeds=[s + EXTRA_SEED_OFFSET for s in seeds])
+    return case
+
+
 # ----------------------------------------------------------------------------
 # The five workloads (shapes, distributions and structure of the decode
 # batches the pages describe; sizes as stated in each docstring)
@@ -346,6 +369,20 @@ def config4_sparse(batch: int = 64, lens=None, width: int = 2048) -> MlaCase:
     lens = config4_sparse_lens(4, batch) if lens is None else lens
     return mla_case(lens, 128, 1.0 / math.sqrt(192.0), 64, structure_seed=4, std=0.5,
                     topk_width=width)
+
+
+def config4_extra_lens(seed: int = 4, batch: int = 64) -> np.ndarray:
+    return lens_uniform(np.random.default_rng([seed, 2]), batch, 512, 8192)
+
+
+def config4_sparse_extra(batch: int = 64) -> MlaCase:
+    """Sparse MLA with an extra KV source: the config-4 main set (lens
+    uniform in [2048, 65536], 2048 top-k positions) plus, per row, 512
+    positions drawn without replacement from an extra cache of its own with
+    lens uniform in [512, 8192] (64-token pages).  The pages name the extra
+    source but give no sizes; these are this workload's choice."""
+    return mla_extra_case(config4_sparse_lens(4, batch), config4_extra_lens(4, batch), 128,
+                          1.0 / math.sqrt(192.0), 64, structure_seed=4, topk_width=2048, extra_width=512)
 
 
 PROBE_LEN = 16384
