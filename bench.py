@@ -189,6 +189,39 @@ def cold_steps(dc, torch, n):
     return times
 
 
+def sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes, calls=100):
+    """The config-4 sparse batch (B=64, 2048 top-k positions per row) and the
+    same batch with an extra KV source (512 more positions per row from a
+    second cache): warm and cold (1 GiB flush first) call times and gathered
+    KV GB/s.  The gathered bytes (151 MB, 189 MB with the extra set) fit in
+    the 256 MB Infinity Cache, so the cold figure is the HBM one."""
+    res = {}
+    stream = torch.cuda.current_stream()
+    for name, make in (("sparse_b64_k2048", synth.config4_sparse),
+                       ("sparse_extra_b64_k2048_x512", synth.config4_sparse_extra)):
+        case = make()
+        dc = DeviceCase(case)
+        kvb = kv_bytes(case)
+        for _ in range(20):
+            dc.run(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(calls):
+            dc.run(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        warm = a.elapsed_time(b) / calls
+        cold = float(np.median(cold_steps(dc, torch, 30)))
+        info = dc.plan.info()
+        res[name] = {"gathered_tokens": kvb // (synth.MLA_DQK * 2), "splits": info["num_segments"],
+                     "warm_ms_per_call": round(warm, 5), "warm_kv_gbs": round(kvb / (warm * 1e-3) / 1e9, 2),
+                     "cold_ms_per_call": round(cold, 5), "cold_kv_gbs": round(kvb / (cold * 1e-3) / 1e9, 2)}
+        dc.close()
+        del dc
+        torch.cuda.empty_cache()
+    return res
+
+
 def invariance_pass_rate(case, out_bits, lse_bits, mode, synth, DeviceCase, rows):
     """Rows re-run alone in a freshly permuted page pool with a fresh plan:
     bit equality of out (bf16) and lse (fp32) with the batched run."""
@@ -363,6 +396,8 @@ def main():
             dcb.close()
             log("per-row vs balanced at batch sizes 1, 2, 8, 32, 128 (invariance-stress lengths)")
             res["per_row_over_balanced_by_batch"] = per_row_vs_balanced_sizes(isk, synth, torch, np)
+        log("sparse decode (config-4 batch) with and without an extra KV source")
+        res["sparse"] = sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes)
         if not args.no_cpu_baseline:
             log(f"CPU baseline: fp64 oracle for ~{args.cpu_seconds:.0f} s")
             res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
