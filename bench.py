@@ -13,9 +13,10 @@ region is exactly `--steps` steps after `--warmup` untimed ones, bracketed by
 device synchronisation, with nothing else recorded on the stream (per-step
 timing events would add their own gaps to the step).  The split kernel's
 duration for the roofline comes from a second pass of `--steps` steps right
-after it, in which the library records HIP events around each launch on the
-same stream.  Prints one JSON line: the metric, the roofline of the split
-kernel and the CPU oracle baseline.
+after it, in which the library launches the split kernel through
+hipExtLaunchKernel with a start and a stop HIP event, so the events carry the
+kernel's own start and end on its stream.  Prints one JSON line: the metric,
+the roofline of the split kernel and the CPU oracle baseline.
 """
 
 import argparse
@@ -97,8 +98,9 @@ class HipEvents:
 
 def timed_steps(dc, isk, torch, evs, steps, warmup, lens_host, instrument):
     """Warm up, then time exactly `steps` steps.  With `instrument`, the
-    library's timing hook records HIP events around every split and combine
-    launch and their per-step durations are returned too (None otherwise)."""
+    library's timing hook stamps HIP events with every split kernel's start and
+    end and records one after every combine; their per-step durations are
+    returned too (None otherwise)."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         dc.plan.update(lens_host)
@@ -314,7 +316,7 @@ def main():
 
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps (mode {args.mode})")
     total_ms, wall, _, _ = timed_steps(dc, isk, torch, evs, args.steps, args.warmup, lens_host, False)
-    log(f"kernel durations: {args.steps} more steps with HIP events around each launch")
+    log(f"kernel durations: {args.steps} more steps with kernel-bound HIP events")
     inst_ms, _, split, comb = timed_steps(dc, isk, torch, evs, args.steps, 0, lens_host, True)
     ms_step = total_ms / args.steps
     # Host cost of re-planning the batch (part of every step above).
