@@ -215,6 +215,14 @@ __device__ __forceinline__ void wait_lgkm() {
 //    three vector-ALU instructions in each MFMA's shadow.
 constexpr int kPBytes = kWaves * 2 * 1024;   // pl[4][2][64] x 16 B
 constexpr int kXBytes = 32 * 16;             // per-head floats [n][ht]: alpha, later l
+// Sparse segments: the pool rows of a window of kWinSlots top-k slots are
+// resolved once per window (index, then block-table entry) into LDS, so a
+// tile's loads need no dependent global reads (whose waits would also wait
+// for the tile loads already in flight).
+constexpr int kWinSlots = 1024;
+constexpr int kWinBytes = kWinSlots * 4;
+constexpr uint32_t kNoRow = 0xffffffffu;     // masked slot
+static_assert(kWinSlots % 256 == 0 && kWinSlots % kTok == 0, "window fill and tile alignment");
 
 template <int VF>
 struct VFrag {
@@ -533,16 +541,48 @@ struct Stager {
     }
   }
 
-  // All 9 loads of a sparse tile (slots u0 .. u0+31 of the top-k list).
-  __device__ __forceinline__ uint32_t issue_sparse(int u0, ISK_LDS unsigned char* buf, int wave, int lane) const {
+  // Sparse: pool rows of slots [w0, w0 + kWinSlots) into the LDS window
+  // (kNoRow where the slot is past the segment, its position is outside
+  // [0, len) or its page is outside the pool); kWinSlots / 256 slots per
+  // thread of the workgroup.  The caller makes the writes visible (lgkmcnt
+  // wait and barrier) before any issue_sparse reads them.  With kGroup =
+  // kWinSlots / 256 all index reads go out together, then all table reads
+  // (segment start); with kGroup = 1 one slot is resolved at a time, which
+  // keeps few registers live (window moves inside the tile loop).
+  template <int kGroup>
+  __device__ __forceinline__ void fill_window(int w0, ISK_LDS uint32_t* win, int tid) const {
+    static_assert((kWinSlots / 256) % kGroup == 0, "group size");
+    // Opaque to the compiler here, so the division set-up below is not
+    // hoisted out of the tile loop and kept live across it.
+    int ps = page_size;
+    asm volatile("" : "+s"(ps));
+#pragma unroll
+    for (int k0 = 0; k0 < kWinSlots / 256; k0 += kGroup) {
+      int pos[kGroup];
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        const int slot = w0 + 256 * (k0 + k) + tid;
+        pos[k] = slot < seg_end ? idx_row[slot] : -1;
+      }
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        bool ok = pos[k] >= 0 && pos[k] < len;
+        const int pg = ok ? bt_row[pos[k] / ps] : 0;
+        ok = ok && pg >= 0 && pg < num_pages;
+        win[256 * (k0 + k) + tid] = ok ? (uint32_t)pg * (uint32_t)ps + (uint32_t)(pos[k] % ps) : kNoRow;
+      }
+    }
+  }
+
+  // All 9 loads of a sparse tile (slots u0 .. u0+31 of the top-k list); the
+  // slots' pool rows come from the LDS window that starts at slot wbase
+  // (u0 - wbase is in [0, kWinSlots - kTok]).
+  __device__ __forceinline__ uint32_t issue_sparse(int u0, ISK_LDS unsigned char* buf, int wave, int lane,
+                                                   const ISK_LDS uint32_t* win, int wbase) const {
     const unsigned char* zero = (const unsigned char*)g_zero_piece;
-    const int slot = u0 + (lane & 31);
-    bool ok = lane < 32 && slot < seg_end;
-    const int pos = ok ? idx_row[slot] : -1;
-    ok = ok && pos >= 0 && pos < len;
-    const int pg = ok ? bt_row[pos / page_size] : 0;
-    ok = ok && pg >= 0 && pg < num_pages;
-    const uint32_t my_row = ok ? (uint32_t)pg * (uint32_t)page_size + (uint32_t)(pos % page_size) : 0u;
+    const uint32_t row = win[u0 - wbase + (lane & 31)];
+    const bool ok = lane < 32 && row != kNoRow;
+    const uint32_t my_row = ok ? row : 0u;
     const uint32_t mask = (uint32_t)__ballot(ok);
     int l = lane;
     asm volatile("" : "+v"(l));
@@ -559,33 +599,32 @@ struct Stager {
     return mask;
   }
 
-  // Whole tile at once; returns the row-valid mask.
+  // Whole dense tile at once; returns the row-valid mask.
   __device__ __forceinline__ uint32_t operator()(int u0, ISK_LDS unsigned char* buf, int wave, int lane,
                                                  const LoadOffsets& so, int pbase, int pwin) const {
-    if constexpr (kSparse) {
-      return issue_sparse(u0, buf, wave, lane);
-    } else {
-      const DenseTile t = plan(u0, u0 / page_size, u0 % page_size, pbase, pwin);
-      if (t.mask == ~0u) {
+    const DenseTile t = plan(u0, u0 / page_size, u0 % page_size, pbase, pwin);
+    if (t.mask == ~0u) {
 #pragma unroll
-        for (int jj = 0; jj < kLoadsPerWave; ++jj)
-          load_lds_16(t.base + (size_t)so(jj), buf + (wave + kWaves * jj) * 1024);
-      } else {
-        issue_masked(t, buf, wave, lane, so);
-      }
-      return t.mask;
+      for (int jj = 0; jj < kLoadsPerWave; ++jj)
+        load_lds_16(t.base + (size_t)so(jj), buf + (wave + kWaves * jj) * 1024);
+    } else {
+      issue_masked(t, buf, wave, lane, so);
     }
+    return t.mask;
   }
 };
 
 template <bool kSparse>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(231)))
 mla_split_h32_kernel(MlaLaunch a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kBufs * kTileBytes + kPBytes + kXBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char
+      lds_raw[kBufs * kTileBytes + kPBytes + kXBytes + (kSparse ? kWinBytes : 0)];
   ISK_LDS unsigned char* tiles = (ISK_LDS unsigned char*)lds_raw;
   const uint32_t tiles_u32 = (uint32_t)(uintptr_t)tiles;
   const uint32_t pl_u32 = tiles_u32 + kBufs * kTileBytes;   // fp16 P of the current tile, all heads
   const uint32_t x_u32 = pl_u32 + kPBytes;                  // per-head alpha (per tile) or l (epilogue)
+  // sparse: pool rows of the current window of top-k slots
+  ISK_LDS uint32_t* const win = (ISK_LDS uint32_t*)(lds_raw + kBufs * kTileBytes + kPBytes + kXBytes);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n32 = lane & 31, hh = lane >> 5, i16 = lane & 15, gp = (lane >> 4) & 1;
@@ -661,6 +700,14 @@ mla_split_h32_kernel(MlaLaunch a) {
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) qr[kk] = qrow[2 * kk];
     }
+    // Sparse: the row window of the segment's first kWinSlots slots (its
+    // index and table reads are waited for here, together with the query).
+    int wbase = sg.begin;
+    if constexpr (kSparse) {
+      stage.template fill_window<kWinSlots / 256>(wbase, win, (int)threadIdx.x);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+    }
     // The window has landed once only the query loads are younger.
     wait_vmcnt<kKSteps>();
 
@@ -676,7 +723,10 @@ mla_split_h32_kernel(MlaLaunch a) {
     for (int t = 0; t < 3; ++t) {
       ISK_LDS unsigned char* tb = tiles + t * kTileBytes;
       if (t < n_tiles) {
-        mk[t] = stage(sg.begin + t * kTok, tb, wave_u, lane, so, pbase, pwin);
+        if constexpr (kSparse)
+          mk[t] = stage.issue_sparse(sg.begin + t * kTok, tb, wave_u, lane, win, wbase);
+        else
+          mk[t] = stage(sg.begin + t * kTok, tb, wave_u, lane, so, pbase, pwin);
       } else {
         mk[t] = 0u;
         stage.issue_masked(DenseTile{(const unsigned char*)a.kv, 0u}, tb, wave_u, lane, so);
@@ -740,7 +790,15 @@ mla_split_h32_kernel(MlaLaunch a) {
       const int u0n = sg.begin + (it + 3) * kTok;
       if (stage_on) {
         if constexpr (kSparse) {
-          mk2 = stage.issue_sparse(u0n, nbuf, wave_u, lane);
+          if (u0n - wbase >= kWinSlots) {   // every 32 tiles: the next window
+            // Every wave issued its last tile from the old window before
+            // the barrier at the top of this step.
+            wbase += kWinSlots;
+            stage.template fill_window<1>(wbase, win, (int)threadIdx.x);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+          }
+          mk2 = stage.issue_sparse(u0n, nbuf, wave_u, lane, win, wbase);
         } else if (pn - pbase >= 64) {   // every 64 pages: the next window
           pbase = pn;
           load_window();
