@@ -224,6 +224,45 @@ def sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes, calls=100):
     return res
 
 
+def gqa_extras(isk, synth, torch, np, DeviceCase, kv_bytes, calls=50):
+    """The dense GQA Llama-8B-shaped batch (B=32, Hq=32, Hkv=8, D=128, lens
+    uniform in [128, 8192], 16-token pages): warm and cold call times, KV
+    GB/s and the split kernel's share of the 8 TB/s peak (kernel-bound
+    events)."""
+    stream = torch.cuda.current_stream()
+    case = synth.config2_gqa()
+    dc = DeviceCase(case)
+    kvb = kv_bytes(case)
+    for _ in range(20):
+        dc.run(stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(calls):
+        dc.run(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    warm = a.elapsed_time(b) / calls
+    cold = float(np.median(cold_steps(dc, torch, 20)))
+    evs = HipEvents()
+    marks = [(evs.create(), evs.create()) for _ in range(calls)]
+    for m in marks:
+        isk.plan_set_timing_events(dc.plan.handle, m[0], m[1], None)
+        dc.run(stream)
+    torch.cuda.synchronize()
+    isk.plan_set_timing_events(dc.plan.handle, None, None, None)
+    split = float(np.mean([evs.elapsed_ms(x, y) for x, y in marks]))
+    for x, y in marks:
+        evs.destroy(x)
+        evs.destroy(y)
+    info = dc.plan.info()
+    dc.close()
+    q_bytes = case.batch * case.hq * case.d * 2
+    return {"kv_bytes": kvb, "splits": info["num_segments"], "warm_ms_per_call": round(warm, 5),
+            "warm_kv_gbs": round(kvb / (warm * 1e-3) / 1e9, 2), "cold_ms_per_call": round(cold, 5),
+            "cold_kv_gbs": round(kvb / (cold * 1e-3) / 1e9, 2), "split_kernel_ms": round(split, 5),
+            "split_kernel_frac_of_hbm_peak": round((kvb + q_bytes) / (split * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def invariance_pass_rate(case, out_bits, lse_bits, mode, synth, DeviceCase, rows):
     """Rows re-run alone in a freshly permuted page pool with a fresh plan:
     bit equality of out (bf16) and lse (fp32) with the batched run."""
@@ -398,6 +437,8 @@ def main():
             dcb.close()
             log("per-row vs balanced at batch sizes 1, 2, 8, 32, 128 (invariance-stress lengths)")
             res["per_row_over_balanced_by_batch"] = per_row_vs_balanced_sizes(isk, synth, torch, np)
+        log("dense GQA (Llama-8B-shaped batch)")
+        res["gqa"] = gqa_extras(isk, synth, torch, np, DeviceCase, kv_bytes)
         log("sparse decode (config-4 batch) with and without an extra KV source")
         res["sparse"] = sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes)
         if not args.no_cpu_baseline:
