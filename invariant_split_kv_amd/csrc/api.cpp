@@ -45,11 +45,37 @@ struct isk_plan {
   hipEvent_t staged[kRing] = {};
   int ring_next = 0;
   hipEvent_t t_split_begin = nullptr, t_split_end = nullptr, t_combine_end = nullptr;   // profiling hook
+  isk::InlinePlan inl{};                  // n_segs > 0: passed by value, no upload
 };
 
 namespace {
 
+// Dense per-row plans that fit go to the kernels by value (see InlinePlan).
+void build_inline(isk_plan* p) {
+  const PlanData& d = p->data;
+  isk::InlinePlan& inl = p->inl;
+  inl = isk::InlinePlan{};
+  const bool fits = d.desc.split_mode == ISK_SPLIT_PER_ROW && d.desc.topk_width == 0 && !d.has_extra &&
+                    !d.segs.empty() && d.segs.size() <= (size_t)isk::kInlineSegs && d.batch <= isk::kInlineRows &&
+                    d.groups.size() == d.segs.size() + 1;
+  if (!fits) return;
+  for (size_t j = 0; j < d.segs.size(); ++j) {
+    const isk::Seg& sg = d.segs[j];
+    const int32_t i = sg.begin / d.split_units;
+    // The kernels rebuild exactly this segment from (row, i) and the row's length.
+    if (d.groups[j] != (int32_t)j || i > 0xffff || sg.begin != i * d.split_units ||
+        sg.end != std::min((i + 1) * d.split_units, d.units[sg.row]))
+      return;
+    inl.seg[j] = ((uint32_t)sg.row << 16) | (uint32_t)i;
+  }
+  for (int b = 0; b < d.batch; ++b) inl.rows[b] = d.rows[b];
+  inl.split_units = d.split_units;
+  inl.cap = (int32_t)std::min<long long>((long long)d.desc.max_pages_per_row * d.desc.page_size, 0x7fffffffLL);
+  inl.n_segs = (int32_t)d.segs.size();
+}
+
 void serialise(isk_plan* p) {
+  build_inline(p);
   p->layout = isk::meta_layout(p->data);
   p->meta_host.assign(p->layout.bytes, 0);
   std::memcpy(p->meta_host.data() + p->layout.segs_off, p->data.segs.data(), p->data.segs.size() * sizeof(isk::Seg));
@@ -355,32 +381,36 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
     if (rc != ISK_OK) return rc;
   }
 
-  // Upload the metadata through a pinned staging slot.
-  const int slot = plan->ring_next;
-  plan->ring_next = (slot + 1) % kRing;
+  // Upload the metadata through a pinned staging slot (plans passed by value
+  // in the kernel arguments need none).
   hipError_t e;
-  if (plan->staged[slot] != nullptr) {
-    e = hipEventSynchronize(plan->staged[slot]);
-    if (e != hipSuccess) return hip_err(e, "waiting for an earlier metadata upload");
-  } else {
-    e = hipEventCreateWithFlags(&plan->staged[slot], hipEventDisableTiming);
-    if (e != hipSuccess) return hip_err(e, "hipEventCreate");
-  }
-  const size_t mbytes = plan->layout.bytes;
-  if (plan->staging_bytes[slot] < mbytes) {
-    if (plan->staging[slot] != nullptr) (void)hipHostFree(plan->staging[slot]);
-    plan->staging[slot] = nullptr;
-    plan->staging_bytes[slot] = 0;
-    e = hipHostMalloc(&plan->staging[slot], mbytes, hipHostMallocDefault);
-    if (e != hipSuccess) return hip_err(e, "hipHostMalloc (metadata staging)");
-    plan->staging_bytes[slot] = mbytes;
-  }
-  std::memcpy(plan->staging[slot], plan->meta_host.data(), mbytes);
+  const bool by_value = plan->inl.n_segs > 0;
   unsigned char* ws = (unsigned char*)workspace;
-  e = hipMemcpyAsync(ws, plan->staging[slot], mbytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (metadata upload)");
-  e = hipEventRecord(plan->staged[slot], stream);
-  if (e != hipSuccess) return hip_err(e, "hipEventRecord");
+  if (!by_value) {
+    const int slot = plan->ring_next;
+    plan->ring_next = (slot + 1) % kRing;
+    if (plan->staged[slot] != nullptr) {
+      e = hipEventSynchronize(plan->staged[slot]);
+      if (e != hipSuccess) return hip_err(e, "waiting for an earlier metadata upload");
+    } else {
+      e = hipEventCreateWithFlags(&plan->staged[slot], hipEventDisableTiming);
+      if (e != hipSuccess) return hip_err(e, "hipEventCreate");
+    }
+    const size_t mbytes = plan->layout.bytes;
+    if (plan->staging_bytes[slot] < mbytes) {
+      if (plan->staging[slot] != nullptr) (void)hipHostFree(plan->staging[slot]);
+      plan->staging[slot] = nullptr;
+      plan->staging_bytes[slot] = 0;
+      e = hipHostMalloc(&plan->staging[slot], mbytes, hipHostMallocDefault);
+      if (e != hipSuccess) return hip_err(e, "hipHostMalloc (metadata staging)");
+      plan->staging_bytes[slot] = mbytes;
+    }
+    std::memcpy(plan->staging[slot], plan->meta_host.data(), mbytes);
+    e = hipMemcpyAsync(ws, plan->staging[slot], mbytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (metadata upload)");
+    e = hipEventRecord(plan->staged[slot], stream);
+    if (e != hipSuccess) return hip_err(e, "hipEventRecord");
+  }
 
   const isk::Seg* segs = (const isk::Seg*)(ws + plan->layout.segs_off);
   const int32_t* groups = (const int32_t*)(ws + plan->layout.groups_off);
@@ -396,14 +426,14 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
   if (d.kind == ISK_KIND_GQA) {
     isk::GqaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, segs, groups, part_o, part_lse,
                      out, lse, n_groups, d.num_q_heads, d.num_kv_heads, d.head_dim_qk, d.page_size, d.num_pages,
-                     d.max_pages_per_row, d.out_dtype == ISK_OUT_F32, scale_log2};
+                     d.max_pages_per_row, d.out_dtype == ISK_OUT_F32, scale_log2, plan->inl};
     e = isk::launch_gqa_split(a, stream, ev);
     if (e != hipSuccess) return hip_err(e, "launching the GQA split kernel");
   } else {
     isk::MlaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, sparse ? topk_idx : nullptr,
                      segs, groups, part_o, part_lse, out, lse, n_groups, d.num_q_heads, d.page_size, d.num_pages,
                      d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2,
-                     nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0};
+                     nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, plan->inl};
     if (extra != nullptr) {
       a.xkv = (const uint16_t*)extra->kv_pages;
       a.xblock_table = extra->block_table;
@@ -420,7 +450,7 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
   }
   if (pd.any_combine) {
     isk::CombineLaunch c{rows, part_o, part_lse, out, lse, pd.batch, d.num_q_heads, d.head_dim_v,
-                         d.out_dtype == ISK_OUT_F32};
+                         d.out_dtype == ISK_OUT_F32, plan->inl};
     e = isk::launch_combine(c, stream);
     if (e != hipSuccess) return hip_err(e, "launching the combine kernel");
   }

@@ -50,7 +50,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= a.batch * a.hq) return;
   const int b = pair / a.hq, h = pair - b * a.hq;
-  const RowInfo ri = a.rows[b];
+  const RowInfo ri = a.inl.n_segs > 0 ? a.inl.rows[b] : a.rows[b];
   if (ri.n_parts == 1) return;
 
   float o[DPL];

@@ -90,11 +90,12 @@ __global__ void __launch_bounds__(256) gqa_split_kernel(GqaLaunch a) {
   const int g = a.hq / a.hkv;
   const int hk = blockIdx.y;
   const int task = blockIdx.x;
-  const int seg_first = a.groups[task], seg_last = a.groups[task + 1];
+  const bool inl = a.inl.n_segs > 0;   // segments by value: one per task
+  const int seg_first = inl ? task : a.groups[task], seg_last = inl ? task + 1 : a.groups[task + 1];
   ISK_LDS float* my_p = p_lds + wave * HPW * kTile;
 
   for (int si = seg_first; si < seg_last; ++si) {
-    const Seg sg = a.segs[si];
+    const Seg sg = fetch_seg(a.inl, a.segs, a.lens, si);
     const int b = sg.row;
     __syncthreads();   // LDS tiles of the previous segment are no longer read
 

@@ -43,6 +43,33 @@ struct RowInfo {
   int32_t n_parts;    // 0: empty row; 1: written directly; >1: combined
 };
 
+// Dense per-row plans small enough for the kernel arguments travel there
+// instead of through the workspace, so a decode call enqueues no upload copy
+// before its kernels.  Segment j (one per workgroup task, launch order) is
+// stored as row << 16 | split index i, and its range is rebuilt from the
+// row's length: [i*S, min((i+1)*S, min(lens[row], cap))); its partial slot
+// is rows[row].part_off + i when the row has more than one split, else -1.
+constexpr int kInlineSegs = 640;
+constexpr int kInlineRows = 128;
+struct InlinePlan {
+  int32_t n_segs;        // 0: the plan is read from the workspace
+  int32_t split_units;   // S
+  int32_t cap;           // max_pages_per_row * page_size
+  int32_t reserved;
+  uint32_t seg[kInlineSegs];
+  RowInfo rows[kInlineRows];
+};
+
+// Segment si of a launch; `lens` is the device copy of the row lengths.
+__device__ __forceinline__ Seg fetch_seg(const InlinePlan& p, const Seg* segs, const int32_t* lens, int si) {
+  if (p.n_segs == 0) return segs[si];
+  const uint32_t e = p.seg[si];
+  const int row = (int)(e >> 16), i = (int)(e & 0xffffu);
+  const int L = min(max(lens[row], 0), p.cap);
+  const RowInfo ri = p.rows[row];
+  return Seg{row, i * p.split_units, min((i + 1) * p.split_units, L), ri.n_parts > 1 ? ri.part_off + i : -1};
+}
+
 struct PlanData {
   isk_desc desc{};
   int32_t batch = 0;
@@ -104,6 +131,7 @@ struct GqaLaunch {
   float* part_o; float* part_lse; void* out; float* lse;
   int32_t n_groups, hq, hkv, d, page_size, num_pages, max_pages, out_f32;
   float scale_log2;
+  InlinePlan inl;   // n_segs > 0: segments by value (groups are one segment each)
 };
 hipError_t launch_gqa_split(const GqaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});
 
@@ -120,6 +148,7 @@ struct MlaLaunch {
   // [begin - topk_width, end - topk_width).
   const uint16_t* xkv; const int32_t* xblock_table; const int32_t* xlens; const int32_t* xtopk_idx;
   int32_t xpage_size, xnum_pages, xmax_pages, xtopk_width;
+  InlinePlan inl;   // n_segs > 0: segments by value (groups are one segment each; dense only)
 };
 hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});       // 16 heads per wave
 hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});   // 32 heads per wave, hq % 128 == 0
@@ -128,7 +157,12 @@ struct CombineLaunch {
   const RowInfo* rows; const float* part_o; const float* part_lse;
   void* out; float* lse;
   int32_t batch, hq, dv, out_f32;
+  InlinePlan inl;   // n_segs > 0: per-row partial slots by value
 };
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t s);
+
+// Each launch struct is one kernel argument; HIP takes up to 4 KB of them.
+static_assert(sizeof(GqaLaunch) <= 4096 && sizeof(MlaLaunch) <= 4096 && sizeof(CombineLaunch) <= 4096,
+              "kernel arguments exceed 4 KB");
 
 }  // namespace isk

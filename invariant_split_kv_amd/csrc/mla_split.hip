@@ -176,7 +176,8 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
   const int hb = (bid >> 3) % n_hb;
   if (g >= a.n_groups) return;
   const int head0 = hb * nw * 16 + wave * 16 + i16;
-  const int seg_first = a.groups[g], seg_last = a.groups[g + 1];
+  const bool inl = a.inl.n_segs > 0;   // segments by value: one per task
+  const int seg_first = inl ? g : a.groups[g], seg_last = inl ? g + 1 : a.groups[g + 1];
   const unsigned char* kv = (const unsigned char*)a.kv;
 
   // Per-lane LDS byte offsets of the MFMA operand reads.  With the XOR key
@@ -213,7 +214,7 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
   };
 
   for (int si = seg_first; si < seg_last; ++si) {
-    Seg sg = a.segs[si];
+    Seg sg = fetch_seg(a.inl, a.segs, a.lens, si);
     const int b = sg.row;
     // A sparse segment past the main index width gathers from the extra KV
     // source, at its slots [begin - topk_width, end - topk_width).  The

@@ -639,7 +639,8 @@ mla_split_h32_kernel(MlaLaunch a) {
   // Wave index as a wave-uniform (scalar) value for address arithmetic.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int head = hb * kHeadsPerBlock + wave * 32 + n32;
-  const int seg_first = a.groups[g], seg_last = a.groups[g + 1];
+  const bool inl = a.inl.n_segs > 0;   // segments by value: one per task
+  const int seg_first = inl ? g : a.groups[g], seg_last = inl ? g + 1 : a.groups[g + 1];
 
   // Per-lane LDS byte offsets of the operand reads (compile-time parts at the use).
   //  K (A operand of S^T), k-step kk: tile row n32, piece 2*kk + hh
@@ -660,7 +661,7 @@ mla_split_h32_kernel(MlaLaunch a) {
   so.init(wave_u, lane);
 
   for (int si = seg_first; si < seg_last; ++si) {
-    Seg sg = a.segs[si];
+    Seg sg = fetch_seg(a.inl, a.segs, a.lens, si);
     const int b = sg.row;
     // A sparse segment past the main index width gathers from the extra KV
     // source, at its slots [begin - topk_width, end - topk_width).  The
