@@ -8,7 +8,8 @@ to [64, 32768], 64-token pages with a seeded permuted block table.  Inputs
 are synthetic and resident in HBM before timing starts.
 
 One step = the whole hot path: host re-planning of the per-row splits, the
-split-list upload, the split kernel and the fixed-order combine.  The timed
+split list's hand-over (by value in the kernel arguments for this batch),
+the split kernel and the fixed-order combine.  The timed
 region is exactly `--steps` steps after `--warmup` untimed ones, bracketed by
 device synchronisation, with nothing else recorded on the stream (per-step
 timing events would add their own gaps to the step).  The split kernel's
