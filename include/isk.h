@@ -185,8 +185,10 @@ ISK_API int isk_plan_segments(const isk_plan* plan, int32_t* records_out, int32_
  * lse         [B, Hq] fp32 natural-log LSE of the scaled scores (-inf for
  *             rows with nothing to attend).  May be NULL.
  * workspace   device memory of at least isk_plan_workspace_bytes(plan) bytes,
- *             256-byte aligned; holds the uploaded split list and the fp32
- *             partials.  Must not be shared by calls in flight at the same time.
+ *             256-byte aligned; holds the fp32 partials and the uploaded
+ *             split list (a dense per-row plan of at most 640 splits and 128
+ *             rows goes to the kernels in their arguments instead, with no
+ *             upload).  Must not be shared by calls in flight at the same time.
  * stream      hipStream_t (as void*).
  *
  * Out-of-range block-table entries and top-k positions are masked in the
