@@ -287,3 +287,38 @@ def test_sparse_extra_source_16_head_kernel():
     out, lse, _, _ = run_case(case)
     ro, rl = reference(case)
     parity(out, lse, ro, rl, False, "sparse + extra, 64 heads")
+
+
+# ----------------------------------------------------------------------------
+# Plans passed in the kernel arguments (dense per-row plans of at most 640
+# splits and 128 rows) and plans uploaded through the workspace
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,split", [(128, 1536), (129, 1536), (40, 64)])
+def test_plans_by_value_and_uploaded_at_the_size_limits(rows, split):
+    """128 rows fit the by-value plan, 129 do not; 40 rows of up to 2600
+    tokens with 64-token splits need more than 640 splits (uploaded)."""
+    rng = np.random.default_rng(80 + rows)
+    lens = rng.integers(0, 2600 if split == 64 else 3000, rows)
+    lens[:3] = [0, 1, 1536]
+    case = synth.mla_case(lens, 128, 1.0 / math.sqrt(192.0), 64, structure_seed=81 + rows, split_tokens=split)
+    n_splits = int(sum(-(-int(L) // split) for L in lens))
+    print(f"[case] rows={rows} splits={n_splits}", flush=True)
+    out, lse, _, _ = run_case(case)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, f"plan size rows={rows} splits={n_splits}")
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+def test_gqa_plan_by_value_matches_uploaded_plan_bits():
+    """The same GQA rows decoded as a by-value plan (32 rows) and inside an
+    uploaded plan (the rows repeated to 160) give identical bits."""
+    small = synth.config2_gqa()
+    _, _, bits_small, lbits_small = run_case(small)
+    big_lens = np.concatenate([small.lens] * 5)
+    paging = synth.make_paging(big_lens, 16, np.random.default_rng(82))
+    big = synth.GqaCase(small.rows * 5, big_lens, 32, 8, 128, small.scale, paging)
+    _, _, bits_big, lbits_big = run_case(big)
+    for k in range(5):
+        sl = slice(32 * k, 32 * (k + 1))
+        assert np.array_equal(bits_big[sl], bits_small) and np.array_equal(lbits_big[sl], lbits_small)
