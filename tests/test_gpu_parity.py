@@ -322,3 +322,21 @@ def test_gqa_plan_by_value_matches_uploaded_plan_bits():
     for k in range(5):
         sl = slice(32 * k, 32 * (k + 1))
         assert np.array_equal(bits_big[sl], bits_small) and np.array_equal(lbits_big[sl], lbits_small)
+
+
+@pytest.mark.parametrize("hq", [128, 64])
+def test_sparse_segments_longer_than_the_row_window(hq):
+    """Sparse splits of 3072 slots: the 128-head kernel resolves pool rows in
+    windows of 1024 slots, so these segments move the window twice.  Masked
+    slots sit at window boundaries; one segment ends inside a window."""
+    W = 3000
+    lens = [70000, 5000, 2999]
+    case = synth.mla_case(lens, hq, 1.0 / math.sqrt(192.0), 64, structure_seed=90, topk_width=W,
+                          split_tokens=3072)
+    rows = case.rows
+    rows[0].topk_idx[[1023, 1024, 2047, 2048, 2999]] = -1          # at the window edges
+    rows[1].topk_idx[[0, 1500]] = [70000, 5000]                    # >= len: skipped
+    rows[2].topk_len = 2100                                        # ends inside the third window
+    out, lse, _, _ = run_case(case, fill=GARBAGE)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, f"sparse 3072-slot splits hq={hq}")
