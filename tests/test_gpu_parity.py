@@ -340,3 +340,37 @@ def test_sparse_segments_longer_than_the_row_window(hq):
     out, lse, _, _ = run_case(case, fill=GARBAGE)
     ro, rl = reference(case)
     parity(out, lse, ro, rl, False, f"sparse 3072-slot splits hq={hq}")
+
+
+@pytest.mark.parametrize("which", ["gqa", "mla"])
+def test_timing_hook_launch_gives_the_same_bits(which):
+    """With timing events set, the split kernel goes through
+    hipExtLaunchKernel; its output bits equal the plain launch's and the
+    events bracket a positive kernel time."""
+    import ctypes
+    rt = ctypes.CDLL("libamdhip64.so")   # the runtime torch (and libisk) already use
+    rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    case = synth.config1_gqa_tiny() if which == "gqa" else synth.config3_mla(batch=8)
+    dc = DeviceCase(case)
+    dc.run()
+    _, _, bits0, lbits0 = dc.result()
+    evs = []
+    for _ in range(3):
+        e = ctypes.c_void_p()
+        assert rt.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    isk.plan_set_timing_events(dc.plan.handle, *evs)
+    dc.run()
+    _, _, bits1, lbits1 = dc.result()
+    isk.plan_set_timing_events(dc.plan.handle, None, None, None)
+    ms = ctypes.c_float()
+    assert rt.hipEventSynchronize(evs[2]) == 0
+    assert rt.hipEventElapsedTime(ctypes.byref(ms), evs[0], evs[1]) == 0 and ms.value > 0.0
+    assert rt.hipEventElapsedTime(ctypes.byref(ms), evs[1], evs[2]) == 0 and ms.value >= 0.0
+    for e in evs:
+        rt.hipEventDestroy(e)
+    dc.close()
+    assert np.array_equal(bits0, bits1) and np.array_equal(lbits0, lbits1)
