@@ -264,6 +264,34 @@ def gqa_extras(isk, synth, torch, np, DeviceCase, kv_bytes, calls=50):
             "split_kernel_frac_of_hbm_peak": round((kvb + q_bytes) / (split * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def rmsnorm_extras(isk, torch, calls=200):
+    """Batch-invariant RMSNorm (one workgroup per row) at hidden size 7168:
+    a decode batch of 64 rows and a large batch of 16384 rows; bytes moved
+    are x read + y written (+ w once), against the 8 TB/s peak."""
+    res = {}
+    stream = torch.cuda.current_stream()
+    dim = 7168
+    g = torch.Generator(device="cuda").manual_seed(5)
+    w = (1.0 + 0.1 * torch.randn(dim, generator=g, device="cuda")).to(torch.bfloat16)
+    for rows in (64, 16384):
+        x = torch.randn((rows, dim), generator=g, device="cuda").to(torch.bfloat16)
+        y = torch.empty_like(x)
+        for _ in range(20):
+            isk.rmsnorm(x, w, y, rows, dim, 1e-6, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(calls):
+            isk.rmsnorm(x, w, y, rows, dim, 1e-6, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / calls
+        nbytes = 2 * rows * dim * 2 + dim * 2
+        res[f"rows{rows}_dim{dim}"] = {"us_per_call": round(ms * 1e3, 2), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                       "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del x, y
+    return res
+
+
 def invariance_pass_rate(case, out_bits, lse_bits, mode, synth, DeviceCase, rows):
     """Rows re-run alone in a freshly permuted page pool with a fresh plan:
     bit equality of out (bf16) and lse (fp32) with the batched run."""
@@ -440,6 +468,8 @@ def main():
             res["per_row_over_balanced_by_batch"] = per_row_vs_balanced_sizes(isk, synth, torch, np)
         log("dense GQA (Llama-8B-shaped batch)")
         res["gqa"] = gqa_extras(isk, synth, torch, np, DeviceCase, kv_bytes)
+        log("batch-invariant RMSNorm")
+        res["rmsnorm"] = rmsnorm_extras(isk, torch)
         log("sparse decode (config-4 batch) with and without an extra KV source")
         res["sparse"] = sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes)
         if not args.no_cpu_baseline:

@@ -293,6 +293,26 @@ ISK_API int isk_attn_decode_extra(const isk_plan* plan, const void* q, const voi
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * isk_rmsnorm - batch-invariant RMS normalisation of `rows` rows:
+ *     y[r, i] = x[r, i] / sqrt(mean_j x[r, j]^2 + eps) * w[i].
+ * The inference-research gotcha "batch-invariance-is-not-universal-across-
+ * kernel-paths" (section "Root cause") names small-batch split reductions in
+ * RMSNorm as a batch-invariance breaker; here one workgroup reduces each row
+ * in one fixed fp32 order whatever `rows` is, so a row's output bits do not
+ * depend on the other rows.
+ *
+ * x      [rows, dim] bf16, 16-byte aligned (device).
+ * w      [dim] bf16, 16-byte aligned (device).
+ * y      [rows, dim] bf16 (device), rounded to nearest even; may equal x.
+ * rows   >= 0 (0 is a no-op).
+ * dim    a multiple of 8 in [8, 16384].
+ * eps    finite, >= 0.
+ * stream hipStream_t (as void*); the call only enqueues the kernel.
+ * Errors: ISK_ERR_INVALID_ARG, ISK_ERR_UNSUPPORTED (dim), ISK_ERR_HIP.
+ */
+ISK_API int isk_rmsnorm(const void* x, const void* w, void* y, int32_t rows, int32_t dim, float eps, void* stream);
+
+/*
  * isk_plan_set_timing_events - profiling hook.  Subsequent isk_attn_decode
  * calls with this plan launch the split kernel through hipExtLaunchKernel
  * with `split_begin` and `split_end` as its start and stop events, so they

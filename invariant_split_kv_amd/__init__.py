@@ -22,7 +22,7 @@ __all__ = [
     "SPLIT_BATCH_BALANCED", "OUT_BF16", "OUT_F32", "LIB_PATH", "lib", "plan_create",
     "plan_update", "plan_destroy", "plan_query", "plan_workspace_bytes", "plan_segments",
     "plan_set_timing_events", "plan_create_extra",
-    "attn_decode", "attn_decode_extra", "attn_decode_oneshot", "last_error", "numerics_id", "Plan",
+    "attn_decode", "attn_decode_extra", "attn_decode_oneshot", "rmsnorm", "last_error", "numerics_id", "Plan",
 ]
 
 KIND_GQA, KIND_MLA = 0, 1
@@ -93,6 +93,7 @@ def _load() -> ctypes.CDLL:
                                                   I32P, I32P, I32P, ctypes.POINTER(P)]),
         "isk_attn_decode_extra": (ctypes.c_int, [P, P, P, P, P, P, P, ctypes.POINTER(IskExtraKv), P, P, P,
                                                   ctypes.c_size_t, P]),
+        "isk_rmsnorm": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P]),
         "isk_last_error": (ctypes.c_char_p, []),
         "isk_numerics_id": (ctypes.c_char_p, []),
     }
@@ -237,6 +238,16 @@ def attn_decode_oneshot(desc: IskDesc, lens_host, topk_len_host, q, kv_pages, bl
     _check(lib.isk_attn_decode_oneshot(ctypes.byref(desc), len(lh), _i32p(lh), _i32p(th), _ptr(q), _ptr(kv_pages),
                                        _ptr(block_table), _ptr(lens), _ptr(topk_idx), _ptr(topk_len), _ptr(out),
                                        _ptr(lse), stream))
+
+
+def rmsnorm(x, w, y, rows: int, dim: int, eps: float, stream=None) -> None:
+    """Enqueue isk_rmsnorm: y = x / sqrt(mean(x^2) + eps) * w per row (bf16)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(lib.isk_rmsnorm(_ptr(x), _ptr(w), _ptr(y), int(rows), int(dim), float(eps), stream))
 
 
 class Plan:

@@ -514,6 +514,24 @@ int isk_attn_decode_oneshot(const isk_desc* desc, int32_t batch, const int32_t* 
   return ISK_OK;
 }
 
+int isk_rmsnorm(const void* x, const void* w, void* y, int32_t rows, int32_t dim, float eps, void* stream) {
+  if (rows < 0) return set_err(ISK_ERR_INVALID_ARG, "rows must be >= 0");
+  if (dim < 8 || dim > isk::kRmsNormMaxDim || dim % 8 != 0) {
+    std::ostringstream s;
+    s << "dim must be a multiple of 8 in [8, " << isk::kRmsNormMaxDim << "]";
+    return set_err(ISK_ERR_UNSUPPORTED, s.str());
+  }
+  if (!std::isfinite(eps) || eps < 0.f) return set_err(ISK_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (rows == 0) return ISK_OK;
+  if (x == nullptr || w == nullptr || y == nullptr) return set_err(ISK_ERR_INVALID_ARG, "x, w and y must be non-NULL");
+  if ((uintptr_t)x % 16 != 0 || (uintptr_t)w % 16 != 0 || (uintptr_t)y % 16 != 0)
+    return set_err(ISK_ERR_INVALID_ARG, "x, w and y must be 16-byte aligned");
+  isk::RmsNormLaunch a{(const uint16_t*)x, (const uint16_t*)w, (uint16_t*)y, rows, dim, eps};
+  const hipError_t e = isk::launch_rmsnorm(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_err(e, "launching the RMSNorm kernel");
+  return ISK_OK;
+}
+
 int isk_plan_set_timing_events(isk_plan* plan, void* split_begin, void* split_end, void* combine_end) {
   if (plan == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
   plan->t_split_begin = (hipEvent_t)split_begin;

@@ -161,6 +161,15 @@ struct CombineLaunch {
 };
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t s);
 
+// Batch-invariant RMSNorm: one workgroup per row.
+constexpr int kRmsNormMaxDim = 16384;
+struct RmsNormLaunch {
+  const uint16_t* x; const uint16_t* w; uint16_t* y;
+  int32_t rows, dim;
+  float eps;
+};
+hipError_t launch_rmsnorm(const RmsNormLaunch& a, hipStream_t s);
+
 // Each launch struct is one kernel argument; HIP takes up to 4 KB of them.
 static_assert(sizeof(GqaLaunch) <= 4096 && sizeof(MlaLaunch) <= 4096 && sizeof(CombineLaunch) <= 4096,
               "kernel arguments exceed 4 KB");

@@ -42,7 +42,7 @@ def segments(desc, lens, topk=None):
 def test_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "isk.h")).read()
     declared = set(re.findall(r"ISK_API\s+[\w\s\*]+?\b(isk_\w+)\s*\(", header))
-    assert len(declared) == 13
+    assert len(declared) == 14
     for name in declared:
         assert hasattr(isk.lib, name), name
     assert "gfx950" in isk.numerics_id()
@@ -284,3 +284,17 @@ def test_decode_entry_points_match_the_plan_kind():
         with pytest.raises(isk.IskError) as e:
             isk.attn_decode_extra(p.handle, A, A, A, A, A, A, A, A, A, A, A, A, A, A, p.workspace_bytes, 0)
         assert "no extra KV source" in e.value.message
+
+
+def test_rmsnorm_arguments_are_checked_before_any_device_work():
+    A = 1 << 20
+    bad = [(-1, 64, 1e-6, -1, "rows"), (4, 12, 1e-6, -2, "multiple of 8"), (4, 16392, 1e-6, -2, "multiple of 8"),
+           (4, 0, 1e-6, -2, "multiple of 8"), (4, 64, float("nan"), -1, "eps"), (4, 64, -1.0, -1, "eps")]
+    for rows, dim, eps, status, text in bad:
+        with pytest.raises(isk.IskError) as e:
+            isk.rmsnorm(A, A, A, rows, dim, eps, 0)
+        assert e.value.status == status and text in e.value.message, (e.value.status, e.value.message)
+    with pytest.raises(isk.IskError) as e:
+        isk.rmsnorm(A + 8, A, A, 4, 64, 1e-6, 0)
+    assert e.value.status == -1 and "aligned" in e.value.message
+    isk.rmsnorm(None, None, None, 0, 64, 1e-6, 0)          # no rows: nothing to do
