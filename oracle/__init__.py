@@ -5,7 +5,8 @@ CPU-baseline leg are the only callers.  The product path never imports it.
 """
 from .attention import (attend, gqa_decode, merge, merge_many, mla_decode,
                         mla_sparse_decode, mla_sparse_extra_decode, sparse_positions)
+from .gemm import linear
 from .norm import rmsnorm
 
 __all__ = ["attend", "gqa_decode", "mla_decode", "mla_sparse_decode",
-           "mla_sparse_extra_decode", "sparse_positions", "merge", "merge_many", "rmsnorm"]
+           "mla_sparse_extra_decode", "sparse_positions", "merge", "merge_many", "rmsnorm", "linear"]
