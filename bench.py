@@ -292,6 +292,37 @@ def rmsnorm_extras(isk, torch, calls=200):
     return res
 
 
+def linear_extras(isk, torch, calls=50):
+    """Batch-invariant linear layer at n = k = 7168 (weights 103 MB, bf16):
+    decode-sized rows (1, 8, 32: the 16-row tile shape, bound by the weight
+    read) and 4096 rows (the 64-row shape, bound by the matrix cores)."""
+    res = {}
+    stream = torch.cuda.current_stream()
+    n = k = 7168
+    g = torch.Generator(device="cuda").manual_seed(7)
+    w = (0.02 * torch.randn((n, k), generator=g, device="cuda")).to(torch.bfloat16)
+    for m in (1, 8, 32, 4096):
+        x = torch.randn((m, k), generator=g, device="cuda").to(torch.bfloat16)
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        for _ in range(5):
+            isk.linear_bf16(x, w, y, m, n, k, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(calls):
+            isk.linear_bf16(x, w, y, m, n, k, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / calls
+        nbytes = n * k * 2 + m * k * 2 + m * n * 4
+        flops = 2.0 * m * n * k
+        res[f"m{m}"] = {"us_per_call": round(ms * 1e3, 2), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                        "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4)}
+        del x, y
+    return res
+
+
 def invariance_pass_rate(case, out_bits, lse_bits, mode, synth, DeviceCase, rows):
     """Rows re-run alone in a freshly permuted page pool with a fresh plan:
     bit equality of out (bf16) and lse (fp32) with the batched run."""
@@ -468,6 +499,8 @@ def main():
             res["per_row_over_balanced_by_batch"] = per_row_vs_balanced_sizes(isk, synth, torch, np)
         log("dense GQA (Llama-8B-shaped batch)")
         res["gqa"] = gqa_extras(isk, synth, torch, np, DeviceCase, kv_bytes)
+        log("batch-invariant linear layer")
+        res["linear"] = linear_extras(isk, torch)
         log("batch-invariant RMSNorm")
         res["rmsnorm"] = rmsnorm_extras(isk, torch)
         log("sparse decode (config-4 batch) with and without an extra KV source")

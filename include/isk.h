@@ -313,6 +313,28 @@ ISK_API int isk_attn_decode_extra(const isk_plan* plan, const void* q, const voi
 ISK_API int isk_rmsnorm(const void* x, const void* w, void* y, int32_t rows, int32_t dim, float eps, void* stream);
 
 /*
+ * isk_linear_bf16 - batch-invariant linear layer y = x w^T:
+ *     y[r, j] = sum_k x[r, k] * w[j, k]   (bf16 inputs, fp32 accumulation).
+ * The gllm issue "Greedy outputs depend on batch composition (NVFP4
+ * GEMV/GEMM switch at 32 rows is a candidate)" (sections "Candidate cause"
+ * and "Next steps") traces batch dependence to a kernel switch by row count
+ * whose two sides round activations differently.  This entry point also
+ * switches its tile shape at 32 rows (16-row tiles below, 64-row tiles
+ * above), but both shapes take bf16 activations and compute each element
+ * with the same instruction sequence (K split in four fixed quarters, each
+ * an MFMA chain in ascending k, the quarters added in order), so the switch
+ * changes speed only: a row's outputs do not depend on m.
+ *
+ * x  [m, k] bf16, 16-byte aligned (device).
+ * w  [n, k] bf16 (one row per output feature), 16-byte aligned (device).
+ * y  [m, n] fp32 (device); must not overlap x or w.
+ * m >= 0 (0 is a no-op); n a positive multiple of 16; k a positive multiple
+ * of 128.  stream: hipStream_t (as void*); the call only enqueues the kernel.
+ * Errors: ISK_ERR_INVALID_ARG, ISK_ERR_UNSUPPORTED (n, k), ISK_ERR_HIP.
+ */
+ISK_API int isk_linear_bf16(const void* x, const void* w, float* y, int32_t m, int32_t n, int32_t k, void* stream);
+
+/*
  * isk_plan_set_timing_events - profiling hook.  Subsequent isk_attn_decode
  * calls with this plan launch the split kernel through hipExtLaunchKernel
  * with `split_begin` and `split_end` as its start and stop events, so they

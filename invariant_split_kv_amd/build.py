@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libisk.so")
 
-SOURCES = ["plan.cpp", "api.cpp", "gqa_split.hip", "mla_split.hip", "mla_split_h32.hip", "combine.hip", "rmsnorm.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "gqa_split.hip", "mla_split.hip", "mla_split_h32.hip", "combine.hip", "rmsnorm.hip", "linear.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions stay disabled (the compiler would otherwise form
 # v_pk_* ops from scalar float code).

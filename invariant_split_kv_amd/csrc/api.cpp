@@ -532,6 +532,20 @@ int isk_rmsnorm(const void* x, const void* w, void* y, int32_t rows, int32_t dim
   return ISK_OK;
 }
 
+int isk_linear_bf16(const void* x, const void* w, float* y, int32_t m, int32_t n, int32_t k, void* stream) {
+  if (m < 0) return set_err(ISK_ERR_INVALID_ARG, "m must be >= 0");
+  if (n <= 0 || n % 16 != 0) return set_err(ISK_ERR_UNSUPPORTED, "n must be a positive multiple of 16");
+  if (k <= 0 || k % 128 != 0) return set_err(ISK_ERR_UNSUPPORTED, "k must be a positive multiple of 128");
+  if (m == 0) return ISK_OK;
+  if (x == nullptr || w == nullptr || y == nullptr) return set_err(ISK_ERR_INVALID_ARG, "x, w and y must be non-NULL");
+  if ((uintptr_t)x % 16 != 0 || (uintptr_t)w % 16 != 0 || (uintptr_t)y % 4 != 0)
+    return set_err(ISK_ERR_INVALID_ARG, "x and w must be 16-byte aligned, y 4-byte aligned");
+  isk::LinearLaunch a{(const uint16_t*)x, (const uint16_t*)w, y, m, n, k};
+  const hipError_t e = isk::launch_linear(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_err(e, "launching the linear kernel");
+  return ISK_OK;
+}
+
 int isk_plan_set_timing_events(isk_plan* plan, void* split_begin, void* split_end, void* combine_end) {
   if (plan == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
   plan->t_split_begin = (hipEvent_t)split_begin;

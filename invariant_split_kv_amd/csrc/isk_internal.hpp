@@ -170,6 +170,14 @@ struct RmsNormLaunch {
 };
 hipError_t launch_rmsnorm(const RmsNormLaunch& a, hipStream_t s);
 
+// Batch-invariant linear layer: tile shape chosen by row count, same bits.
+constexpr int kLinearSmallRows = 32;
+struct LinearLaunch {
+  const uint16_t* x; const uint16_t* w; float* y;
+  int32_t m, n, k;
+};
+hipError_t launch_linear(const LinearLaunch& a, hipStream_t s);
+
 // Each launch struct is one kernel argument; HIP takes up to 4 KB of them.
 static_assert(sizeof(GqaLaunch) <= 4096 && sizeof(MlaLaunch) <= 4096 && sizeof(CombineLaunch) <= 4096,
               "kernel arguments exceed 4 KB");

@@ -42,7 +42,7 @@ def segments(desc, lens, topk=None):
 def test_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "isk.h")).read()
     declared = set(re.findall(r"ISK_API\s+[\w\s\*]+?\b(isk_\w+)\s*\(", header))
-    assert len(declared) == 14
+    assert len(declared) == 15
     for name in declared:
         assert hasattr(isk.lib, name), name
     assert "gfx950" in isk.numerics_id()
@@ -298,3 +298,17 @@ def test_rmsnorm_arguments_are_checked_before_any_device_work():
         isk.rmsnorm(A + 8, A, A, 4, 64, 1e-6, 0)
     assert e.value.status == -1 and "aligned" in e.value.message
     isk.rmsnorm(None, None, None, 0, 64, 1e-6, 0)          # no rows: nothing to do
+
+
+def test_linear_arguments_are_checked_before_any_device_work():
+    A = 1 << 20
+    bad = [(-1, 64, 128, -1, "m must"), (4, 24, 128, -2, "multiple of 16"), (4, 0, 128, -2, "multiple of 16"),
+           (4, 64, 96, -2, "multiple of 128"), (4, 64, 0, -2, "multiple of 128")]
+    for m, n, k, status, text in bad:
+        with pytest.raises(isk.IskError) as e:
+            isk.linear_bf16(A, A, A, m, n, k, 0)
+        assert e.value.status == status and text in e.value.message, (e.value.status, e.value.message)
+    with pytest.raises(isk.IskError) as e:
+        isk.linear_bf16(A + 4, A, A, 4, 64, 128, 0)
+    assert e.value.status == -1 and "aligned" in e.value.message
+    isk.linear_bf16(None, None, None, 0, 64, 128, 0)      # no rows: nothing to do

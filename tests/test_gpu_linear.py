@@ -1,0 +1,78 @@
+"""Batch-invariant linear layer (isk_linear_bf16) on the GPU: parity with the
+fp64 oracle and bit equality of a row across row counts that cross the
+32-row tile-shape switch.
+
+Bar: bf16 x bf16 products are exact in fp32, so the only errors are the
+fp32 additions of the K products; whatever their order, the error of an
+element is at most (K + 3) * 2^-24 * sum_k |x_k w_k| (K products plus three
+partial sums).  Integer inputs whose sums stay below 2^24 must come out
+exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_split_kv_amd as isk
+import oracle
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def run(xbits, wbits):
+    m, k = xbits.shape
+    n = wbits.shape[0]
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    isk.linear_bf16(to_dev(xbits), to_dev(wbits), y, m, n, k)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def rows(m, k, seed, std=1.0):
+    out = np.empty((m, k), np.uint16)
+    for r in range(m):
+        out[r] = synth.draw_bf16(np.random.default_rng([seed, r]), (k,), std)
+    return out
+
+
+@pytest.mark.parametrize("m", [1, 20, 33, 100])
+def test_integer_inputs_are_exact(m):
+    rng = np.random.default_rng(m)
+    k, n = 512, 64
+    xb = synth.bf16_bits(rng.integers(-3, 4, (m, k)).astype(np.float32))
+    wb = synth.bf16_bits(rng.integers(-3, 4, (n, k)).astype(np.float32))
+    y = run(xb, wb)
+    ref = oracle.linear(synth.bf16_value(xb), synth.bf16_value(wb))
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (16, 256, 4096), (32, 64, 1024), (33, 128, 4096),
+                                   (257, 48, 512), (64, 4096, 1024)])
+def test_linear_parity(m, n, k):
+    xb, wb = rows(m, k, 40 + m), rows(n, k, 41, std=0.05)
+    y = run(xb, wb).astype(np.float64)
+    xv, wv = synth.bf16_value(xb).astype(np.float64), synth.bf16_value(wb).astype(np.float64)
+    ref = oracle.linear(xv, wv)
+    bound = (k + 3) * 2.0 ** -24 * (np.abs(xv) @ np.abs(wv).T)
+    err = np.abs(y - ref)
+    print(f"[linear] m={m} n={n} k={k} max_abs={err.max():.3g} max_err/bound={np.max(err / bound):.3g}", flush=True)
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("k", [1024, 4096])
+def test_row_bits_do_not_depend_on_the_row_count(k):
+    n = 256
+    wb = rows(n, k, 51, std=0.05)
+    probe = rows(1, k, 52)[0]
+    solo = run(probe[None, :], wb)[0]
+    for m in (2, 16, 31, 32, 33, 64, 100, 1000):
+        xb = rows(m, k, 53 + m)
+        pos = (5 * m) // 7
+        xb[pos] = probe
+        y = run(xb, wb)
+        assert np.array_equal(y[pos], solo), f"m={m}: probe row bits differ"
