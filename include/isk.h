@@ -319,11 +319,12 @@ ISK_API int isk_rmsnorm(const void* x, const void* w, void* y, int32_t rows, int
  * GEMV/GEMM switch at 32 rows is a candidate)" (sections "Candidate cause"
  * and "Next steps") traces batch dependence to a kernel switch by row count
  * whose two sides round activations differently.  This entry point also
- * switches its tile shape at 32 rows (16-row tiles below, 64-row tiles
- * above), but both shapes take bf16 activations and compute each element
- * with the same instruction sequence (K split in four fixed quarters, each
- * an MFMA chain in ascending k, the quarters added in order), so the switch
- * changes speed only: a row's outputs do not depend on m.
+ * switches tile shapes by row count (16-row tiles up to 32 rows, 64-row
+ * tiles up to 256, 128 x 128 LDS-staged tiles above), but every shape takes
+ * bf16 activations and computes each element with the same arithmetic (K
+ * split in four fixed quarters, each an MFMA chain in ascending k from
+ * zero, the quarters added in order), so the switch changes speed only: a
+ * row's outputs do not depend on m.
  *
  * x  [m, k] bf16, 16-byte aligned (device).
  * w  [n, k] bf16 (one row per output feature), 16-byte aligned (device).

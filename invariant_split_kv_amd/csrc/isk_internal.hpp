@@ -171,7 +171,8 @@ struct RmsNormLaunch {
 hipError_t launch_rmsnorm(const RmsNormLaunch& a, hipStream_t s);
 
 // Batch-invariant linear layer: tile shape chosen by row count, same bits.
-constexpr int kLinearSmallRows = 32;
+constexpr int kLinearSmallRows = 32;    // up to here: 16-row tiles
+constexpr int kLinearTiledRows = 256;   // up to here: 64-row tiles; above: 128 x 128 LDS tiles
 struct LinearLaunch {
   const uint16_t* x; const uint16_t* w; float* y;
   int32_t m, n, k;

@@ -7,12 +7,12 @@
 // kernels round the activations differently, so a row's result depends on
 // how many rows share the call; its section "Next steps" proposes that both
 // kernels use the same activation precision, so that the switch changes
-// speed only.  This library's two tile shapes follow that rule and go
-// further: they compute every output element with the same instructions.
+// speed only.  This library's tile shapes follow that rule and go further:
+// they compute every output element with the same instructions.
 //   * Rows <= 32 (decode-sized, weight-bandwidth bound): 16-row tiles.
-//     Rows > 32: 64-row tiles, which reuse each weight fragment for four
-//     row tiles.
-//   * Both take bf16 activations.  The four waves of a workgroup each own a
+//     Rows <= 256: 64-row tiles, which reuse each weight fragment for four
+//     row tiles.  More rows: 128 x 128 tiles staged through LDS (below).
+//   * All take bf16 activations.  The four waves of a workgroup each own a
 //     quarter of K and run v_mfma_f32_16x16x32_bf16 over it in ascending k
 //     from zero; the partial sums are added in wave order,
 //     ((c0 + c1) + c2) + c3.  Rows of a tile past M contribute nothing to
@@ -95,14 +95,105 @@ __global__ void __launch_bounds__(256) linear_kernel(LinearLaunch a) {
   }
 }
 
+// Large row counts: 128 x 128 output tiles staged through LDS.  Wave
+// (wm, wn) computes rows 64*wm .. +63 and columns 64*wn .. +63 as 4 x 4
+// MFMA tiles.  K is walked in 32-wide stages, quarter by quarter: within a
+// quarter the MFMA chain starts from zero and runs in ascending k; at the end
+// of quarter q its sums are added to the running total (total = c0, then
+// total + c1, + c2, + c3) -- the same arithmetic per element as the
+// 16/64-row kernel above, only computed by one wave instead of four.
+constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kStageBytes = (kBM + kBN) * kBK * 2;   // A then B, 64 B per row
+
+__global__ void __launch_bounds__(256) linear_tiled_kernel(LinearLaunch a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStageBytes];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g16 = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+
+  // Staging: 16 wave-wide 16-byte loads per stage (8 for A, 8 for B), four
+  // per wave.  Load i covers LDS bytes [1024 i, 1024 i + 1024) of the stage:
+  // tile row (1024 i + 16 lane) / 64, 8-element chunk lane % 4.  Rows past
+  // m or n read the last valid row (their results are never stored).
+  const unsigned char* src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = wave + 4 * j;            // 0..7: A rows, 8..15: B rows
+    const int r = (1024 * (i & 7) + 16 * lane) / 64, c = lane & 3;
+    if (i < 8) {
+      const int m = min(m0 + r, a.m - 1);
+      src[j] = (const unsigned char*)(a.x + (size_t)m * a.k + 8 * c);
+    } else {
+      const int n = min(n0 + r, a.n - 1);
+      src[j] = (const unsigned char*)(a.w + (size_t)n * a.k + 8 * c);
+    }
+  }
+  auto stage = [&](int s, int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = wave + 4 * j;
+      load_lds_16(src[j] + (size_t)s * kBK * 2, (ISK_LDS unsigned char*)lds + buf * kStageBytes + 1024 * i);
+    }
+  };
+
+  f32x4 acc[4][4], total[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = total[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int n_stages = a.k / kBK, per_quarter = n_stages / 4;
+  stage(0, 0);
+  for (int s = 0; s < n_stages; ++s) {
+    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0): this wave's loads of stage s landed
+    __syncthreads();                 // ... and every wave's; every wave is done with buffer (s+1) & 1
+    if (s + 1 < n_stages) stage(s + 1, (s + 1) & 1);
+    const ISK_LDS unsigned char* A = (const ISK_LDS unsigned char*)lds + (s & 1) * kStageBytes;
+    const ISK_LDS unsigned char* B = A + kBM * kBK * 2;
+    bf16x8 af[4], bf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = *(const ISK_LDS bf16x8*)(A + (64 * wm + 16 * i + i16) * 64 + 16 * g16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = *(const ISK_LDS bf16x8*)(B + (64 * wn + 16 * j + i16) * 64 + 16 * g16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    if ((s + 1) % per_quarter == 0) {   // end of a K quarter
+      const bool first = s + 1 == per_quarter;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          total[i][j] = first ? acc[i][j] : total[i][j] + acc[i][j];
+          acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 64 * wn + 16 * j + i16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 64 * wm + 16 * i + 4 * g16 + r;
+        if (m < a.m && n < a.n) a.y[(size_t)m * a.n + n] = total[i][j][r];
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_linear(const LinearLaunch& a, hipStream_t s) {
   if (a.m == 0) return hipSuccess;
   if (a.m <= kLinearSmallRows) {
     hipLaunchKernelGGL(linear_kernel<16>, dim3(a.n / 16, (a.m + 15) / 16), dim3(256), 0, s, a);
-  } else {
+  } else if (a.m <= kLinearTiledRows) {
     hipLaunchKernelGGL(linear_kernel<64>, dim3(a.n / 16, (a.m + 63) / 64), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(linear_tiled_kernel, dim3((a.n + kBN - 1) / kBN, (a.m + kBM - 1) / kBM), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
