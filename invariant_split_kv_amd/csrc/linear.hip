@@ -9,9 +9,10 @@
 // kernels use the same activation precision, so that the switch changes
 // speed only.  This library's tile shapes follow that rule and go further:
 // they compute every output element with the same instructions.
-//   * Rows <= 32 (decode-sized, weight-bandwidth bound): 16-row tiles.
-//     Rows <= 256: 64-row tiles, which reuse each weight fragment for four
-//     row tiles.  More rows: 128 x 128 tiles staged through LDS (below).
+//   * Rows <= 32 (decode-sized, weight-bandwidth bound): one 16- or 32-row
+//     tile, so the weights are read once.  Rows <= 256: 64-row tiles, which
+//     reuse each weight fragment for four row tiles.  More rows: 128 x 128
+//     tiles staged through LDS (below).
 //   * All take bf16 activations.  The four waves of a workgroup each own a
 //     quarter of K and run v_mfma_f32_16x16x32_bf16 over it in ascending k
 //     from zero; the partial sums are added in wave order,
@@ -188,8 +189,10 @@ __global__ void __launch_bounds__(256) linear_tiled_kernel(LinearLaunch a) {
 
 hipError_t launch_linear(const LinearLaunch& a, hipStream_t s) {
   if (a.m == 0) return hipSuccess;
-  if (a.m <= kLinearSmallRows) {
-    hipLaunchKernelGGL(linear_kernel<16>, dim3(a.n / 16, (a.m + 15) / 16), dim3(256), 0, s, a);
+  if (a.m <= 16) {
+    hipLaunchKernelGGL(linear_kernel<16>, dim3(a.n / 16, 1), dim3(256), 0, s, a);
+  } else if (a.m <= kLinearSmallRows) {
+    hipLaunchKernelGGL(linear_kernel<32>, dim3(a.n / 16, 1), dim3(256), 0, s, a);
   } else if (a.m <= kLinearTiledRows) {
     hipLaunchKernelGGL(linear_kernel<64>, dim3(a.n / 16, (a.m + 63) / 64), dim3(256), 0, s, a);
   } else {
