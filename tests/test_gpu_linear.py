@@ -1,6 +1,6 @@
 """Batch-invariant linear layer (isk_linear_bf16) on the GPU: parity with the
 fp64 oracle and bit equality of a row across row counts that cross the
-tile-shape switches at 32 and 256 rows.
+tile-shape switches at 16, 32 and 256 rows.
 
 Bar: bf16 x bf16 products are exact in fp32, so the only errors are the
 fp32 additions of the K products; whatever their order, the error of an
@@ -51,7 +51,7 @@ def test_integer_inputs_are_exact(m):
     assert np.array_equal(y.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (16, 256, 4096), (32, 64, 1024), (33, 128, 4096),
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (16, 256, 4096), (17, 96, 2048), (32, 64, 1024), (33, 128, 4096),
                                    (256, 48, 512), (257, 48, 512), (64, 4096, 1024), (300, 256, 1024),
                                    (1000, 400, 4096)])
 def test_linear_parity(m, n, k):
@@ -71,7 +71,7 @@ def test_row_bits_do_not_depend_on_the_row_count(k):
     wb = rows(n, k, 51, std=0.05)
     probe = rows(1, k, 52)[0]
     solo = run(probe[None, :], wb)[0]
-    for m in (2, 16, 31, 32, 33, 64, 100, 256, 257, 1000):
+    for m in (2, 16, 17, 31, 32, 33, 64, 100, 256, 257, 1000):
         xb = rows(m, k, 53 + m)
         pos = (5 * m) // 7
         xb[pos] = probe
