@@ -132,16 +132,29 @@ def timed_steps(dc, isk, torch, evs, steps, warmup, lens_host, instrument):
     return total_ms, wall, split, comb
 
 
+# Length-band split tables (isk_plan_create_banded) for two regimes.  Both
+# keep a row's splits a function of its own length; they differ in which
+# batches they favour.  Latency: rows up to 16384 tokens get 512-token splits
+# (a lone row spreads over more compute units).  Throughput: rows above 32768
+# tokens get at most 24 splits (fewer partials for very long rows).
+BANDS_LATENCY = [(16384, 512), (1 << 30, 1536)]
+BANDS_THROUGHPUT = [(32768, 1536), (1 << 30, 1536, 24)]
+
+
 def per_row_vs_balanced_sizes(isk, synth, torch, np, sizes=(1, 2, 8, 32, 128), calls=50):
     """Per-row over balanced call time on the invariance-stress batches (probe
     row of 16384 tokens among batchmates of 1..131072 tokens, composition 0),
-    one batch per size.  Values are drawn on the GPU (N(0, 0.5^2), bf16); only
-    the timing is used."""
+    one batch per size, with the per-row plan under the two band tables too.
+    Values are drawn on the GPU (N(0, 0.5^2), bf16); only the timing is used."""
     res = {}
     stream = torch.cuda.current_stream()
-    for B in sizes:
-        lens, _, _ = synth.config5_composition(B, 0)
+    batches = [(str(B), synth.config5_composition(B, 0)[0]) for B in sizes]
+    # Two lognormal batches (median 4096, sigma 1, at most 32768 tokens) on
+    # either side of the B=64 headline batch.
+    batches += [(f"lognormal_{B}", synth.config3_mla_lens(100, B)) for B in (16, 128)]
+    for key, lens in batches:
         lens = np.asarray(lens, dtype=np.int32)
+        B = len(lens)
         paging = synth.make_paging(lens, 64, np.random.default_rng([B, 77]))
         g = torch.Generator(device="cuda").manual_seed(B)
         pool = (torch.randn((paging.num_pages, 64, synth.MLA_DQK), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
@@ -151,10 +164,13 @@ def per_row_vs_balanced_sizes(isk, synth, torch, np, sizes=(1, 2, 8, 32, 128), c
         out = torch.empty((B, 128, synth.MLA_DV), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((B, 128), dtype=torch.float32, device="cuda")
         ms = {}
-        for name, mode in (("per_row", isk.SPLIT_PER_ROW), ("balanced", isk.SPLIT_BATCH_BALANCED)):
+        for name, mode, bands in (("per_row", isk.SPLIT_PER_ROW, None),
+                                  ("bands_latency", isk.SPLIT_PER_ROW, BANDS_LATENCY),
+                                  ("bands_throughput", isk.SPLIT_PER_ROW, BANDS_THROUGHPUT),
+                                  ("balanced", isk.SPLIT_BATCH_BALANCED, None)):
             desc = isk.IskDesc(isk.KIND_MLA, 128, 1, synth.MLA_DQK, synth.MLA_DV, 64, paging.num_pages,
                                paging.max_pages_per_row, 0, mode, 0, isk.OUT_BF16, 0, 1.0 / math.sqrt(192.0))
-            with isk.Plan(desc, lens) as plan:
+            with isk.Plan(desc, lens, bands=bands) as plan:
                 ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
                 call = lambda: isk.attn_decode(plan.handle, q, pool, bt, lens_d, None, None, out, lse, ws,
                                                ws.numel(), stream)
@@ -167,9 +183,11 @@ def per_row_vs_balanced_sizes(isk, synth, torch, np, sizes=(1, 2, 8, 32, 128), c
                 b.record(stream)
                 torch.cuda.synchronize()
                 ms[name] = a.elapsed_time(b) / calls
-        res[str(B)] = {"kv_tokens": int(lens.sum()), "per_row_ms": round(ms["per_row"], 5),
+        res[key] = {"kv_tokens": int(lens.sum()), "per_row_ms": round(ms["per_row"], 5),
                        "balanced_ms": round(ms["balanced"], 5),
-                       "per_row_over_balanced": round(ms["per_row"] / ms["balanced"], 4)}
+                       "per_row_over_balanced": round(ms["per_row"] / ms["balanced"], 4),
+                       "bands_latency_ms": round(ms["bands_latency"], 5),
+                       "bands_throughput_ms": round(ms["bands_throughput"], 5)}
         del pool, q
         torch.cuda.empty_cache()
     return res
@@ -495,7 +513,7 @@ def main():
                                "per_row_over_balanced": round(ms_step / (tb / args.steps), 4),
                                "invariance_pass": okb, "invariance_total": len(range(0, case.batch, 4))}
             dcb.close()
-            log("per-row vs balanced at batch sizes 1, 2, 8, 32, 128 (invariance-stress lengths)")
+            log("per-row (plain and two band tables) vs balanced: stress batches B=1..128, lognormal B=16, 128")
             res["per_row_over_balanced_by_batch"] = per_row_vs_balanced_sizes(isk, synth, torch, np)
         log("dense GQA (Llama-8B-shaped batch)")
         res["gqa"] = gqa_extras(isk, synth, torch, np, DeviceCase, kv_bytes)

@@ -101,7 +101,8 @@ typedef struct isk_plan isk_plan;   /* opaque, host-owned */
 
 typedef struct isk_plan_info {
   int32_t batch;
-  int32_t split_tokens;      /* resolved split length in units (tokens or slots)     */
+  int32_t split_tokens;      /* resolved split length in units (tokens or slots);
+                                with a band table, the longest one any row uses   */
   int32_t num_segments;      /* splits (one partial output each, or a direct write)  */
   int32_t num_groups;        /* workgroup tasks the split kernel is launched with    */
   int32_t num_partials;      /* partial (o, lse) slots in the workspace              */
@@ -130,10 +131,52 @@ ISK_API int isk_plan_create(const isk_desc* desc, int32_t batch, const int32_t* 
                     const int32_t* topk_len_host, isk_plan** plan_out);
 
 /*
+ * Length band of a per-row split table.  The FlashMLA issue page (section
+ * "Question") asks for split counts that depend only on a row's own length
+ * and fixed constants; a band table is such a function, piecewise in the
+ * length: each band has its own split length and an optional split cap.
+ *   max_units    rows with units U <= max_units belong to the first such band
+ *                (bounds strictly increasing; the last band also takes every
+ *                longer row).
+ *   split_units  S of the band: a positive multiple of 64.
+ *   max_splits   0: no cap.  Else, when ceil(U / S) > max_splits, the row's
+ *                split length becomes 64 * ceil(ceil(U / max_splits) / 64),
+ *                so it gets at most max_splits longer splits.
+ *   reserved     must be 0.
+ */
+typedef struct isk_split_band {
+  int32_t max_units;
+  int32_t split_units;
+  int32_t max_splits;
+  int32_t reserved;
+} isk_split_band;
+
+/*
+ * isk_plan_create_banded - isk_plan_create with a per-row split length taken
+ * from a band table instead of one constant.  Row b (units U_b: tokens, or
+ * valid top-k slots when sparse) gets n_b = ceil(U_b / S_b) splits
+ * [i*S_b, min((i+1)*S_b, U_b)), S_b the band rule above, so its splits, and
+ * its output bits, still depend on U_b and the table only.  A table whose
+ * first band covers every length with split_units S and no cap plans exactly
+ * as isk_plan_create with split_tokens S.
+ *
+ * bands      [n_bands] host array (copied), 1 <= n_bands <= 16.
+ * desc       as for isk_plan_create, with split_mode ISK_SPLIT_PER_ROW and
+ *            split_tokens 0.  Other arguments as for isk_plan_create.
+ * isk_plan_update re-plans with the same table.  Plans of this kind are not
+ * combined with an extra KV source.  Host only.
+ * Errors: ISK_ERR_INVALID_ARG (table or descriptor), ISK_ERR_UNSUPPORTED.
+ */
+ISK_API int isk_plan_create_banded(const isk_desc* desc, const isk_split_band* bands, int32_t n_bands,
+                                   int32_t batch, const int32_t* lens_host, const int32_t* topk_len_host,
+                                   isk_plan** plan_out);
+
+/*
  * isk_plan_update - re-plan an existing plan in place for new lengths (the
- * next decode step), keeping its descriptor and its pinned staging buffers.
- * Host only.  Same arguments and errors as isk_plan_create.  Decode calls
- * already enqueued keep the split list they uploaded.
+ * next decode step), keeping its descriptor, its band table (if any) and its
+ * pinned staging buffers.  Host only.  Same arguments and errors as
+ * isk_plan_create.  Decode calls already enqueued keep the split list they
+ * uploaded.
  */
 ISK_API int isk_plan_update(isk_plan* plan, int32_t batch, const int32_t* lens_host,
                     const int32_t* topk_len_host);

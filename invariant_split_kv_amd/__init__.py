@@ -59,6 +59,11 @@ class IskExtraKv(ctypes.Structure):
                 ("topk_idx", ctypes.c_void_p), ("topk_len", ctypes.c_void_p)]
 
 
+class IskSplitBand(ctypes.Structure):
+    _fields_ = [("max_units", ctypes.c_int32), ("split_units", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 class IskPlanInfo(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("split_tokens", ctypes.c_int32), ("num_segments", ctypes.c_int32),
                 ("num_groups", ctypes.c_int32), ("num_partials", ctypes.c_int32), ("reserved", ctypes.c_int32),
@@ -91,6 +96,8 @@ def _load() -> ctypes.CDLL:
         "isk_plan_set_timing_events": (ctypes.c_int, [P, P, P, P]),
         "isk_plan_create_extra": (ctypes.c_int, [ctypes.POINTER(IskDesc), ctypes.POINTER(IskExtraDesc), ctypes.c_int32,
                                                   I32P, I32P, I32P, ctypes.POINTER(P)]),
+        "isk_plan_create_banded": (ctypes.c_int, [ctypes.POINTER(IskDesc), ctypes.POINTER(IskSplitBand), ctypes.c_int32,
+                                                   ctypes.c_int32, I32P, I32P, ctypes.POINTER(P)]),
         "isk_attn_decode_extra": (ctypes.c_int, [P, P, P, P, P, P, P, ctypes.POINTER(IskExtraKv), P, P, P,
                                                   ctypes.c_size_t, P]),
         "isk_rmsnorm": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P]),
@@ -155,6 +162,25 @@ def plan_create_extra(desc: IskDesc, extra: IskExtraDesc, lens_host, topk_len_ho
     out = ctypes.c_void_p()
     _check(lib.isk_plan_create_extra(ctypes.byref(desc), ctypes.byref(extra), len(lens), _i32p(lens), _i32p(tl),
                                      _i32p(xtl), ctypes.byref(out)))
+    return out.value
+
+
+def split_bands(bands) -> ctypes.Array:
+    """ctypes array of isk_split_band from (max_units, split_units[, max_splits]) tuples."""
+    rows = [tuple(b) + (0,) * (3 - len(b)) for b in bands]
+    arr = (IskSplitBand * len(rows))()
+    for i, (mu, su, ms) in enumerate(rows):
+        arr[i] = IskSplitBand(int(mu), int(su), int(ms), 0)
+    return arr
+
+
+def plan_create_banded(desc: IskDesc, bands, lens_host, topk_len_host=None) -> int:
+    arr = bands if isinstance(bands, ctypes.Array) else split_bands(bands)
+    lens = _i32_host(lens_host)
+    tl = _i32_host(topk_len_host)
+    out = ctypes.c_void_p()
+    _check(lib.isk_plan_create_banded(ctypes.byref(desc), arr, len(arr), len(lens), _i32p(lens), _i32p(tl),
+                                      ctypes.byref(out)))
     return out.value
 
 
@@ -265,10 +291,15 @@ class Plan:
     """Owning wrapper of an isk_plan handle (destroyed on close/garbage collection)."""
 
     def __init__(self, desc: IskDesc, lens_host, topk_len_host=None, extra: Optional[IskExtraDesc] = None,
-                 extra_topk_len_host=None):
+                 extra_topk_len_host=None, bands=None):
         self.desc = desc
         self.extra = extra
-        if extra is None:
+        self.handle = None
+        if bands is not None:
+            if extra is not None:
+                raise ValueError("a band table is not combined with an extra KV source")
+            self.handle = plan_create_banded(desc, bands, lens_host, topk_len_host)
+        elif extra is None:
             self.handle = plan_create(desc, lens_host, topk_len_host)
         else:
             self.handle = plan_create_extra(desc, extra, lens_host, topk_len_host, extra_topk_len_host)

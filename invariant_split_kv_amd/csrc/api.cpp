@@ -274,13 +274,34 @@ int isk_plan_create_extra(const isk_desc* desc, const isk_extra_desc* extra, int
   return ISK_OK;
 }
 
+int isk_plan_create_banded(const isk_desc* desc, const isk_split_band* bands, int32_t n_bands, int32_t batch,
+                           const int32_t* lens_host, const int32_t* topk_len_host, isk_plan** plan_out) {
+  if (plan_out == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan_out is NULL");
+  *plan_out = nullptr;
+  if (desc == nullptr || bands == nullptr) return set_err(ISK_ERR_INVALID_ARG, "desc or bands is NULL");
+  isk_plan* p = new (std::nothrow) isk_plan();
+  if (p == nullptr) return set_err(ISK_ERR_INVALID_ARG, "out of host memory");
+  int status = ISK_OK;
+  std::string msg = isk::plan_build(p->data, *desc, batch, lens_host, topk_len_host, &status, nullptr, nullptr,
+                                    bands, n_bands);
+  if (status != ISK_OK) {
+    delete p;
+    return set_err(status, msg);
+  }
+  serialise(p);
+  *plan_out = p;
+  return ISK_OK;
+}
+
 int isk_plan_update(isk_plan* plan, int32_t batch, const int32_t* lens_host, const int32_t* topk_len_host) {
   if (plan == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
   if (plan->data.has_extra)
     return set_err(ISK_ERR_INVALID_ARG, "a plan with an extra KV source is re-planned with isk_plan_create_extra");
   PlanData fresh;
   int status = ISK_OK;
-  std::string msg = isk::plan_build(fresh, plan->data.desc, batch, lens_host, topk_len_host, &status);
+  const std::vector<isk_split_band>& bands = plan->data.bands;
+  std::string msg = isk::plan_build(fresh, plan->data.desc, batch, lens_host, topk_len_host, &status, nullptr,
+                                    nullptr, bands.empty() ? nullptr : bands.data(), (int32_t)bands.size());
   if (status != ISK_OK) return set_err(status, msg);
   plan->data = std::move(fresh);
   serialise(plan);

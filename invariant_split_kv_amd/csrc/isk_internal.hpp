@@ -86,7 +86,11 @@ struct PlanData {
   bool has_extra = false;
   isk_extra_desc extra{};
   std::vector<int32_t> extra_units; // per-row valid extra top-k counts
+  // Length bands (empty: one split length S for every row).
+  std::vector<isk_split_band> bands;
 };
+
+constexpr int kMaxBands = 16;
 
 // Byte layout of the per-call metadata at the head of the workspace.
 struct MetaLayout {
@@ -99,9 +103,12 @@ MetaLayout meta_layout(const PlanData& p);
 // otherwise the error message; *status receives the isk_status.
 // With `extra` non-NULL the plan also covers an extra KV source
 // (extra_topk_len_host gives its per-row valid counts).
+// With `bands` non-NULL each row's split length comes from the band table
+// (n_bands entries) instead of one S.
 std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int32_t* lens_host,
                        const int32_t* topk_len_host, int* status, const isk_extra_desc* extra = nullptr,
-                       const int32_t* extra_topk_len_host = nullptr);
+                       const int32_t* extra_topk_len_host = nullptr, const isk_split_band* bands = nullptr,
+                       int32_t n_bands = 0);
 
 // ---------------------------------------------------------------- launchers
 // Optional profiling events of a split-kernel launch.  When set, the kernel

@@ -12,6 +12,15 @@
 // an extra KV source gets the same rule applied to its extra top-k count;
 // those splits follow the main set's in the row's partial order.
 //
+// With a length-band table the split length is chosen per row, again from
+// the row's own units only: the first band whose bound covers U_b (the last
+// band covers everything longer) gives S_band, and a band with a split cap
+// n_max stretches its splits when ceil(U_b / S_band) > n_max:
+//   S_b = 64 * ceil(ceil(U_b / n_max) / 64),  n_b = ceil(U_b / S_b) <= n_max.
+// This is the piecewise n = f(L) with per-band S and N_max that the FlashMLA
+// issue page leaves open (section "Question") as the way to trade occupancy
+// against partial traffic without making a row depend on its batch.
+//
 // Batch-balanced mode exists for comparison only.  It reproduces the
 // scheduler that page describes (same section: a block quota per part derived
 // from the total over the whole batch, then greedy packing that cuts rows at
@@ -85,11 +94,42 @@ static std::string check_desc(const isk_desc& d, int* status) {
   return "";
 }
 
+// Split length of a row with `U` units under a band table.
+static int32_t band_split(const std::vector<isk_split_band>& bands, int32_t U) {
+  size_t k = 0;
+  while (k + 1 < bands.size() && U > bands[k].max_units) ++k;
+  const isk_split_band& bd = bands[k];
+  const int32_t n = (int32_t)(((long long)U + bd.split_units - 1) / bd.split_units);
+  if (bd.max_splits <= 0 || n <= bd.max_splits) return bd.split_units;
+  const long long per = ((long long)U + bd.max_splits - 1) / bd.max_splits;
+  return (int32_t)((per + 63) / 64 * 64);
+}
+
 std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int32_t* lens_host,
                        const int32_t* topk_len_host, int* status, const isk_extra_desc* extra,
-                       const int32_t* extra_topk_len_host) {
+                       const int32_t* extra_topk_len_host, const isk_split_band* bands, int32_t n_bands) {
   std::string err = check_desc(d, status);
   if (*status != ISK_OK) return err;
+  if (bands != nullptr) {
+    if (n_bands < 1 || n_bands > kMaxBands)
+      return fail(status, ISK_ERR_INVALID_ARG, "n_bands must be in [1, 16]");
+    if (d.split_mode != ISK_SPLIT_PER_ROW)
+      return fail(status, ISK_ERR_INVALID_ARG, "a band table needs split_mode ISK_SPLIT_PER_ROW");
+    if (d.split_tokens != 0)
+      return fail(status, ISK_ERR_INVALID_ARG, "desc.split_tokens must be 0 with a band table (the bands give S)");
+    if (extra != nullptr) return fail(status, ISK_ERR_UNSUPPORTED, "band tables are not combined with an extra KV source");
+    for (int32_t k = 0; k < n_bands; ++k) {
+      const isk_split_band& bd = bands[k];
+      std::ostringstream e;
+      e << "bands[" << k << "]: ";
+      if (bd.split_units <= 0 || bd.split_units % 64 != 0)
+        return fail(status, ISK_ERR_INVALID_ARG, e.str() + "split_units must be a positive multiple of 64");
+      if (bd.max_splits < 0) return fail(status, ISK_ERR_INVALID_ARG, e.str() + "max_splits must be >= 0");
+      if (bd.reserved != 0) return fail(status, ISK_ERR_INVALID_ARG, e.str() + "reserved must be 0");
+      if (bd.max_units < 0 || (k > 0 && bd.max_units <= bands[k - 1].max_units))
+        return fail(status, ISK_ERR_INVALID_ARG, e.str() + "max_units must be >= 0 and strictly increasing");
+    }
+  }
   if (extra != nullptr) {
     if (d.kind != ISK_KIND_MLA || d.topk_width <= 0)
       return fail(status, ISK_ERR_UNSUPPORTED, "an extra KV source needs a sparse MLA descriptor (topk_width > 0)");
@@ -130,6 +170,7 @@ std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int3
   p.desc = d;
   p.batch = batch;
   p.split_units = S;
+  p.bands.assign(bands, bands != nullptr ? bands + n_bands : bands);
   p.units = units;
   p.segs.clear();
   p.seg_group.clear();
@@ -146,16 +187,19 @@ std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int3
   std::vector<int32_t> seg_part_of;   // group index per segment (balanced)
 
   if (d.split_mode == ISK_SPLIT_PER_ROW) {
+    if (!p.bands.empty()) p.split_units = 0;
     for (int b = 0; b < batch; ++b) {
       const int32_t U = units[b];
-      const int32_t n = (U + S - 1) / S;
-      for (int32_t i = 0; i < n; ++i) row_segs[b].push_back(Seg{b, i * S, std::min((i + 1) * S, U), 0});
+      const int32_t S = p.bands.empty() ? p.split_units : band_split(p.bands, U);
+      if (!p.bands.empty() && U > 0) p.split_units = std::max(p.split_units, S);
+      const int32_t n = (int32_t)(((long long)U + S - 1) / S);
+      for (int32_t i = 0; i < n; ++i) row_segs[b].push_back(Seg{b, i * S, (int32_t)std::min<long long>((long long)(i + 1) * S, U), 0});
       if (p.has_extra) {
         // The extra set's splits follow the main set's, by the same rule;
         // their units are offset by the main index width.
         const int32_t W = d.topk_width, X = p.extra_units[b];
-        const int32_t nx = (X + S - 1) / S;
-        for (int32_t i = 0; i < nx; ++i) row_segs[b].push_back(Seg{b, W + i * S, W + std::min((i + 1) * S, X), 0});
+        const int32_t nx = (int32_t)(((long long)X + S - 1) / S);
+        for (int32_t i = 0; i < nx; ++i) row_segs[b].push_back(Seg{b, W + i * S, W + (int32_t)std::min<long long>((long long)(i + 1) * S, X), 0});
       }
     }
   } else {

@@ -42,7 +42,7 @@ def segments(desc, lens, topk=None):
 def test_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "isk.h")).read()
     declared = set(re.findall(r"ISK_API\s+[\w\s\*]+?\b(isk_\w+)\s*\(", header))
-    assert len(declared) == 15
+    assert len(declared) == 16
     for name in declared:
         assert hasattr(isk.lib, name), name
     assert "gfx950" in isk.numerics_id()
@@ -312,3 +312,137 @@ def test_linear_arguments_are_checked_before_any_device_work():
         isk.linear_bf16(A + 4, A, A, 4, 64, 128, 0)
     assert e.value.status == -1 and "aligned" in e.value.message
     isk.linear_bf16(None, None, None, 0, 64, 128, 0)      # no rows: nothing to do
+
+
+# ----------------------------------------------------------------------------
+# Length-band split tables (isk_plan_create_banded).
+
+def band_rule(bands, U):
+    """Split length of a row with U units, written from the band definition:
+    the first band whose bound covers U (the last takes longer rows), and a
+    split cap that stretches the splits to the next multiple of 64."""
+    k = 0
+    while k + 1 < len(bands) and U > bands[k][0]:
+        k += 1
+    _, S, cap = (tuple(bands[k]) + (0,))[:3]
+    n = -(-U // S)
+    if cap == 0 or n <= cap:
+        return S
+    per = -(-U // cap)
+    return -(-per // 64) * 64
+
+
+def banded_segments(desc, bands, lens, topk=None):
+    with isk.Plan(desc, lens, topk, bands=bands) as p:
+        return p.segments(), p.info()
+
+
+BAND_TABLES = [
+    [(1 << 30, 1536)],
+    [(4096, 512), (32768, 1536), (1 << 30, 4096)],
+    [(8192, 1024, 4), (65536, 2048, 16), (1 << 30, 1536, 24)],
+    [(0, 64), (100, 128, 1), (2000, 192)],
+]
+
+
+@settings(max_examples=60, deadline=None)
+@given(lens=st.lists(st.integers(0, 131072), min_size=1, max_size=20), table=st.sampled_from(range(len(BAND_TABLES))))
+def test_banded_plan_follows_the_band_rule(lens, table):
+    bands = BAND_TABLES[table]
+    segs, info = banded_segments(mla_desc(max_pages_per_row=2048), bands, lens)
+    _check_tiling(segs, info, lens, None)
+    used = 0
+    for r, U in enumerate(lens):
+        mine = sorted((int(b), int(e)) for rr, b, e, _, _ in segs if rr == r)
+        if U == 0:
+            assert mine == []
+            continue
+        S = band_rule(bands, U)
+        used = max(used, S)
+        assert mine == [(i * S, min((i + 1) * S, U)) for i in range(-(-U // S))]
+        cap = (tuple(bands[min(k for k in range(len(bands)) if U <= bands[k][0] or k == len(bands) - 1)]) + (0,))[2]
+        assert cap == 0 or len(mine) <= cap
+    assert info["split_tokens"] == used
+
+
+def test_band_rule_examples():
+    """Hand-worked values of the rule (a pin independent of the loop above)."""
+    bands = [(8192, 1024, 4), (65536, 2048, 16), (1 << 30, 1536, 24)]
+    assert band_rule(bands, 4096) == 1024          # 4 splits, at the cap
+    assert band_rule(bands, 4097) == 1088          # 5 > 4: ceil(4097/4) = 1025 -> 1088
+    assert band_rule(bands, 8192) == 2048          # ceil(8192/4) = 2048
+    assert band_rule(bands, 8193) == 2048          # second band, 5 splits
+    assert band_rule(bands, 65536) == 4096         # 32 > 16 splits: 65536/16
+    assert band_rule(bands, 65537) == 2752         # third band: 43 > 24, ceil(65537/24) = 2731 -> 2752
+    segs, _ = banded_segments(mla_desc(max_pages_per_row=2048), bands, [4097, 65537])
+    r0 = sorted((int(b), int(e)) for r, b, e, _, _ in segs if r == 0)
+    assert r0 == [(0, 1088), (1088, 2176), (2176, 3264), (3264, 4097)]
+    assert sum(1 for r, *_ in segs if r == 1) == 24
+
+
+def test_one_uncapped_band_plans_like_a_single_split_length():
+    lens = [0, 1, 100, 1536, 1537, 40000, 131072]
+    for S in (64, 512, 1536, 4096):
+        a, ia = segments(mla_desc(max_pages_per_row=2048, split_tokens=S), lens)
+        b, ib = banded_segments(mla_desc(max_pages_per_row=2048), [(1 << 30, S)], lens)
+        assert np.array_equal(a, b) and ia == ib
+
+
+@settings(max_examples=40, deadline=None)
+@given(lens=st.lists(st.integers(0, 100000), min_size=1, max_size=24), probe=st.integers(0, 100000),
+       pos=st.integers(0, 24), table=st.sampled_from(range(len(BAND_TABLES))))
+def test_banded_splits_do_not_depend_on_batchmates(lens, probe, pos, table):
+    desc, bands = mla_desc(max_pages_per_row=2048), BAND_TABLES[table]
+    solo, _ = banded_segments(desc, bands, [probe])
+    pos = min(pos, len(lens))
+    batch = lens[:pos] + [probe] + lens[pos:]
+    segs, _ = banded_segments(desc, bands, batch)
+    assert sorted((b, e) for r, b, e, _, _ in segs if r == pos) == sorted((b, e) for _, b, e, _, _ in solo)
+
+
+def test_banded_sparse_plan_uses_topk_len_and_update_keeps_the_table():
+    bands = [(1024, 256), (1 << 30, 1024, 2)]
+    desc = mla_desc(topk_width=4096, max_pages_per_row=2048)
+    with isk.Plan(desc, [9000, 9000, 9000], [1000, 4096, 3000], bands=bands) as p:
+        segs = p.segments()
+        assert sorted((int(b), int(e)) for r, b, e, _, _ in segs if r == 0) == [(0, 256), (256, 512), (512, 768), (768, 1000)]
+        assert sorted((int(b), int(e)) for r, b, e, _, _ in segs if r == 1) == [(0, 2048), (2048, 4096)]
+        assert sorted((int(b), int(e)) for r, b, e, _, _ in segs if r == 2) == [(0, 1536), (1536, 3000)]
+        p.update([10, 10], [300, 4096])
+        segs = p.segments()
+        assert sorted((int(b), int(e)) for r, b, e, _, _ in segs if r == 0) == [(0, 256), (256, 300)]
+        assert sorted((int(b), int(e)) for r, b, e, _, _ in segs if r == 1) == [(0, 2048), (2048, 4096)]
+        assert p.info()["split_tokens"] == 2048
+
+
+def test_band_table_arguments_are_checked():
+    lens = [100]
+    cases = [
+        (mla_desc(), [], "n_bands"),
+        (mla_desc(), [(1 << 20 + k, 64) for k in range(17)], "n_bands"),
+        (mla_desc(), [(100, 100)], "multiple of 64"),
+        (mla_desc(), [(100, 0)], "multiple of 64"),
+        (mla_desc(), [(100, 64, -1)], "max_splits"),
+        (mla_desc(), [(100, 64), (100, 128)], "increasing"),
+        (mla_desc(), [(-1, 64)], "increasing"),
+        (mla_desc(split_tokens=512), [(100, 64)], "split_tokens"),
+        (mla_desc(split_mode=isk.SPLIT_BATCH_BALANCED), [(100, 64)], "ISK_SPLIT_PER_ROW"),
+    ]
+    for desc, bands, needle in cases:
+        with pytest.raises(isk.IskError) as ei:
+            if bands:
+                isk.plan_create_banded(desc, bands, lens)
+            else:
+                arr = isk.split_bands([(100, 64)])
+                out = isk.ctypes.c_void_p()
+                rc = isk.lib.isk_plan_create_banded(isk.ctypes.byref(desc), arr, 0, 1, isk._i32p(isk._i32_host(lens)),
+                                                    None, isk.ctypes.byref(out))
+                isk._check(rc)
+        assert ei.value.status == -1 and needle in ei.value.message, (needle, ei.value.message)
+    arr = isk.split_bands([(100, 64)])
+    arr[0].reserved = 3
+    with pytest.raises(isk.IskError, match="reserved"):
+        isk.plan_create_banded(mla_desc(), arr, lens)
+    out = isk.ctypes.c_void_p()
+    assert isk.lib.isk_plan_create_banded(isk.ctypes.byref(mla_desc()), None, 1, 1,
+                                          isk._i32p(isk._i32_host(lens)), None, isk.ctypes.byref(out)) == -1

@@ -128,7 +128,7 @@ def _gpu_row(seed, length, hq):
     return q, lat[:length]
 
 
-def _gpu_batch_run(lens, seeds, paging_seed, split_mode=isk.SPLIT_PER_ROW, hq=128):
+def _gpu_batch_run(lens, seeds, paging_seed, split_mode=isk.SPLIT_PER_ROW, hq=128, bands=None):
     lens = np.asarray(lens, dtype=np.int32)
     paging = synth.make_paging(lens, 64, np.random.default_rng(paging_seed))
     pool = torch.zeros((paging.num_pages * 64, synth.MLA_DQK), dtype=torch.bfloat16, device="cuda")
@@ -145,7 +145,7 @@ def _gpu_batch_run(lens, seeds, paging_seed, split_mode=isk.SPLIT_PER_ROW, hq=12
     lens_d = torch.from_numpy(lens).cuda()
     out = torch.empty((len(lens), hq, synth.MLA_DV), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((len(lens), hq), dtype=torch.float32, device="cuda")
-    with isk.Plan(desc, lens) as plan:
+    with isk.Plan(desc, lens, bands=bands) as plan:
         ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
         isk.attn_decode(plan.handle, q, pool.view(paging.num_pages, 64, synth.MLA_DQK), bt, lens_d, None, None,
                         out, lse, ws, ws.numel())
@@ -156,10 +156,11 @@ def _gpu_batch_run(lens, seeds, paging_seed, split_mode=isk.SPLIT_PER_ROW, hq=12
 _SOLO = {}
 
 
-def _solo(seed, length, mode):
-    key = (seed, length, mode)
+def _solo(seed, length, mode, bands=None):
+    key = (seed, length, mode, None if bands is None else tuple(map(tuple, bands)))
     if key not in _SOLO:
-        ob, lb, _, _, _ = _gpu_batch_run([length], [seed], paging_seed=9000 + len(_SOLO), split_mode=mode)
+        ob, lb, _, _, _ = _gpu_batch_run([length], [seed], paging_seed=9000 + len(_SOLO), split_mode=mode,
+                                         bands=bands)
         _SOLO[key] = (ob[0], lb[0])
     return _SOLO[key]
 
@@ -181,6 +182,27 @@ def test_config5_probe_bits_in_every_composition(B):
                 f"batchmate {j} (len {lens[j]}) differs from its solo run at B={B}"
             checked += 1
     print(f"[config5] B={B}: probe identical in 3/3 compositions, {checked} sampled batchmates identical", flush=True)
+
+
+# A band table whose bands all touch the stress lengths: the probe (16384)
+# takes the capped middle band, batchmates up to 131072 all three.
+STRESS_BANDS = [(4096, 512), (20000, 1024, 10), (1 << 30, 2048, 24)]
+
+
+@pytest.mark.parametrize("B", [2, 32, 128])
+def test_config5_probe_bits_under_a_band_table(B):
+    probe = _solo(synth.PROBE_SEED, synth.PROBE_LEN, isk.SPLIT_PER_ROW, STRESS_BANDS)
+    for comp in range(2):
+        lens, seeds, pos = synth.config5_composition(B, comp)
+        print(f"[config5 bands] B={B} composition={comp} probe at {pos}", flush=True)
+        ob, lb, _, _, _ = _gpu_batch_run(lens, seeds, paging_seed=100 * B + comp, bands=STRESS_BANDS)
+        assert np.array_equal(ob[pos], probe[0]) and np.array_equal(lb[pos], probe[1]), \
+            f"probe differs under the band table at B={B} composition {comp}"
+        others = [j for j in range(B) if j != pos]
+        for j in np.random.default_rng([B, comp, 1]).choice(others, size=min(4, len(others)), replace=False):
+            so = _solo(seeds[j], int(lens[j]), isk.SPLIT_PER_ROW, STRESS_BANDS)
+            assert np.array_equal(ob[j], so[0]) and np.array_equal(lb[j], so[1]), \
+                f"batchmate {j} (len {lens[j]}) differs from its solo run under the band table at B={B}"
 
 
 def test_config5_probe_matches_oracle():

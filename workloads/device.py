@@ -73,7 +73,7 @@ class DeviceCase:
 
     def __init__(self, case, device="cuda", split_mode=isk.SPLIT_PER_ROW, out_f32=False, check_inputs=False,
                  split_tokens: Optional[int] = None, pool: Optional[torch.Tensor] = None,
-                 fill: Optional[int] = None):
+                 fill: Optional[int] = None, bands=None):
         self.case = case
         self.device = device
         self.desc = make_desc(case, split_mode, out_f32, check_inputs, split_tokens)
@@ -100,7 +100,7 @@ class DeviceCase:
             self.plan = isk.Plan(self.desc, self.lens_host, self.topk_len_host, extra=xdesc,
                                  extra_topk_len_host=self.x_topk_len_host)
         else:
-            self.plan = isk.Plan(self.desc, self.lens_host, self.topk_len_host)
+            self.plan = isk.Plan(self.desc, self.lens_host, self.topk_len_host, bands=bands)
         dv = self.desc.head_dim_v
         self.out = torch.empty((case.batch, case.hq, dv), dtype=torch.float32 if out_f32 else torch.bfloat16,
                                device=device)
