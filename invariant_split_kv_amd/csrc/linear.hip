@@ -52,25 +52,57 @@ __global__ void __launch_bounds__(256) linear_kernel(LinearLaunch a) {
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // k-steps of 32, the next step's fragments loaded before this step's MFMAs.
+  // k-steps of 32 through a register ring of D steps: step s's fragments are
+  // loaded D steps ahead, so D loads per operand are in flight per wave (the
+  // weight stream is what bounds the few-row shapes).  The MFMA chain itself
+  // still runs over s in ascending order.
+  constexpr int D = T == 1 ? 8 : (T == 2 ? 4 : 2);
   const int steps = kq / 32;
-  bf16x8 bcur = wp[0], acur[T];
+  bf16x8 bq[D], aq[T][D];
+  // Prologue in the main loop's load order, unconditional (slots past the
+  // last step reload it and are never used).
 #pragma unroll
-  for (int t = 0; t < T; ++t) acur[t] = xok[t] ? xp[t][0] : zero;
-  for (int s = 0; s < steps; ++s) {
-    bf16x8 bnext = bcur, anext[T];
+  for (int j = 0; j < D; ++j) {
+    const int st = min(j, steps - 1);
+    bq[j] = wp[4 * st];
 #pragma unroll
-    for (int t = 0; t < T; ++t) anext[t] = acur[t];
-    if (s + 1 < steps) {
-      bnext = wp[4 * (s + 1)];
-#pragma unroll
-      for (int t = 0; t < T; ++t) anext[t] = xok[t] ? xp[t][4 * (s + 1)] : zero;
+    for (int t = 0; t < T; ++t) {
+      const bf16x8 v = xp[t][4 * st];
+      aq[t][j] = xok[t] ? v : zero;
     }
+  }
+  // Main loop: every refill is in range, so the body is straight-line code and
+  // the loads of one pass stay in flight while the next pass's MFMAs run.
+  // (Rows past m read row 0 and are replaced by zeros.)
+  int s0 = 0;
+  for (; s0 + 2 * D <= steps; s0 += D) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[t], bcur, acc[t], 0, 0, 0);
-    bcur = bnext;
+    for (int j = 0; j < D; ++j) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) acur[t] = anext[t];
+      for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[t][j], bq[j], acc[t], 0, 0, 0);
+      bq[j] = wp[4 * (s0 + j + D)];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const bf16x8 v = xp[t][4 * (s0 + j + D)];
+        aq[t][j] = xok[t] ? v : zero;
+      }
+    }
+  }
+  // Tail: the last (fewer than 2 D) steps, refilling only in range.
+  for (; s0 < steps; s0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int st = s0 + j;
+      if (st < steps) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[t][j], bq[j], acc[t], 0, 0, 0);
+        if (st + D < steps) {
+          bq[j] = wp[4 * (st + D)];
+#pragma unroll
+          for (int t = 0; t < T; ++t) aq[t][j] = xok[t] ? xp[t][4 * (st + D)] : zero;
+        }
+      }
+    }
   }
 
   // Partial sums of waves 1..3 through LDS; wave 0 adds them in wave order.
