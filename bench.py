@@ -397,6 +397,8 @@ def main():
                     help="only the timed region (for profiler runs); no balanced/cold/invariance/CPU legs")
     ap.add_argument("--mode", choices=["per_row", "balanced"], default="per_row",
                     help="split rule of the timed region (the headline line uses per_row)")
+    ap.add_argument("--only", choices=["linear", "rmsnorm", "gqa", "sparse"], default=None,
+                    help="run one side measurement alone and print its JSON (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy three times (byte-counter calibration run)")
     args = ap.parse_args()
@@ -419,6 +421,13 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.only is not None:
+        legs = {"linear": lambda: linear_extras(isk, torch), "rmsnorm": lambda: rmsnorm_extras(isk, torch),
+                "gqa": lambda: gqa_extras(isk, synth, torch, np, DeviceCase, kv_bytes),
+                "sparse": lambda: sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes)}
+        log(f"side measurement {args.only} only")
+        print(json.dumps({args.only: legs[args.only]()}), flush=True)
+        return
     mode = isk.SPLIT_PER_ROW if args.mode == "per_row" else isk.SPLIT_BATCH_BALANCED
 
     log("generating the B=64 MLA batch")
