@@ -16,11 +16,13 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libisk.so")
 
-SOURCES = ["plan.cpp", "api.cpp", "gqa_split.hip", "mla_split.hip", "mla_split_h32.hip", "combine.hip", "rmsnorm.hip", "linear.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "gqa_split.hip", "mla_split.hip", "mla_split_h32.hip", "mla_h128.hip", "combine.hip",
+           "rmsnorm.hip", "linear.hip"]
+GEN_DIR = os.path.join(BUILD_DIR, "gen")
 ARCH = "gfx950"
 # Packed fp32 instructions stay disabled (the compiler would otherwise form
 # v_pk_* ops from scalar float code).
-FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC, "-I", GEN_DIR,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function", "-fvisibility=hidden"]
 
 
@@ -31,12 +33,34 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
 EXTRA_FLAGS = {
     "mla_split_h32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-spill-vgpr-to-agpr=0",
                           "-mllvm", "-disable-promote-alloca-to-lds"],
+    "mla_h128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-spill-vgpr-to-agpr=0",
+                     "-mllvm", "-disable-promote-alloca-to-lds"],
 }
 
 # Sources whose inline asm owns registers the compiler must never touch: all
 # AGPRs (the output accumulator), v231 (an asm scratch register) and
 # v232..v255 (the LDS operand ring).
 ASM_OWNED = ["mla_split_h32.hip"]
+# mla_h128.hip keeps its output block in AGPRs between its inline-asm blocks;
+# the compiler's own code may use any VGPR but no AGPR.
+AGPR_OWNED = ["mla_h128.hip"]
+
+
+def check_agpr_ownership(asm_text: str) -> list:
+    """Instructions outside inline-asm blocks that name an AGPR (must be none)."""
+    bad, in_asm = [], False
+    agpr = re.compile(r"(?<![\w.])a(\d+|\[)")
+    for n, line in enumerate(asm_text.splitlines(), 1):
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif s.startswith(";;#ASMEND"):
+            in_asm = False
+        elif not in_asm and s and not s.startswith((";", ".")) and not s.endswith(":"):
+            parts = s.split(";")[0].split(None, 1)
+            if len(parts) == 2 and agpr.search(parts[1]):
+                bad.append((n, s))
+    return bad
 
 
 def check_register_ownership(asm_text: str) -> list:
@@ -76,6 +100,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     """Compile every source and link libisk.so; returns the library path."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     os.makedirs(BUILD_DIR, exist_ok=True)
+    # generated tile loop of the dense 128-head MLA kernel
+    sys.path.insert(0, CSRC)
+    try:
+        import gen_mla_h128
+    finally:
+        sys.path.pop(0)
+    gen_mla_h128.write_header(os.path.join(GEN_DIR, "mla_h128_seg.inc"))
     objs, procs = [], []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
@@ -96,6 +127,14 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             bad = check_register_ownership(f.read())
         if bad:
             raise RuntimeError(f"{src}: compiler-generated code uses registers owned by inline asm: {bad[:5]}")
+    for src in AGPR_OWNED:
+        asm = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".device.s")
+        _run([hipcc, *FLAGS, *EXTRA_FLAGS.get(src, []), "--cuda-device-only", "-S", os.path.join(CSRC, src),
+              "-o", asm], verbose)
+        with open(asm) as f:
+            bad = check_agpr_ownership(f.read())
+        if bad:
+            raise RuntimeError(f"{src}: compiler-generated code uses AGPRs owned by inline asm: {bad[:5]}")
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

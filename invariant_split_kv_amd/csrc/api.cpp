@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <sstream>
@@ -49,6 +50,17 @@ struct isk_plan {
 };
 
 namespace {
+
+// Diagnostic switch: ISK_DENSE_MLA_KERNEL=h32 routes dense 128-head MLA
+// through the gather kernel (mla_split_h32) instead of the generated tile
+// loop, so tests can compare the two on the same inputs.  Read once.
+bool dense_h128_off() {
+  static const bool off = [] {
+    const char* v = std::getenv("ISK_DENSE_MLA_KERNEL");
+    return v != nullptr && std::strcmp(v, "h32") == 0;
+  }();
+  return off;
+}
 
 // Dense per-row plans that fit go to the kernels by value (see InlinePlan).
 void build_inline(isk_plan* p) {
@@ -465,8 +477,15 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
       a.xmax_pages = pd.extra.max_pages_per_row;
       a.xtopk_width = pd.extra.topk_width;
     }
-    // 128-head blocks (32 heads per wave) when the head count allows it.
-    e = d.num_q_heads % 128 == 0 ? isk::launch_mla_split_h32(a, stream, ev) : isk::launch_mla_split(a, stream, ev);
+    // 128-head blocks (32 heads per wave) when the head count allows it:
+    // dense rows through the generated tile loop, sparse rows through the
+    // gather kernel.
+    if (d.num_q_heads % 128 != 0)
+      e = isk::launch_mla_split(a, stream, ev);
+    else if (!sparse && !dense_h128_off())
+      e = isk::launch_mla_h128(a, stream, ev);
+    else
+      e = isk::launch_mla_split_h32(a, stream, ev);
     if (e != hipSuccess) return hip_err(e, "launching the MLA split kernel");
   }
   if (pd.any_combine) {

@@ -159,6 +159,7 @@ struct MlaLaunch {
 };
 hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});       // 16 heads per wave
 hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});   // 32 heads per wave, hq % 128 == 0
+hipError_t launch_mla_h128(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});        // dense, hq % 128 == 0
 
 struct CombineLaunch {
   const RowInfo* rows; const float* part_o; const float* part_lse;

@@ -1,0 +1,194 @@
+// Dense absorbed-MLA split kernel for gfx950, one workgroup per split and
+// block of 128 query heads (used for dense MLA when the head count is a
+// multiple of 128).
+//
+// The split stage of the split-KV scheme on the FlashMLA issue page "Sparse
+// MLA decode is not batch-invariant ..." (section "Where it comes from"), with
+// split boundaries from the host planner that depend only on the row's own
+// length.  Four waves, one per SIMD: for S^T = K Q^T wave w owns heads
+// [32w, 32w + 32) of the block (their 576-dim query slice in VGPRs), for
+// O^T += V^T P^T it owns dims [128w, 128w + 128) of all 128 heads (the fp32
+// output block in AGPRs).  The tile loop of a segment is one generated
+// inline-asm block (gen_mla_h128.py, run by the build), which documents the
+// schedule and the register plan; this file plans the segment, runs the block
+// and writes the output from the accumulator.  The arithmetic is the one of
+// mla_split_h32.hip (same operands, same orders), so both give the same bits.
+
+#include <utility>
+
+#include "device.hpp"
+#include "isk_internal.hpp"
+#include "mla_h128_seg.inc"
+
+namespace isk {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kHeadsPerBlock = 128;
+constexpr int kTok = 32;
+constexpr int kXOff = 4 * kTok * kMlaDqk * 2 + 8192;   // per-head floats after the tiles and the P exchange
+constexpr float kPShift = 7.0f;                        // p carries a factor 2^7 (taken out of the LSE)
+static_assert(ISK_H128_LDS_BYTES == kXOff + 512, "LDS layout of the generated block");
+
+#define ISK_H128_A10(p) "a" #p "0", "a" #p "1", "a" #p "2", "a" #p "3", "a" #p "4", \
+                        "a" #p "5", "a" #p "6", "a" #p "7", "a" #p "8", "a" #p "9"
+#define ISK_H128_ALL_AGPRS                                                                                   \
+  ISK_H128_A10(), ISK_H128_A10(1), ISK_H128_A10(2), ISK_H128_A10(3), ISK_H128_A10(4), ISK_H128_A10(5),      \
+      ISK_H128_A10(6), ISK_H128_A10(7), ISK_H128_A10(8), ISK_H128_A10(9), ISK_H128_A10(10), ISK_H128_A10(11), \
+      ISK_H128_A10(12), ISK_H128_A10(13), ISK_H128_A10(14), ISK_H128_A10(15), ISK_H128_A10(16),               \
+      ISK_H128_A10(17), ISK_H128_A10(18), ISK_H128_A10(19), ISK_H128_A10(20), ISK_H128_A10(21),               \
+      ISK_H128_A10(22), ISK_H128_A10(23), ISK_H128_A10(24), "a250", "a251", "a252", "a253", "a254", "a255"
+
+// Accumulator tile T (16 fp32 per lane) out of AGPRs.  The last MFMA that
+// wrote it must be at least 16 wait states back (acc_settle).
+template <int T>
+__device__ __forceinline__ void acc_read(float (&o)[16]) {
+  asm volatile(
+      "v_accvgpr_read_b32 %0, a[%16*16+0]\n\tv_accvgpr_read_b32 %1, a[%16*16+1]\n\t"
+      "v_accvgpr_read_b32 %2, a[%16*16+2]\n\tv_accvgpr_read_b32 %3, a[%16*16+3]\n\t"
+      "v_accvgpr_read_b32 %4, a[%16*16+4]\n\tv_accvgpr_read_b32 %5, a[%16*16+5]\n\t"
+      "v_accvgpr_read_b32 %6, a[%16*16+6]\n\tv_accvgpr_read_b32 %7, a[%16*16+7]\n\t"
+      "v_accvgpr_read_b32 %8, a[%16*16+8]\n\tv_accvgpr_read_b32 %9, a[%16*16+9]\n\t"
+      "v_accvgpr_read_b32 %10, a[%16*16+10]\n\tv_accvgpr_read_b32 %11, a[%16*16+11]\n\t"
+      "v_accvgpr_read_b32 %12, a[%16*16+12]\n\tv_accvgpr_read_b32 %13, a[%16*16+13]\n\t"
+      "v_accvgpr_read_b32 %14, a[%16*16+14]\n\tv_accvgpr_read_b32 %15, a[%16*16+15]"
+      : "=v"(o[0]), "=v"(o[1]), "=v"(o[2]), "=v"(o[3]), "=v"(o[4]), "=v"(o[5]), "=v"(o[6]), "=v"(o[7]),
+        "=v"(o[8]), "=v"(o[9]), "=v"(o[10]), "=v"(o[11]), "=v"(o[12]), "=v"(o[13]), "=v"(o[14]), "=v"(o[15])
+      : "n"(T));
+}
+
+__global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[ISK_H128_LDS_BYTES];
+  asm volatile("" ::: ISK_H128_ALL_AGPRS);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // block id -> (task, head block): head blocks of one task sit 8 ids apart
+  // (the same XCD under round-robin dealing of workgroups to the 8 XCDs).
+  const int n_hb = a.hq / kHeadsPerBlock;
+  const int bid = blockIdx.x;
+  const int g = (bid / (8 * n_hb)) * 8 + (bid & 7);
+  const int hb = (bid >> 3) % n_hb;
+  if (g >= a.n_groups) return;
+  const bool inl = a.inl.n_segs > 0;
+  const int seg_first = inl ? g : a.groups[g], seg_last = inl ? g + 1 : a.groups[g + 1];
+  const uint32_t lds = (uint32_t)(uintptr_t)lds_raw;
+  ISK_LDS float* const xs = (ISK_LDS float*)(lds_raw + kXOff);   // [n32][ht]
+
+  for (int si = seg_first; si < seg_last; ++si) {
+    const Seg sg = fetch_seg(a.inl, a.segs, a.lens, si);
+    const int b = sg.row;
+    // Every wave is done with the previous segment's LDS.
+    __syncthreads();
+    const int ntiles = (sg.end - sg.begin + kTok - 1) / kTok;
+    float m_ref = -INFINITY, l_run = 0.f;
+    if (ntiles > 0) {
+      const uint16_t* qw = a.q + ((size_t)b * a.hq + hb * kHeadsPerBlock + wave * 32) * kMlaDqk;
+      const uintptr_t kv = (uintptr_t)a.kv;
+      const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+      const int P = a.page_size;
+      const int pbase = sg.begin / P, on0 = sg.begin % P;
+      const int pend = (sg.end + P - 1) / P;   // pages of the row holding tokens below the end
+      asm volatile(ISK_H128_SEG_ASM
+                   : "={v224}"(m_ref), "={v225}"(l_run)
+                   : [q] "s"(qw), [kv_lo] "s"((uint32_t)kv), [kv_hi] "s"((uint32_t)(kv >> 32)), [bt] "s"(bt),
+                     [ntiles] "s"(ntiles), [begin] "s"(sg.begin), [end] "s"(sg.end), [P] "s"(P),
+                     [npg] "s"(a.num_pages), [pbase] "s"(pbase), [on0] "s"(on0), [pend] "s"(pend),
+                     [scale] "s"(a.scale_log2), [w] "s"(wave), [lds] "s"(lds)
+                   : ISK_H128_SEG_CLOBBERS);
+    } else {
+      asm volatile(
+          ".irp i, 0,16,32,48,64,80,96,112,128,144,160,176,192,208,224,240\n\t"
+          ".irp k, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15\n\t"
+          "v_accvgpr_write_b32 a[\\i+\\k], 0\n\t.endr\n\t.endr\n\ts_nop 4" ::: ISK_H128_ALL_AGPRS);
+    }
+
+    // Lane values are derived here, after the block (which owns every VGPR),
+    // so that none has to be kept in memory across it.
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int n32 = lane & 31, hh = lane >> 5;
+    // ---- o = acc / l, lse = ln 2 (m_ref - 7 + log2 l); the lane pair of a
+    // head adds its two halves of l in the same order in both lanes.
+    float l_tot;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+      l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const bool empty = !(l_tot > 0.f);
+    const float lse_v = empty ? -INFINITY : (m_ref - kPShift + fast_log2(l_tot)) * kLn2;
+    __syncthreads();   // every wave is done with the last alphas
+    if (hh == 0) xs[4 * n32 + wave] = l_tot;
+    __syncthreads();
+    // inv of the head tile of accumulator group gg: (gg + wave) & 3
+    float inv[4];
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const float l = xs[4 * n32 + ((gg + wave) & 3)];
+      inv[gg] = l > 0.f ? 1.f / l : 0.f;
+    }
+    asm volatile("s_nop 7\n\ts_nop 7");
+    const int head = hb * kHeadsPerBlock + wave * 32 + n32;
+    float* of32 = nullptr;
+    uint16_t* obf = nullptr;
+    const size_t hb0 = (size_t)(hb * kHeadsPerBlock + n32);   // head of head tile 0
+    const size_t base = (sg.part >= 0 ? (size_t)sg.part : (size_t)b) * a.hq + hb0;
+    const size_t eo = base * kMlaDv + 128 * (size_t)wave + 4 * hh;
+    if (sg.part >= 0) {
+      of32 = a.part_o + eo;
+      if (hh == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
+    } else {
+      if (a.out_f32)
+        of32 = (float*)a.out + eo;
+      else
+        obf = (uint16_t*)a.out + eo;
+      if (a.lse != nullptr && hh == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
+    }
+    // lane holds O^T[128w + 32 dt + 8 q + 4 hh + e][32 ht + n32] at
+    // acc[4 dt + gg][4 q + e], ht = (gg + wave) & 3
+    auto store_tile = [&](int t, const float (&o)[16]) {
+      const int dt = t >> 2, gg = t & 3, ht = (gg + wave) & 3;
+      const size_t off = (size_t)ht * 32 * kMlaDv + 32 * dt;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 r = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]} * inv[gg];
+        if (of32 != nullptr) {
+          *(f32x4*)(of32 + off + 8 * q) = r;
+        } else {
+          uint2 w;
+          w.x = pack_bf16x2(r[0], r[1]);
+          w.y = pack_bf16x2(r[2], r[3]);
+          *(uint2*)(obf + off + 8 * q) = w;
+        }
+      }
+    };
+    {
+      float o[16];
+      acc_read<0>(o); store_tile(0, o);
+      acc_read<1>(o); store_tile(1, o);
+      acc_read<2>(o); store_tile(2, o);
+      acc_read<3>(o); store_tile(3, o);
+      acc_read<4>(o); store_tile(4, o);
+      acc_read<5>(o); store_tile(5, o);
+      acc_read<6>(o); store_tile(6, o);
+      acc_read<7>(o); store_tile(7, o);
+      acc_read<8>(o); store_tile(8, o);
+      acc_read<9>(o); store_tile(9, o);
+      acc_read<10>(o); store_tile(10, o);
+      acc_read<11>(o); store_tile(11, o);
+      acc_read<12>(o); store_tile(12, o);
+      acc_read<13>(o); store_tile(13, o);
+      acc_read<14>(o); store_tile(14, o);
+      acc_read<15>(o); store_tile(15, o);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mla_h128(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev) {
+  if (a.n_groups == 0) return hipSuccess;
+  if (a.hq % kHeadsPerBlock != 0 || a.topk_idx != nullptr) return hipErrorInvalidValue;
+  const int n_hb = a.hq / kHeadsPerBlock;
+  const int n_blocks = ((a.n_groups + 7) / 8) * 8 * n_hb;
+  return launch_one(mla_h128_kernel, dim3(n_blocks), dim3(64 * kWaves), s, a, ev);
+}
+
+}  // namespace isk
