@@ -74,17 +74,16 @@ S_U0 = "s67"        # its first token
 S_PBASE = "s68"     # first page of the block-table window
 S_LI = "s69"        # window lane of S_PN
 S_NV1, S_NV2, S_NV3 = "s70", "s71", "s72"   # valid rows of tiles it+1, it+2, it+3
-S_NV0 = "s73"       # valid rows of tile 0 (prologue)
+S_NV0 = "s81"       # valid rows of tile 0 (prologue only; shares S_T3)
 S_VOTE, S_VOTE_LO, S_VOTE_HI = "s[74:75]", "s74", "s75"
 S_B, S_B0, S_B1 = "s[76:77]", "s76", "s77"  # source base of the tile being streamed
 S_T0, S_T1, S_T2, S_T3 = "s78", "s79", "s80", "s81"
 S_M0B = "s82"       # LDS address of this wave's first load of the streamed tile
 S_LDSW = "s83"      # LDS base + 1024 wave
 S_KB = "s84"        # LDS base of tile it+1
-S_VB = "s85"        # LDS base of tile it+1 + 256 wave ... (V^T reads use VL0)
+S_M0SAVE = "s85"    # the compiler's M0, restored at the end of the block
 S_EXEC = "s[86:87]"
-S_PEND = "s88"      # pages holding tokens below the segment's end
-OWNED_SGPRS = [f"s{i}" for i in range(64, 89)]
+OWNED_SGPRS = [f"s{i}" for i in range(64, 73)] + [f"s{i}" for i in range(74, 88)]
 
 
 def Q(kk):
@@ -330,7 +329,7 @@ def window_load(em):
     em.op("v_mbcnt_hi_u32_b32 v208, -1, v208")
     em.op(f"v_add_u32 v208, {S_PBASE}, v208")
     em.op(f"v_mov_b32 {PWIN}, -1")
-    em.op(f"v_cmp_gt_u32 vcc, {S_PEND}, v208")
+    em.op("v_cmp_gt_u32 vcc, %[pend], v208")
     em.op(f"s_and_saveexec_b64 {S_EXEC}, vcc")
     em.op("v_lshlrev_b32 v208, 2, v208")
     em.op(f"global_load_dword {PWIN}, v208, %[bt]")
@@ -610,10 +609,11 @@ def pv(em, name, cur, nxt, has_next, has_n3):
         items += mx_move_items(nxt, False, earliest=10)
         # V^T (dt, 0) of tile it+1: addresses (its LDS base is S_KB), reads once
         # phase 0 has issued (MFMA 15 is the last to read v176..v191)
-        items.append(Item(set_va_ins(S_KB), earliest=15))
+        setva = Item(set_va_ins(S_KB), earliest=15)
+        items.append(setva)
         for dt in range(4):
             ins = vfrag_read_ins(V0_BASE + 4 * dt, dt, 0)
-            it = Item(ins, earliest=16)
+            it = Item(ins, earliest=16, deps=[(setva, 0)])
             v0r.append(it)
             items.append(it)
         # V^T (0, 0) and (1, 0) of tile it+1 to fp16 here; (2, 0), (3, 0) in
@@ -644,6 +644,7 @@ def pv(em, name, cur, nxt, has_next, has_n3):
 
 
 def prologue(em):
+    em.op(f"s_mov_b32 {S_M0SAVE}, m0")
     em.op("v_mbcnt_lo_u32_b32 v208, -1, 0")
     em.op("v_mbcnt_hi_u32_b32 v208, -1, v208")      # lane
     em.op("v_and_b32 v209, 31, v208")               # n32
@@ -714,7 +715,6 @@ def prologue(em):
     em.op(f"s_mov_b32 {S_ON}, %[on0]")
     em.op(f"s_mov_b32 {S_U0}, %[begin]")
     em.op(f"s_mov_b32 {S_LI}, 0")
-    em.op(f"s_mov_b32 {S_PEND}, %[pend]")
     for s in (S_NV1, S_NV2, S_NV3):
         em.op(f"s_mov_b32 {s}, {TOK}")
     # window first, then the query (36 loads)
@@ -823,6 +823,7 @@ def generate():
     step(em, "T2", 1, True, False, False)
     step(em, "T1", 0, False, False, False)
     em.op("s_waitcnt lgkmcnt(0)")
+    em.op(f"s_mov_b32 m0, {S_M0SAVE}")
     return "\n".join(em.lines) + "\n"
 
 
@@ -830,7 +831,9 @@ def clobber_list():
     v = [f'"v{i}"' for i in range(256) if i not in (224, 225)]
     a = [f'"a{i}"' for i in range(256)]
     s = [f'"{x}"' for x in OWNED_SGPRS]
-    return ", ".join(v + a + s + ['"vcc"', '"scc"', '"exec"', '"m0"', '"memory"'])
+    # EXEC leaves the block as it entered (masked sections restore it) and M0
+    # is saved and restored, so neither is listed.
+    return ", ".join(v + a + s + ['"vcc"', '"scc"', '"memory"'])
 
 
 def header_text():

@@ -28,6 +28,7 @@ constexpr int kHeadsPerBlock = 128;
 constexpr int kTok = 32;
 constexpr int kXOff = 4 * kTok * kMlaDqk * 2 + 8192;   // per-head floats after the tiles and the P exchange
 constexpr float kPShift = 7.0f;                        // p carries a factor 2^7 (taken out of the LSE)
+constexpr int kStageRow = 144;                         // bytes per head row of the output staging (128 + 16)
 static_assert(ISK_H128_LDS_BYTES == kXOff + 512, "LDS layout of the generated block");
 
 #define ISK_H128_A10(p) "a" #p "0", "a" #p "1", "a" #p "2", "a" #p "3", "a" #p "4", \
@@ -103,7 +104,10 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
 
     // Lane values are derived here, after the block (which owns every VGPR),
     // so that none has to be kept in memory across it.
-    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(lane));   // no lane-dependent value of the epilogue is computed earlier
+    int part = __builtin_amdgcn_readfirstlane(sg.part), brow = __builtin_amdgcn_readfirstlane(b);
+    asm volatile("" : "+s"(part), "+s"(brow));
     const int n32 = lane & 31, hh = lane >> 5;
     // ---- o = acc / l, lse = ln 2 (m_ref - 7 + log2 l); the lane pair of a
     // head adds its two halves of l in the same order in both lanes.
@@ -126,58 +130,70 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
     }
     asm volatile("s_nop 7\n\ts_nop 7");
     const int head = hb * kHeadsPerBlock + wave * 32 + n32;
-    float* of32 = nullptr;
-    uint16_t* obf = nullptr;
-    const size_t hb0 = (size_t)(hb * kHeadsPerBlock + n32);   // head of head tile 0
-    const size_t base = (sg.part >= 0 ? (size_t)sg.part : (size_t)b) * a.hq + hb0;
-    const size_t eo = base * kMlaDv + 128 * (size_t)wave + 4 * hh;
-    if (sg.part >= 0) {
-      of32 = a.part_o + eo;
-      if (hh == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
-    } else {
-      if (a.out_f32)
-        of32 = (float*)a.out + eo;
-      else
-        obf = (uint16_t*)a.out + eo;
-      if (a.lse != nullptr && hh == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
+    const bool to_part = part >= 0;
+    const size_t row0 = (to_part ? (size_t)part : (size_t)brow) * a.hq + (size_t)hb * kHeadsPerBlock;   // head 0 of the block
+    if (to_part) {
+      if (hh == 0) a.part_lse[(size_t)part * a.hq + head] = lse_v;
+    } else if (a.lse != nullptr && hh == 0) {
+      a.lse[(size_t)brow * a.hq + head] = lse_v;
     }
-    // lane holds O^T[128w + 32 dt + 8 q + 4 hh + e][32 ht + n32] at
-    // acc[4 dt + gg][4 q + e], ht = (gg + wave) & 3
-    auto store_tile = [&](int t, const float (&o)[16]) {
-      const int dt = t >> 2, gg = t & 3, ht = (gg + wave) & 3;
-      const size_t off = (size_t)ht * 32 * kMlaDv + 32 * dt;
+    // Output rows [row0, row0 + 128) of 2 KB (fp32) or 1 KB (bf16): a
+    // uniform base plus a 32-bit lane offset.
+    const bool f32 = to_part || a.out_f32;
+    unsigned char* const blk = f32 ? (unsigned char*)(to_part ? a.part_o : (float*)a.out) + row0 * kMlaDv * 4
+                                   : (unsigned char*)a.out + row0 * kMlaDv * 2;
+    // The output block goes through LDS (the tile buffers are free now) so
+    // that every store instruction writes whole rows of the output: round dt
+    // stages dims 32 dt .. 32 dt + 31 of the wave's 128 for all 128 heads
+    // ([head][dim], rows padded to 144 bytes against bank conflicts), then
+    // eight lanes write one head's 32 dims.
+    ISK_LDS float* const stage = (ISK_LDS float*)(lds_raw + wave * (kHeadsPerBlock * kStageRow));
+    const int sh = lane >> 3, sc = lane & 7;
+    auto stage_tile = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      constexpr int gg = t & 3;
+      const int ht = (gg + wave) & 3;
+      float o[16];
+      acc_read<t>(o);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4 r = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]} * inv[gg];
-        if (of32 != nullptr) {
-          *(f32x4*)(of32 + off + 8 * q) = r;
+        *(ISK_LDS f32x4*)(stage + ((32 * ht + n32) * kStageRow + 32 * q + 16 * hh) / 4) = r;
+      }
+    };
+    auto store_round = [&](int dt) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's LDS writes of the round have landed
+      uint32_t voff = (uint32_t)sh * kMlaDv * (f32 ? 4 : 2) + (128u * wave + 32u * dt + 4u * sc) * (f32 ? 4 : 2);
+#pragma unroll
+      for (int s16 = 0; s16 < 16; ++s16) {
+        const int hl = 8 * s16 + sh;                       // head within the block
+        const f32x4 r = *(const ISK_LDS f32x4*)(stage + (hl * kStageRow + 16 * sc) / 4);
+        if (f32) {
+          *(f32x4*)(blk + voff) = r;
         } else {
           uint2 w;
           w.x = pack_bf16x2(r[0], r[1]);
           w.y = pack_bf16x2(r[2], r[3]);
-          *(uint2*)(obf + off + 8 * q) = w;
+          *(uint2*)(blk + voff) = w;
         }
+        voff += 8u * kMlaDv * (f32 ? 4 : 2);
+        asm volatile("" : "+v"(voff));
       }
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // the reads are done before the next round writes
     };
-    {
-      float o[16];
-      acc_read<0>(o); store_tile(0, o);
-      acc_read<1>(o); store_tile(1, o);
-      acc_read<2>(o); store_tile(2, o);
-      acc_read<3>(o); store_tile(3, o);
-      acc_read<4>(o); store_tile(4, o);
-      acc_read<5>(o); store_tile(5, o);
-      acc_read<6>(o); store_tile(6, o);
-      acc_read<7>(o); store_tile(7, o);
-      acc_read<8>(o); store_tile(8, o);
-      acc_read<9>(o); store_tile(9, o);
-      acc_read<10>(o); store_tile(10, o);
-      acc_read<11>(o); store_tile(11, o);
-      acc_read<12>(o); store_tile(12, o);
-      acc_read<13>(o); store_tile(13, o);
-      acc_read<14>(o); store_tile(14, o);
-      acc_read<15>(o); store_tile(15, o);
-    }
+    __syncthreads();   // every wave is done with the tile buffers
+    stage_tile(std::integral_constant<int, 0>{}); stage_tile(std::integral_constant<int, 1>{});
+    stage_tile(std::integral_constant<int, 2>{}); stage_tile(std::integral_constant<int, 3>{});
+    store_round(0);
+    stage_tile(std::integral_constant<int, 4>{}); stage_tile(std::integral_constant<int, 5>{});
+    stage_tile(std::integral_constant<int, 6>{}); stage_tile(std::integral_constant<int, 7>{});
+    store_round(1);
+    stage_tile(std::integral_constant<int, 8>{}); stage_tile(std::integral_constant<int, 9>{});
+    stage_tile(std::integral_constant<int, 10>{}); stage_tile(std::integral_constant<int, 11>{});
+    store_round(2);
+    stage_tile(std::integral_constant<int, 12>{}); stage_tile(std::integral_constant<int, 13>{});
+    stage_tile(std::integral_constant<int, 14>{}); stage_tile(std::integral_constant<int, 15>{});
+    store_round(3);
   }
 }
 
