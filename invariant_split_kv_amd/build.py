@@ -85,6 +85,29 @@ def check_register_ownership(asm_text: str) -> list:
     return bad
 
 
+def check_no_scalar_loads_in_tile_loop(asm_text: str) -> list:
+    """Scalar memory loads inside an inner loop (loop depth >= 2: the tile
+    loop inside the segment loop).  The hand-counted LDS waits in the tile
+    loop of mla_split_h32.hip are correct only while in-order LDS operations
+    are the only traffic on that counter; a scalar load completes out of
+    order and would break them."""
+    bad, depth = [], 0
+    label = re.compile(r"^(\.LBB\d+_\d+:|; %bb\.\d+:)")
+    for n, line in enumerate(asm_text.splitlines(), 1):
+        s = line.strip()
+        if label.match(s) or s.startswith("; =>"):
+            m = re.search(r"Depth=(\d+)", s)
+            if label.match(s):
+                depth = int(m.group(1)) if m else 0
+            elif m:
+                depth = int(m.group(1))
+        elif re.match(r"^(s_load|s_buffer_load)", s) and depth >= 2:
+            bad.append((n, s))
+        elif re.match(r"^\w+:$", s) and not s.startswith("."):
+            depth = 0   # a new function
+    return bad
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -104,8 +127,12 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     sys.path.insert(0, CSRC)
     try:
         import gen_mla_h128
+        import check_mla_h128
     finally:
         sys.path.pop(0)
+    errors = check_mla_h128.check()
+    if errors:
+        raise RuntimeError("generated MLA tile loop fails its schedule check:\n  " + "\n  ".join(errors[:10]))
     gen_mla_h128.write_header(os.path.join(GEN_DIR, "mla_h128_seg.inc"))
     objs, procs = [], []
     for src in SOURCES:
@@ -124,9 +151,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         _run([hipcc, *FLAGS, *EXTRA_FLAGS.get(src, []), "--cuda-device-only", "-S", os.path.join(CSRC, src),
               "-o", asm], verbose)
         with open(asm) as f:
-            bad = check_register_ownership(f.read())
+            text = f.read()
+        bad = check_register_ownership(text)
         if bad:
             raise RuntimeError(f"{src}: compiler-generated code uses registers owned by inline asm: {bad[:5]}")
+        bad = check_no_scalar_loads_in_tile_loop(text)
+        if bad:
+            raise RuntimeError(f"{src}: scalar loads inside the tile loop: {bad[:5]}")
     for src in AGPR_OWNED:
         asm = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".device.s")
         _run([hipcc, *FLAGS, *EXTRA_FLAGS.get(src, []), "--cuda-device-only", "-S", os.path.join(CSRC, src),
