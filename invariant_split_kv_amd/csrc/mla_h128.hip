@@ -29,6 +29,11 @@ constexpr int kTok = 32;
 constexpr int kXOff = 4 * kTok * kMlaDqk * 2 + 8192;   // per-head floats after the tiles and the P exchange
 constexpr float kPShift = 7.0f;                        // p carries a factor 2^7 (taken out of the LSE)
 constexpr int kStageRow = 144;                         // bytes per head row of the output staging (128 + 16)
+// global-memory pointer types (the stores use a scalar base)
+typedef __attribute__((address_space(1))) unsigned char GU8;
+typedef __attribute__((address_space(1))) f32x4 GF32x4;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) u32x2 GU32x2;
 static_assert(ISK_H128_LDS_BYTES == kXOff + 512, "LDS layout of the generated block");
 
 #define ISK_H128_A10(p) "a" #p "0", "a" #p "1", "a" #p "2", "a" #p "3", "a" #p "4", \
@@ -102,6 +107,10 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
           "v_accvgpr_write_b32 a[\\i+\\k], 0\n\t.endr\n\t.endr\n\ts_nop 4" ::: ISK_H128_ALL_AGPRS);
     }
 
+    // The launch arguments are read again here rather than kept in SGPRs
+    // across the block.
+    const MlaLaunch* ka = (const MlaLaunch*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ka));
     // Lane values are derived here, after the block (which owns every VGPR),
     // so that none has to be kept in memory across it.
     int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
@@ -131,17 +140,22 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
     asm volatile("s_nop 7\n\ts_nop 7");
     const int head = hb * kHeadsPerBlock + wave * 32 + n32;
     const bool to_part = part >= 0;
-    const size_t row0 = (to_part ? (size_t)part : (size_t)brow) * a.hq + (size_t)hb * kHeadsPerBlock;   // head 0 of the block
+    const size_t row0 = (to_part ? (size_t)part : (size_t)brow) * ka->hq + (size_t)hb * kHeadsPerBlock;   // head 0 of the block
     if (to_part) {
-      if (hh == 0) a.part_lse[(size_t)part * a.hq + head] = lse_v;
-    } else if (a.lse != nullptr && hh == 0) {
-      a.lse[(size_t)brow * a.hq + head] = lse_v;
+      if (hh == 0) ka->part_lse[(size_t)part * ka->hq + head] = lse_v;
+    } else if (ka->lse != nullptr && hh == 0) {
+      ka->lse[(size_t)brow * ka->hq + head] = lse_v;
     }
     // Output rows [row0, row0 + 128) of 2 KB (fp32) or 1 KB (bf16): a
     // uniform base plus a 32-bit lane offset.
-    const bool f32 = to_part || a.out_f32;
-    unsigned char* const blk = f32 ? (unsigned char*)(to_part ? a.part_o : (float*)a.out) + row0 * kMlaDv * 4
-                                   : (unsigned char*)a.out + row0 * kMlaDv * 2;
+    const bool f32 = to_part || ka->out_f32;
+    // The launch arguments come from the kernarg segment, so the compiler
+    // no longer knows the pointers are global memory: say so, and keep the
+    // block base uniform (scalar base + 32-bit lane offset stores).
+    const uintptr_t base = (uintptr_t)(f32 ? (unsigned char*)(to_part ? ka->part_o : (float*)ka->out) + row0 * kMlaDv * 4
+                                           : (unsigned char*)ka->out + row0 * kMlaDv * 2);
+    GU8* const blk = (GU8*)(((uintptr_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base));
     // The output block goes through LDS (the tile buffers are free now) so
     // that every store instruction writes whole rows of the output: round dt
     // stages dims 32 dt .. 32 dt + 31 of the wave's 128 for all 128 heads
@@ -161,39 +175,48 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
         *(ISK_LDS f32x4*)(stage + ((32 * ht + n32) * kStageRow + 32 * q + 16 * hh) / 4) = r;
       }
     };
-    auto store_round = [&](int dt) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's LDS writes of the round have landed
-      uint32_t voff = (uint32_t)sh * kMlaDv * (f32 ? 4 : 2) + (128u * wave + 32u * dt + 4u * sc) * (f32 ? 4 : 2);
+    // One round: the 16 reads of the staged rows are all issued before the
+    // first store; F32 picks fp32 rows (partials, or fp32 output) or bf16.
+    auto rounds = [&](auto fc) {
+      constexpr bool F32 = decltype(fc)::value;
+      constexpr uint32_t esz = F32 ? 4 : 2;
+      auto store_round = [&](int dt) {
+        asm volatile("" ::: "memory");   // the round's staging writes come first (other lanes read them)
+        f32x4 r[16];
 #pragma unroll
-      for (int s16 = 0; s16 < 16; ++s16) {
-        const int hl = 8 * s16 + sh;                       // head within the block
-        const f32x4 r = *(const ISK_LDS f32x4*)(stage + (hl * kStageRow + 16 * sc) / 4);
-        if (f32) {
-          *(f32x4*)(blk + voff) = r;
-        } else {
-          uint2 w;
-          w.x = pack_bf16x2(r[0], r[1]);
-          w.y = pack_bf16x2(r[2], r[3]);
-          *(uint2*)(blk + voff) = w;
+        for (int s16 = 0; s16 < 16; ++s16)
+          r[s16] = *(const ISK_LDS f32x4*)(stage + ((8 * s16 + sh) * kStageRow + 16 * sc) / 4);
+        uint32_t voff = ((uint32_t)sh * kMlaDv + 128u * wave + 32u * dt + 4u * sc) * esz;
+#pragma unroll
+        for (int s16 = 0; s16 < 16; ++s16) {
+          if constexpr (F32) {
+            *(GF32x4*)(blk + voff) = r[s16];
+          } else {
+            *(GU32x2*)(blk + voff) = u32x2{pack_bf16x2(r[s16][0], r[s16][1]), pack_bf16x2(r[s16][2], r[s16][3])};
+          }
+          voff += 8u * kMlaDv * esz;
+          asm volatile("" : "+v"(voff));
         }
-        voff += 8u * kMlaDv * (f32 ? 4 : 2);
-        asm volatile("" : "+v"(voff));
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);   // the reads are done before the next round writes
+        asm volatile("" ::: "memory");   // the reads come before the next round's writes
+      };
+      stage_tile(std::integral_constant<int, 0>{}); stage_tile(std::integral_constant<int, 1>{});
+      stage_tile(std::integral_constant<int, 2>{}); stage_tile(std::integral_constant<int, 3>{});
+      store_round(0);
+      stage_tile(std::integral_constant<int, 4>{}); stage_tile(std::integral_constant<int, 5>{});
+      stage_tile(std::integral_constant<int, 6>{}); stage_tile(std::integral_constant<int, 7>{});
+      store_round(1);
+      stage_tile(std::integral_constant<int, 8>{}); stage_tile(std::integral_constant<int, 9>{});
+      stage_tile(std::integral_constant<int, 10>{}); stage_tile(std::integral_constant<int, 11>{});
+      store_round(2);
+      stage_tile(std::integral_constant<int, 12>{}); stage_tile(std::integral_constant<int, 13>{});
+      stage_tile(std::integral_constant<int, 14>{}); stage_tile(std::integral_constant<int, 15>{});
+      store_round(3);
     };
     __syncthreads();   // every wave is done with the tile buffers
-    stage_tile(std::integral_constant<int, 0>{}); stage_tile(std::integral_constant<int, 1>{});
-    stage_tile(std::integral_constant<int, 2>{}); stage_tile(std::integral_constant<int, 3>{});
-    store_round(0);
-    stage_tile(std::integral_constant<int, 4>{}); stage_tile(std::integral_constant<int, 5>{});
-    stage_tile(std::integral_constant<int, 6>{}); stage_tile(std::integral_constant<int, 7>{});
-    store_round(1);
-    stage_tile(std::integral_constant<int, 8>{}); stage_tile(std::integral_constant<int, 9>{});
-    stage_tile(std::integral_constant<int, 10>{}); stage_tile(std::integral_constant<int, 11>{});
-    store_round(2);
-    stage_tile(std::integral_constant<int, 12>{}); stage_tile(std::integral_constant<int, 13>{});
-    stage_tile(std::integral_constant<int, 14>{}); stage_tile(std::integral_constant<int, 15>{});
-    store_round(3);
+    if (f32)
+      rounds(std::true_type{});
+    else
+      rounds(std::false_type{});
   }
 }
 
