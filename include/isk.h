@@ -398,8 +398,13 @@ ISK_API int isk_plan_set_timing_events(isk_plan* plan, void* split_begin, void* 
 ISK_API const char* isk_last_error(void);
 
 /* isk_numerics_id - the build's numerics identity: target architecture, the
- * frozen split and tile constants and the kernel versions.  Output bits are
- * claimed batch-invariant for a fixed value of this string (and GPU model). */
+ * frozen split and tile constants, the operand precisions and the kernel
+ * versions.  Output bits are claimed batch-invariant for a fixed value of
+ * this string (and GPU model) only: the page "batch-invariance-is-not-
+ * universal-across-kernel-paths" (section "Workaround") says invariance has
+ * to be measured on the exact configuration that ships, since another kernel
+ * path or precision changes the arithmetic.  Never NULL; owned by the
+ * library. */
 ISK_API const char* isk_numerics_id(void);
 
 #ifdef __cplusplus

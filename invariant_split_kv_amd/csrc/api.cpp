@@ -242,6 +242,7 @@ const char* isk_numerics_id(void) {
       << " split_topk=" << isk::kSparseSplitDefault
       << " gqa=vdot2-bf16/fp32-pv"
       << " mla(hq%128=0)=qk:mfma32x32x16-bf16/pv:mfma32x32x16-f16(p-fp16-rne-x2^7,v-bf16-to-fp16-rtz)/tile32/rescale-thr8"
+      << "/partials-fp16-rne(bf16-out)"
       << " mla(other)=mfma16x16x32-bf16/tile64/p-hi+lo-bf16/rescale-thr8 combine=fixed-order-fp32"
       << " balanced=blk" << isk::kBalancedBlock << "-parts" << isk::kBalancedParts << "-ovh" << isk::kBalancedOverhead;
     return s.str();
@@ -453,6 +454,9 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
   const int32_t n_groups = (int32_t)pd.groups.size() - 1;
   const float scale_log2 = d.scale * isk::kLog2eHost;
 
+  // Partials of the 128-head MLA kernels (fp16 PV operand) are fp16 when the
+  // output is bf16; every other kernel, and fp32 output, keeps fp32 partials.
+  const int32_t part_f16 = d.kind != ISK_KIND_GQA && d.num_q_heads % 128 == 0 && d.out_dtype != ISK_OUT_F32;
   isk::LaunchEvents ev;
   ev.begin = plan->t_split_begin;
   ev.end = plan->t_split_end;
@@ -465,7 +469,7 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
   } else {
     isk::MlaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, sparse ? topk_idx : nullptr,
                      segs, groups, part_o, part_lse, out, lse, n_groups, d.num_q_heads, d.page_size, d.num_pages,
-                     d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2,
+                     d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2, part_f16,
                      nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, plan->inl};
     if (extra != nullptr) {
       a.xkv = (const uint16_t*)extra->kv_pages;
@@ -490,7 +494,7 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
   }
   if (pd.any_combine) {
     isk::CombineLaunch c{rows, part_o, part_lse, out, lse, pd.batch, d.num_q_heads, d.head_dim_v,
-                         d.out_dtype == ISK_OUT_F32, plan->inl};
+                         d.out_dtype == ISK_OUT_F32, part_f16, plan->inl};
     e = isk::launch_combine(c, stream);
     if (e != hipSuccess) return hip_err(e, "launching the combine kernel");
   }

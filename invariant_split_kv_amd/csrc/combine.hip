@@ -10,6 +10,8 @@
 // count (no per-count code variants, no atomics):
 //   m = max_i lse_i;  e_i = 2^((lse_i - m) * log2 e);  S = sum_i e_i;
 //   lse = m + ln S;   out = sum_i (e_i / S) * o_i   (fp32 FMA chain, i ascending)
+// Partials are fp32, or fp16 for the 128-head MLA kernels with bf16 output
+// (widened exactly to fp32 on load; the arithmetic is the same).
 // One wave handles one (row, head); lane l owns Dv/64 consecutive dims.  The
 // LSEs are loaded lane-parallel and the partials up to eight at a time, so a
 // row costs a few memory round trips instead of one per split.
@@ -40,11 +42,35 @@ __device__ __forceinline__ void load_part(const float* src, float (&v)[DPL]) {
   }
 }
 
+// fp16 partials (exact widening to fp32).
+template <int DPL>
+__device__ __forceinline__ void load_part(const uint16_t* src, float (&v)[DPL]) {
+  auto half = [](uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); };
+  if constexpr (DPL % 8 == 0) {
+#pragma unroll
+    for (int j = 0; j < DPL; j += 8) {
+      const uint4 x = *(const uint4*)(src + j);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[j + 2 * k] = half(w[k] & 0xffffu);
+        v[j + 2 * k + 1] = half(w[k] >> 16);
+      }
+    }
+  } else if constexpr (DPL == 2) {
+    const uint32_t x = *(const uint32_t*)src;
+    v[0] = half(x & 0xffffu); v[1] = half(x >> 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) v[j] = half(src[j]);
+  }
+}
+
 // The partials' LSEs are loaded lane-parallel (lane l of chunk c holds split
 // 64c + l); the sum of the weights and the output FMA chain still run over
 // the splits one at a time in ascending order (v_readlane of the lane that
 // holds split i), so every value is the one the sequential definition gives.
-template <int DPL>
+template <int DPL, typename P>
 __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -85,7 +111,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
       }
       const float inv = 1.f / ssum;
       lse_out = m + fast_log2(ssum) * kLn2;
-      const float* op = a.part_o + ((size_t)ri.part_off * a.hq + h) * a.dv + DPL * lane;
+      const P* op = (const P*)a.part_o + ((size_t)ri.part_off * a.hq + h) * a.dv + DPL * lane;
       const size_t stride = (size_t)a.hq * a.dv;
       // out = sum_i (e_i / S) o_i, an FMA chain with i ascending; the
       // partials' loads go out eight (then four, then the rest) at a time.
@@ -145,10 +171,15 @@ hipError_t launch_combine(const CombineLaunch& a, hipStream_t s) {
   const int pairs = a.batch * a.hq;
   if (pairs == 0) return hipSuccess;
   const dim3 grid((pairs + 3) / 4), block(256);
+  if (a.part_f16) {
+    if (a.dv != 512) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((combine_kernel<8, uint16_t>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   switch (a.dv) {
-    case 64: hipLaunchKernelGGL(combine_kernel<1>, grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, s, a); break;
-    case 512: hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((combine_kernel<1, float>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<2, float>), grid, block, 0, s, a); break;
+    case 512: hipLaunchKernelGGL((combine_kernel<8, float>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

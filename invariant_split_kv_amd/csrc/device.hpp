@@ -42,6 +42,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, to_bf16x2(a, b));
 }
 
+// Two floats to fp16 (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
 // Butterfly reductions inside a wave: every lane ends with the same bits
 // (fp32 max is exact; the add tree pairs the same operands in every lane).
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

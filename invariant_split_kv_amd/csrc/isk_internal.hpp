@@ -150,6 +150,9 @@ struct MlaLaunch {
   float* part_o; float* part_lse; void* out; float* lse;
   int32_t n_groups, hq, page_size, num_pages, max_pages, topk_width, out_f32;
   float scale_log2;
+  // Partials in fp16 (2 bytes a value) instead of fp32; only the 128-head
+  // kernels, whose PV operand is fp16 already, take it.
+  int32_t part_f16;
   // Extra KV source (sparse only; xtopk_idx NULL when absent).  A segment
   // whose begin is >= topk_width gathers from it, at extra slots
   // [begin - topk_width, end - topk_width).
@@ -165,6 +168,7 @@ struct CombineLaunch {
   const RowInfo* rows; const float* part_o; const float* part_lse;
   void* out; float* lse;
   int32_t batch, hq, dv, out_f32;
+  int32_t part_f16;   // partials stored as fp16 (part_o then holds 2-byte values)
   InlinePlan inl;   // n_segs > 0: per-row partial slots by value
 };
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t s);

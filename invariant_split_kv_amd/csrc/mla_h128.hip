@@ -28,7 +28,8 @@ constexpr int kHeadsPerBlock = 128;
 constexpr int kTok = 32;
 constexpr int kXOff = 4 * kTok * kMlaDqk * 2 + 8192;   // per-head floats after the tiles and the P exchange
 constexpr float kPShift = 7.0f;                        // p carries a factor 2^7 (taken out of the LSE)
-constexpr int kStageRow = 144;                         // bytes per head row of the output staging (128 + 16)
+constexpr int kStageRow = 144;
+constexpr int kFmtF32 = 0, kFmtBF16 = 1, kFmtF16 = 2;   // output row formats                         // bytes per head row of the output staging (128 + 16)
 // global-memory pointer types (the stores use a scalar base)
 typedef __attribute__((address_space(1))) unsigned char GU8;
 typedef __attribute__((address_space(1))) f32x4 GF32x4;
@@ -146,14 +147,14 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
     } else if (ka->lse != nullptr && hh == 0) {
       ka->lse[(size_t)brow * ka->hq + head] = lse_v;
     }
-    // Output rows [row0, row0 + 128) of 2 KB (fp32) or 1 KB (bf16): a
-    // uniform base plus a 32-bit lane offset.
-    const bool f32 = to_part || ka->out_f32;
+    // Output rows [row0, row0 + 128): fp32 (2 KB a row: fp32 output, or
+    // partials of an fp32-output launch), bf16 output or fp16 partials (1 KB).
+    const int fmt = to_part ? (ka->part_f16 ? kFmtF16 : kFmtF32) : (ka->out_f32 ? kFmtF32 : kFmtBF16);
+    const size_t esz = fmt == kFmtF32 ? 4 : 2;
     // The launch arguments come from the kernarg segment, so the compiler
     // no longer knows the pointers are global memory: say so, and keep the
     // block base uniform (scalar base + 32-bit lane offset stores).
-    const uintptr_t base = (uintptr_t)(f32 ? (unsigned char*)(to_part ? ka->part_o : (float*)ka->out) + row0 * kMlaDv * 4
-                                           : (unsigned char*)ka->out + row0 * kMlaDv * 2);
+    const uintptr_t base = (uintptr_t)((unsigned char*)(to_part ? (void*)ka->part_o : ka->out) + row0 * kMlaDv * esz);
     GU8* const blk = (GU8*)(((uintptr_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
                             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base));
     // The output block goes through LDS (the tile buffers are free now) so
@@ -176,10 +177,10 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
       }
     };
     // One round: the 16 reads of the staged rows are all issued before the
-    // first store; F32 picks fp32 rows (partials, or fp32 output) or bf16.
+    // first store; FMT is the row format.
     auto rounds = [&](auto fc) {
-      constexpr bool F32 = decltype(fc)::value;
-      constexpr uint32_t esz = F32 ? 4 : 2;
+      constexpr int FMT = decltype(fc)::value;
+      constexpr uint32_t esz = FMT == kFmtF32 ? 4 : 2;
       auto store_round = [&](int dt) {
         asm volatile("" ::: "memory");   // the round's staging writes come first (other lanes read them)
         f32x4 r[16];
@@ -189,10 +190,12 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
         uint32_t voff = ((uint32_t)sh * kMlaDv + 128u * wave + 32u * dt + 4u * sc) * esz;
 #pragma unroll
         for (int s16 = 0; s16 < 16; ++s16) {
-          if constexpr (F32) {
+          if constexpr (FMT == kFmtF32) {
             *(GF32x4*)(blk + voff) = r[s16];
-          } else {
+          } else if constexpr (FMT == kFmtBF16) {
             *(GU32x2*)(blk + voff) = u32x2{pack_bf16x2(r[s16][0], r[s16][1]), pack_bf16x2(r[s16][2], r[s16][3])};
+          } else {
+            *(GU32x2*)(blk + voff) = u32x2{pack_f16x2(r[s16][0], r[s16][1]), pack_f16x2(r[s16][2], r[s16][3])};
           }
           voff += 8u * kMlaDv * esz;
           asm volatile("" : "+v"(voff));
@@ -213,10 +216,12 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
       store_round(3);
     };
     __syncthreads();   // every wave is done with the tile buffers
-    if (f32)
-      rounds(std::true_type{});
+    if (fmt == kFmtF32)
+      rounds(std::integral_constant<int, kFmtF32>{});
+    else if (fmt == kFmtBF16)
+      rounds(std::integral_constant<int, kFmtBF16>{});
     else
-      rounds(std::false_type{});
+      rounds(std::integral_constant<int, kFmtF16>{});
   }
 }
 

@@ -989,13 +989,19 @@ mla_split_h32_kernel(MlaLaunch a) {
     int head_e = head;
     asm volatile("" : "+v"(head_e));
     float* of32 = nullptr;
-    uint16_t* obf = nullptr;
+    uint16_t* obf = nullptr;   // bf16 output, or fp16 partials (f16out)
+    bool f16out = false;
     {
       const size_t hb0 = (size_t)(hb * kHeadsPerBlock + n32);   // head of tile ht = 0
       const size_t base = (sg.part >= 0 ? (size_t)sg.part : (size_t)b) * a.hq + hb0;
       const size_t eo = base * kMlaDv + 128 * (size_t)wave_u + 4 * hh;
       if (sg.part >= 0) {
-        of32 = a.part_o + eo;
+        if (a.part_f16) {
+          obf = (uint16_t*)a.part_o + eo;
+          f16out = true;
+        } else {
+          of32 = a.part_o + eo;
+        }
         if (hh == 0) a.part_lse[(size_t)sg.part * a.hq + head_e] = lse_v;
       } else {
         if (a.out_f32)
@@ -1013,6 +1019,11 @@ mla_split_h32_kernel(MlaLaunch a) {
         const f32x4 r = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]} * inv[ht];
         if (of32 != nullptr) {
           *(f32x4*)(of32 + off + 8 * q) = r;
+        } else if (f16out) {
+          uint2 w;
+          w.x = pack_f16x2(r[0], r[1]);
+          w.y = pack_f16x2(r[2], r[3]);
+          *(uint2*)(obf + off + 8 * q) = w;
         } else {
           uint2 w;
           w.x = pack_bf16x2(r[0], r[1]);
