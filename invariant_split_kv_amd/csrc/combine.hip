@@ -90,6 +90,18 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
     // The LSEs of chunk c (splits 64c .. 64c+63, lane-parallel); with at most
     // 64 splits (every row up to 98304 tokens) the one chunk is loaded once.
     const float x0 = lane < n ? lse_p[(size_t)lane * a.hq] : -INFINITY;
+    // Up to eight splits (most rows): the partials do not depend on the
+    // weights, so their loads go out with the LSEs' and the row costs one
+    // memory round trip.
+    const P* op = (const P*)a.part_o + ((size_t)ri.part_off * a.hq + h) * a.dv + DPL * lane;
+    const size_t stride = (size_t)a.hq * a.dv;
+    constexpr int kEarly = 8;
+    float ve[kEarly][DPL];
+    if (n <= kEarly) {
+#pragma unroll
+      for (int k = 0; k < kEarly; ++k)
+        if (k < n) load_part<DPL>(op + (size_t)k * stride, ve[k]);
+    }
     auto lse_chunk = [&](int c) { return c == 0 ? x0 : (c + lane < n ? lse_p[(size_t)(c + lane) * a.hq] : -INFINITY); };
     // m = max_i lse_i (exact, any order).
     float m = -INFINITY;
@@ -111,11 +123,20 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
       }
       const float inv = 1.f / ssum;
       lse_out = m + fast_log2(ssum) * kLn2;
-      const P* op = (const P*)a.part_o + ((size_t)ri.part_off * a.hq + h) * a.dv + DPL * lane;
-      const size_t stride = (size_t)a.hq * a.dv;
       // out = sum_i (e_i / S) o_i, an FMA chain with i ascending; the
       // partials' loads go out eight (then four, then the rest) at a time.
-      for (int c = 0; c < n; c += 64) {
+      if (n <= kEarly) {
+        const float wl = fast_exp2((x0 - m) * kLog2e) * inv;
+#pragma unroll
+        for (int k = 0; k < kEarly; ++k) {
+          if (k < n) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k));
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) o[j] = fmaf(w, ve[k][j], o[j]);
+          }
+        }
+      }
+      for (int c = 0; n > kEarly && c < n; c += 64) {
         const float x = lse_chunk(c);
         const float wl = fast_exp2((x - m) * kLog2e) * inv;
         const int cn = min(64, n - c);

@@ -229,3 +229,22 @@ def test_balanced_mode_is_caught_by_the_harness():
     print(f"[negative control] balanced mode: probe bit-identical in {total - differing}/{total} compositions",
           flush=True)
     assert differing > 0
+
+
+def test_config5_longest_batchmates_match_oracle():
+    """The two longest batchmates of a B=32 stress composition (tens of
+    thousands of tokens, more than 64 splits for the longest) against the
+    oracle, so that an error shared by solo and batched runs (which the bit
+    comparisons above cannot see) would still show."""
+    lens, seeds, pos = synth.config5_composition(32, 0)
+    ob, lb, q, pool, paging = _gpu_batch_run(lens, seeds, paging_seed=3200)
+    import oracle
+    longest = [int(j) for j in np.argsort(lens)[::-1][:2]]
+    print(f"[config5 oracle] rows {longest} lens {[int(lens[j]) for j in longest]}", flush=True)
+    for j in longest:
+        L = int(lens[j])
+        lat = pool[torch.from_numpy(paging.token_slots(j, np.arange(L))).cuda()]
+        ro, rl = oracle.mla_decode(q[j:j + 1].float().cpu().numpy(), [lat.float().cpu().numpy()], MLA_SCALE)
+        out = torch.from_numpy(ob[j:j + 1]).view(torch.bfloat16).float().numpy()
+        lse = torch.from_numpy(lb[j:j + 1]).view(torch.float32).numpy()
+        parity(out, lse, ro, rl, False, f"config5 batchmate {j} (len {L})")

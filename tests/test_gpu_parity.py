@@ -99,6 +99,18 @@ def test_mla_page_size_128_and_custom_split():
     parity(out, lse, ro, rl, False, "mla P=128 S=256")
 
 
+@pytest.mark.parametrize("hq,out_f32", [(128, False), (128, True), (64, False)])
+def test_combine_over_64_splits(hq, out_f32):
+    """Rows with more than 64 splits (79 and 313 at S = 64) take the
+    combine's chunked path (LSEs loaded 64 at a time, then chained); fp16
+    partials (128 heads, bf16 output) and fp32 partials (fp32 output, or the
+    16-head kernel) both go through it."""
+    case = synth.mla_case([5000, 20000, 70, 1], hq, 0.07, 64, structure_seed=53, split_tokens=64)
+    out, lse, _, _ = run_case(case, out_f32=out_f32)
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, out_f32, f"mla >64 splits hq={hq} f32={out_f32}")
+
+
 def _grow_rope_scores(case, growth):
     """Scale the 64 rope dims of each cached token by growth(t / L): the
     scores climb (or jump) across the row while the values (the first 512
