@@ -9,15 +9,20 @@ are synthetic and resident in HBM before timing starts.
 
 One step = the whole hot path: host re-planning of the per-row splits, the
 split list's hand-over (by value in the kernel arguments for this batch),
-the split kernel and the fixed-order combine.  The timed
-region is exactly `--steps` steps after `--warmup` untimed ones, bracketed by
-device synchronisation, with nothing else recorded on the stream (per-step
-timing events would add their own gaps to the step).  The split kernel's
+the split kernel and the fixed-order combine.  Untimed steps first run for
+`--settle-ms` of wall time while the shader clock settles (reported as
+`clock_settle`, apart from `warmup`); then the timed region is exactly
+`--steps` steps after `--warmup` untimed ones, bracketed by device
+synchronisation, with nothing else recorded on the stream (per-step timing
+events would add their own gaps to the step).  The split kernel's
 duration for the roofline comes from a second pass of `--steps` steps right
 after it, in which the library launches the split kernel through
 hipExtLaunchKernel with a start and a stop HIP event, so the events carry the
 kernel's own start and end on its stream.  Prints one JSON line: the metric,
-the roofline of the split kernel and the CPU oracle baseline.
+the roofline of the split kernel (against the 8 TB/s published peak and the
+read peak the streaming-read probe measures), the CPU oracle baseline and
+the parity of the timed configuration against the oracle on the rows the
+baseline computed.
 """
 
 import argparse
@@ -33,12 +38,18 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mla_split_b64_hbm_traffic.txt")
-SPLIT_KERNEL_SRC = os.path.join(ROOT, "invariant_split_kv_amd", "csrc", "mla_split_h32.hip")
+# The B=64 split kernel: mla_h128.hip with the tile loop gen_mla_h128.py writes.
+SPLIT_KERNEL_SRC = [os.path.join(ROOT, "invariant_split_kv_amd", "csrc", f)
+                    for f in ("mla_h128.hip", "gen_mla_h128.py")]
+SPLIT_KERNEL_NAME = "mla_h128_kernel"
 
 
 def kernel_source_hash() -> str:
     import hashlib
-    return hashlib.sha256(open(SPLIT_KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in SPLIT_KERNEL_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -97,6 +108,49 @@ class HipEvents:
         self.rt.hipEventDestroy(ev)
 
 
+def clock_settle(dc, torch, lens_host, settle_ms):
+    """Untimed steps until `settle_ms` of wall time has passed (checked every
+    ten steps, after a device synchronisation): the shader clock of a cold
+    part takes some tens of milliseconds of this load to reach its steady
+    level.  Reported as its own field, apart from `warmup`."""
+    stream = torch.cuda.current_stream()
+    steps = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(10):
+            dc.plan.update(lens_host)
+            dc.run(stream)
+        steps += 10
+        torch.cuda.synchronize()
+    return {"steps": steps, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
+
+
+def hbm_read_peak(isk, torch, nbytes=2 << 30, launches=10):
+    """Achievable HBM read rate: isk_hbm_read_probe over a 2 GiB buffer (8x
+    the 256 MB last-level cache), best of four grid sizes, each timed over
+    `launches` launches after two untimed ones."""
+    stream = torch.cuda.current_stream()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.empty(16384, dtype=torch.int32, device="cuda")
+    by_blocks = {}
+    for blocks in (1024, 2048, 4096, 8192):
+        for _ in range(2):
+            isk.hbm_read_probe(buf, nbytes, sink, blocks, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(launches):
+            isk.hbm_read_probe(buf, nbytes, sink, blocks, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        by_blocks[blocks] = round(nbytes * launches / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    del buf, sink
+    torch.cuda.empty_cache()
+    best = max(by_blocks, key=by_blocks.get)
+    return {"gbs": by_blocks[best], "bytes": nbytes, "blocks": best, "gbs_by_blocks": by_blocks,
+            "frac_of_published_peak": round(by_blocks[best] / HBM_PEAK_GBS, 4)}
+
+
 def timed_steps(dc, isk, torch, evs, steps, warmup, lens_host, instrument):
     """Warm up, then time exactly `steps` steps.  With `instrument`, the
     library's timing hook stamps HIP events with every split kernel's start and
@@ -132,6 +186,30 @@ def timed_steps(dc, isk, torch, evs, steps, warmup, lens_host, instrument):
     return total_ms, wall, split, comb
 
 
+def interleaved_ms(torch, calls_by_name, rounds=10, calls=10, warm=20):
+    """Median milliseconds per call of each named step under the same clock
+    state: after `warm` untimed calls of each, `rounds` rounds in which every
+    step is timed over `calls` calls in turn (the order reversed on every
+    other round, so that a drifting clock favours neither)."""
+    stream = torch.cuda.current_stream()
+    names = list(calls_by_name)
+    for n in names:
+        for _ in range(warm):
+            calls_by_name[n]()
+    per = {n: [] for n in names}
+    for r in range(rounds):
+        for n in (names if r % 2 == 0 else names[::-1]):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(calls):
+                calls_by_name[n]()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per[n].append(a.elapsed_time(b) / calls)
+    import numpy as np
+    return {n: float(np.median(v)) for n, v in per.items()}
+
+
 # Length-band split tables (isk_plan_create_banded) for two regimes.  Both
 # keep a row's splits a function of its own length; they differ in which
 # batches they favour.  Latency: rows up to 16384 tokens get 512-token splits
@@ -145,7 +223,9 @@ def per_row_vs_balanced_sizes(isk, synth, torch, np, sizes=(1, 2, 8, 32, 128), c
     """Per-row over balanced call time on the invariance-stress batches (probe
     row of 16384 tokens among batchmates of 1..131072 tokens, composition 0),
     one batch per size, with the per-row plan under the two band tables too.
-    Values are drawn on the GPU (N(0, 0.5^2), bf16); only the timing is used."""
+    The four plans of a batch are timed interleaved (interleaved_ms), so they
+    see the same clock state.  Values are drawn on the GPU (N(0, 0.5^2),
+    bf16); only the timing is used."""
     res = {}
     stream = torch.cuda.current_stream()
     batches = [(str(B), synth.config5_composition(B, 0)[0]) for B in sizes]
@@ -163,26 +243,21 @@ def per_row_vs_balanced_sizes(isk, synth, torch, np, sizes=(1, 2, 8, 32, 128), c
         lens_d = torch.from_numpy(lens).cuda()
         out = torch.empty((B, 128, synth.MLA_DV), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((B, 128), dtype=torch.float32, device="cuda")
-        ms = {}
+        plans, steps = [], {}
         for name, mode, bands in (("per_row", isk.SPLIT_PER_ROW, None),
                                   ("bands_latency", isk.SPLIT_PER_ROW, BANDS_LATENCY),
                                   ("bands_throughput", isk.SPLIT_PER_ROW, BANDS_THROUGHPUT),
                                   ("balanced", isk.SPLIT_BATCH_BALANCED, None)):
             desc = isk.IskDesc(isk.KIND_MLA, 128, 1, synth.MLA_DQK, synth.MLA_DV, 64, paging.num_pages,
                                paging.max_pages_per_row, 0, mode, 0, isk.OUT_BF16, 0, 1.0 / math.sqrt(192.0))
-            with isk.Plan(desc, lens, bands=bands) as plan:
-                ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
-                call = lambda: isk.attn_decode(plan.handle, q, pool, bt, lens_d, None, None, out, lse, ws,
-                                               ws.numel(), stream)
-                for _ in range(20):
-                    call()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(calls):
-                    call()
-                b.record(stream)
-                torch.cuda.synchronize()
-                ms[name] = a.elapsed_time(b) / calls
+            plan = isk.Plan(desc, lens, bands=bands)
+            ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+            plans.append((plan, ws))
+            steps[name] = (lambda plan=plan, ws=ws: isk.attn_decode(plan.handle, q, pool, bt, lens_d, None, None,
+                                                                    out, lse, ws, ws.numel(), stream))
+        ms = interleaved_ms(torch, steps, rounds=6, calls=max(1, calls // 6))
+        for plan, _ in plans:
+            plan.close()
         res[key] = {"kv_tokens": int(lens.sum()), "per_row_ms": round(ms["per_row"], 5),
                        "balanced_ms": round(ms["balanced"], 5),
                        "per_row_over_balanced": round(ms["per_row"] / ms["balanced"], 4),
@@ -356,41 +431,99 @@ def invariance_pass_rate(case, out_bits, lse_bits, mode, synth, DeviceCase, rows
     return ok
 
 
-def cpu_baseline(case, seconds):
-    """The fp64 oracle on the host cores over a bounded sample of rows."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(case, seconds, gpu_out=None, gpu_lse=None):
+    """The fp64 oracle on the host cores over a bounded sample of rows: most
+    of `seconds` with the BLAS pool as configured, a quarter more with one
+    thread.  With the GPU's output of the batch, the sampled rows also give
+    the parity statistics of the timed configuration against the oracle."""
     import numpy as np
     import oracle
     from workloads import synth
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     q = synth.bf16_value(case.q_bits())
     lat = [synth.bf16_value(r.latent) for r in case.rows]
-    done_tokens, rows, passes = 0, 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:   # whole passes over the batch, row by row
-        for b in range(case.batch):
-            oracle.mla_decode(q[b:b + 1], [lat[b]], case.scale)
-            done_tokens += int(case.lens[b])
-            rows += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        passes += 1
-    dt = time.perf_counter() - t0
-    gbs = done_tokens * synth.MLA_DQK * 2 / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows} rows ({done_tokens} KV tokens; {passes} pass(es) over the 64-row batch) of the "
-                      f"same workload, fp64 numpy oracle, {dt:.1f} s wall"}
+    refs = {}
+
+    def run(budget, keep):
+        done_tokens, rows, passes = 0, 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget:   # whole passes over the batch, row by row
+            for b in range(case.batch):
+                ro, rl = oracle.mla_decode(q[b:b + 1], [lat[b]], case.scale)
+                if keep and b not in refs:
+                    refs[b] = (ro[0], rl[0])
+                done_tokens += int(case.lens[b])
+                rows += 1
+                if time.perf_counter() - t0 >= budget:
+                    break
+            passes += 1
+        return done_tokens, rows, passes, time.perf_counter() - t0
+
+    tokens, rows, passes, dt = run(seconds, True)
+    gbs = tokens * synth.MLA_DQK * 2 / dt / 1e9
+    res = {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{rows} rows ({tokens} KV tokens; {passes} pass(es) over the 64-row batch) of the "
+                     f"same workload, fp64 numpy oracle, {dt:.1f} s wall",
+           "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            t1, r1, _, d1 = run(seconds / 4, False)
+        res["single_thread"] = {"value": round(t1 * synth.MLA_DQK * 2 / d1 / 1e9, 4), "unit": "GB/s",
+                                "sample": f"{r1} rows ({t1} KV tokens), {d1:.1f} s wall, 1 BLAS thread"}
+    if gpu_out is not None and refs:
+        def ordered(bits):   # bf16 bit patterns -> integers in value order
+            bits = bits.astype(np.int32)
+            return np.where(bits & 0x8000, -(bits & 0x7fff), bits & 0x7fff)
+
+        def to_bf16_bits(x):   # float64 -> bf16 bits, round to nearest even (via fp32)
+            u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+            u = (u + 0x7fff + ((u >> 16) & 1)) >> 16
+            return u.astype(np.int32) & 0xffff
+
+        errs, over, lerr, n = [], [], [], 0
+        hist = np.zeros(4, np.int64)   # ulp distance 0, 1, 2, > 2
+        for b, (ro, rl) in refs.items():
+            e = np.abs(gpu_out[b] - ro)
+            ax = np.maximum(np.abs(ro), 2.0 ** -126)
+            bar = np.maximum(2e-3, 2.0 ** (np.floor(np.log2(ax)) - 7))
+            errs.append(e.max())
+            over.append((e / bar).max())
+            d = np.abs(ordered(to_bf16_bits(gpu_out[b])) - ordered(to_bf16_bits(ro)))
+            hist += np.bincount(np.minimum(d, 3).ravel(), minlength=4)[:4]
+            lerr.append(np.max(np.abs(np.where(np.isneginf(rl), 0, gpu_lse[b] - rl))))
+            n += e.size
+        res["parity"] = {"rows": len(refs), "elements": int(n), "max_abs": float(max(errs)),
+                         "max_err_over_bar": round(float(max(over)), 4), "lse_max_abs": float(max(lerr)),
+                         "bf16_ulp_distance_to_rounded_oracle": {"0": int(hist[0]), "1": int(hist[1]), "2": int(hist[2]),
+                                                                 ">2": int(hist[3])},
+                         "bar": "|gpu - oracle| <= max(2e-3, 1 bf16 ulp of the oracle value); lse 1e-3"}
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # The shader clock takes on the order of a hundred steps to settle.
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    # The shader clock of a cold part takes some tens of milliseconds of this
+    # load to settle; that phase runs before the warm-up and is reported as
+    # its own field (clock_settle), never counted in warmup.
+    ap.add_argument("--settle-ms", type=float, default=60.0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -440,6 +573,8 @@ def main():
     q_bytes = case.batch * case.hq * synth.MLA_DQK * 2
     evs = HipEvents()
 
+    log(f"clock settle: {args.settle_ms:.0f} ms of untimed steps")
+    settle = clock_settle(dc, torch, lens_host, args.settle_ms)
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps (mode {args.mode})")
     total_ms, wall, _, _ = timed_steps(dc, isk, torch, evs, args.steps, args.warmup, lens_host, False)
     log(f"kernel durations: {args.steps} more steps with kernel-bound HIP events")
@@ -483,7 +618,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
-            "kernel": "mla_split_h32_kernel<dense>",
+            "kernel": SPLIT_KERNEL_NAME,
             "algorithmic_bytes_per_launch": kvb + q_bytes,
             "avg_launch_ms": round(split_ms, 5),
         },
@@ -495,13 +630,20 @@ def main():
         "host_plan_us": round(float(np.median(plan_us)), 1),
         "mfma_tflops_split": round(float(lens_host.sum()) * case.hq * (576 + 512) * 2 / (split_ms * 1e-3) / 1e12, 1),
         "wall_s_timed_region": round(wall, 4),
+        "clock_settle": settle,
         "ms_per_step_with_kernel_events": round(inst_ms / args.steps, 5),
         "numerics_id": isk.numerics_id(),
     }
 
     if not args.no_extras:
+        log("HBM read peak: streaming-read probe over 2 GiB")
+        peak = hbm_read_peak(isk, torch)
+        res["hbm_read_probe"] = peak
+        res["roofline"]["measured_read_peak_gbs"] = peak["gbs"]
+        res["roofline"]["frac_of_measured_read_peak"] = round(achieved / peak["gbs"], 4)
+        res["pct_measured_read_peak"] = round(100.0 * (kvb + iob) / (ms_step * 1e-3) / 1e9 / peak["gbs"], 2)
         torch.cuda.synchronize()
-        _, _, bits, lbits = dc.result()
+        gpu_out, gpu_lse, bits, lbits = dc.result()
         log("invariance: every row re-run alone vs batched")
         ok = invariance_pass_rate(case, bits, lbits, mode, synth, DeviceCase, range(case.batch))
         res["invariance"] = {"pass": ok, "total": case.batch, "rate": round(ok / case.batch, 4),
@@ -511,15 +653,26 @@ def main():
         res["cold_ms_per_call"] = round(float(np.median(cold)), 5)
         res["cold_kv_gbs"] = round(kvb / (np.median(cold) * 1e-3) / 1e9, 2)
         if mode == isk.SPLIT_PER_ROW:
-            log("batch-balanced comparison mode on the same batch")
+            log("batch-balanced comparison mode on the same batch, interleaved with per-row steps")
             dcb = DeviceCase(case, split_mode=isk.SPLIT_BATCH_BALANCED, pool=dc.pool)
-            tb, _, _, _ = timed_steps(dcb, isk, torch, evs, args.steps, args.warmup, lens_host, False)
+            stream = torch.cuda.current_stream()
+
+            def step_of(d):
+                def step():
+                    d.plan.update(lens_host)
+                    d.run(stream)
+                return step
+
+            il = interleaved_ms(torch, {"per_row": step_of(dc), "balanced": step_of(dcb)}, rounds=10, calls=20)
             _, _, sb, _ = timed_steps(dcb, isk, torch, evs, args.steps, 0, lens_host, True)
             _, _, bb, bl = dcb.result()
             okb = invariance_pass_rate(case, bb, bl, isk.SPLIT_BATCH_BALANCED, synth, DeviceCase,
                                        range(0, case.batch, 4))
-            res["balanced"] = {"ms_per_step": round(tb / args.steps, 5), "split_ms": round(float(np.mean(sb)), 5),
-                               "per_row_over_balanced": round(ms_step / (tb / args.steps), 4),
+            res["balanced"] = {"per_row_ms_per_step": round(il["per_row"], 5),
+                               "balanced_ms_per_step": round(il["balanced"], 5),
+                               "per_row_over_balanced": round(il["per_row"] / il["balanced"], 4),
+                               "timing": "interleaved: 10 rounds of 20 steps of each, order alternating",
+                               "balanced_split_ms": round(float(np.mean(sb)), 5),
                                "invariance_pass": okb, "invariance_total": len(range(0, case.batch, 4))}
             dcb.close()
             log("per-row (plain and two band tables) vs balanced: stress batches B=1..128, lognormal B=16, 128")
@@ -534,7 +687,9 @@ def main():
         res["sparse"] = sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes)
         if not args.no_cpu_baseline:
             log(f"CPU baseline: fp64 oracle for ~{args.cpu_seconds:.0f} s")
-            res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+            res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, gpu_out, gpu_lse)
+            if "parity" in res["cpu_baseline"]:
+                res["parity"] = res["cpu_baseline"].pop("parity")
     dc.close()
     print(json.dumps(res), flush=True)
 

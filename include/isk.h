@@ -379,6 +379,25 @@ ISK_API int isk_rmsnorm(const void* x, const void* w, void* y, int32_t rows, int
 ISK_API int isk_linear_bf16(const void* x, const void* w, float* y, int32_t m, int32_t n, int32_t k, void* stream);
 
 /*
+ * isk_hbm_read_probe - measurement utility: one streaming read of `bytes`
+ * bytes at `src` (16-byte pieces, grid-stride, nontemporal loads, four in
+ * flight per thread), folded with XOR into one 32-bit word per workgroup at
+ * sink[0 .. blocks).  Timed with HIP events over a buffer larger than the
+ * 256 MB last-level cache, it gives this part's achievable HBM read rate:
+ * the second roofline denominator next to the 8 TB/s published figure (the
+ * FlashMLA issue page "Sparse MLA decode is not batch-invariant ..." quotes
+ * its bandwidth figures against the hardware's memory roofline, section
+ * "Measurement / Environment").
+ *
+ * src    device buffer, 16-byte aligned; bytes a positive multiple of 16.
+ * sink   device array of at least `blocks` uint32 (written).
+ * blocks workgroups of 256 threads, in [1, 65536].
+ * stream hipStream_t (as void*); the call only enqueues the kernel.
+ * Errors: ISK_ERR_INVALID_ARG, ISK_ERR_HIP.
+ */
+ISK_API int isk_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
+
+/*
  * isk_plan_set_timing_events - profiling hook.  Subsequent isk_attn_decode
  * calls with this plan launch the split kernel through hipExtLaunchKernel
  * with `split_begin` and `split_end` as its start and stop events, so they

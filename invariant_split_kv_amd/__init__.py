@@ -22,7 +22,8 @@ __all__ = [
     "SPLIT_BATCH_BALANCED", "OUT_BF16", "OUT_F32", "LIB_PATH", "lib", "plan_create",
     "plan_update", "plan_destroy", "plan_query", "plan_workspace_bytes", "plan_segments",
     "plan_set_timing_events", "plan_create_extra",
-    "attn_decode", "attn_decode_extra", "attn_decode_oneshot", "rmsnorm", "linear_bf16", "last_error", "numerics_id", "Plan",
+    "attn_decode", "attn_decode_extra", "attn_decode_oneshot", "rmsnorm", "linear_bf16", "hbm_read_probe",
+    "last_error", "numerics_id", "Plan",
 ]
 
 KIND_GQA, KIND_MLA = 0, 1
@@ -102,6 +103,7 @@ def _load() -> ctypes.CDLL:
                                                   ctypes.c_size_t, P]),
         "isk_rmsnorm": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P]),
         "isk_linear_bf16": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]),
+        "isk_hbm_read_probe": (ctypes.c_int, [P, ctypes.c_size_t, P, ctypes.c_int32, P]),
         "isk_last_error": (ctypes.c_char_p, []),
         "isk_numerics_id": (ctypes.c_char_p, []),
     }
@@ -285,6 +287,16 @@ def linear_bf16(x, w, y, m: int, n: int, k: int, stream=None) -> None:
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
     _check(lib.isk_linear_bf16(_ptr(x), _ptr(w), _ptr(y), int(m), int(n), int(k), stream))
+
+
+def hbm_read_probe(src, nbytes: int, sink, blocks: int, stream=None) -> None:
+    """Enqueue isk_hbm_read_probe: one streaming read of nbytes at src."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(lib.isk_hbm_read_probe(_ptr(src), int(nbytes), _ptr(sink), int(blocks), stream))
 
 
 class Plan:

@@ -576,6 +576,16 @@ int isk_rmsnorm(const void* x, const void* w, void* y, int32_t rows, int32_t dim
   return ISK_OK;
 }
 
+int isk_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream) {
+  if (src == nullptr || sink == nullptr) return set_err(ISK_ERR_INVALID_ARG, "src and sink must be non-NULL");
+  if (bytes == 0 || bytes % 16 != 0 || (uintptr_t)src % 16 != 0)
+    return set_err(ISK_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and src 16-byte aligned");
+  if (blocks < 1 || blocks > 65536) return set_err(ISK_ERR_INVALID_ARG, "blocks must be in [1, 65536]");
+  const hipError_t e = isk::launch_hbm_read(src, bytes, sink, blocks, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_err(e, "launching the HBM read probe");
+  return ISK_OK;
+}
+
 int isk_linear_bf16(const void* x, const void* w, float* y, int32_t m, int32_t n, int32_t k, void* stream) {
   if (m < 0) return set_err(ISK_ERR_INVALID_ARG, "m must be >= 0");
   if (n <= 0 || n % 16 != 0) return set_err(ISK_ERR_UNSUPPORTED, "n must be a positive multiple of 16");

@@ -182,6 +182,9 @@ struct RmsNormLaunch {
 };
 hipError_t launch_rmsnorm(const RmsNormLaunch& a, hipStream_t s);
 
+// Streaming-read microbenchmark (isk_hbm_read_probe).
+hipError_t launch_hbm_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
+
 // Batch-invariant linear layer: tile shape chosen by row count, same bits.
 constexpr int kLinearSmallRows = 32;    // up to here: 16-row tiles
 constexpr int kLinearTiledRows = 256;   // up to here: 64-row tiles; above: 128 x 128 LDS tiles

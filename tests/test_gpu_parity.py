@@ -386,3 +386,19 @@ def test_timing_hook_launch_gives_the_same_bits(which):
         rt.hipEventDestroy(e)
     dc.close()
     assert np.array_equal(bits0, bits1) and np.array_equal(lbits0, lbits1)
+
+
+@pytest.mark.parametrize("nbytes,blocks", [(1 << 20, 64), ((1 << 24) + 48, 1000), (4096 * 16, 4096)])
+def test_hbm_read_probe_reads_every_word_once(nbytes, blocks):
+    """The streaming-read probe behind the measured HBM read peak folds every
+    32-bit word of its buffer into the per-workgroup XOR words exactly once
+    (a word read twice, or not at all, changes the fold)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(nbytes)
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, device="cuda", dtype=torch.int32)
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    isk.hbm_read_probe(buf, nbytes, sink, blocks)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
