@@ -61,7 +61,8 @@ typedef enum isk_status {
   ISK_ERR_UNSUPPORTED = -2,   /* valid request this build has no kernel for      */
   ISK_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required      */
   ISK_ERR_INDEX = -4,         /* check_inputs found a table/index entry invalid   */
-  ISK_ERR_HIP = -5            /* a HIP runtime call failed (message has detail)  */
+  ISK_ERR_HIP = -5,           /* a HIP runtime call failed (message has detail)  */
+  ISK_ERR_RANGE = -6          /* check_inputs found a value the kernel cannot take */
 } isk_status;
 
 typedef enum isk_kind { ISK_KIND_GQA = 0, ISK_KIND_MLA = 1 } isk_kind;
@@ -210,11 +211,9 @@ ISK_API int isk_plan_segments(const isk_plan* plan, int32_t* records_out, int32_
  * plan        from isk_plan_create/update; not modified.
  * q           [B, Hq, head_dim_qk] bf16.
  * kv_pages    GQA: [num_pages, 2, Hkv, page_size, head_dim] bf16 (index 0 = K,
- *             1 = V).  MLA: [num_pages, page_size, 576] bf16.  With Hq a
- *             multiple of 128 the MLA kernel multiplies P by V in fp16: the
- *             first 512 latent values (V) are exact there when their magnitude
- *             lies in [2^-14, 65504]; larger ones are clamped to 65504 and
- *             smaller ones rounded toward zero to fp16 subnormals.
+ *             1 = V).  MLA: [num_pages, page_size, 576] bf16; with Hq a
+ *             multiple of 128 the V part enters the PV product as fp16 (see
+ *             "Value range" below).
  * block_table [B, max_pages_per_row] int32; entry j of row b is the page
  *             holding the row's tokens [j*page_size, (j+1)*page_size).
  * lens        [B] int32 device copy of lens_host.
@@ -228,7 +227,8 @@ ISK_API int isk_plan_segments(const isk_plan* plan, int32_t* records_out, int32_
  * lse         [B, Hq] fp32 natural-log LSE of the scaled scores (-inf for
  *             rows with nothing to attend).  May be NULL.
  * workspace   device memory of at least isk_plan_workspace_bytes(plan) bytes,
- *             256-byte aligned; holds the fp32 partials and the uploaded
+ *             256-byte aligned; holds the split partials (fp32, or fp16 on
+ *             the 128-head MLA path with bf16 output) and the uploaded
  *             split list (a dense per-row plan of at most 640 splits and 128
  *             rows goes to the kernels in their arguments instead, with no
  *             upload).  Must not be shared by calls in flight at the same time.
@@ -237,8 +237,19 @@ ISK_API int isk_plan_segments(const isk_plan* plan, int32_t* records_out, int32_
  * Out-of-range block-table entries and top-k positions are masked in the
  * kernels (never dereferenced); with desc.check_inputs = 1 they are instead
  * reported as ISK_ERR_INDEX before any kernel runs (this synchronises the
- * stream and copies the tables to the host).  Errors: ISK_ERR_INVALID_ARG,
- * ISK_ERR_WORKSPACE, ISK_ERR_INDEX, ISK_ERR_HIP.
+ * stream and copies the tables to the host).
+ *
+ * Value range: with Hq a multiple of 128 the MLA kernels take V (the first
+ * 512 latent dims of the attended rows) into their PV product as fp16.
+ * Every bf16 value of magnitude in [2^-14, 65280] converts exactly; smaller
+ * ones become fp16 subnormals (rounded toward zero, absolute error below
+ * 2^-24); 65536 and above, infinities and NaN do not fit (a finite one is
+ * taken as 65504).  The 16-head path (other head counts) and GQA take any
+ * finite bf16 value.  With desc.check_inputs = 1 on the 128-head path, an
+ * attended V value of magnitude 65536 or more (or not finite) is reported
+ * as ISK_ERR_RANGE, naming its row, position and dim, before any attention
+ * kernel runs.  Errors: ISK_ERR_INVALID_ARG, ISK_ERR_WORKSPACE,
+ * ISK_ERR_INDEX, ISK_ERR_RANGE, ISK_ERR_HIP.
  */
 ISK_API int isk_attn_decode(const isk_plan* plan, const void* q, const void* kv_pages,
                     const int32_t* block_table, const int32_t* lens,

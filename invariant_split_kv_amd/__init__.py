@@ -30,7 +30,8 @@ KIND_GQA, KIND_MLA = 0, 1
 SPLIT_PER_ROW, SPLIT_BATCH_BALANCED = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 STATUS_NAMES = {0: "ISK_OK", -1: "ISK_ERR_INVALID_ARG", -2: "ISK_ERR_UNSUPPORTED",
-                -3: "ISK_ERR_WORKSPACE", -4: "ISK_ERR_INDEX", -5: "ISK_ERR_HIP"}
+                -3: "ISK_ERR_WORKSPACE", -4: "ISK_ERR_INDEX", -5: "ISK_ERR_HIP",
+                -6: "ISK_ERR_RANGE"}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libisk.so")
 

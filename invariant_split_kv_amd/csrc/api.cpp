@@ -114,6 +114,42 @@ void release_staging(isk_plan* p) {
 // device tables to the host (synchronising the stream).
 int audit_extra(const isk_plan* p, const isk_extra_kv& x, hipStream_t stream);
 
+// The value-range audit (128-head MLA): V of every attended row must fit the
+// fp16 PV operand.  `found` is four ints of device workspace.
+int audit_v_range(const isk_plan* p, const void* kv_pages, const int32_t* block_table, const int32_t* lens,
+                  const int32_t* topk_idx, const int32_t* topk_len, const isk_extra_kv* extra, int32_t* found,
+                  hipStream_t stream) {
+  const isk_desc& d = p->data.desc;
+  int32_t h[4] = {0, 0, 0, 0};
+  for (int set = 0; set < (extra != nullptr ? 2 : 1); ++set) {
+    const bool x = set == 1;
+    isk::VRangeAudit a{};
+    a.kv = (const uint16_t*)(x ? extra->kv_pages : kv_pages);
+    a.block_table = x ? extra->block_table : block_table;
+    a.lens = x ? extra->lens : lens;
+    a.topk_idx = x ? extra->topk_idx : (d.topk_width > 0 ? topk_idx : nullptr);
+    a.topk_len = x ? extra->topk_len : topk_len;
+    a.batch = p->data.batch;
+    a.max_pages = x ? p->data.extra.max_pages_per_row : d.max_pages_per_row;
+    a.page_size = x ? p->data.extra.page_size : d.page_size;
+    a.num_pages = x ? p->data.extra.num_pages : d.num_pages;
+    a.topk_width = x ? p->data.extra.topk_width : d.topk_width;
+    a.found = found;
+    hipError_t e = hipMemsetAsync(found, 0, 4 * sizeof(int32_t), stream);
+    if (e == hipSuccess) e = isk::launch_v_range_audit(a, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(h, found, sizeof(h), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_err(e, "check_inputs: value-range audit");
+    if (h[0] != 0) {
+      std::ostringstream s;
+      s << "check_inputs: " << (x ? "extra " : "") << "row " << h[1] << " position " << h[2] << " has V[" << h[3]
+        << "] of magnitude 65536 or more (or not finite), outside the fp16 PV operand of the 128-head MLA kernels";
+      return set_err(ISK_ERR_RANGE, s.str());
+    }
+  }
+  return ISK_OK;
+}
+
 int audit_inputs(const isk_plan* p, const int32_t* block_table, const int32_t* lens, const int32_t* topk_idx,
                  const int32_t* topk_len, const isk_extra_kv* extra, hipStream_t stream) {
   const isk_desc& d = p->data.desc;
@@ -411,7 +447,10 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
   if (((uintptr_t)workspace & 255u) != 0) return set_err(ISK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
   if (d.check_inputs) {
-    const int rc = audit_inputs(plan, block_table, lens, topk_idx, topk_len, extra, stream);
+    int rc = audit_inputs(plan, block_table, lens, topk_idx, topk_len, extra, stream);
+    if (rc == ISK_OK && d.kind == ISK_KIND_MLA && d.num_q_heads % 128 == 0)
+      rc = audit_v_range(plan, kv_pages, block_table, lens, topk_idx, topk_len, extra,
+                         (int32_t*)((unsigned char*)workspace + plan->layout.audit_off), stream);
     if (rc != ISK_OK) return rc;
   }
 

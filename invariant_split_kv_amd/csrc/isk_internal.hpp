@@ -95,7 +95,7 @@ constexpr int kMaxBands = 16;
 // Byte layout of the per-call metadata at the head of the workspace.
 struct MetaLayout {
   size_t segs_off, groups_off, rows_off, bytes;        // meta block
-  size_t part_o_off, part_lse_off, total;               // whole workspace
+  size_t part_o_off, part_lse_off, audit_off, total;    // whole workspace
 };
 MetaLayout meta_layout(const PlanData& p);
 
@@ -181,6 +181,17 @@ struct RmsNormLaunch {
   float eps;
 };
 hipError_t launch_rmsnorm(const RmsNormLaunch& a, hipStream_t s);
+
+// Value-range audit of the latent cache for the 128-head MLA kernels
+// (check_inputs): found[0] becomes 1 and found[1..3] = (row, position, dim)
+// of one V value of magnitude >= 65536 (or not finite).
+struct VRangeAudit {
+  const uint16_t* kv; const int32_t* block_table; const int32_t* lens;
+  const int32_t* topk_idx; const int32_t* topk_len;   // topk_idx NULL: dense rows
+  int32_t batch, max_pages, page_size, num_pages, topk_width;
+  int32_t* found;
+};
+hipError_t launch_v_range_audit(const VRangeAudit& a, hipStream_t s);
 
 // Streaming-read microbenchmark (isk_hbm_read_probe).
 hipError_t launch_hbm_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);

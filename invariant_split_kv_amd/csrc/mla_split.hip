@@ -231,7 +231,7 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
                                      min(a.xlens[b], a.xmax_pages * a.xpage_size), sg.begin, sg.end}
                    : Stager<kSparse>{kv, a.block_table + (size_t)b * a.max_pages,
                                      kSparse ? a.topk_idx + (size_t)b * a.topk_width : nullptr, a.page_size,
-                                     a.num_pages, a.lens[b], sg.begin, sg.end};
+                                     a.num_pages, min(a.lens[b], a.max_pages * a.page_size), sg.begin, sg.end};
 
     __syncthreads();   // every wave is done with the LDS tiles of the previous segment
 

@@ -678,7 +678,7 @@ mla_split_h32_kernel(MlaLaunch a) {
                                      min(a.xlens[b], a.xmax_pages * a.xpage_size), sg.end}
                    : Stager<kSparse>{(const unsigned char*)a.kv, a.block_table + (size_t)b * a.max_pages,
                                      kSparse ? a.topk_idx + (size_t)b * a.topk_width : nullptr, a.page_size,
-                                     a.num_pages, a.lens[b], sg.end};
+                                     a.num_pages, __builtin_amdgcn_readfirstlane(min(a.lens[b], a.max_pages * a.page_size)), sg.end};
 
     // Every wave is done reading the previous segment's tiles.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

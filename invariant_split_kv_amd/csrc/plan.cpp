@@ -53,7 +53,8 @@ MetaLayout meta_layout(const PlanData& p) {
   const int dv = p.desc.head_dim_v;
   m.part_o_off = m.bytes;
   m.part_lse_off = align256(m.part_o_off + (size_t)p.n_partials * p.desc.num_q_heads * dv * sizeof(float));
-  m.total = align256(m.part_lse_off + (size_t)p.n_partials * p.desc.num_q_heads * sizeof(float));
+  m.audit_off = align256(m.part_lse_off + (size_t)p.n_partials * p.desc.num_q_heads * sizeof(float));
+  m.total = m.audit_off + 256;   // four ints of the value-range audit (check_inputs)
   return m;
 }
 
@@ -72,6 +73,9 @@ static std::string check_desc(const isk_desc& d, int* status) {
   if (!std::isfinite(d.scale) || !(d.scale > 0.f))
     return fail(status, ISK_ERR_INVALID_ARG, "desc.scale must be finite and positive");
   if (d.topk_width < 0) return fail(status, ISK_ERR_INVALID_ARG, "desc.topk_width must be >= 0");
+  // Row lengths and token positions are 32-bit in the kernels.
+  if ((long long)d.max_pages_per_row * d.page_size > 0x7fffffffLL)
+    return fail(status, ISK_ERR_UNSUPPORTED, "max_pages_per_row * page_size must fit in int32");
   if (d.kind == ISK_KIND_GQA) {
     if (d.num_q_heads % d.num_kv_heads != 0) return fail(status, ISK_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
     const int g = d.num_q_heads / d.num_kv_heads;

@@ -61,6 +61,7 @@ def test_invalid_arguments_are_rejected_with_status_and_message():
         (mla_desc(num_q_heads=96), [5], -2, "multiple of 16"),
         (mla_desc(page_size=16), [5], -2, "page_size"),
         (mla_desc(num_pages=2 ** 25), [5], -2, "2^31"),            # 2^25 pages x 64 rows = 2^31 rows
+        (mla_desc(max_pages_per_row=2 ** 25), [5], -2, "int32"),   # a row table of 2^31 token positions
         (gqa_desc(topk_width=16), [5], -2, "MLA only"),
         (gqa_desc(scale=float("nan")), [5], -1, "finite"),
         (gqa_desc(scale=0.0), [5], -1, "positive"),

@@ -169,6 +169,26 @@ def test_sparse_edges():
     assert np.all(out[5] == 0) and np.all(np.isneginf(lse[5]))
 
 
+@pytest.mark.parametrize("hq", [128, 64])
+def test_sparse_device_length_beyond_the_table_is_clamped(hq):
+    """A device length above max_pages_per_row * page_size (the plan saw the
+    true length; inputs are not audited) does not let a top-k position past
+    the row's block table through: such positions are masked like positions
+    past the length.  (The positions used stay below twice the cap, so even
+    an unclamped read would stay inside the block-table allocation.)"""
+    case = synth.mla_case([600, 300], hq, 0.1, 64, structure_seed=67, topk_width=256)
+    cap = case.paging.max_pages_per_row * 64
+    assert cap == 640
+    case.rows[0].topk_idx[[2, 50, 100]] = [700, cap, 2 * cap - 1]   # past the table (and the length)
+    dc = DeviceCase(case, fill=GARBAGE)
+    dc.lens[0] = 2 * cap - 40                                        # device length past the table
+    dc.run()
+    out, lse, _, _ = dc.result()
+    dc.close()
+    ro, rl = reference(case)
+    parity(out, lse, ro, rl, False, f"sparse device length past the table hq={hq}")
+
+
 def test_all_masked_sparse_row_gives_zero_and_neg_inf():
     case = synth.mla_case([100, 50], 64, 0.1, 64, structure_seed=62, topk_width=128)
     case.rows[0].topk_idx[:] = -1
