@@ -124,9 +124,14 @@ typedef struct isk_plan_info {
  * plan_out       receives the new plan.
  *
  * Per-row mode implements the per-row split rule requested in the FlashMLA
- * issue page, section "Question".  Pure host work: no HIP call is made, so it
- * may run on a machine without a GPU.  Errors: ISK_ERR_INVALID_ARG,
- * ISK_ERR_UNSUPPORTED (no kernel for the shape).
+ * issue page, section "Question".  The planning is host work.  A plan whose
+ * split list is uploaded to the device (sparse, extra source, balanced mode,
+ * or more than 640 splits or 128 rows) also gets its pinned staging ring
+ * here: four host buffers of the split-list size with half again of
+ * headroom, and four events, so that isk_attn_decode allocates nothing.  On
+ * a machine without a usable GPU the plan is still made (for host-side use:
+ * query, segments) but cannot be decoded with (ISK_ERR_HIP).  Errors:
+ * ISK_ERR_INVALID_ARG, ISK_ERR_UNSUPPORTED (no kernel for the shape).
  */
 ISK_API int isk_plan_create(const isk_desc* desc, int32_t batch, const int32_t* lens_host,
                     const int32_t* topk_len_host, isk_plan** plan_out);
@@ -175,9 +180,11 @@ ISK_API int isk_plan_create_banded(const isk_desc* desc, const isk_split_band* b
 /*
  * isk_plan_update - re-plan an existing plan in place for new lengths (the
  * next decode step), keeping its descriptor, its band table (if any) and its
- * pinned staging buffers.  Host only.  Same arguments and errors as
- * isk_plan_create.  Decode calls already enqueued keep the split list they
- * uploaded.
+ * pinned staging ring.  When the new split list outgrows the ring's buffers
+ * they are re-allocated here (each after its last upload has executed);
+ * otherwise no allocation.  Same arguments and errors as isk_plan_create.
+ * Decode calls already enqueued keep the split list they uploaded.  Must not
+ * run while another thread decodes with the same plan.
  */
 ISK_API int isk_plan_update(isk_plan* plan, int32_t batch, const int32_t* lens_host,
                     const int32_t* topk_len_host);
@@ -208,7 +215,11 @@ ISK_API int isk_plan_segments(const isk_plan* plan, int32_t* records_out, int32_
 /*
  * isk_attn_decode - run split kernels and the fixed-order combine.
  *
- * plan        from isk_plan_create/update; not modified.
+ * plan        from isk_plan_create/update.  Its split list is not changed;
+ *             an uploaded one goes through the plan's staging ring, whose
+ *             slot cursor a lock guards, so threads may decode with one
+ *             plan at the same time (each with its own workspace).  The
+ *             call allocates no memory and creates no HIP object.
  * q           [B, Hq, head_dim_qk] bf16.
  * kv_pages    GQA: [num_pages, 2, Hkv, page_size, head_dim] bf16 (index 0 = K,
  *             1 = V).  MLA: [num_pages, page_size, 576] bf16; with Hq a

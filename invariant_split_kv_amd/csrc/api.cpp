@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <sstream>
 #include <string>
@@ -41,10 +42,15 @@ struct isk_plan {
   PlanData data;
   MetaLayout layout{};
   std::vector<unsigned char> meta_host;   // serialised metadata
+  // Staging ring of an uploaded plan, sized at plan time (prepare_staging):
+  // isk_attn_decode itself allocates nothing.  ring_mu serialises decode
+  // calls of several threads on the slot cursor and the slots.
   void* staging[kRing] = {};
   size_t staging_bytes[kRing] = {};
   hipEvent_t staged[kRing] = {};
   int ring_next = 0;
+  hipError_t staging_error = hipSuccess;  // why the ring could not be prepared
+  std::mutex ring_mu;
   hipEvent_t t_split_begin = nullptr, t_split_end = nullptr, t_combine_end = nullptr;   // profiling hook
   isk::InlinePlan inl{};                  // n_segs > 0: passed by value, no upload
 };
@@ -93,6 +99,45 @@ void serialise(isk_plan* p) {
   std::memcpy(p->meta_host.data() + p->layout.segs_off, p->data.segs.data(), p->data.segs.size() * sizeof(isk::Seg));
   std::memcpy(p->meta_host.data() + p->layout.groups_off, p->data.groups.data(), p->data.groups.size() * sizeof(int32_t));
   std::memcpy(p->meta_host.data() + p->layout.rows_off, p->data.rows.data(), p->data.rows.size() * sizeof(isk::RowInfo));
+}
+
+// The pinned staging ring of a plan whose metadata is uploaded (not passed
+// by value) is created and sized here, at plan time, so that the decode path
+// allocates nothing: kRing slots of at least the metadata size (with half
+// again of headroom, so that a growing batch re-allocates rarely) and one
+// event each.  A slot is only freed after its last upload has completed.
+// Without a usable GPU the ring stays unprepared and staging_error says why;
+// a decode of such a plan then fails with ISK_ERR_HIP.
+void prepare_staging(isk_plan* p) {
+  p->staging_error = hipSuccess;
+  if (p->inl.n_segs > 0) return;
+  const size_t need = std::max<size_t>(p->layout.bytes, 256);
+  for (int i = 0; i < kRing; ++i) {
+    if (p->staged[i] == nullptr) {
+      const hipError_t e = hipEventCreateWithFlags(&p->staged[i], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        p->staged[i] = nullptr;
+        p->staging_error = e;
+        return;
+      }
+    }
+    if (p->staging_bytes[i] < need) {
+      if (p->staging[i] != nullptr) {
+        (void)hipEventSynchronize(p->staged[i]);
+        (void)hipHostFree(p->staging[i]);
+      }
+      p->staging[i] = nullptr;
+      p->staging_bytes[i] = 0;
+      const size_t cap = need + need / 2;
+      const hipError_t e = hipHostMalloc(&p->staging[i], cap, hipHostMallocDefault);
+      if (e != hipSuccess) {
+        p->staging[i] = nullptr;
+        p->staging_error = e;
+        return;
+      }
+      p->staging_bytes[i] = cap;
+    }
+  }
 }
 
 void release_staging(isk_plan* p) {
@@ -300,6 +345,7 @@ int isk_plan_create(const isk_desc* desc, int32_t batch, const int32_t* lens_hos
     return set_err(status, msg);
   }
   serialise(p);
+  prepare_staging(p);
   *plan_out = p;
   return ISK_OK;
 }
@@ -319,6 +365,7 @@ int isk_plan_create_extra(const isk_desc* desc, const isk_extra_desc* extra, int
     return set_err(status, msg);
   }
   serialise(p);
+  prepare_staging(p);
   *plan_out = p;
   return ISK_OK;
 }
@@ -338,6 +385,7 @@ int isk_plan_create_banded(const isk_desc* desc, const isk_split_band* bands, in
     return set_err(status, msg);
   }
   serialise(p);
+  prepare_staging(p);
   *plan_out = p;
   return ISK_OK;
 }
@@ -354,6 +402,7 @@ int isk_plan_update(isk_plan* plan, int32_t batch, const int32_t* lens_host, con
   if (status != ISK_OK) return set_err(status, msg);
   plan->data = std::move(fresh);
   serialise(plan);
+  prepare_staging(plan);
   return ISK_OK;
 }
 
@@ -418,7 +467,7 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
                        const isk_extra_kv* extra, void* out, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream_v) {
   if (plan_c == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
-  isk_plan* plan = const_cast<isk_plan*>(plan_c);   // staging ring only; the plan itself is not changed
+  isk_plan* plan = const_cast<isk_plan*>(plan_c);   // staging ring only (under ring_mu); the plan itself is not changed
   const PlanData& pd = plan->data;
   const isk_desc& d = pd.desc;
   const bool sparse = d.topk_width > 0;
@@ -460,24 +509,15 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
   const bool by_value = plan->inl.n_segs > 0;
   unsigned char* ws = (unsigned char*)workspace;
   if (!by_value) {
+    std::lock_guard<std::mutex> lock(plan->ring_mu);
     const int slot = plan->ring_next;
-    plan->ring_next = (slot + 1) % kRing;
-    if (plan->staged[slot] != nullptr) {
-      e = hipEventSynchronize(plan->staged[slot]);
-      if (e != hipSuccess) return hip_err(e, "waiting for an earlier metadata upload");
-    } else {
-      e = hipEventCreateWithFlags(&plan->staged[slot], hipEventDisableTiming);
-      if (e != hipSuccess) return hip_err(e, "hipEventCreate");
-    }
     const size_t mbytes = plan->layout.bytes;
-    if (plan->staging_bytes[slot] < mbytes) {
-      if (plan->staging[slot] != nullptr) (void)hipHostFree(plan->staging[slot]);
-      plan->staging[slot] = nullptr;
-      plan->staging_bytes[slot] = 0;
-      e = hipHostMalloc(&plan->staging[slot], mbytes, hipHostMallocDefault);
-      if (e != hipSuccess) return hip_err(e, "hipHostMalloc (metadata staging)");
-      plan->staging_bytes[slot] = mbytes;
-    }
+    if (plan->staged[slot] == nullptr || plan->staging_bytes[slot] < mbytes)
+      return hip_err(plan->staging_error != hipSuccess ? plan->staging_error : hipErrorNotInitialized,
+                     "the plan's metadata staging (prepared when the plan was made) is missing");
+    plan->ring_next = (slot + 1) % kRing;
+    e = hipEventSynchronize(plan->staged[slot]);
+    if (e != hipSuccess) return hip_err(e, "waiting for an earlier metadata upload");
     std::memcpy(plan->staging[slot], plan->meta_host.data(), mbytes);
     e = hipMemcpyAsync(ws, plan->staging[slot], mbytes, hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (metadata upload)");
