@@ -535,7 +535,7 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
 
   // Partials of the 128-head MLA kernels (fp16 PV operand) are fp16 when the
   // output is bf16; every other kernel, and fp32 output, keeps fp32 partials.
-  const int32_t part_f16 = d.kind != ISK_KIND_GQA && d.num_q_heads % 128 == 0 && d.out_dtype != ISK_OUT_F32;
+  const int32_t part_f16 = isk::partials_fp16(d);
   isk::LaunchEvents ev;
   ev.begin = plan->t_split_begin;
   ev.end = plan->t_split_end;

@@ -24,6 +24,13 @@ constexpr int kMlaSplitDefault = 1536;
 constexpr int kSparseSplitDefault = 512;
 constexpr int kMlaDqk = 576;
 constexpr float kLog2eHost = 1.44269504088896340736f;   // log2(e), rounded to float
+
+// Split partials are fp16 (2 bytes a value) for the 128-head MLA kernels with
+// bf16 output (their PV operand is fp16, so every partial is in fp16 range);
+// fp32 everywhere else.
+inline bool partials_fp16(const isk_desc& d) {
+  return d.kind == ISK_KIND_MLA && d.num_q_heads % 128 == 0 && d.out_dtype != ISK_OUT_F32;
+}
 constexpr int kMlaDv = 512;
 // Batch-balanced comparison mode: block granularity, parts and per-row
 // overhead charge of the batch-wide scheduler it reproduces.

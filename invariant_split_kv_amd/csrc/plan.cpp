@@ -52,7 +52,8 @@ MetaLayout meta_layout(const PlanData& p) {
   m.bytes = align256(m.rows_off + p.rows.size() * sizeof(RowInfo));
   const int dv = p.desc.head_dim_v;
   m.part_o_off = m.bytes;
-  m.part_lse_off = align256(m.part_o_off + (size_t)p.n_partials * p.desc.num_q_heads * dv * sizeof(float));
+  const size_t part_elem = partials_fp16(p.desc) ? 2 : sizeof(float);
+  m.part_lse_off = align256(m.part_o_off + (size_t)p.n_partials * p.desc.num_q_heads * dv * part_elem);
   m.audit_off = align256(m.part_lse_off + (size_t)p.n_partials * p.desc.num_q_heads * sizeof(float));
   m.total = m.audit_off + 256;   // four ints of the value-range audit (check_inputs)
   return m;

@@ -192,8 +192,14 @@ def test_workspace_size_covers_partials():
         S = info["split_tokens"]
         expect = sum(-(-L // S) for L in lens if -(-L // S) > 1)   # rows with one split need no partial
         assert info["num_partials"] == expect > 0
-        assert info["workspace_bytes"] >= expect * 128 * (512 + 1) * 4
+        # 128-head MLA with bf16 output: fp16 partials (2 bytes) and fp32 LSEs
+        assert info["workspace_bytes"] >= expect * 128 * (512 * 2 + 4)
         assert p.workspace_bytes == info["workspace_bytes"]
+    with isk.Plan(mla_desc(out_dtype=isk.OUT_F32), lens) as p:   # fp32 output: fp32 partials
+        assert p.info()["workspace_bytes"] >= expect * 128 * (512 + 1) * 4
+    with isk.Plan(mla_desc(num_q_heads=64), lens) as p:           # 16-head kernel: fp32 partials
+        assert p.info()["workspace_bytes"] >= expect * 64 * (512 + 1) * 4
+    with isk.Plan(mla_desc(), lens) as p:
         p.update([100, 100])
         assert p.info()["num_partials"] == 0 and p.info()["batch"] == 2
 
