@@ -358,6 +358,23 @@ ISK_API int isk_attn_decode_extra(const isk_plan* plan, const void* q, const voi
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * isk_attn_decode_static - isk_attn_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * fixed 64 MiB device array inside the library (one per GPU the library
+ * runs on, held until the process ends); the call allocates nothing.  Same
+ * kernels, bits and arguments as isk_attn_decode otherwise (no extra KV
+ * source).  A plan that needs more than 64 MiB of workspace
+ * (isk_plan_workspace_bytes) is rejected with ISK_ERR_WORKSPACE.  Every
+ * call on a GPU uses the same array, which keeps the last call's contents:
+ * calls that overlap on one GPU (other streams, other threads) race.
+ * Errors: those of isk_attn_decode.
+ */
+ISK_API int isk_attn_decode_static(const isk_plan* plan, const void* q, const void* kv_pages,
+                                   const int32_t* block_table, const int32_t* lens, const int32_t* topk_idx,
+                                   const int32_t* topk_len, void* out, float* lse, void* stream);
+
+/*
  * isk_rmsnorm - batch-invariant RMS normalisation of `rows` rows:
  *     y[r, i] = x[r, i] / sqrt(mean_j x[r, j]^2 + eps) * w[i].
  * The inference-research gotcha "batch-invariance-is-not-universal-across-

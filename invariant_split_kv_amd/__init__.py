@@ -22,7 +22,7 @@ __all__ = [
     "SPLIT_BATCH_BALANCED", "OUT_BF16", "OUT_F32", "LIB_PATH", "lib", "plan_create",
     "plan_update", "plan_destroy", "plan_query", "plan_workspace_bytes", "plan_segments",
     "plan_set_timing_events", "plan_create_extra",
-    "attn_decode", "attn_decode_extra", "attn_decode_oneshot", "rmsnorm", "linear_bf16", "hbm_read_probe",
+    "attn_decode", "attn_decode_extra", "attn_decode_oneshot", "attn_decode_static", "rmsnorm", "linear_bf16", "hbm_read_probe",
     "last_error", "numerics_id", "Plan",
 ]
 
@@ -105,6 +105,7 @@ def _load() -> ctypes.CDLL:
         "isk_rmsnorm": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P]),
         "isk_linear_bf16": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]),
         "isk_hbm_read_probe": (ctypes.c_int, [P, ctypes.c_size_t, P, ctypes.c_int32, P]),
+        "isk_attn_decode_static": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P]),
         "isk_last_error": (ctypes.c_char_p, []),
         "isk_numerics_id": (ctypes.c_char_p, []),
     }
@@ -237,6 +238,19 @@ def attn_decode(plan: int, q, kv_pages, block_table, lens, topk_idx, topk_len, o
     _check(lib.isk_attn_decode(plan, _ptr(q), _ptr(kv_pages), _ptr(block_table), _ptr(lens), _ptr(topk_idx),
                                _ptr(topk_len), _ptr(out), _ptr(lse), _ptr(workspace), int(workspace_bytes),
                                stream))
+
+
+def attn_decode_static(plan: int, q, kv_pages, block_table, lens, topk_idx, topk_len, out, lse,
+                       stream=None) -> None:
+    """attn_decode with the library's fixed device workspace (no workspace
+    argument; nothing is allocated)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(lib.isk_attn_decode_static(plan, _ptr(q), _ptr(kv_pages), _ptr(block_table), _ptr(lens), _ptr(topk_idx),
+                                      _ptr(topk_len), _ptr(out), _ptr(lse), stream))
 
 
 def attn_decode_extra(plan: int, q, kv_pages, block_table, lens, topk_idx, topk_len, extra_kv_pages,

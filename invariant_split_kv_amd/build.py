@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libisk.so")
 
 SOURCES = ["plan.cpp", "api.cpp", "gqa_split.hip", "mla_split.hip", "mla_split_h32.hip", "mla_h128.hip", "combine.hip",
-           "rmsnorm.hip", "linear.hip", "hbm_probe.hip", "audit.hip"]
+           "rmsnorm.hip", "linear.hip", "hbm_probe.hip", "audit.hip", "noalloc.hip"]
 GEN_DIR = os.path.join(BUILD_DIR, "gen")
 ARCH = "gfx950"
 # Packed fp32 instructions stay disabled (the compiler would otherwise form

@@ -600,6 +600,23 @@ int isk_attn_decode_extra(const isk_plan* plan, const void* q, const void* kv_pa
                      workspace_bytes, stream);
 }
 
+int isk_attn_decode_static(const isk_plan* plan, const void* q, const void* kv_pages, const int32_t* block_table,
+                           const int32_t* lens, const int32_t* topk_idx, const int32_t* topk_len, void* out,
+                           float* lse, void* stream) {
+  if (plan == nullptr) return set_err(ISK_ERR_INVALID_ARG, "plan is NULL");
+  const size_t cap = isk::static_workspace_bytes();
+  if (plan->layout.total > cap) {
+    std::ostringstream s;
+    s << "the plan needs a workspace of " << plan->layout.total << " bytes; the static workspace holds " << cap
+      << " (use isk_attn_decode with a workspace of its own)";
+    return set_err(ISK_ERR_WORKSPACE, s.str());
+  }
+  void* ws = nullptr;
+  const hipError_t e = isk::static_workspace(&ws);
+  if (e != hipSuccess) return hip_err(e, "hipGetSymbolAddress (static workspace)");
+  return decode_impl(plan, q, kv_pages, block_table, lens, topk_idx, topk_len, nullptr, out, lse, ws, cap, stream);
+}
+
 int isk_attn_decode_oneshot(const isk_desc* desc, int32_t batch, const int32_t* lens_host,
                             const int32_t* topk_len_host, const void* q, const void* kv_pages,
                             const int32_t* block_table, const int32_t* lens, const int32_t* topk_idx,

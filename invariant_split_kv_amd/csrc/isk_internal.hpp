@@ -200,6 +200,10 @@ struct VRangeAudit {
 };
 hipError_t launch_v_range_audit(const VRangeAudit& a, hipStream_t s);
 
+// Fixed device workspace of isk_attn_decode_static (noalloc.hip).
+size_t static_workspace_bytes();
+hipError_t static_workspace(void** ptr);   // device address on the current device
+
 // Streaming-read microbenchmark (isk_hbm_read_probe).
 hipError_t launch_hbm_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
 
