@@ -27,6 +27,7 @@ baseline computed.
 
 import argparse
 import ctypes
+import gc
 import json
 import math
 import os
@@ -162,6 +163,11 @@ def timed_steps(dc, isk, torch, evs, steps, warmup, lens_host, instrument):
         dc.run(stream)
     torch.cuda.synchronize()
     marks = [(evs.create(), evs.create(), evs.create()) for _ in range(steps)] if instrument else None
+    # Python's cyclic collector paused over the timed loop: a full collection
+    # of this process's objects takes tens of milliseconds of host time,
+    # which would show up as idle GPU time inside the region.
+    gc.collect()
+    gc.disable()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -174,6 +180,7 @@ def timed_steps(dc, isk, torch, evs, steps, warmup, lens_host, instrument):
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     total_ms = t_start.elapsed_time(t_end)
     if not instrument:
         return total_ms, wall, None, None
@@ -285,6 +292,59 @@ def cold_steps(dc, torch, n):
     return times
 
 
+def gather_rows(case, np):
+    """Pool rows a sparse case attends, row by row in top-k slot order."""
+    out = []
+    for b, r in enumerate(case.rows):
+        n = min(max(int(r.topk_len), 0), len(r.topk_idx))
+        pos = np.asarray(r.topk_idx[:n])
+        pos = pos[(pos >= 0) & (pos < int(case.lens[b]))]
+        out.append(case.paging.token_slots(b, pos))
+    return np.concatenate(out).astype(np.int32)
+
+
+def gather_ceiling(isk, torch, np, dc, rows, launches=20):
+    """isk_hbm_gather_probe over the rows a sparse batch gathers from its
+    pool (the same bytes as its split kernels' tile loads, in the same 1 KiB
+    pieces): warm (best of four grid sizes, `launches` launches) and cold
+    (1 GiB flush before each launch, median of 15) rates."""
+    stream = torch.cuda.current_stream()
+    rows_d = torch.from_numpy(rows).cuda()
+    row_bytes = 2 * 576
+    src_bytes = dc.pool.numel() * dc.pool.element_size()
+    sink = torch.empty(16384, dtype=torch.int32, device="cuda")
+    nbytes = len(rows) * row_bytes
+    probe = lambda blocks: isk.hbm_gather_probe(dc.pool, src_bytes, rows_d, len(rows), row_bytes, sink, blocks,
+                                                stream)
+    warm = {}
+    for blocks in (512, 1024, 2048, 4096):
+        for _ in range(2):
+            probe(blocks)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(launches):
+            probe(blocks)
+        b.record(stream)
+        torch.cuda.synchronize()
+        warm[blocks] = a.elapsed_time(b) / launches
+    best = min(warm, key=warm.get)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(15):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        probe(best)
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush, rows_d, sink
+    cold_ms = float(np.median(cold))
+    return {"bytes": nbytes, "blocks": best, "warm_ms": round(warm[best], 5),
+            "warm_gbs": round(nbytes / (warm[best] * 1e-3) / 1e9, 1), "cold_ms": round(cold_ms, 5),
+            "cold_gbs": round(nbytes / (cold_ms * 1e-3) / 1e9, 1)}
+
+
 def sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes, calls=100):
     """The config-4 sparse batch (B=64, 2048 top-k positions per row) and the
     same batch with an extra KV source (512 more positions per row from a
@@ -300,18 +360,26 @@ def sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes, calls=100):
         kvb = kv_bytes(case)
         for _ in range(20):
             dc.run(stream)
+        gc.collect()
+        gc.disable()   # no cyclic collection inside the timed calls
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(calls):
             dc.run(stream)
         b.record(stream)
         torch.cuda.synchronize()
+        gc.enable()
         warm = a.elapsed_time(b) / calls
         cold = float(np.median(cold_steps(dc, torch, 30)))
         info = dc.plan.info()
         res[name] = {"gathered_tokens": kvb // (synth.MLA_DQK * 2), "splits": info["num_segments"],
+                     "split_kernel": info["split_kernel"],
                      "warm_ms_per_call": round(warm, 5), "warm_kv_gbs": round(kvb / (warm * 1e-3) / 1e9, 2),
                      "cold_ms_per_call": round(cold, 5), "cold_kv_gbs": round(kvb / (cold * 1e-3) / 1e9, 2)}
+        if getattr(case, "extra", None) is None:
+            g = gather_ceiling(isk, torch, np, dc, gather_rows(case, np))
+            g["cold_call_over_gather"] = round(cold / g["cold_ms"], 3)
+            res[name]["gather_probe"] = g
         dc.close()
         del dc
         torch.cuda.empty_cache()

@@ -107,9 +107,28 @@ typedef struct isk_plan_info {
   int32_t num_segments;      /* splits (one partial output each, or a direct write)  */
   int32_t num_groups;        /* workgroup tasks the split kernel is launched with    */
   int32_t num_partials;      /* partial (o, lse) slots in the workspace              */
-  int32_t reserved;
+  int32_t split_kernel;      /* ISK_KERNEL_* family the plan's decode launches       */
   uint64_t workspace_bytes;  /* minimum workspace size for isk_attn_decode           */
 } isk_plan_info;
+
+/*
+ * Split-kernel families (isk_plan_info.split_kernel).  Every family computes
+ * the same arithmetic for a given kind and head count, so which one runs
+ * changes speed, never bits:
+ *   ISK_KERNEL_GQA       GQA split kernel.
+ *   ISK_KERNEL_MLA_H16   MLA, 16 query heads per wave (head counts that are
+ *                        not a multiple of 128).
+ *   ISK_KERNEL_MLA_H32   MLA, blocks of 128 heads, 32 heads per wave, tiles
+ *                        gathered by compiled code (sparse plans the
+ *                        generated loop does not take: a split of more than
+ *                        1024 slots, or a latent pool above 4 GiB).
+ *   ISK_KERNEL_MLA_H128  MLA, blocks of 128 heads, the generated tile loop
+ *                        (dense rows; sparse rows within the limits above).
+ */
+#define ISK_KERNEL_GQA 1
+#define ISK_KERNEL_MLA_H16 2
+#define ISK_KERNEL_MLA_H32 3
+#define ISK_KERNEL_MLA_H128 4
 
 /*
  * isk_plan_create - plan the splits of one decode batch on the host.
@@ -435,6 +454,29 @@ ISK_API int isk_linear_bf16(const void* x, const void* w, float* y, int32_t m, i
  * Errors: ISK_ERR_INVALID_ARG, ISK_ERR_HIP.
  */
 ISK_API int isk_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
+
+/*
+ * isk_hbm_gather_probe - measurement utility: one read of the `n_rows` rows
+ * of `row_bytes` bytes at src + rows[r] * row_bytes (r = 0 .. n_rows-1), in
+ * 16-byte pieces in list order (each wave's load instruction covers 1 KiB of
+ * consecutive pieces, the same pattern as a sparse top-k tile load), folded
+ * with XOR into one 32-bit word per workgroup at sink[0 .. blocks).  With the
+ * rows a sparse batch gathers (the FlashMLA issue page "Sparse MLA decode is
+ * not batch-invariant ...", section "Where it comes from", top-k attention)
+ * it gives the achievable rate of that gather, the sparse path's roofline
+ * next to the streaming rate of isk_hbm_read_probe.
+ *
+ * src        device buffer of src_bytes bytes, 16-byte aligned.
+ * rows       [n_rows] device int32 row indices; the caller keeps every
+ *            (rows[r] + 1) * row_bytes <= src_bytes (not checked on the device).
+ * row_bytes  a positive multiple of 16; n_rows >= 1.
+ * sink       device array of at least `blocks` uint32 (written).
+ * blocks     workgroups of 256 threads, in [1, 65536].
+ * stream     hipStream_t (as void*); the call only enqueues the kernel.
+ * Errors: ISK_ERR_INVALID_ARG, ISK_ERR_HIP.
+ */
+ISK_API int isk_hbm_gather_probe(const void* src, size_t src_bytes, const int32_t* rows, int32_t n_rows,
+                                 int32_t row_bytes, uint32_t* sink, int32_t blocks, void* stream);
 
 /*
  * isk_plan_set_timing_events - profiling hook.  Subsequent isk_attn_decode

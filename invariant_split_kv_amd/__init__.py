@@ -19,16 +19,20 @@ import numpy as np
 
 __all__ = [
     "IskError", "IskDesc", "IskExtraDesc", "IskExtraKv", "IskPlanInfo", "KIND_GQA", "KIND_MLA", "SPLIT_PER_ROW",
-    "SPLIT_BATCH_BALANCED", "OUT_BF16", "OUT_F32", "LIB_PATH", "lib", "plan_create",
+    "SPLIT_BATCH_BALANCED", "OUT_BF16", "OUT_F32", "KERNEL_GQA", "KERNEL_MLA_H16", "KERNEL_MLA_H32",
+    "KERNEL_MLA_H128", "LIB_PATH", "lib", "plan_create",
     "plan_update", "plan_destroy", "plan_query", "plan_workspace_bytes", "plan_segments",
     "plan_set_timing_events", "plan_create_extra",
     "attn_decode", "attn_decode_extra", "attn_decode_oneshot", "attn_decode_static", "rmsnorm", "linear_bf16", "hbm_read_probe",
+    "hbm_gather_probe",
     "last_error", "numerics_id", "Plan",
 ]
 
 KIND_GQA, KIND_MLA = 0, 1
 SPLIT_PER_ROW, SPLIT_BATCH_BALANCED = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
+# split-kernel families (plan_query()["split_kernel"])
+KERNEL_GQA, KERNEL_MLA_H16, KERNEL_MLA_H32, KERNEL_MLA_H128 = 1, 2, 3, 4
 STATUS_NAMES = {0: "ISK_OK", -1: "ISK_ERR_INVALID_ARG", -2: "ISK_ERR_UNSUPPORTED",
                 -3: "ISK_ERR_WORKSPACE", -4: "ISK_ERR_INDEX", -5: "ISK_ERR_HIP",
                 -6: "ISK_ERR_RANGE"}
@@ -68,7 +72,7 @@ class IskSplitBand(ctypes.Structure):
 
 class IskPlanInfo(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("split_tokens", ctypes.c_int32), ("num_segments", ctypes.c_int32),
-                ("num_groups", ctypes.c_int32), ("num_partials", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_groups", ctypes.c_int32), ("num_partials", ctypes.c_int32), ("split_kernel", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64)]
 
 
@@ -105,6 +109,8 @@ def _load() -> ctypes.CDLL:
         "isk_rmsnorm": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P]),
         "isk_linear_bf16": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]),
         "isk_hbm_read_probe": (ctypes.c_int, [P, ctypes.c_size_t, P, ctypes.c_int32, P]),
+        "isk_hbm_gather_probe": (ctypes.c_int, [P, ctypes.c_size_t, P, ctypes.c_int32, ctypes.c_int32, P,
+                                                ctypes.c_int32, P]),
         "isk_attn_decode_static": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P]),
         "isk_last_error": (ctypes.c_char_p, []),
         "isk_numerics_id": (ctypes.c_char_p, []),
@@ -201,7 +207,7 @@ def plan_destroy(plan: int) -> None:
 def plan_query(plan: int) -> dict:
     info = IskPlanInfo()
     _check(lib.isk_plan_query(plan, ctypes.byref(info)))
-    return {f: getattr(info, f) for f, _ in IskPlanInfo._fields_ if f != "reserved"}
+    return {f: getattr(info, f) for f, _ in IskPlanInfo._fields_}
 
 
 def plan_workspace_bytes(plan: int) -> int:
@@ -312,6 +318,18 @@ def hbm_read_probe(src, nbytes: int, sink, blocks: int, stream=None) -> None:
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
     _check(lib.isk_hbm_read_probe(_ptr(src), int(nbytes), _ptr(sink), int(blocks), stream))
+
+
+def hbm_gather_probe(src, src_bytes: int, rows, n_rows: int, row_bytes: int, sink, blocks: int,
+                     stream=None) -> None:
+    """Enqueue isk_hbm_gather_probe: one read of the listed rows of src."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(lib.isk_hbm_gather_probe(_ptr(src), int(src_bytes), _ptr(rows), int(n_rows), int(row_bytes), _ptr(sink),
+                                    int(blocks), stream))
 
 
 class Plan:

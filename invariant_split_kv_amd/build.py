@@ -130,7 +130,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         import check_mla_h128
     finally:
         sys.path.pop(0)
-    errors = check_mla_h128.check()
+    errors = check_mla_h128.check_all()
     if errors:
         raise RuntimeError("generated MLA tile loop fails its schedule check:\n  " + "\n  ".join(errors[:10]))
     gen_mla_h128.write_header(os.path.join(GEN_DIR, "mla_h128_seg.inc"))

@@ -68,6 +68,35 @@ bool dense_h128_off() {
   return off;
 }
 
+// Diagnostic switch: ISK_SPARSE_MLA_KERNEL=h32 routes sparse 128-head MLA
+// through the gather kernel even where the generated tile loop takes it.
+// Read once.
+bool sparse_h128_off() {
+  static const bool off = [] {
+    const char* v = std::getenv("ISK_SPARSE_MLA_KERNEL");
+    return v != nullptr && std::strcmp(v, "h32") == 0;
+  }();
+  return off;
+}
+
+// Sparse plans the generated tile loop takes: every split within its slot
+// window, every latent pool within its 32-bit tile offsets.
+bool sparse_h128_fits(const PlanData& pd) {
+  const isk_desc& d = pd.desc;
+  return pd.max_seg_units <= isk::kMlaH128MaxSparseSlots && isk::mla_h128_pool_fits(d.num_pages, d.page_size) &&
+         (!pd.has_extra || isk::mla_h128_pool_fits(pd.extra.num_pages, pd.extra.page_size));
+}
+
+// Split-kernel family of a plan's decode (ISK_KERNEL_*).
+int split_kernel_of(const PlanData& pd) {
+  const isk_desc& d = pd.desc;
+  if (d.kind == ISK_KIND_GQA) return ISK_KERNEL_GQA;
+  if (d.num_q_heads % 128 != 0) return ISK_KERNEL_MLA_H16;
+  const bool sparse = d.topk_width > 0;
+  if (!sparse) return dense_h128_off() ? ISK_KERNEL_MLA_H32 : ISK_KERNEL_MLA_H128;
+  return sparse_h128_fits(pd) && !sparse_h128_off() ? ISK_KERNEL_MLA_H128 : ISK_KERNEL_MLA_H32;
+}
+
 // Dense per-row plans that fit go to the kernels by value (see InlinePlan).
 void build_inline(isk_plan* p) {
   const PlanData& d = p->data;
@@ -420,7 +449,7 @@ int isk_plan_query(const isk_plan* plan, isk_plan_info* info) {
   info->num_segments = (int32_t)plan->data.segs.size();
   info->num_groups = (int32_t)plan->data.groups.size() - 1;
   info->num_partials = plan->data.n_partials;
-  info->reserved = 0;
+  info->split_kernel = split_kernel_of(plan->data);
   info->workspace_bytes = plan->layout.total;
   return ISK_OK;
 }
@@ -549,7 +578,7 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
     isk::MlaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, sparse ? topk_idx : nullptr,
                      segs, groups, part_o, part_lse, out, lse, n_groups, d.num_q_heads, d.page_size, d.num_pages,
                      d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2, part_f16,
-                     nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, plan->inl};
+                     nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, pd.max_seg_units, plan->inl};
     if (extra != nullptr) {
       a.xkv = (const uint16_t*)extra->kv_pages;
       a.xblock_table = extra->block_table;
@@ -561,14 +590,14 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
       a.xtopk_width = pd.extra.topk_width;
     }
     // 128-head blocks (32 heads per wave) when the head count allows it:
-    // dense rows through the generated tile loop, sparse rows through the
-    // gather kernel.
-    if (d.num_q_heads % 128 != 0)
-      e = isk::launch_mla_split(a, stream, ev);
-    else if (!sparse && !dense_h128_off())
-      e = isk::launch_mla_h128(a, stream, ev);
-    else
-      e = isk::launch_mla_split_h32(a, stream, ev);
+    // the generated tile loop for dense rows, and for sparse rows whose
+    // splits fit its slot window (pools within its 32-bit offsets); the
+    // gather kernel (same bits) otherwise.
+    switch (split_kernel_of(pd)) {
+      case ISK_KERNEL_MLA_H16: e = isk::launch_mla_split(a, stream, ev); break;
+      case ISK_KERNEL_MLA_H128: e = isk::launch_mla_h128(a, stream, ev); break;
+      default: e = isk::launch_mla_split_h32(a, stream, ev); break;
+    }
     if (e != hipSuccess) return hip_err(e, "launching the MLA split kernel");
   }
   if (pd.any_combine) {
@@ -679,6 +708,20 @@ int isk_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t bl
   if (blocks < 1 || blocks > 65536) return set_err(ISK_ERR_INVALID_ARG, "blocks must be in [1, 65536]");
   const hipError_t e = isk::launch_hbm_read(src, bytes, sink, blocks, (hipStream_t)stream);
   if (e != hipSuccess) return hip_err(e, "launching the HBM read probe");
+  return ISK_OK;
+}
+
+int isk_hbm_gather_probe(const void* src, size_t src_bytes, const int32_t* rows, int32_t n_rows, int32_t row_bytes,
+                         uint32_t* sink, int32_t blocks, void* stream) {
+  if (src == nullptr || rows == nullptr || sink == nullptr)
+    return set_err(ISK_ERR_INVALID_ARG, "src, rows and sink must be non-NULL");
+  if (row_bytes <= 0 || row_bytes % 16 != 0 || (uintptr_t)src % 16 != 0 || (uintptr_t)rows % 4 != 0)
+    return set_err(ISK_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 16, src 16-byte and rows 4-byte aligned");
+  if (n_rows < 1) return set_err(ISK_ERR_INVALID_ARG, "n_rows must be >= 1");
+  if (src_bytes < (size_t)row_bytes) return set_err(ISK_ERR_INVALID_ARG, "src_bytes is smaller than one row");
+  if (blocks < 1 || blocks > 65536) return set_err(ISK_ERR_INVALID_ARG, "blocks must be in [1, 65536]");
+  const hipError_t e = isk::launch_hbm_gather(src, rows, n_rows, row_bytes, sink, blocks, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_err(e, "launching the HBM gather probe");
   return ISK_OK;
 }
 

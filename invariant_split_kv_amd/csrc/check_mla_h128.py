@@ -19,7 +19,12 @@ checks, instruction by instruction:
     buffer, converted from bf16 to fp16 exactly once;
   * tile buffers: no LDS read of a buffer before this wave's direct loads
     into it have landed and a barrier has passed, and no direct load into a
-    buffer before a barrier has passed since this wave's last read of it.
+    buffer before a barrier has passed since this wave's last read of it;
+  * tile loads: each direct load uses the source offset of the piece slot
+    its LDS destination names; in the sparse body it adds that offset to
+    the window value of its tile row, read for the tile whose buffer it
+    fills (tile it+3 in the steps), and the row-valid mask tested before a
+    tile's rows are cleared or its scores masked is that tile's.
 
 Used by the build (a failing check stops it) and by the CPU tests.
 """
@@ -48,11 +53,23 @@ def _regs(tok):
     return [f"{m.group(3)}{i}" for i in range(int(m.group(4)), int(m.group(5)) + 1)]
 
 
+def sparse_mask(t):
+    """Row-valid mask the checker gives tile t of a sparse segment: mostly
+    full, some partial, some empty, so that every branch is taken."""
+    if t % 7 == 5:
+        return 0
+    if t % 3 == 1:
+        return (0xFFFFFFFF >> (t % 5 + 1)) ^ (1 << (t % 4))
+    return 0xFFFFFFFF
+
+
 class _Wave:
-    def __init__(self, lines, inputs, rescale):
+    def __init__(self, lines, inputs, rescale, sparse=False):
         self.lines = lines
         self.inp = inputs
         self.rescale = rescale
+        self.sparse = sparse
+        self.mask_tile = {}     # SGPR -> tile whose row-valid mask it holds (sparse)
         self.sg = {}
         self.scc = None
         self.lgkm = []          # outstanding LDS ops: (dst regs, buffer read or None)
@@ -75,7 +92,7 @@ class _Wave:
         if tok.startswith("%["):
             return self.inp.get(tok[2:-1])
         if re.match(r"^-?\d+$", tok):
-            return int(tok)
+            return int(tok) & 0xFFFFFFFF
         if re.match(r"^0x[0-9a-fA-F]+$", tok):
             return int(tok, 16)
         if re.match(r"^s\d+$", tok) or tok == "m0":
@@ -173,6 +190,7 @@ class _Wave:
                 self.err(i, "direct load with an unknown LDS destination")
             elif buf in self.read_unfenced:
                 self.err(i, f"direct load into buffer {buf} with no barrier since this wave read it")
+            self.check_load_source(i, ops[0], buf)
             self.buf_state[buf] = "pending"
             self.vm.append((set(), buf))
             return None
@@ -189,8 +207,50 @@ class _Wave:
             return None
         return self.valu(i, op, ops, dst)
 
+    def expected_tile(self, ahead):
+        it = self.sg.get(g.S_IT)
+        return None if it is None else it + ahead
+
+    def check_load_source(self, i, vaddr, buf):
+        """The piece slot the LDS destination names, and the offset used."""
+        m0 = self.sg.get("m0")
+        if buf is None or m0 is None:
+            return
+        rel = m0 - self.inp["lds"] - g.TILE * buf - 1024 * self.inp["w"]
+        if rel % 4096 != 0 or not 0 <= rel // 4096 < g.LOADS:
+            self.err(i, f"LDS destination {m0} is not a piece row of this wave")
+            return
+        pi = rel // 4096
+        if not self.sparse:
+            if vaddr != g.LO(pi):
+                self.err(i, f"load {pi} of a tile uses offset {vaddr}, not {g.LO(pi)}")
+            return
+        tg = self.tag.get(vaddr) or ("",)
+        if tg[0] != "ld_addr" or tg[2] != pi:
+            self.err(i, f"load {pi} of a tile uses {vaddr} holding {tg}")
+            return
+        tile = tg[1]
+        want = self.expected_tile(3) if self.in_steps else buf
+        if tile is None or tile & 3 != buf or tile != want:
+            self.err(i, f"load into buffer {buf} reads the window of tile {tile} (expected {want})")
+
+    def check_mask(self, i, sreg):
+        """A row-valid mask is tested for the tile about to be cleared or scored."""
+        want = self.expected_tile(1) if self.in_steps else 0
+        have = self.mask_tile.get(sreg)
+        if have != want:
+            self.err(i, f"mask in {sreg} is tile {have}'s, expected tile {want}'s")
+
     def lds_op(self, i, op, ops, mods, dst):
         buf = None
+        if op == "ds_read_b32" and self.sparse:
+            tg = self.tag.get(ops[1]) or ("",)
+            if tg[0] == "ew_addr":
+                self.lgkm.append((set(dst), None))
+                for r in dst:
+                    self.tag[r] = ("ew",) + tg[1:]
+                    self.mfma_at.pop(r, None)
+                return None
         if op.startswith("ds_read"):
             addr = ops[1]
             if addr in K_ADDR or addr in V_ADDR:
@@ -256,8 +316,33 @@ class _Wave:
         elif op == "v_xor_b32" and dst and (dst[0] in K_ADDR[1:] or dst[0] in V_ADDR[1:]):
             self.tag[dst[0]] = self.tag.get(_regs(ops[2])[0])
         elif op == "v_readlane_b32":
-            self.sg[ops[0]] = 0     # block-table entry: page 0, a page of the pool
+            if self.sparse:
+                t = self.sg.get(ops[2])
+                self.sg[ops[0]] = None if t is None else sparse_mask(t)
+                self.mask_tile[ops[0]] = t
+            else:
+                self.sg[ops[0]] = 0     # block-table entry: page 0, a page of the pool
+        elif op == "v_add_u32_sdwa":
+            line = self.lines[i]
+            src0, src1 = _regs(ops[1]), _regs(ops[2])
+            pi = g.LO_REGS.index(src1[0]) if src1 and src1[0] in g.LO_REGS else None
+            if "src1_sel:WORD_1" in line and ops[1] == g.S_WINU:
+                base = self.sg.get(g.S_WINU)
+                winb = self.sg.get(g.S_WINB)
+                tile = None if base is None or winb is None or (base - winb) % 128 else (base - winb) // 128
+                self.tag[dst[0]] = ("ew_addr", tile, pi)
+            elif "src1_sel:WORD_0" in line and src0:
+                tg = self.tag.get(src0[0]) or ("",)
+                if tg[0] != "ew" or tg[2] != pi:
+                    self.err(i, f"piece offset {pi} added to {src0[0]} holding {tg}")
+                    self.tag[dst[0]] = ("valu",)
+                else:
+                    self.tag[dst[0]] = ("ld_addr", tg[1], pi)
+            else:
+                self.err(i, "unexpected SDWA form")
         else:
+            if op == "v_lshrrev_b32_e64" and self.sparse and re.match(r"^s\d+$", ops[2]):
+                self.check_mask(i, ops[2])
             for r in dst:
                 self.tag[r] = ("valu",)
         for r in dst:
@@ -271,6 +356,8 @@ class _Wave:
         def put(x):
             if d is not None and (re.match(r"^s\d+$", d) or d == "m0"):
                 self.sg[d] = None if x is None else x & 0xFFFFFFFF
+                if op != "s_mov_b32":
+                    self.mask_tile.pop(d, None)   # no longer a tile's mask
 
         def two(f):
             return None if v[1] is None or v[2] is None else f(v[1], v[2])
@@ -280,6 +367,8 @@ class _Wave:
 
         if op == "s_mov_b32":
             put(v[1])
+            if d in self.mask_tile or ops[1] in self.mask_tile:
+                self.mask_tile[d] = self.mask_tile.get(ops[1])
         elif op in ("s_add_u32", "s_add_i32"):
             put(two(lambda a, b: a + b))
         elif op in ("s_sub_u32", "s_sub_i32"):
@@ -296,6 +385,8 @@ class _Wave:
             put(None if self.scc is None else (v[1] if self.scc else v[2]))
         elif op.startswith("s_cmp_"):
             a, b = v[0], v[1]
+            if self.sparse and op == "s_cmp_eq_u32" and ops[1] == "-1":
+                self.check_mask(i, ops[0])
             kind = op.split("_")[2]
             if a is None or b is None:
                 self.scc = None
@@ -307,9 +398,10 @@ class _Wave:
             self.err(i, f"instruction {op} is not modelled")
 
 
-def check_segment(body, tokens, begin=0, page=64, rescale="never", wave=1):
+def check_segment(body, tokens, begin=0, page=64, rescale="never", wave=1, sparse=False):
     """Errors found when one wave runs `body` over a segment of `tokens`
-    tokens starting at `begin` (rescale: "never", "always" or "alternate")."""
+    tokens starting at `begin` (rescale: "never", "always" or "alternate");
+    a sparse body gets the tile masks of sparse_mask."""
     end = begin + tokens
     inputs = dict(ntiles=(tokens + g.TOK - 1) // g.TOK, begin=begin, end=end, P=page, npg=1 << 20,
                   pbase=begin // page, on0=begin % page, pend=(end + page - 1) // page, lds=0, w=wave,
@@ -320,7 +412,7 @@ def check_segment(body, tokens, begin=0, page=64, rescale="never", wave=1):
         count[0] += 1
         return {"never": False, "always": True, "alternate": count[0] % 2 == 0}[rescale]
 
-    return _Wave(body.split("\n"), inputs, policy).run()
+    return _Wave(body.split("\n"), inputs, policy, sparse).run()
 
 
 # (tokens, first token, page size): fewer than 4 tiles, each tail step after
@@ -330,20 +422,31 @@ SEGMENTS = [(n, 0, 64) for n in (1, 31, 32, 33, 64, 65, 96, 97, 128, 129, 160, 1
     [(300, 1600, 128), (4200, 0, 64), (9000, 1536, 128)]
 
 
-def check(body=None, segments=SEGMENTS):
+# sparse segments: slot counts up to the window's 1024
+SPARSE_SEGMENTS = [(n, 0, 64) for n in (1, 31, 32, 33, 64, 65, 96, 97, 128, 129, 160, 191, 192, 256, 511, 512,
+                                         513, 1000, 1024)]
+
+
+def check(body=None, segments=SEGMENTS, sparse=False):
     """All errors over `segments` under the three rescale policies."""
-    body = g.generate() if body is None else body
+    body = g.generate(sparse=sparse) if body is None else body
     errors = []
     for n, begin, page in segments:
         # long segments repeat the steady state; one policy covers them
         for pol in ("never", "always", "alternate") if n <= 600 else ("alternate",):
-            for e in check_segment(body, n, begin=begin, page=page, rescale=pol):
-                errors.append(f"[{n} tokens from {begin}, page {page}, rescale {pol}] {e}")
+            for e in check_segment(body, n, begin=begin, page=page, rescale=pol, sparse=sparse):
+                errors.append(f"[{'sparse ' if sparse else ''}{n} tokens from {begin}, page {page}, "
+                              f"rescale {pol}] {e}")
     return errors
 
 
+def check_all():
+    """The dense body over SEGMENTS and the sparse body over SPARSE_SEGMENTS."""
+    return check() + check(segments=SPARSE_SEGMENTS, sparse=True)
+
+
 if __name__ == "__main__":
-    errs = check()
+    errs = check_all()
     for e in errs[:40]:
         print(e)
     print(f"{len(errs)} errors")

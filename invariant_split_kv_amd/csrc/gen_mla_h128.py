@@ -30,6 +30,18 @@ token range.  What differs is the schedule:
     the pool) are streamed from a valid page and then cleared in LDS, so
     every tile load takes the same scalar-base form.
 
+The same generator writes a second body for sparse (top-k) segments, the
+sparse attention of the FlashMLA issue page (section "Where it comes from"):
+the kernel first resolves the segment's top-k slots (at most 1024) into an
+LDS window, one 32-bit value per slot that, added to a lane's piece offset,
+gives the byte offset of that piece in the latent pool (invalid slots point
+at pool row 0), plus one row-valid mask per tile.  Each of a tile's nine
+loads then reads its lane's window value, adds the piece offset and loads
+from the pool base; masks replace the valid-row counts, so masked rows
+anywhere in a tile are cleared in LDS and their scores set to -inf.  The
+arithmetic is the dense body's, so a sparse segment gives the bits of the
+32-head gather kernel.
+
 Registers (one wave per SIMD, 256 VGPRs + 256 AGPRs):
   a0..a255   output block O^T; tile T = 4 dt + g holds dims 32 dt.. of the
              wave's 128 and head tile (g + wave) & 3
@@ -41,8 +53,10 @@ Registers (one wave per SIMD, 256 VGPRs + 256 AGPRs):
   v216..v223 this wave's fp16 P (j = 0, 1)
   v224..v228 m_ref, l_run, m_sub, two temporaries
   v229..v244 lane offsets and LDS addresses (K, V^T, P, alphas)
-  v245..v253 source offsets of the nine tile loads
-  v254       conversion scratch, v255 block-table window
+  v245..v253 source offsets of the nine tile loads (sparse: the piece
+             offset in the low half, 4 x the piece's tile row in the high)
+  v254       conversion scratch, v255 block-table window (sparse: lane t
+             holds the row-valid mask of tile t)
 """
 
 import os
@@ -56,6 +70,11 @@ NBUF = 4
 P_OFF = NBUF * TILE      # fp16 P exchange, 8 KB: [ht][j][lane] x 16 B
 X_OFF = P_OFF + 8192     # per-head floats [n32][ht] (alpha; l in the epilogue)
 LDS_BYTES = X_OFF + 512  # 156160
+# sparse segments: window values of up to 1024 slots, then 32 tile masks
+WIN_SLOTS = 1024
+WIN_OFF = LDS_BYTES
+MASK_OFF = WIN_OFF + 4 * WIN_SLOTS
+SPARSE_LDS_BYTES = MASK_OFF + 4 * (WIN_SLOTS // 32)   # 160384
 KSTEPS = 36
 KDEPTH = 4
 LOADS = 9                # 16-byte direct loads per wave per tile
@@ -83,6 +102,8 @@ S_LDSW = "s83"      # LDS base + 1024 wave
 S_KB = "s84"        # LDS base of tile it+1
 S_M0SAVE = "s85"    # the compiler's M0, restored at the end of the block
 S_EXEC = "s[86:87]"
+S_WINU = S_PN       # sparse: LDS address of the window values of the tile being planned
+S_WINB = S_PBASE    # sparse: LDS address of the window
 OWNED_SGPRS = [f"s{i}" for i in range(64, 73)] + [f"s{i}" for i in range(74, 88)]
 
 
@@ -151,6 +172,9 @@ XW, XR = "v243", "v244"
 
 def LO(i):
     return f"v{245 + i}"
+
+
+LO_REGS = [LO(i) for i in range(9)]
 
 
 CV = "v254"
@@ -322,6 +346,34 @@ def dma_groups(m0_base_sgpr):
              f"global_load_lds_dwordx4 {LO(pi)}, {S_B}"] for pi in range(LOADS)]
 
 
+def sparse_plan_groups(nv_dst):
+    """Sparse plan of the next tile to stream (its index in the segment is in
+    S_LI): its row-valid mask in nv_dst and the LDS address of its window
+    values in S_WINU; the tile cursor advances by one."""
+    return [
+        [f"v_readlane_b32 {nv_dst}, {PWIN}, {S_LI}"],
+        [f"s_lshl_b32 {S_WINU}, {S_LI}, 7", f"s_add_u32 {S_WINU}, {S_WINU}, {S_WINB}"],
+        [f"s_add_u32 {S_LI}, {S_LI}, 1"],
+    ]
+
+
+def sparse_ew_read(pi, tmp):
+    """Window value of the tile row of load pi's piece (4 x row in the high
+    half of LO(pi)) into tmp."""
+    return [f"v_add_u32_sdwa {tmp}, {S_WINU}, {LO(pi)} dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+            "src1_sel:WORD_1",
+            f"ds_read_b32 {tmp}, {tmp}"]
+
+
+def sparse_dma(pi, tmp, m0_base_sgpr):
+    """Load pi of the planned sparse tile: window value + piece offset (low
+    half of LO(pi)) from the pool base; the add is M0's wait state."""
+    return [f"s_add_u32 m0, {m0_base_sgpr}, {4096 * pi}",
+            f"v_add_u32_sdwa {tmp}, {tmp}, {LO(pi)} dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+            "src1_sel:WORD_0",
+            f"global_load_lds_dwordx4 {tmp}, {S_B}"]
+
+
 def window_load(em):
     """Block-table window: lane i holds the entry of page S_PBASE + i, or -1
     for pages at or past the segment's end (those are never loaded)."""
@@ -336,13 +388,17 @@ def window_load(em):
     em.op(f"s_mov_b64 exec, {S_EXEC}")
 
 
-def zero_masked_rows(em, nv_sgpr, buf_sgpr, tag):
-    """Rows >= nv of the tile in the LDS buffer at buf_sgpr become zero.  Each
-    wave clears the 16-byte pieces its own nine loads wrote, which have
-    landed (so no load can overwrite the zeros); the caller's barrier makes
-    them visible."""
-    em.op(f"s_cmp_lt_u32 {nv_sgpr}, {TOK}")
-    em.op(f"s_cbranch_scc0 {em.ref('zskip_' + tag)}")
+def zero_masked_rows(em, nv_sgpr, buf_sgpr, tag, sparse=False):
+    """Rows >= nv of the tile in the LDS buffer at buf_sgpr become zero
+    (sparse: rows whose bit in the mask nv is clear).  Each wave clears the
+    16-byte pieces its own nine loads wrote, which have landed (so no load
+    can overwrite the zeros); the caller's barrier makes them visible."""
+    if sparse:
+        em.op(f"s_cmp_eq_u32 {nv_sgpr}, -1")
+        em.op(f"s_cbranch_scc1 {em.ref('zskip_' + tag)}")
+    else:
+        em.op(f"s_cmp_lt_u32 {nv_sgpr}, {TOK}")
+        em.op(f"s_cbranch_scc0 {em.ref('zskip_' + tag)}")
     for r in (212, 213, 214, 215):
         em.op(f"v_mov_b32 v{r}, 0")
     em.op("v_mbcnt_lo_u32_b32 v208, -1, 0")
@@ -357,7 +413,12 @@ def zero_masked_rows(em, nv_sgpr, buf_sgpr, tag):
         em.op(f"v_add_u32 v211, {256 * pi}, v209")
         em.op(f"v_mul_u32_u24 v211, {DIV72_MUL}, v211")
         em.op(f"v_lshrrev_b32 v211, {DIV72_SHIFT}, v211")   # row of this lane's piece
-        em.op(f"v_cmp_le_u32 vcc, {nv_sgpr}, v211")
+        if sparse:
+            em.op(f"v_lshrrev_b32_e64 v211, v211, {nv_sgpr}")
+            em.op("v_and_b32 v211, 1, v211")
+            em.op("v_cmp_eq_u32 vcc, 0, v211")
+        else:
+            em.op(f"v_cmp_le_u32 vcc, {nv_sgpr}, v211")
         em.op(f"s_and_saveexec_b64 {S_EXEC}, vcc")
         em.lds(f"ds_write_b128 v210, v[212:215] offset:{4096 * pi}")
         em.op(f"s_mov_b64 exec, {S_EXEC}")
@@ -365,23 +426,34 @@ def zero_masked_rows(em, nv_sgpr, buf_sgpr, tag):
     em.label("zskip_" + tag)
 
 
-def mask_scores(em, p, nv_sgpr, tag):
-    """Scores of rows >= nv become -inf (lane (n, hh) holds tokens
-    8 (e >> 2) + 4 hh + (e & 3) of head n); entered at least 16 wait states
-    after the last MFMA that wrote the block."""
-    em.op(f"s_cmp_lt_u32 {nv_sgpr}, {TOK}")
-    em.op(f"s_cbranch_scc0 {em.ref('mskip_' + tag)}")
+def mask_scores(em, p, nv_sgpr, tag, sparse=False):
+    """Scores of rows >= nv (sparse: of rows whose mask bit is clear) become
+    -inf (lane (n, hh) holds tokens 8 (e >> 2) + 4 hh + (e & 3) of head n);
+    entered at least 16 wait states after the last MFMA that wrote the
+    block."""
+    if sparse:
+        em.op(f"s_cmp_eq_u32 {nv_sgpr}, -1")
+        em.op(f"s_cbranch_scc1 {em.ref('mskip_' + tag)}")
+    else:
+        em.op(f"s_cmp_lt_u32 {nv_sgpr}, {TOK}")
+        em.op(f"s_cbranch_scc0 {em.ref('mskip_' + tag)}")
     em.op("s_nop 7")
     em.op("s_nop 7")
     em.op(f"v_mbcnt_lo_u32_b32 {T0}, -1, 0")
     em.op(f"v_mbcnt_hi_u32_b32 {T0}, -1, {T0}")
     em.op(f"v_lshrrev_b32 {T0}, 5, {T0}")
     em.op(f"v_lshlrev_b32 {T0}, 2, {T0}")                 # 4 hh
+    if sparse:
+        em.op(f"v_lshrrev_b32_e64 {T0}, {T0}, {nv_sgpr}")  # the lane's half of the mask
     em.op(f"v_mov_b32 {CV}, {NEG_INF}")
     for e in range(16):
         c = 8 * (e >> 2) + (e & 3)
-        em.op(f"v_add_u32 {T1}, {c}, {T0}")
-        em.op(f"v_cmp_gt_u32 vcc, {nv_sgpr}, {T1}")
+        if sparse:
+            em.op(f"v_bfe_u32 {T1}, {T0}, {c}, 1")
+            em.op(f"v_cmp_ne_u32 vcc, 0, {T1}")
+        else:
+            em.op(f"v_add_u32 {T1}, {c}, {T0}")
+            em.op(f"v_cmp_gt_u32 vcc, {nv_sgpr}, {T1}")
         em.op(f"v_cndmask_b32 {Se(p, e)}, {CV}, {Se(p, e)}, vcc")
     em.label("mskip_" + tag)
 
@@ -452,7 +524,29 @@ def rescale(em):
 # ---------------------------------------------------------------- one step
 
 
-def step(em, name, cur, has_next, has_n2, has_n3):
+ST_LOADS = 4   # sparse: loads 0..3 of tile it+3 go in the S^T stream (address temporaries v212..v215)
+
+
+def sparse_load_items(pis, temps, first_dep, earliest, read_dist):
+    """Window reads and loads pi of `pis` (address temporary temps[k]) as
+    placement items: the reads chained from first_dep, each load at least
+    read_dist steps after its read and one step after the previous load."""
+    reads, loads = [], []
+    prev = first_dep
+    for pi, tmp in zip(pis, temps):
+        r = Item(sparse_ew_read(pi, tmp), earliest=earliest, deps=[(prev, 0)] if prev else [])
+        reads.append(r)
+        prev = r
+    prev = first_dep
+    for r, (pi, tmp) in zip(reads, zip(pis, temps)):
+        deps = [(r, read_dist)] + ([(prev, 1 if prev in loads else 0)] if prev else [])
+        ld = Item(sparse_dma(pi, tmp, S_M0B), earliest=earliest, deps=deps, wait=(lambda ri=r: ri.lds_idx))
+        loads.append(ld)
+        prev = ld
+    return reads + loads
+
+
+def step(em, name, cur, has_next, has_n2, has_n3, sparse=False):
     """Tile step `it`: S^T of tile it+1 (if any) with the softmax of tile it,
     then PV of tile it.  Entering: score block `cur` holds tile it's raw
     scores, m_sub/m_ref/l_run are moved for tile it, its alphas are in LDS,
@@ -465,7 +559,7 @@ def step(em, name, cur, has_next, has_n2, has_n3):
     em.op("s_waitcnt lgkmcnt(0)")
     em.reset()
     em.op("s_barrier")
-    if has_n3:
+    if has_n3 and not sparse:
         em.op(f"s_cmp_lt_u32 {S_LI}, 64")
         em.op(f"s_cbranch_scc1 {em.ref('win_ok_' + name)}")
         em.op(f"s_mov_b32 {S_PBASE}, {S_PN}")
@@ -486,13 +580,16 @@ def step(em, name, cur, has_next, has_n2, has_n3):
     if has_n3:
         # scalar plan and loads of tile it+3 (its buffer was freed at the top)
         prev = None
-        for g in plan_groups(S_NV3):
+        for g in (sparse_plan_groups if sparse else plan_groups)(S_NV3):
             prev = Item(g, earliest=0, deps=[(prev, 0)] if prev else [])
             items.append(prev)
         prev = Item([f"s_add_u32 {S_T3}, {S_IT}, 3", f"s_and_b32 {S_T3}, {S_T3}, 3",
                      f"s_mul_i32 {S_T3}, {S_T3}, {TILE}", f"s_add_u32 {S_M0B}, {S_T3}, {S_LDSW}"],
                     deps=[(prev, 0)])
         items.append(prev)
+        if sparse:
+            # the first ST_LOADS loads here, the rest in the PV stream
+            items += sparse_load_items(range(ST_LOADS), [f"v{212 + k}" for k in range(ST_LOADS)], prev, 0, 4)
     adds, cvts = [], []
     prev = None
     for e in range(1, 16):
@@ -539,7 +636,7 @@ def step(em, name, cur, has_next, has_n2, has_n3):
             emit_items(em, slots[kk])
         # masked rows of tile it+1 (landed at the top) are cleared before any
         # wave reads its V^T (after the barrier)
-        zero_masked_rows(em, S_NV1, S_KB, name)
+        zero_masked_rows(em, S_NV1, S_KB, name, sparse)
     else:
         # last tile: the softmax alone; exps, then dependent work
         slots = place(items, KSTEPS, 64)
@@ -555,13 +652,13 @@ def step(em, name, cur, has_next, has_n2, has_n3):
     rescale(em)
     em.reset()
     em.label("norescale_" + name)
-    pv(em, name, cur, nxt, has_next, has_n3)
+    pv(em, name, cur, nxt, has_next, has_n3, sparse)
     em.op(f"s_add_u32 {S_IT}, {S_IT}, 1")
     em.op(f"s_mov_b32 {S_NV1}, {S_NV2}")
     em.op(f"s_mov_b32 {S_NV2}, {S_NV3}")
 
 
-def pv(em, name, cur, nxt, has_next, has_n3):
+def pv(em, name, cur, nxt, has_next, has_n3, sparse=False):
     """O^T += V^T P^T for tile it: MFMA q has j = q >> 4, group g =
     (q >> 2) & 3 (head tile (g + wave) & 3) and dim tile dt = q & 3.  Group 0
     takes this wave's own P from registers, groups 1..3 read theirs from LDS
@@ -585,7 +682,7 @@ def pv(em, name, cur, nxt, has_next, has_n3):
             idx = em.lds(x)
         v1_idx.append(idx)
     if has_next:
-        mask_scores(em, nxt, S_NV1, name)
+        mask_scores(em, nxt, S_NV1, name, sparse)
 
     items = []
     # V^T (dt, 1) conversions: fragment dt is first read by MFMA 16 + dt, and
@@ -597,7 +694,12 @@ def pv(em, name, cur, nxt, has_next, has_n3):
             it.frag = dt
             v1c.append(it)
             items.append(it)
-    if has_n3:
+    if has_n3 and sparse:
+        # loads ST_LOADS.. of tile it+3; the address temporaries are the
+        # current score block, dead once the S^T stream has taken its P
+        pis = range(ST_LOADS, LOADS)
+        items += sparse_load_items(pis, [Se(cur, k) for k in range(len(pis))], None, 1, 3)
+    elif has_n3:
         # the nine loads of tile it+3 (planned in the S^T stream; its buffer
         # was freed at the top of the step)
         prev = None
@@ -643,7 +745,7 @@ def pv(em, name, cur, nxt, has_next, has_n3):
 # ---------------------------------------------------------------- segment
 
 
-def prologue(em):
+def prologue(em, sparse=False):
     em.op(f"s_mov_b32 {S_M0SAVE}, m0")
     em.op("v_mbcnt_lo_u32_b32 v208, -1, 0")
     em.op("v_mbcnt_hi_u32_b32 v208, -1, v208")      # lane
@@ -706,39 +808,68 @@ def prologue(em):
         em.op("v_lshl_or_b32 v216, v216, 2, v217")
         em.op("v_xor_b32 v214, v214, v216")
         em.op(f"v_lshlrev_b32 {LO(pi)}, 4, v214")
+        if sparse:
+            em.op(f"v_lshl_or_b32 {LO(pi)}, v215, 18, {LO(pi)}")   # 4 x tile row in the high half
     em.op(f"s_lshl_b32 {S_T1}, %[w], 10")
     em.op(f"s_add_u32 {S_LDSW}, %[lds], {S_T1}")
     # segment state
     em.op(f"s_mov_b32 {S_IT}, 0")
-    em.op(f"s_mov_b32 {S_PBASE}, %[pbase]")
-    em.op(f"s_mov_b32 {S_PN}, %[pbase]")
-    em.op(f"s_mov_b32 {S_ON}, %[on0]")
-    em.op(f"s_mov_b32 {S_U0}, %[begin]")
-    em.op(f"s_mov_b32 {S_LI}, 0")
-    for s in (S_NV1, S_NV2, S_NV3):
-        em.op(f"s_mov_b32 {s}, {TOK}")
-    # window first, then the query (36 loads)
-    window_load(em)
+    if sparse:
+        em.op(f"s_mov_b32 {S_LI}, 0")
+        em.op(f"s_add_u32 {S_WINB}, %[lds], {WIN_OFF}")
+        em.op(f"s_mov_b32 {S_B0}, %[kv_lo]")
+        em.op(f"s_mov_b32 {S_B1}, %[kv_hi]")
+        for s in (S_NV1, S_NV2, S_NV3):
+            em.op(f"s_mov_b32 {s}, -1")
+        # tile masks: lane t (and t + 32) reads the mask of tile t
+        em.op("v_and_b32 v214, 31, v208")
+        em.op(f"s_add_u32 {S_T1}, %[lds], {MASK_OFF}")
+        em.op(f"v_lshl_add_u32 v214, v214, 2, {S_T1}")
+        em.lds(f"ds_read_b32 {PWIN}, v214")
+    else:
+        em.op(f"s_mov_b32 {S_PBASE}, %[pbase]")
+        em.op(f"s_mov_b32 {S_PN}, %[pbase]")
+        em.op(f"s_mov_b32 {S_ON}, %[on0]")
+        em.op(f"s_mov_b32 {S_U0}, %[begin]")
+        em.op(f"s_mov_b32 {S_LI}, 0")
+        for s in (S_NV1, S_NV2, S_NV3):
+            em.op(f"s_mov_b32 {s}, {TOK}")
+        # window first, then the query (36 loads)
+        window_load(em)
     for kk in range(KSTEPS):
         em.op(f"global_load_dwordx4 {Q(kk)}, v211, %[q] offset:{32 * kk}")
     for a in range(256):
         em.op(f"v_accvgpr_write_b32 a{a}, 0")
     em.op(f"v_mov_b32 {M_REF}, {NEG_INF}")
     em.op(f"v_mov_b32 {L_RUN}, 0")
-    em.op(f"s_waitcnt vmcnt({KSTEPS})")              # the window has landed
+    if sparse:
+        em.wait_all()                                  # the masks have landed
+    else:
+        em.op(f"s_waitcnt vmcnt({KSTEPS})")          # the window has landed
     nv = [S_NV0, S_NV1, S_NV2]
     for t in range(3):
         if t > 0:
             em.op(f"s_cmp_gt_u32 %[ntiles], {t}")
             em.op(f"s_cbranch_scc0 {em.ref('pro_done')}")
-        for g in plan_groups(nv[t]):
+        for g in (sparse_plan_groups if sparse else plan_groups)(nv[t]):
             for x in g:
                 em.op(x)
         em.op(f"s_add_u32 {S_M0B}, {S_LDSW}, {t * TILE}")
-        for g in dma_groups(S_M0B):
-            for x in g:
-                em.op(x)
+        if sparse:
+            # the nine window reads first (score blocks as temporaries), then the loads
+            for pi in range(LOADS):
+                for x in sparse_ew_read(pi, f"v{S_BASE[0] + pi}"):
+                    em.op(x)
+            em.wait_all()
+            for pi in range(LOADS):
+                for x in sparse_dma(pi, f"v{S_BASE[0] + pi}", S_M0B):
+                    em.op(x)
+        else:
+            for g in dma_groups(S_M0B):
+                for x in g:
+                    em.op(x)
     em.label("pro_done")
+    em.reset()
     # the query and tile 0 have landed once only the loads of tiles 1, 2 are younger
     em.op("s_cmp_ge_u32 %[ntiles], 3")
     em.op(f"s_cbranch_scc0 {em.ref('pro_w2')}")
@@ -754,7 +885,7 @@ def prologue(em):
     em.label("pro_w")
     em.op("s_barrier")
     em.op(f"s_mov_b32 {S_KB}, %[lds]")
-    zero_masked_rows(em, S_NV0, S_KB, "pro")
+    zero_masked_rows(em, S_NV0, S_KB, "pro", sparse)
     # S^T of tile 0 into score block 0
     for x in set_ka_ins(S_KB):
         em.op(x)
@@ -781,7 +912,7 @@ def prologue(em):
         for g in conv_groups(V0_BASE + 4 * dt):
             for x in g:
                 em.op(x)
-    mask_scores(em, 0, S_NV0, "pro")
+    mask_scores(em, 0, S_NV0, "pro", sparse)
     em.op("s_nop 7")
     em.op("s_nop 7")
     for it in mx_move_items(0, True, 0):
@@ -793,10 +924,10 @@ def prologue(em):
     em.op(f"s_mov_b32 {S_VOTE_HI}, 0")
 
 
-def generate():
+def generate(sparse=False):
     em = Emitter()
-    em.comment("segment prologue")
-    prologue(em)
+    em.comment("segment prologue (sparse)" if sparse else "segment prologue")
+    prologue(em, sparse)
     em.op("s_cmp_ge_u32 %[ntiles], 4")
     em.op(f"s_cbranch_scc1 {em.ref('MA')}")
     em.op("s_cmp_eq_u32 %[ntiles], 3")
@@ -807,21 +938,21 @@ def generate():
         em.op(f"v_mov_b64 v[{S_BASE[1] + e}:{S_BASE[1] + e + 1}], v[{S_BASE[0] + e}:{S_BASE[0] + e + 1}]")
     em.op(f"s_branch {em.ref('T2')}")
     # steady state: two bodies with the score blocks swapped
-    step(em, "MA", 0, True, True, True)
+    step(em, "MA", 0, True, True, True, sparse)
     em.op(f"s_add_u32 {S_T0}, {S_IT}, 3")
     em.op(f"s_cmp_lt_u32 {S_T0}, %[ntiles]")
     em.op(f"s_cbranch_scc1 {em.ref('MB')}")
     for e in range(0, 16, 2):
         em.op(f"v_mov_b64 v[{S_BASE[0] + e}:{S_BASE[0] + e + 1}], v[{S_BASE[1] + e}:{S_BASE[1] + e + 1}]")
     em.op(f"s_branch {em.ref('T3')}")
-    step(em, "MB", 1, True, True, True)
+    step(em, "MB", 1, True, True, True, sparse)
     em.op(f"s_add_u32 {S_T0}, {S_IT}, 3")
     em.op(f"s_cmp_lt_u32 {S_T0}, %[ntiles]")
     em.op(f"s_cbranch_scc1 {em.ref('MA')}")
     # the last three tiles (no further loads)
-    step(em, "T3", 0, True, True, False)
-    step(em, "T2", 1, True, False, False)
-    step(em, "T1", 0, False, False, False)
+    step(em, "T3", 0, True, True, False, sparse)
+    step(em, "T2", 1, True, False, False, sparse)
+    step(em, "T1", 0, False, False, False, sparse)
     em.op("s_waitcnt lgkmcnt(0)")
     em.op(f"s_mov_b32 m0, {S_M0SAVE}")
     return "\n".join(em.lines) + "\n"
@@ -836,16 +967,25 @@ def clobber_list():
     return ", ".join(v + a + s + ['"vcc"', '"scc"', '"memory"'])
 
 
-def header_text():
-    body = generate()
+def asm_macro(name, body):
     esc = body.replace("\\", "\\\\").replace('"', '\\"')
-    out = ["// Generated by gen_mla_h128.py (the build runs it); do not edit.", "#pragma once",
-           "#define ISK_H128_SEG_ASM \\"]
+    out = [f"#define {name} \\"]
     for l in esc.rstrip("\n").split("\n"):
         out.append(f'  "{l}\\n" \\')
     out.append('  ""')
+    return out
+
+
+def header_text():
+    out = ["// Generated by gen_mla_h128.py (the build runs it); do not edit.", "#pragma once"]
+    out += asm_macro("ISK_H128_SEG_ASM", generate())
+    out += asm_macro("ISK_H128_SPARSE_SEG_ASM", generate(sparse=True))
     out.append("#define ISK_H128_SEG_CLOBBERS " + clobber_list())
     out.append(f"#define ISK_H128_LDS_BYTES {LDS_BYTES}")
+    out.append(f"#define ISK_H128_SPARSE_LDS_BYTES {SPARSE_LDS_BYTES}")
+    out.append(f"#define ISK_H128_WIN_OFF {WIN_OFF}")
+    out.append(f"#define ISK_H128_MASK_OFF {MASK_OFF}")
+    out.append(f"#define ISK_H128_WIN_SLOTS {WIN_SLOTS}")
     return "\n".join(out) + "\n"
 
 

@@ -95,6 +95,7 @@ struct PlanData {
   std::vector<int32_t> extra_units; // per-row valid extra top-k counts
   // Length bands (empty: one split length S for every row).
   std::vector<isk_split_band> bands;
+  int32_t max_seg_units = 0;        // longest segment (units)
 };
 
 constexpr int kMaxBands = 16;
@@ -165,11 +166,19 @@ struct MlaLaunch {
   // [begin - topk_width, end - topk_width).
   const uint16_t* xkv; const int32_t* xblock_table; const int32_t* xlens; const int32_t* xtopk_idx;
   int32_t xpage_size, xnum_pages, xmax_pages, xtopk_width;
+  int32_t max_seg_units;   // longest segment of the launch (units)
   InlinePlan inl;   // n_segs > 0: segments by value (groups are one segment each; dense only)
 };
 hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});       // 16 heads per wave
 hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});   // 32 heads per wave, hq % 128 == 0
-hipError_t launch_mla_h128(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});        // dense, hq % 128 == 0
+// 128-head kernel: dense, or sparse when every segment holds at most
+// kMlaH128MaxSparseSlots slots and each latent pool the kernel gathers from
+// spans at most 4 GiB (its tile loads take 32-bit offsets from the pool base).
+constexpr int kMlaH128MaxSparseSlots = 1024;
+inline bool mla_h128_pool_fits(int64_t num_pages, int64_t page_size) {
+  return num_pages * page_size * (int64_t)(2 * kMlaDqk) <= ((int64_t)1 << 32);
+}
+hipError_t launch_mla_h128(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});        // hq % 128 == 0
 
 struct CombineLaunch {
   const RowInfo* rows; const float* part_o; const float* part_lse;
@@ -206,6 +215,9 @@ hipError_t static_workspace(void** ptr);   // device address on the current devi
 
 // Streaming-read microbenchmark (isk_hbm_read_probe).
 hipError_t launch_hbm_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
+// Row-gather microbenchmark (isk_hbm_gather_probe).
+hipError_t launch_hbm_gather(const void* src, const int32_t* rows, int n_rows, int row_bytes, uint32_t* sink,
+                             int blocks, hipStream_t s);
 
 // Batch-invariant linear layer: tile shape chosen by row count, same bits.
 constexpr int kLinearSmallRows = 32;    // up to here: 16-row tiles

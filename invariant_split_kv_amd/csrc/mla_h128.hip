@@ -1,6 +1,7 @@
-// Dense absorbed-MLA split kernel for gfx950, one workgroup per split and
-// block of 128 query heads (used for dense MLA when the head count is a
-// multiple of 128).
+// Absorbed-MLA split kernel for gfx950, one workgroup per split and block of
+// 128 query heads (used for MLA when the head count is a multiple of 128:
+// dense rows, and sparse top-k rows whose splits hold at most 1024 slots of
+// a latent pool under 4 GiB).
 //
 // The split stage of the split-KV scheme on the FlashMLA issue page "Sparse
 // MLA decode is not batch-invariant ..." (section "Where it comes from"), with
@@ -13,6 +14,15 @@
 // schedule and the register plan; this file plans the segment, runs the block
 // and writes the output from the accumulator.  The arithmetic is the one of
 // mla_split_h32.hip (same operands, same orders), so both give the same bits.
+//
+// Sparse splits (the top-k gather of the same page): before the block, the
+// workgroup resolves the split's slots into an LDS window -- per slot the
+// value 1152 (r - t) mod 2^32, r the slot's pool row (0 for an invalid slot:
+// a position outside [0, len), a page outside the pool, or past the split's
+// end) and t its row in its 32-slot tile -- and one row-valid mask per tile.
+// A tile load adds its lane's piece offset 16 (72 t + piece) to the window
+// value, which gives the piece's byte offset 1152 r + 16 piece in the pool,
+// so every load is one 32-bit offset from the pool base.
 
 #include <utility>
 
@@ -35,7 +45,14 @@ typedef __attribute__((address_space(1))) unsigned char GU8;
 typedef __attribute__((address_space(1))) f32x4 GF32x4;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) u32x2 GU32x2;
+typedef __attribute__((address_space(4))) MlaLaunch KArg;   // the kernel arguments
 static_assert(ISK_H128_LDS_BYTES == kXOff + 512, "LDS layout of the generated block");
+static_assert(ISK_H128_WIN_OFF >= ISK_H128_LDS_BYTES && ISK_H128_MASK_OFF == ISK_H128_WIN_OFF + 4 * ISK_H128_WIN_SLOTS &&
+                  ISK_H128_SPARSE_LDS_BYTES >= ISK_H128_MASK_OFF + 4 * (ISK_H128_WIN_SLOTS / kTok) &&
+                  ISK_H128_SPARSE_LDS_BYTES <= 160 * 1024,
+              "LDS layout of the sparse window");
+static_assert(ISK_H128_WIN_SLOTS == kMlaH128MaxSparseSlots, "sparse split limit of the dispatch");
+constexpr uint32_t kRowBytes = 2 * kMlaDqk;   // 1152
 
 #define ISK_H128_A10(p) "a" #p "0", "a" #p "1", "a" #p "2", "a" #p "3", "a" #p "4", \
                         "a" #p "5", "a" #p "6", "a" #p "7", "a" #p "8", "a" #p "9"
@@ -64,8 +81,56 @@ __device__ __forceinline__ void acc_read(float (&o)[16]) {
       : "n"(T));
 }
 
+// Sparse split: slots [0, n) of the segment's top-k list `idx` (1 <= n <=
+// 1024) into the window (see the file comment).  The 256 threads take slots
+// 256 k + tid; the index reads of all four rounds go out together (clamped
+// to slot n - 1, so no read is predicated), then the table reads.  Wave w's
+// ballot of round k is the mask of tiles 8 k + 2 w and 8 k + 2 w + 1.  The
+// lane is derived here rather than kept across the segment's asm block.
+__device__ __forceinline__ void resolve_window(unsigned char* lds_raw, const int32_t* idx, const int32_t* bt, int n,
+                                               int len, int P, int npg, int wave) {
+  ISK_LDS uint32_t* const win = (ISK_LDS uint32_t*)(lds_raw + ISK_H128_WIN_OFF);
+  ISK_LDS uint32_t* const masks = (ISK_LDS uint32_t*)(lds_raw + ISK_H128_MASK_OFF);
+  constexpr int kRounds = ISK_H128_WIN_SLOTS / 256;
+  int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(lane));
+  const int tid = 64 * wave + lane;
+  int pos[kRounds];
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) pos[k] = idx[min(256 * k + tid, n - 1)];
+  // page index and in-page offset of each valid position (table entry 0 is
+  // read for the others, so the four table reads carry no predicate either)
+  const uint32_t pu = (uint32_t)P;
+  bool ok[kRounds];
+  uint32_t pi[kRounds], po[kRounds];
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    ok[k] = 256 * k + tid < n && pos[k] >= 0 && pos[k] < len;
+    const uint32_t p = ok[k] ? (uint32_t)pos[k] : 0u;
+    pi[k] = p / pu;
+    po[k] = p - pi[k] * pu;
+  }
+  int pg[kRounds];
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) pg[k] = bt[pi[k]];
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    const int u = 256 * k + tid;
+    const bool valid = ok[k] && pg[k] >= 0 && pg[k] < npg;
+    const uint32_t r = valid ? (uint32_t)pg[k] * pu + po[k] : 0u;
+    win[u] = kRowBytes * (r - (uint32_t)(u & (kTok - 1)));
+    const uint64_t bal = __ballot(valid);
+    if (lane == 0) {
+      masks[2 * (4 * k + wave)] = (uint32_t)bal;
+      masks[2 * (4 * k + wave) + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+}
+
+template <bool kSparse>
 __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[ISK_H128_LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char
+      lds_raw[kSparse ? ISK_H128_SPARSE_LDS_BYTES : ISK_H128_LDS_BYTES];
   asm volatile("" ::: ISK_H128_ALL_AGPRS);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // block id -> (task, head block): head blocks of one task sit 8 ids apart
@@ -87,7 +152,33 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
     __syncthreads();
     const int ntiles = (sg.end - sg.begin + kTok - 1) / kTok;
     float m_ref = -INFINITY, l_run = 0.f;
-    if (ntiles > 0) {
+    if (kSparse && ntiles > 0) {
+      const uint16_t* qw = a.q + ((size_t)b * a.hq + hb * kHeadsPerBlock + wave * 32) * kMlaDqk;
+      // The source fields are read from the kernel arguments here, per
+      // split, rather than held in SGPRs across the tile loop.
+      // (constant address space: scalar loads).
+      const KArg* sa = (const KArg*)__builtin_amdgcn_kernarg_segment_ptr();
+      asm volatile("" : "+s"(sa));
+      // A split past the main index width gathers from the extra KV source,
+      // at its slots [begin - topk_width, end - topk_width).
+      const bool from_extra = sg.begin >= sa->topk_width;
+      const int u0 = from_extra ? sg.begin - sa->topk_width : sg.begin;
+      const uintptr_t kv = (uintptr_t)(from_extra ? sa->xkv : sa->kv);
+      const int P = from_extra ? sa->xpage_size : sa->page_size;
+      const int cap = from_extra ? sa->xmax_pages * sa->xpage_size : sa->max_pages * sa->page_size;
+      const int len = min(from_extra ? sa->xlens[b] : sa->lens[b], cap);
+      const int32_t* idx = from_extra ? sa->xtopk_idx + (size_t)b * sa->xtopk_width + u0
+                                      : sa->topk_idx + (size_t)b * sa->topk_width + u0;
+      const int32_t* bt = from_extra ? sa->xblock_table + (size_t)b * sa->xmax_pages
+                                     : sa->block_table + (size_t)b * sa->max_pages;
+      resolve_window(lds_raw, idx, bt, sg.end - sg.begin, len, P, from_extra ? sa->xnum_pages : sa->num_pages, wave);
+      __syncthreads();
+      asm volatile(ISK_H128_SPARSE_SEG_ASM
+                   : "={v224}"(m_ref), "={v225}"(l_run)
+                   : [q] "s"(qw), [kv_lo] "s"((uint32_t)kv), [kv_hi] "s"((uint32_t)(kv >> 32)), [ntiles] "s"(ntiles),
+                     [scale] "s"(a.scale_log2), [w] "s"(wave), [lds] "s"(lds)
+                   : ISK_H128_SEG_CLOBBERS);
+    } else if (!kSparse && ntiles > 0) {
       const uint16_t* qw = a.q + ((size_t)b * a.hq + hb * kHeadsPerBlock + wave * 32) * kMlaDqk;
       const uintptr_t kv = (uintptr_t)a.kv;
       const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
@@ -229,10 +320,15 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
 
 hipError_t launch_mla_h128(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev) {
   if (a.n_groups == 0) return hipSuccess;
-  if (a.hq % kHeadsPerBlock != 0 || a.topk_idx != nullptr) return hipErrorInvalidValue;
+  if (a.hq % kHeadsPerBlock != 0) return hipErrorInvalidValue;
   const int n_hb = a.hq / kHeadsPerBlock;
   const int n_blocks = ((a.n_groups + 7) / 8) * 8 * n_hb;
-  return launch_one(mla_h128_kernel, dim3(n_blocks), dim3(64 * kWaves), s, a, ev);
+  if (a.topk_idx == nullptr) return launch_one(mla_h128_kernel<false>, dim3(n_blocks), dim3(64 * kWaves), s, a, ev);
+  // Sparse: every split fits the window and every pool the 32-bit offsets.
+  if (a.max_seg_units > ISK_H128_WIN_SLOTS || !mla_h128_pool_fits(a.num_pages, a.page_size) ||
+      (a.xtopk_idx != nullptr && !mla_h128_pool_fits(a.xnum_pages, a.xpage_size)))
+    return hipErrorInvalidValue;
+  return launch_one(mla_h128_kernel<true>, dim3(n_blocks), dim3(64 * kWaves), s, a, ev);
 }
 
 }  // namespace isk

@@ -269,6 +269,8 @@ std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int3
     for (int32_t g : p.seg_group) p.groups[g + 1]++;
     for (int g = 0; g < n_groups; ++g) p.groups[g + 1] += p.groups[g];
   }
+  p.max_seg_units = 0;
+  for (const Seg& s : p.segs) p.max_seg_units = std::max(p.max_seg_units, s.end - s.begin);
   *status = ISK_OK;
   return "";
 }

@@ -42,7 +42,7 @@ def segments(desc, lens, topk=None):
 def test_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "isk.h")).read()
     declared = set(re.findall(r"ISK_API\s+[\w\s\*]+?\b(isk_\w+)\s*\(", header))
-    assert len(declared) == 18
+    assert len(declared) == 19
     for name in declared:
         assert hasattr(isk.lib, name), name
     assert "gfx950" in isk.numerics_id()
@@ -453,3 +453,37 @@ def test_band_table_arguments_are_checked():
     out = isk.ctypes.c_void_p()
     assert isk.lib.isk_plan_create_banded(isk.ctypes.byref(mla_desc()), None, 1, 1,
                                           isk._i32p(isk._i32_host(lens)), None, isk.ctypes.byref(out)) == -1
+
+
+# ----------------------------------------------------------------------------
+# Split-kernel family of a plan
+# ----------------------------------------------------------------------------
+
+def test_split_kernel_family_follows_kind_heads_and_sparse_limits():
+    """GQA and 64-head MLA have one family each; 128-head MLA runs the
+    generated tile loop for dense rows and for sparse rows whose splits hold
+    at most 1024 slots of pools of at most 4 GiB, the gather kernel for other
+    sparse plans (a longer split, a larger main or extra pool)."""
+    lens, tl = [5000, 3000], [2048, 700]
+    fam = lambda desc, topk=None, **kw: isk.Plan(desc, lens, topk, **kw).info()["split_kernel"]
+    # 50000 pages of 64 rows: a 3.7 GB pool (the default descriptor's 100000 pages exceed 4 GiB)
+    sp = lambda **kw: mla_desc(topk_width=2048, num_pages=50000, **kw)
+    assert fam(gqa_desc()) == isk.KERNEL_GQA
+    assert fam(mla_desc(num_q_heads=64)) == isk.KERNEL_MLA_H16
+    assert fam(mla_desc(num_q_heads=64, topk_width=2048), tl) == isk.KERNEL_MLA_H16
+    assert fam(mla_desc()) == isk.KERNEL_MLA_H128
+    assert fam(mla_desc(num_q_heads=256)) == isk.KERNEL_MLA_H128
+    assert fam(sp(), tl) == isk.KERNEL_MLA_H128                                       # 512-slot splits
+    assert fam(sp(split_tokens=1024), tl) == isk.KERNEL_MLA_H128
+    assert fam(sp(split_tokens=1088), tl) == isk.KERNEL_MLA_H32
+    rows_4g = (1 << 32) // 1152                                    # pool rows within 4 GiB
+    assert fam(mla_desc(topk_width=2048), tl) == isk.KERNEL_MLA_H32                   # 7.4 GB pool
+    assert fam(mla_desc(topk_width=2048, page_size=1, num_pages=rows_4g, max_pages_per_row=8192), tl) == \
+        isk.KERNEL_MLA_H128
+    assert fam(mla_desc(topk_width=2048, page_size=1, num_pages=rows_4g + 1, max_pages_per_row=8192), tl) == \
+        isk.KERNEL_MLA_H32
+    ok_x, big_x = xdesc(), xdesc(page_size=64, num_pages=rows_4g // 64 + 1)
+    assert fam(sp(), tl, extra=ok_x, extra_topk_len_host=[100, 900]) == isk.KERNEL_MLA_H128
+    assert fam(sp(), tl, extra=big_x, extra_topk_len_host=[100, 900]) == isk.KERNEL_MLA_H32
+    # balanced mode: splits of this batch stay within 1024 slots
+    assert fam(sp(split_mode=isk.SPLIT_BATCH_BALANCED), tl) == isk.KERNEL_MLA_H128

@@ -12,9 +12,11 @@
   * q = 0: every score is 0, so the output is the mean of the values and
     the LSE is ln L (within the parity bar).
 
-Each kernel family is reached through its own dispatch: Hq = 128 dense MLA
-(generated 128-head loop), Hq = 128 sparse MLA (the 32-heads-per-wave gather
-kernel), Hq = 64 MLA dense and sparse (16-head kernel) and GQA.
+Each kernel family is reached through its own dispatch: Hq = 128 dense and
+sparse MLA (the generated 128-head loop; the 32-heads-per-wave gather kernel
+gives the same bits, checked in test_gpu_dense_kernels and
+test_gpu_sparse_kernels), Hq = 64 MLA dense and sparse (16-head kernel) and
+GQA.
 """
 
 import math

@@ -422,3 +422,23 @@ def test_hbm_read_probe_reads_every_word_once(nbytes, blocks):
     want = np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32))
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == want
+
+
+@pytest.mark.parametrize("n_rows,row_bytes,blocks", [(1, 1152, 1), (777, 1152, 64), (5000, 1152, 1024), (300, 16, 7)])
+def test_hbm_gather_probe_reads_every_listed_row_once(n_rows, row_bytes, blocks):
+    """The gather probe behind the sparse path's measured ceiling folds every
+    32-bit word of every listed row (repeats included) into the per-workgroup
+    XOR words exactly once."""
+    import torch
+    rng = np.random.default_rng(n_rows)
+    pool_rows = 4096
+    pool = rng.integers(0, 2 ** 32, (pool_rows, row_bytes // 4), dtype=np.uint64).astype(np.uint32)
+    rows = rng.integers(0, pool_rows, n_rows).astype(np.int32)
+    buf = torch.from_numpy(pool.view(np.int32)).cuda()
+    rows_d = torch.from_numpy(rows).cuda()
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    isk.hbm_gather_probe(buf, pool.nbytes, rows_d, n_rows, row_bytes, sink, blocks)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(pool[rows].reshape(-1)) if n_rows else 0
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want

@@ -109,3 +109,55 @@ def test_scalar_load_check_of_the_gather_kernel_loop():
     assert build.check_no_scalar_loads_in_tile_loop(text) == []
     planted = text.replace("\tv_mov_b32 v0, 0", "\ts_load_dword s7, s[0:1], 0xc")
     assert [s for _, s in build.check_no_scalar_loads_in_tile_loop(planted)] == ["s_load_dword s7, s[0:1], 0xc"]
+
+
+# ----------------------------------------------------------------------------
+# Sparse body: window-based tile loads and row-valid masks
+# ----------------------------------------------------------------------------
+
+SPARSE_SHORT = [(65, 0, 64), (300, 0, 64)]
+
+
+@pytest.fixture(scope="module")
+def sparse_body():
+    return gen.generate(sparse=True)
+
+
+def test_generated_sparse_loop_passes(sparse_body):
+    assert chk.check(sparse_body, chk.SPARSE_SEGMENTS, sparse=True) == []
+
+
+def test_sparse_load_with_the_wrong_piece_offset_is_reported(sparse_body):
+    # a load adds the piece offset of another load to its window value
+    old = f"v_add_u32_sdwa v146, v146, {gen.LO(6)} "
+    assert old in sparse_body
+    errs = chk.check(sparse_body.replace(old, f"v_add_u32_sdwa v146, v146, {gen.LO(5)} ", 1), SPARSE_SHORT,
+                     sparse=True)
+    assert any("piece offset" in e for e in errs)
+
+
+def test_sparse_window_of_the_wrong_tile_is_reported(sparse_body):
+    # window values read at 64 bytes a tile instead of 128
+    old = f"s_lshl_b32 {gen.S_WINU}, {gen.S_LI}, 7"
+    assert old in sparse_body
+    errs = chk.check(sparse_body.replace(old, f"s_lshl_b32 {gen.S_WINU}, {gen.S_LI}, 6"), SPARSE_SHORT, sparse=True)
+    assert any("reads the window of tile" in e for e in errs)
+
+
+def test_sparse_mask_of_the_wrong_tile_is_reported(sparse_body):
+    # scores of tile it+1 masked with tile it+2's mask
+    old = f"v_lshrrev_b32_e64 {gen.T0}, {gen.T0}, {gen.S_NV1}"
+    assert old in sparse_body
+    errs = chk.check(sparse_body.replace(old, f"v_lshrrev_b32_e64 {gen.T0}, {gen.T0}, {gen.S_NV2}", 1),
+                     SPARSE_SHORT, sparse=True)
+    assert any("mask in" in e for e in errs)
+
+
+def test_sparse_clobbered_tile0_mask_is_reported(sparse_body):
+    # a scalar temporary that shares tile 0's mask register written in the
+    # prologue before the mask is used (the kind of slip a prologue edit makes)
+    lines = sparse_body.split("\n")
+    z = _index(lines, lambda l: l.startswith("zskip_pro") or l.startswith(f"s_cmp_eq_u32 {gen.S_NV0}, -1"))
+    planted = lines[:z] + [f"\ts_sub_u32 {gen.S_T3}, %[ntiles], 1"] + lines[z:]
+    errs = chk.check("\n".join(planted), SPARSE_SHORT, sparse=True)
+    assert any(f"mask in {gen.S_NV0}" in e for e in errs)
