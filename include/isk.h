@@ -144,8 +144,8 @@ typedef struct isk_plan_info {
  *
  * Per-row mode implements the per-row split rule requested in the FlashMLA
  * issue page, section "Question".  The planning is host work.  A plan whose
- * split list is uploaded to the device (sparse, extra source, balanced mode,
- * or more than 640 splits or 128 rows) also gets its pinned staging ring
+ * split list is uploaded to the device (extra source, balanced mode, or more
+ * than 640 splits or 128 rows) also gets its pinned staging ring
  * here: four host buffers of the split-list size with half again of
  * headroom, and four events, so that isk_attn_decode allocates nothing.  On
  * a machine without a usable GPU the plan is still made (for host-side use:
@@ -250,8 +250,9 @@ ISK_API int isk_plan_segments(const isk_plan* plan, int32_t* records_out, int32_
  * topk_idx    sparse MLA: [B, topk_width] int32 row-local token positions;
  *             a slot below topk_len[b] whose value lies outside [0, L_b)
  *             (e.g. -1) is skipped.  NULL when dense.
- * topk_len    sparse MLA: [B] int32 device copy of topk_len_host.  NULL when
- *             dense.
+ * topk_len    sparse MLA: [B] int32 device copy of topk_len_host (a plan
+ *             passed by value rebuilds its split ranges from it, as a dense
+ *             one does from lens).  NULL when dense.
  * out         [B, Hq, head_dim_v] bf16 or fp32 (desc.out_dtype); rows with
  *             nothing to attend get 0.
  * lse         [B, Hq] fp32 natural-log LSE of the scaled scores (-inf for
@@ -259,9 +260,9 @@ ISK_API int isk_plan_segments(const isk_plan* plan, int32_t* records_out, int32_
  * workspace   device memory of at least isk_plan_workspace_bytes(plan) bytes,
  *             256-byte aligned; holds the split partials (fp32, or fp16 on
  *             the 128-head MLA path with bf16 output) and the uploaded
- *             split list (a dense per-row plan of at most 640 splits and 128
- *             rows goes to the kernels in their arguments instead, with no
- *             upload).  Must not be shared by calls in flight at the same time.
+ *             split list (a per-row plan of at most 640 splits and 128 rows,
+ *             dense or sparse without an extra source, goes to the kernels in
+ *             their arguments instead, with no upload).  Must not be shared by calls in flight at the same time.
  * stream      hipStream_t (as void*).
  *
  * Out-of-range block-table entries and top-k positions are masked in the

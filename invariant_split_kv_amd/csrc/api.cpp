@@ -97,12 +97,13 @@ int split_kernel_of(const PlanData& pd) {
   return sparse_h128_fits(pd) && !sparse_h128_off() ? ISK_KERNEL_MLA_H128 : ISK_KERNEL_MLA_H32;
 }
 
-// Dense per-row plans that fit go to the kernels by value (see InlinePlan).
+// Per-row plans (dense, or sparse without an extra source) that fit go to
+// the kernels by value (see InlinePlan).
 void build_inline(isk_plan* p) {
   const PlanData& d = p->data;
   isk::InlinePlan& inl = p->inl;
   inl = isk::InlinePlan{};
-  const bool fits = d.desc.split_mode == ISK_SPLIT_PER_ROW && d.desc.topk_width == 0 && !d.has_extra &&
+  const bool fits = d.desc.split_mode == ISK_SPLIT_PER_ROW && !d.has_extra &&
                     !d.segs.empty() && d.segs.size() <= (size_t)isk::kInlineSegs && d.batch <= isk::kInlineRows &&
                     d.groups.size() == d.segs.size() + 1;
   if (!fits) return;
@@ -117,7 +118,9 @@ void build_inline(isk_plan* p) {
   }
   for (int b = 0; b < d.batch; ++b) inl.rows[b] = d.rows[b];
   inl.split_units = d.split_units;
-  inl.cap = (int32_t)std::min<long long>((long long)d.desc.max_pages_per_row * d.desc.page_size, 0x7fffffffLL);
+  inl.cap = d.desc.topk_width > 0 ? d.desc.topk_width
+                                  : (int32_t)std::min<long long>((long long)d.desc.max_pages_per_row * d.desc.page_size,
+                                                                 0x7fffffffLL);
   inl.n_segs = (int32_t)d.segs.size();
 }
 
@@ -576,8 +579,8 @@ static int decode_impl(const isk_plan* plan_c, const void* q, const void* kv_pag
     if (e != hipSuccess) return hip_err(e, "launching the GQA split kernel");
   } else {
     isk::MlaLaunch a{(const uint16_t*)q, (const uint16_t*)kv_pages, block_table, lens, sparse ? topk_idx : nullptr,
-                     segs, groups, part_o, part_lse, out, lse, n_groups, d.num_q_heads, d.page_size, d.num_pages,
-                     d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2, part_f16,
+                     sparse ? topk_len : nullptr, segs, groups, part_o, part_lse, out, lse, n_groups, d.num_q_heads,
+                     d.page_size, d.num_pages, d.max_pages_per_row, d.topk_width, d.out_dtype == ISK_OUT_F32, scale_log2, part_f16,
                      nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, pd.max_seg_units, plan->inl};
     if (extra != nullptr) {
       a.xkv = (const uint16_t*)extra->kv_pages;

@@ -50,29 +50,32 @@ struct RowInfo {
   int32_t n_parts;    // 0: empty row; 1: written directly; >1: combined
 };
 
-// Dense per-row plans small enough for the kernel arguments travel there
-// instead of through the workspace, so a decode call enqueues no upload copy
-// before its kernels.  Segment j (one per workgroup task, launch order) is
-// stored as row << 16 | split index i, and its range is rebuilt from the
-// row's length: [i*S, min((i+1)*S, min(lens[row], cap))); its partial slot
-// is rows[row].part_off + i when the row has more than one split, else -1.
+// Per-row plans small enough for the kernel arguments travel there instead
+// of through the workspace, so a decode call enqueues no upload copy before
+// its kernels.  Segment j (one per workgroup task, launch order) is stored as
+// row << 16 | split index i, and its range is rebuilt from the row's units:
+// [i*S, min((i+1)*S, min(units[row], cap))), units being the device lengths
+// (dense; cap = max_pages_per_row * page_size) or the device top-k counts
+// (sparse; cap = topk_width); its partial slot is rows[row].part_off + i
+// when the row has more than one split, else -1.
 constexpr int kInlineSegs = 640;
 constexpr int kInlineRows = 128;
 struct InlinePlan {
   int32_t n_segs;        // 0: the plan is read from the workspace
   int32_t split_units;   // S
-  int32_t cap;           // max_pages_per_row * page_size
+  int32_t cap;           // max_pages_per_row * page_size (dense), topk_width (sparse)
   int32_t reserved;
   uint32_t seg[kInlineSegs];
   RowInfo rows[kInlineRows];
 };
 
-// Segment si of a launch; `lens` is the device copy of the row lengths.
-__device__ __forceinline__ Seg fetch_seg(const InlinePlan& p, const Seg* segs, const int32_t* lens, int si) {
+// Segment si of a launch; `units` is the device copy of the row lengths
+// (dense) or of the top-k counts (sparse).
+__device__ __forceinline__ Seg fetch_seg(const InlinePlan& p, const Seg* segs, const int32_t* units, int si) {
   if (p.n_segs == 0) return segs[si];
   const uint32_t e = p.seg[si];
   const int row = (int)(e >> 16), i = (int)(e & 0xffffu);
-  const int L = min(max(lens[row], 0), p.cap);
+  const int L = min(max(units[row], 0), p.cap);
   const RowInfo ri = p.rows[row];
   return Seg{row, i * p.split_units, min((i + 1) * p.split_units, L), ri.n_parts > 1 ? ri.part_off + i : -1};
 }
@@ -153,7 +156,7 @@ hipError_t launch_gqa_split(const GqaLaunch& a, hipStream_t s, const LaunchEvent
 struct MlaLaunch {
   const uint16_t* q; const uint16_t* kv;
   const int32_t* block_table; const int32_t* lens;
-  const int32_t* topk_idx;
+  const int32_t* topk_idx; const int32_t* topk_len;   // sparse rows (NULL when dense)
   const Seg* segs; const int32_t* groups;
   float* part_o; float* part_lse; void* out; float* lse;
   int32_t n_groups, hq, page_size, num_pages, max_pages, topk_width, out_f32;
@@ -167,7 +170,7 @@ struct MlaLaunch {
   const uint16_t* xkv; const int32_t* xblock_table; const int32_t* xlens; const int32_t* xtopk_idx;
   int32_t xpage_size, xnum_pages, xmax_pages, xtopk_width;
   int32_t max_seg_units;   // longest segment of the launch (units)
-  InlinePlan inl;   // n_segs > 0: segments by value (groups are one segment each; dense only)
+  InlinePlan inl;   // n_segs > 0: segments by value (groups are one segment each; no extra source)
 };
 hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});       // 16 heads per wave
 hipError_t launch_mla_split_h32(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev = {});   // 32 heads per wave, hq % 128 == 0

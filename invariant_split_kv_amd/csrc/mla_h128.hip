@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(256, 1) mla_h128_kernel(MlaLaunch a) {
   ISK_LDS float* const xs = (ISK_LDS float*)(lds_raw + kXOff);   // [n32][ht]
 
   for (int si = seg_first; si < seg_last; ++si) {
-    const Seg sg = fetch_seg(a.inl, a.segs, a.lens, si);
+    const Seg sg = fetch_seg(a.inl, a.segs, a.topk_idx != nullptr ? a.topk_len : a.lens, si);
     const int b = sg.row;
     // Every wave is done with the previous segment's LDS.
     __syncthreads();

@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
   };
 
   for (int si = seg_first; si < seg_last; ++si) {
-    Seg sg = fetch_seg(a.inl, a.segs, a.lens, si);
+    Seg sg = fetch_seg(a.inl, a.segs, a.topk_idx != nullptr ? a.topk_len : a.lens, si);
     const int b = sg.row;
     // A sparse segment past the main index width gathers from the extra KV
     // source, at its slots [begin - topk_width, end - topk_width).  The

@@ -661,7 +661,7 @@ mla_split_h32_kernel(MlaLaunch a) {
   so.init(wave_u, lane);
 
   for (int si = seg_first; si < seg_last; ++si) {
-    Seg sg = fetch_seg(a.inl, a.segs, a.lens, si);
+    Seg sg = fetch_seg(a.inl, a.segs, a.topk_idx != nullptr ? a.topk_len : a.lens, si);
     const int b = sg.row;
     // A sparse segment past the main index width gathers from the extra KV
     // source, at its slots [begin - topk_width, end - topk_width).  The

@@ -442,3 +442,22 @@ def test_hbm_gather_probe_reads_every_listed_row_once(n_rows, row_bytes, blocks)
     want = np.bitwise_xor.reduce(pool[rows].reshape(-1)) if n_rows else 0
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == want
+
+
+def test_sparse_plan_by_value_matches_uploaded_plan_bits():
+    """The same sparse rows decoded as a by-value plan (40 rows: split ranges
+    rebuilt in the kernels from the device top-k counts) and inside an
+    uploaded plan (the rows repeated to 160) give identical bits; both run
+    the generated 128-head loop."""
+    small = synth.mla_case(np.random.default_rng(130).integers(1, 5000, 40), 128, 1.0 / math.sqrt(192.0), 64,
+                           structure_seed=131, topk_width=1024)
+    small.rows[3].topk_len = 700                       # a row shorter than its entries
+    small.rows[5].topk_idx[:40] = -1
+    _, _, bits_small, lbits_small = run_case(small)
+    big_lens = np.concatenate([small.lens] * 4)
+    paging = synth.make_paging(big_lens, 64, np.random.default_rng(132))
+    big = synth.MlaCase(small.rows * 4, big_lens, 128, small.scale, paging, small.topk_width)
+    _, _, bits_big, lbits_big = run_case(big)
+    for k in range(4):
+        sl = slice(40 * k, 40 * (k + 1))
+        assert np.array_equal(bits_big[sl], bits_small) and np.array_equal(lbits_big[sl], lbits_small)

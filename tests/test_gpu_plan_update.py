@@ -1,11 +1,12 @@
 """Uploaded plans re-planned with isk_plan_update as the batch grows.
 
-A plan whose split list is uploaded (sparse rows; dense batches of more than
-128 rows) gets its pinned staging ring when it is made and re-sizes it in
-isk_plan_update when the split list outgrows it; isk_attn_decode itself
-allocates nothing.  One plan is re-planned through batches of growing size
-(and back down), each decoded and checked against the oracle, with the
-previous step's decode still in flight when the next update runs.
+A plan whose split list is uploaded (batches of more than 128 rows) gets its
+pinned staging ring when it is made and re-sizes it in isk_plan_update when
+the split list outgrows it; smaller per-row batches go to the kernels by
+value; isk_attn_decode itself allocates nothing.  One plan is re-planned
+through batches of growing size (and back down, crossing between the two
+forms), each decoded and checked against the oracle, with the previous
+step's decode still in flight when the next update runs.
 """
 
 import math
@@ -83,12 +84,12 @@ def test_uploaded_plan_across_update_growth(kind):
 
 
 def test_threads_decode_with_one_uploaded_plan():
-    """Four host threads decode with one uploaded (sparse) plan at the same
-    time, each on its own stream with its own workspace and outputs: the
-    plan's staging ring hands each call its own slot, and every output has
-    the bits of a single-threaded decode."""
+    """Four host threads decode with one uploaded (sparse, 140 rows) plan at
+    the same time, each on its own stream with its own workspace and outputs:
+    the plan's staging ring hands each call its own slot, and every output
+    has the bits of a single-threaded decode."""
     import threading
-    case = synth.mla_case(np.random.default_rng(95).integers(100, 3000, 24), 128, 0.08, 64, structure_seed=96,
+    case = synth.mla_case(np.random.default_rng(95).integers(100, 3000, 140), 128, 0.08, 64, structure_seed=96,
                           topk_width=512)
     desc = isk.IskDesc(isk.KIND_MLA, 128, 1, synth.MLA_DQK, synth.MLA_DV, 64, case.paging.num_pages,
                        case.paging.max_pages_per_row, case.topk_width, isk.SPLIT_PER_ROW, 0, isk.OUT_BF16, 0,

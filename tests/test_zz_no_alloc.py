@@ -2,10 +2,11 @@
 isk_attn_decode with a workspace of the caller's, through the C ABI.
 
 Same kernels, so the same bits: two calls in a row, the second with a
-smaller batch (the array keeps the first call's contents), on a dense
-128-head batch (split list in the kernel arguments), an uploaded sparse
-batch and a dense 64-head batch; a plan that needs more than the array holds
-is refused before anything runs.
+smaller batch (the array keeps the first call's contents), on dense and
+sparse 128-head batches with the split list in the kernel arguments, a
+sparse batch of more than 128 rows (split list uploaded) and a dense 64-head
+batch; a plan that needs more than the array holds is refused before
+anything runs.
 """
 
 import math
@@ -37,12 +38,12 @@ def both(case):
     return (bits, lbits), (sbits, slbits)
 
 
-@pytest.mark.parametrize("kind", ["dense_h128", "sparse_h128", "dense_h64"])
+@pytest.mark.parametrize("kind", ["dense_h128", "sparse_h128", "sparse_h128_uploaded", "dense_h64"])
 def test_static_workspace_matches_own_workspace(kind):
     rng = np.random.default_rng(120)
-    for step, B in enumerate((24, 5)):   # the second call is smaller
+    for step, B in enumerate((140, 130) if kind == "sparse_h128_uploaded" else (24, 5)):   # the second is smaller
         lens = rng.integers(1, 6000, B)
-        if kind == "sparse_h128":
+        if kind.startswith("sparse_h128"):
             case = synth.mla_case(lens, 128, 1.0 / math.sqrt(192.0), 64, structure_seed=121 + step, topk_width=1024)
         else:
             case = synth.mla_case(lens, 128 if kind == "dense_h128" else 64, 1.0 / math.sqrt(192.0), 64,
