@@ -66,6 +66,43 @@ __device__ __forceinline__ void load_part(const uint16_t* src, float (&v)[DPL]) 
   }
 }
 
+// Partials as loaded (the first splits' before the weights are known, later
+// ones a group at a time): fp32 values, or fp16 kept packed (four VGPRs for
+// eight values, widened at the FMA), which keeps the fp16 kernel at 70
+// VGPRs (seven waves a SIMD).
+template <int DPL, typename P>
+struct Early;
+template <int DPL>
+struct Early<DPL, float> {
+  float v[DPL];
+  __device__ __forceinline__ void load(const float* src) { load_part<DPL>(src, v); }
+  __device__ __forceinline__ void fma_into(float w, float (&o)[DPL]) const {
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[j] = fmaf(w, v[j], o[j]);
+  }
+};
+template <int DPL>
+struct Early<DPL, uint16_t> {
+  static_assert(DPL % 8 == 0, "fp16 partials are loaded 8 values at a time");
+  uint4 v[DPL / 8];
+  __device__ __forceinline__ void load(const uint16_t* src) {
+#pragma unroll
+    for (int i = 0; i < DPL / 8; ++i) v[i] = *(const uint4*)(src + 8 * i);
+  }
+  __device__ __forceinline__ void fma_into(float w, float (&o)[DPL]) const {
+    auto half = [](uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); };
+#pragma unroll
+    for (int i = 0; i < DPL / 8; ++i) {
+      const uint32_t x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[8 * i + 2 * k] = fmaf(w, half(x[k] & 0xffffu), o[8 * i + 2 * k]);
+        o[8 * i + 2 * k + 1] = fmaf(w, half(x[k] >> 16), o[8 * i + 2 * k + 1]);
+      }
+    }
+  }
+};
+
 // The partials' LSEs are loaded lane-parallel (lane l of chunk c holds split
 // 64c + l); the sum of the weights and the output FMA chain still run over
 // the splits one at a time in ascending order (v_readlane of the lane that
@@ -96,11 +133,11 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
     const P* op = (const P*)a.part_o + ((size_t)ri.part_off * a.hq + h) * a.dv + DPL * lane;
     const size_t stride = (size_t)a.hq * a.dv;
     constexpr int kEarly = 8;
-    float ve[kEarly][DPL];
+    Early<DPL, P> ve[kEarly];
     if (n <= kEarly) {
 #pragma unroll
       for (int k = 0; k < kEarly; ++k)
-        if (k < n) load_part<DPL>(op + (size_t)k * stride, ve[k]);
+        if (k < n) ve[k].load(op + (size_t)k * stride);
     }
     auto lse_chunk = [&](int c) { return c == 0 ? x0 : (c + lane < n ? lse_p[(size_t)(c + lane) * a.hq] : -INFINITY); };
     // m = max_i lse_i (exact, any order).
@@ -124,15 +161,14 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
       const float inv = 1.f / ssum;
       lse_out = m + fast_log2(ssum) * kLn2;
       // out = sum_i (e_i / S) o_i, an FMA chain with i ascending; the
-      // partials' loads go out eight (then four, then the rest) at a time.
+      // partials' loads go out eight (fp16: four) at a time, then the rest.
       if (n <= kEarly) {
         const float wl = fast_exp2((x0 - m) * kLog2e) * inv;
 #pragma unroll
         for (int k = 0; k < kEarly; ++k) {
           if (k < n) {
             const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k));
-#pragma unroll
-            for (int j = 0; j < DPL; ++j) o[j] = fmaf(w, ve[k][j], o[j]);
+            ve[k].fma_into(w, o);
           }
         }
       }
@@ -143,18 +179,20 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineLaunch a) {
         // Loads of a group go out together, then its FMAs in order.
         auto group = [&](int i0, auto kn) {
           constexpr int K = decltype(kn)::value;
-          float v[K][DPL];
+          Early<DPL, P> v[K];
 #pragma unroll
-          for (int k = 0; k < K; ++k) load_part<DPL>(op + (size_t)(c + i0 + k) * stride, v[k]);
+          for (int k = 0; k < K; ++k) v[k].load(op + (size_t)(c + i0 + k) * stride);
 #pragma unroll
           for (int k = 0; k < K; ++k) {
             const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i0 + k));
-#pragma unroll
-            for (int j = 0; j < DPL; ++j) o[j] = fmaf(w, v[k][j], o[j]);
+            v[k].fma_into(w, o);
           }
         };
+        // (fp16 partials: groups of four, which keeps the kernel's register
+        // count at the early path's)
+        constexpr int kGroup = sizeof(P) == 2 ? 4 : 8;
         int i = 0;
-        for (; i + 8 <= cn; i += 8) group(i, std::integral_constant<int, 8>{});
+        for (; i + kGroup <= cn; i += kGroup) group(i, std::integral_constant<int, kGroup>{});
         if (i + 4 <= cn) {
           group(i, std::integral_constant<int, 4>{});
           i += 4;
