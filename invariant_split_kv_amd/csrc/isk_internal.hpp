@@ -102,6 +102,11 @@ struct PlanData {
 };
 
 constexpr int kMaxBands = 16;
+// Launch-order blocks of the per-row planner: kXcdBlock tasks, of which XCD
+// x (task % kXcds under round-robin dealing) takes kXcdBlock / kXcds
+// consecutive sorted ones.
+constexpr int kXcds = 8;
+constexpr int kXcdBlock = 32;
 
 // Byte layout of the per-call metadata at the head of the workspace.
 struct MetaLayout {

@@ -8,7 +8,9 @@
 // (sparse) and S the frozen split length of the kind.  An exclusive scan over
 // rows assigns workspace slots to the partials; it decides where partials
 // live, never what is computed.  Splits are dispatched longest first, which
-// changes only which compute unit runs a split and when.  A sparse row with
+// changes only which compute unit runs a split and when (within each block of
+// 32 tasks the order is permuted so that a row's consecutive splits share an
+// XCD).  A sparse row with
 // an extra KV source gets the same rule applied to its extra top-k count;
 // those splits follow the main set's in the row's partial order.
 //
@@ -249,11 +251,23 @@ std::string plan_build(PlanData& p, const isk_desc& d, int32_t batch, const int3
   for (int b = 0; b < batch; ++b) p.any_combine |= p.rows[b].n_parts != 1;
 
   if (d.split_mode == ISK_SPLIT_PER_ROW) {
-    // One split per workgroup task, longest first (ties: batch order, split order).
+    // One split per workgroup task, longest first (ties: batch order, split
+    // order), at the granularity of blocks of kXcdBlock tasks.
     for (int b = 0; b < batch; ++b)
       for (const Seg& s : row_segs[b]) p.segs.push_back(s);
     std::stable_sort(p.segs.begin(), p.segs.end(),
                      [](const Seg& x, const Seg& y) { return (x.end - x.begin) > (y.end - y.begin); });
+    // Task t runs on XCD t % 8 (the kernels' block-to-task mapping under
+    // round-robin dealing of workgroups to the 8 XCDs).  In each full block
+    // of 32 tasks, XCD x takes sorted tasks 4x .. 4x+3: consecutive splits
+    // of one row, which read the same query, then share an L2, while the
+    // blocks stay in longest-first order.
+    for (size_t b0 = 0; b0 + kXcdBlock <= p.segs.size(); b0 += kXcdBlock) {
+      Seg blk[kXcdBlock];
+      for (int k = 0; k < kXcdBlock; ++k) blk[k] = p.segs[b0 + k];
+      for (int x = 0; x < kXcds; ++x)
+        for (int j = 0; j < kXcdBlock / kXcds; ++j) p.segs[b0 + kXcds * j + x] = blk[(kXcdBlock / kXcds) * x + j];
+    }
     p.groups.resize(p.segs.size() + 1);
     for (size_t i = 0; i <= p.segs.size(); ++i) p.groups[i] = (int32_t)i;
     p.seg_group.resize(p.segs.size());

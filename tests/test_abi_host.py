@@ -138,9 +138,22 @@ def test_per_row_plan_matches_formula_config_shapes():
                                    head_dim_v=64, page_size=64), lens)
     _check_tiling(segs, info, lens, 64)
     assert info["num_segments"] == sum(-(-L // 64) for L in lens)
-    # longest splits are dispatched first
+    # longest splits are dispatched first, in blocks of 32 tasks
     lengths = segs[:, 2] - segs[:, 1]
-    assert np.all(np.diff(lengths) <= 0)
+    blocks = [lengths[i:i + 32] for i in range(0, len(lengths), 32)]
+    assert all(a.min() >= b.max() for a, b in zip(blocks, blocks[1:]))
+
+
+def test_per_row_launch_order_puts_a_rows_splits_on_one_xcd():
+    """Task t runs on XCD t % 8; in each full block of 32 tasks XCD x takes
+    sorted tasks 4x .. 4x+3, so the four 512-slot splits of a sparse
+    2048-slot row share one XCD."""
+    tl = [2048] * 16
+    segs, info = segments(mla_desc(topk_width=2048), [70000] * 16, tl)
+    assert info["num_segments"] == 64
+    for r in range(16):
+        tasks = [t for t in range(64) if segs[t, 0] == r]
+        assert len(tasks) == 4 and len({t % 8 for t in tasks}) == 1, (r, tasks)
 
 
 def test_sparse_plan_uses_topk_len():
