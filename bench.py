@@ -275,13 +275,35 @@ def per_row_vs_balanced_sizes(isk, synth, torch, np, sizes=(1, 2, 8, 32, 128), c
     return res
 
 
-def cold_steps(dc, torch, n):
-    """Per-call time with L2 and the 256 MB Infinity Cache flushed first."""
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+class CacheFlush:
+    """Evicts the inputs from L2 and the 256 MB Infinity Cache by reading a
+    1 GiB buffer (written once, read once here so that no dirty line of it
+    is left).  A read leaves the caches full of clean lines; a write fill
+    (`dirty=True`) leaves up to 256 MB of dirty lines that the next kernel's
+    reads must first write back to HBM, which charges that kernel for the
+    flush's own traffic."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        self.buf.sum(dtype=torch.int64)
+        torch.cuda.synchronize()
+
+    def __call__(self, dirty=False):
+        if dirty:
+            self.buf.fill_(1)
+        else:
+            self.buf.sum(dtype=self.torch.int64)
+
+
+def cold_steps(dc, torch, n, dirty=False):
+    """Per-call time with L2 and the 256 MB Infinity Cache flushed first (a
+    1 GiB read; `dirty`: a 1 GiB write fill, see CacheFlush)."""
+    flush = CacheFlush(torch)
     times = []
     stream = torch.cuda.current_stream()
     for _ in range(n):
-        flush.fill_(1)
+        flush(dirty)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         dc.run(stream)
@@ -307,7 +329,7 @@ def gather_ceiling(isk, torch, np, dc, rows, launches=20):
     """isk_hbm_gather_probe over the rows a sparse batch gathers from its
     pool (the same bytes as its split kernels' tile loads, in the same 1 KiB
     pieces): warm (best of four grid sizes, `launches` launches) and cold
-    (1 GiB flush before each launch, median of 15) rates."""
+    (1 GiB read flush before each launch, median of 15) rates."""
     stream = torch.cuda.current_stream()
     rows_d = torch.from_numpy(rows).cuda()
     row_bytes = 2 * 576
@@ -328,10 +350,10 @@ def gather_ceiling(isk, torch, np, dc, rows, launches=20):
         torch.cuda.synchronize()
         warm[blocks] = a.elapsed_time(b) / launches
     best = min(warm, key=warm.get)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = CacheFlush(torch)
     cold = []
     for _ in range(15):
-        flush.fill_(1)
+        flush()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         probe(best)
@@ -348,7 +370,7 @@ def gather_ceiling(isk, torch, np, dc, rows, launches=20):
 def sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes, calls=100):
     """The config-4 sparse batch (B=64, 2048 top-k positions per row) and the
     same batch with an extra KV source (512 more positions per row from a
-    second cache): warm and cold (1 GiB flush first) call times and gathered
+    second cache): warm and cold (1 GiB read flush first) call times and gathered
     KV GB/s.  The gathered bytes (151 MB, 189 MB with the extra set) fit in
     the 256 MB Infinity Cache, so the cold figure is the HBM one."""
     res = {}
@@ -377,6 +399,7 @@ def sparse_extras(isk, synth, torch, np, DeviceCase, kv_bytes, calls=100):
                      "warm_ms_per_call": round(warm, 5), "warm_kv_gbs": round(kvb / (warm * 1e-3) / 1e9, 2),
                      "cold_ms_per_call": round(cold, 5), "cold_kv_gbs": round(kvb / (cold * 1e-3) / 1e9, 2)}
         if getattr(case, "extra", None) is None:
+            res[name]["cold_dirty_flush_ms_per_call"] = round(float(np.median(cold_steps(dc, torch, 15, dirty=True))), 5)
             g = gather_ceiling(isk, torch, np, dc, gather_rows(case, np))
             g["cold_call_over_gather"] = round(cold / g["cold_ms"], 3)
             res[name]["gather_probe"] = g
@@ -716,10 +739,12 @@ def main():
         ok = invariance_pass_rate(case, bits, lbits, mode, synth, DeviceCase, range(case.batch))
         res["invariance"] = {"pass": ok, "total": case.batch, "rate": round(ok / case.batch, 4),
                              "check": "out bf16 bits + lse fp32 bits, solo (fresh pages, fresh plan) vs batched"}
-        log("cold-cache calls (1 GiB flush before each)")
+        log("cold-cache calls (1 GiB read flush before each; then a 1 GiB write fill before each)")
         cold = cold_steps(dc, torch, 50)
         res["cold_ms_per_call"] = round(float(np.median(cold)), 5)
         res["cold_kv_gbs"] = round(kvb / (np.median(cold) * 1e-3) / 1e9, 2)
+        cold_dirty = cold_steps(dc, torch, 30, dirty=True)
+        res["cold_dirty_flush_ms_per_call"] = round(float(np.median(cold_dirty)), 5)
         if mode == isk.SPLIT_PER_ROW:
             log("batch-balanced comparison mode on the same batch, interleaved with per-row steps")
             dcb = DeviceCase(case, split_mode=isk.SPLIT_BATCH_BALANCED, pool=dc.pool)

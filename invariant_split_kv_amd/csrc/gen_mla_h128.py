@@ -341,9 +341,14 @@ def plan_groups(nv_dst):
 
 def dma_groups(m0_base_sgpr):
     """Nine direct loads of the planned tile; load PI of wave w fills LDS
-    chunk w + 4 PI (M0 needs one wait state before the load)."""
+    chunk w + 4 PI (M0 needs one wait state before the load).  Dense tiles
+    are read once per call from a pool larger than the Infinity Cache, so
+    the loads are nontemporal: they do not allocate there, and so neither
+    evict other data nor pay for writing back dirty lines they would
+    displace.  (Sparse tile loads allocate: a batch's gathered rows fit in
+    that cache and are read again by the next call.)"""
     return [[f"s_add_u32 m0, {m0_base_sgpr}, {4096 * pi}", "s_nop 0",
-             f"global_load_lds_dwordx4 {LO(pi)}, {S_B}"] for pi in range(LOADS)]
+             f"global_load_lds_dwordx4 {LO(pi)}, {S_B} nt"] for pi in range(LOADS)]
 
 
 def sparse_plan_groups(nv_dst):
