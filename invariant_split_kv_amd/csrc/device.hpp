@@ -61,6 +61,13 @@ __device__ __forceinline__ void load_lds_16(const void* gsrc, ISK_LDS void* lds_
   __builtin_amdgcn_global_load_lds(gsrc, lds_chunk, 16, 0, 0);
 }
 
+// The same load with the nontemporal hint (cache-policy bit nt): for dense
+// KV tiles, read once per call from pools larger than the Infinity Cache, so
+// that they neither allocate there nor displace (and write back) other data.
+__device__ __forceinline__ void load_lds_16_stream(const void* gsrc, ISK_LDS void* lds_chunk) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_chunk, 16, 0, 2);
+}
+
 // Transposing LDS read of four 16-bit values (ds_read_b64_tr_b16).  Within
 // each group of 16 lanes, lane i receives element (i % 4) of the 8-byte rows
 // addressed by lanes 4r + i / 4, r = 0..3.

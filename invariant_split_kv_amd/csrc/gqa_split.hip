@@ -66,8 +66,8 @@ __device__ __forceinline__ uint64_t gqa_stage(const GqaLaunch& a, int b, int hk,
     const size_t off = (size_t)__shfl((long long)my_off, t, 64);
     if (valid) {
       const unsigned char* src = kv + (off + (size_t)c * 8) * 2;
-      load_lds_16(src, kbuf + i * 1024);
-      load_lds_16(src + v_delta * 2, vbuf + i * 1024);
+      load_lds_16_stream(src, kbuf + i * 1024);
+      load_lds_16_stream(src + v_delta * 2, vbuf + i * 1024);
     } else {
       *(ISK_LDS f32x4*)(kbuf + p * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
       *(ISK_LDS f32x4*)(vbuf + p * 16) = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -117,7 +117,7 @@ struct Stager {
       if (nw == 4 && mask == ~0ull) {
         // Full tile of a four-wave workgroup: precomputed offsets, no checks.
 #pragma unroll
-        for (int j = 0; j < kTileInstr / 4; ++j) load_lds_16(dense_base + so.off[j], buf + (wave + 4 * j) * 1024);
+        for (int j = 0; j < kTileInstr / 4; ++j) load_lds_16_stream(dense_base + so.off[j], buf + (wave + 4 * j) * 1024);
         return mask;
       }
     }
@@ -135,7 +135,10 @@ struct Stager {
         src = dense_base + (size_t)t * kRowBytes + c * 16;
       }
       if (valid) {
-        load_lds_16(src, chunk);
+        if constexpr (kSparse)
+          load_lds_16(src, chunk);
+        else
+          load_lds_16_stream(src, chunk);
       } else {
         *(ISK_LDS f32x4*)(buf + p * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
       }
