@@ -83,7 +83,7 @@ RESCALE_THR = "0x41000000"   # 8.0 (log2 units)
 P_SHIFT_NEG = "0xc0e00000"   # -7.0
 FLOOR = "0xf149f2ca"         # -1e30
 HOOK_CAP_QK = 4
-HOOK_CAP_PV = 6
+HOOK_CAP_PV = 4
 
 # SGPRs owned by the asm block (declared clobbered)
 S_IT = "s64"        # tile index of the current step
@@ -248,22 +248,56 @@ class Item:
         self.lds_idx = None
 
 
+TRANSCENDENTAL = ("v_exp_f32", "v_log_f32", "v_rcp_f32", "v_rsq_f32", "v_sqrt_f32")
+
+
+def ins_cost(text):
+    """Issue cost of a hook instruction in the shadow of a 32x32x16 MFMA, in
+    units of one vector-ALU instruction.  Measured with one wave per SIMD:
+    four vector-ALU instructions after each MFMA of a K stream leave it at
+    the MFMA's own rate and every further one adds ~4.5 cycles; a
+    transcendental counts twice; a 1 KB LDS write costs 20 cycles or more;
+    a vector-ALU result read by the scalar unit stalls the wave; scalar-ALU
+    instructions and LDS or vector-memory reads cost next to nothing."""
+    op = text.split()[0]
+    if op in TRANSCENDENTAL:
+        return 2.0
+    if op == "v_readlane_b32":
+        return 2.0
+    if op.startswith("v_"):
+        return 1.0
+    if op == "ds_write_b128":
+        return 4.0
+    if op.startswith("ds_write"):
+        return 1.5
+    if op == "s_nop":
+        return (int(text.split()[1]) + 1) / 4.0
+    if op.startswith(("ds_read", "global_load", "buffer_load")):
+        return 0.25
+    return 0.0
+
+
+def item_cost(it):
+    return sum(ins_cost(x) for x in it.ins)
+
+
 def place(items, n_steps, cap):
     """Greedy placement in list order: each group goes to the first step at
     or after its earliest step and its dependencies' steps plus distance,
-    where the step's hook instructions stay within `cap` (a group larger
-    than `cap` takes an otherwise empty step)."""
-    load = [0] * n_steps
+    where the step's hook cost (ins_cost) stays within `cap` (a group
+    costlier than `cap` takes an otherwise empty step)."""
+    load = [0.0] * n_steps
     for it in items:
+        c = item_cost(it)
         s = it.earliest
         for d, dist in it.deps:
             assert d.step is not None, "dependency placed after its user"
             s = max(s, d.step + dist)
-        while s < n_steps - 1 and load[s] > 0 and load[s] + len(it.ins) > cap:
+        while s < n_steps - 1 and load[s] > 0 and load[s] + c > cap:
             s += 1
         s = min(s, n_steps - 1)
         it.step = s
-        load[s] += len(it.ins)
+        load[s] += c
     slots = [[] for _ in range(n_steps)]
     for it in items:
         slots[it.step].append(it)
@@ -499,10 +533,13 @@ def mx_move_items(p, first, earliest):
 
 
 def vote_ins():
-    return [f"v_cmp_neq_f32 vcc, 1.0, v208", f"v_cmp_neq_f32_e64 {S_VOTE}, 1.0, v209",
-            f"s_or_b64 {S_VOTE}, {S_VOTE}, vcc", f"v_cmp_neq_f32 vcc, 1.0, v210",
-            f"s_or_b64 {S_VOTE}, {S_VOTE}, vcc", f"v_cmp_neq_f32 vcc, 1.0, v211",
-            f"s_or_b64 {S_VOTE}, {S_VOTE}, vcc"]
+    """S_VOTE = lanes where one of the four alphas in v208..v211 is not 1.0.
+    A float equals 1.0 exactly when its bits are 0x3f800000, so the test is
+    on the bits: bitop3 0x7e is (src0 ^ src2) | (src1 ^ src2).  The alphas
+    are consumed (the rescale reads them from LDS again); no scalar
+    instruction waits on a vector compare."""
+    return [f"v_bitop3_b32 v208, v208, v209, 1.0 bitop3:0x7e", f"v_bitop3_b32 v210, v210, v211, 1.0 bitop3:0x7e",
+            f"v_or_b32 v208, v208, v210", f"v_cmp_ne_u32_e64 {S_VOTE}, 0, v208"]
 
 
 def rescale(em):
@@ -560,10 +597,19 @@ def step(em, name, cur, has_next, has_n2, has_n3, sparse=False):
     nxt = cur ^ 1
     em.comment(f"==== step {name}")
     em.label(name)
+    if has_next:
+        # K read addresses of tile it+1 (no data involved) ahead of the barrier
+        for x in [f"s_add_u32 {S_KB}, {S_IT}, 1", f"s_and_b32 {S_KB}, {S_KB}, 3",
+                  f"s_mul_i32 {S_KB}, {S_KB}, {TILE}", f"s_add_u32 {S_KB}, {S_KB}, %[lds]"]:
+            em.op(x)
+        for x in set_ka_ins(S_KB):
+            em.op(x)
     em.op("s_waitcnt vmcnt(9)" if has_n2 else "s_waitcnt vmcnt(0)")
     em.op("s_waitcnt lgkmcnt(0)")
     em.reset()
     em.op("s_barrier")
+    if has_next:
+        kidx = {kk: em.lds(kread(kk)) for kk in range(KDEPTH)}
     if has_n3 and not sparse:
         em.op(f"s_cmp_lt_u32 {S_LI}, 64")
         em.op(f"s_cbranch_scc1 {em.ref('win_ok_' + name)}")
@@ -615,9 +661,10 @@ def step(em, name, cur, has_next, has_n2, has_n3, sparse=False):
             items.append(c)
     lrun = Item([f"v_fma_f32 {L_RUN}, {L_RUN}, {T0}, {T1}"], deps=[(adds[-1], 0)])
     items.append(lrun)
-    pwrite = Item([f"ds_write_b128 {PW}, {PH(0)}", f"ds_write_b128 {PW}, {PH(1)} offset:1024"],
-                  deps=[(cvts[-1], 1)])
-    items.append(pwrite)
+    # the two P writes in shadows of their own (each costs an MFMA's shadow)
+    pwrite0 = Item([f"ds_write_b128 {PW}, {PH(0)}"], deps=[(c, 1) for c in cvts[:4]])
+    pwrite1 = Item([f"ds_write_b128 {PW}, {PH(1)} offset:1024"], deps=[(c, 1) for c in cvts[4:]])
+    items += [pwrite0, pwrite1]
     items.append(Item(vote_ins(), earliest=12, wait=vote_idx))
     # V^T (2, 0) and (3, 0) of tile it to fp16 (read in the previous step)
     for dt in (2, 3):
@@ -625,13 +672,8 @@ def step(em, name, cur, has_next, has_n2, has_n3, sparse=False):
             items.append(Item(g, earliest=0))
 
     if has_next:
-        for x in [f"s_add_u32 {S_KB}, {S_IT}, 1", f"s_and_b32 {S_KB}, {S_KB}, 3",
-                  f"s_mul_i32 {S_KB}, {S_KB}, {TILE}", f"s_add_u32 {S_KB}, {S_KB}, %[lds]"]:
-            em.op(x)
-        for x in set_ka_ins(S_KB):
-            em.op(x)
-        kidx = {kk: em.lds(kread(kk)) for kk in range(KDEPTH)}
         slots = place(items, KSTEPS, HOOK_CAP_QK)
+        v1_idx = []
         for kk in range(KSTEPS):
             em.wait(kidx[kk])
             src_c = "0" if kk == 0 else S(nxt)
@@ -639,9 +681,23 @@ def step(em, name, cur, has_next, has_n2, has_n3, sparse=False):
             if kk + KDEPTH < KSTEPS:
                 kidx[kk + KDEPTH] = em.lds(kread(kk + KDEPTH))
             emit_items(em, slots[kk])
+            if kk >= KSTEPS - 4:
+                # V^T (dt, 1) of tile it into the K operand slot this MFMA
+                # has just read (KR(dt) is V1(dt)); the reads stay in flight
+                # across the barrier and land before the PV stream needs them
+                dt = kk - (KSTEPS - 4)
+                idx = None
+                for x in vfrag_read_ins(V1_BASE + 4 * dt, dt, 1):
+                    idx = em.lds(x)
+                v1_idx.append(idx)
         # masked rows of tile it+1 (landed at the top) are cleared before any
-        # wave reads its V^T (after the barrier)
+        # wave reads its V^T (after the barrier).  That branch drains every
+        # LDS operation; without it only the V^T reads above are in flight
+        # (every older operation completed before the last MFMA's wait), so
+        # the count is carried on as if the clearing did not happen.
+        mark = (em.issued, em.done)
         zero_masked_rows(em, S_NV1, S_KB, name, sparse)
+        em.issued, em.done = mark
     else:
         # last tile: the softmax alone; exps, then dependent work
         slots = place(items, KSTEPS, 64)
@@ -649,43 +705,57 @@ def step(em, name, cur, has_next, has_n2, has_n3, sparse=False):
             if slots[kk]:
                 emit_items(em, slots[kk])
                 em.op("s_nop 0")
-    em.wait_all()
+    if has_next:
+        # every LDS operation older than the V^T reads (the P writes among
+        # them) is complete before the barrier
+        em.wait(v1_idx[0] - 2)
+    else:
+        em.wait_all()
+        em.reset()
+        v1_idx = None
     em.op("s_barrier")
-    em.reset()
     em.op(f"s_cmp_lg_u64 {S_VOTE}, 0")
     em.op(f"s_cbranch_scc0 {em.ref('norescale_' + name)}")
+    # the rescale drains every LDS operation; the count without it is kept
+    mark = (em.issued, em.done)
     rescale(em)
-    em.reset()
+    em.issued, em.done = mark
     em.label("norescale_" + name)
-    pv(em, name, cur, nxt, has_next, has_n3, sparse)
+    pv(em, name, cur, nxt, has_next, has_n3, sparse, v1_idx)
     em.op(f"s_add_u32 {S_IT}, {S_IT}, 1")
     em.op(f"s_mov_b32 {S_NV1}, {S_NV2}")
     em.op(f"s_mov_b32 {S_NV2}, {S_NV3}")
 
 
-def pv(em, name, cur, nxt, has_next, has_n3, sparse=False):
+def pv(em, name, cur, nxt, has_next, has_n3, sparse=False, v1_pre=None):
     """O^T += V^T P^T for tile it: MFMA q has j = q >> 4, group g =
     (q >> 2) & 3 (head tile (g + wave) & 3) and dim tile dt = q & 3.  Group 0
     takes this wave's own P from registers, groups 1..3 read theirs from LDS
     into two alternating slots."""
     preads = [(0, 1), (0, 2), (0, 3), (1, 1), (1, 2), (1, 3)]
-    slot_of = {jg: k & 1 for k, jg in enumerate(preads)}
-    read_before = {8: 2, 12: 3, 16: 4, 24: 5}   # read k issued before MFMA q
+    # four P slots: the two fragment slots and the upper half of the score
+    # block of tile it (dead once the S^T stream has taken its P)
+    pslots = [PR(0), PR(1), f"v[{S_BASE[cur] + 8}:{S_BASE[cur] + 11}]", f"v[{S_BASE[cur] + 12}:{S_BASE[cur] + 15}]"]
+    slot_of = {jg: k % 4 for k, jg in enumerate(preads)}
+    read_before = {8: 4, 12: 5}   # read k issued before MFMA q (its slot's last reader has issued)
     pidx = {}
 
     def pread(k):
         j, g = preads[k]
-        pidx[(j, g)] = em.lds(f"ds_read_b128 {PR(k & 1)}, {PRG(g)} offset:{1024 * j}")
+        pidx[(j, g)] = em.lds(f"ds_read_b128 {pslots[k % 4]}, {PRG(g)} offset:{1024 * j}")
 
-    pread(0)
-    pread(1)
-    # V^T (dt, 1) of tile it
-    v1_idx = []
-    for dt in range(4):
-        idx = None
-        for x in vfrag_read_ins(V1_BASE + 4 * dt, dt, 1):
-            idx = em.lds(x)
-        v1_idx.append(idx)
+    for k in range(4):
+        pread(k)
+    # V^T (dt, 1) of tile it (read in the S^T stream when there was one)
+    if v1_pre is not None:
+        v1_idx = list(v1_pre)
+    else:
+        v1_idx = []
+        for dt in range(4):
+            idx = None
+            for x in vfrag_read_ins(V1_BASE + 4 * dt, dt, 1):
+                idx = em.lds(x)
+            v1_idx.append(idx)
     if has_next:
         mask_scores(em, nxt, S_NV1, name, sparse)
 
@@ -713,9 +783,9 @@ def pv(em, name, cur, nxt, has_next, has_n3, sparse=False):
             items.append(prev)
     v0r = []
     if has_next:
-        items += mx_move_items(nxt, False, earliest=10)
         # V^T (dt, 0) of tile it+1: addresses (its LDS base is S_KB), reads once
-        # phase 0 has issued (MFMA 15 is the last to read v176..v191)
+        # phase 0 has issued (MFMA 15 is the last to read v176..v191); placed
+        # ahead of the max chain so that they go out early
         setva = Item(set_va_ins(S_KB), earliest=15)
         items.append(setva)
         for dt in range(4):
@@ -723,6 +793,7 @@ def pv(em, name, cur, nxt, has_next, has_n3, sparse=False):
             it = Item(ins, earliest=16, deps=[(setva, 0)])
             v0r.append(it)
             items.append(it)
+        items += mx_move_items(nxt, False, earliest=10)
         # V^T (0, 0) and (1, 0) of tile it+1 to fp16 here; (2, 0), (3, 0) in
         # the next step's S^T stream
         for dt in (0, 1):
@@ -738,7 +809,7 @@ def pv(em, name, cur, nxt, has_next, has_n3, sparse=False):
         if g >= 1 and dt == 0:
             em.wait(pidx[(j, g)])
         a_op = V0(dt) if j == 0 else V1(dt)
-        b_op = PH(j) if g == 0 else PR(slot_of[(j, g)])
+        b_op = PH(j) if g == 0 else pslots[slot_of[(j, g)]]
         t = 4 * dt + g
         em.op(f"v_mfma_f32_32x32x16_f16 a[{16 * t}:{16 * t + 15}], {a_op}, {b_op}, a[{16 * t}:{16 * t + 15}]")
         for it in slots[q]:
