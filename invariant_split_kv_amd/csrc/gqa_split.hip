@@ -22,8 +22,9 @@
 //     butterfly at the end of the segment.
 //   * PV: lane l owns D/64 output dims and accumulates p_t * v_t[d] in fp32
 //     over the tile's tokens in order.
-// Heads: with G >= 4 each of the four waves owns G/4 heads; with G < 4 the
-// workgroup has G waves of one head each.
+// Heads: with G = 4 the four waves split each tile by tokens instead
+// (gqa_g4_kernel below); with G = 8 or 16 each of the four waves owns G/4
+// heads; with G < 4 the workgroup has G waves of one head each.
 
 #include "device.hpp"
 #include "isk_internal.hpp"
