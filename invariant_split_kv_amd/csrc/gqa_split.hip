@@ -22,8 +22,8 @@
 //     butterfly at the end of the segment.
 //   * PV: lane l owns D/64 output dims and accumulates p_t * v_t[d] in fp32
 //     over the tile's tokens in order.
-// Heads: with G = 4 the four waves split each tile by tokens instead
-// (gqa_g4_kernel below); with G = 8 or 16 each of the four waves owns G/4
+// Heads: with G = 4 or 8 the four waves split each tile by tokens instead
+// (gqa_tok_kernel below); with G = 16 each of the four waves owns four
 // heads; with G < 4 the workgroup has G waves of one head each.
 
 #include "device.hpp"
@@ -251,67 +251,70 @@ __global__ void __launch_bounds__(256) gqa_split_kernel(GqaLaunch a) {
   }
 }
 
-// Four query heads per kv head (G = 4): the four waves split each 64-token
-// tile by tokens instead of by heads.  Wave w takes tile rows 16w..16w+15
-// for all four heads, so a tile's K and V rows are each read and converted
-// by one wave only, and every wave keeps its own online-softmax state:
-//   * scores: lane (h, t) = (lane >> 4, lane & 15) scores row 16w + t
-//     against head h (the four lanes of a row read the same K bytes, which
-//     LDS broadcasts);
-//   * softmax: the max of head h over the wave's 16 rows is a 16-lane
-//     butterfly; p = 2^(x - m) in fp32; each lane keeps the normaliser of
-//     its (row slot, head) across tiles;
-//   * PV: lane l owns D/64 dims of all four heads and accumulates
-//     p_t * v_t[d] over the wave's rows in order;
+// Four or eight query heads per kv head (G = 4, 8): the four waves split each
+// 64-token tile by tokens instead of by heads.  Wave w takes tile rows
+// 16w..16w+15 for all G heads, so a tile's K and V rows are each read and
+// converted by one wave only, and every wave keeps its own online-softmax
+// state:
+//   * scores: lane (h, t) = (lane / (64/G), lane % (64/G)) scores rows
+//     16w + (64/G) r + t, r < G/4, against head h (the G lanes of a row read
+//     the same K bytes, which LDS broadcasts);
+//   * softmax: the max of a head over the wave's 16 rows is the max of the
+//     lane's rows, then a butterfly over the head's 64/G lanes; p = 2^(x - m)
+//     in fp32; each lane keeps the normaliser of its head over its rows
+//     (rows in ascending order) across tiles;
+//   * PV: lane l owns D/64 dims of all G heads and accumulates p_t * v_t[d]
+//     over the wave's rows in order;
 //   * end of the split: the four waves' (m, l, acc) are merged in wave order
-//     w = 0..3, o = sum_w 2^(m_w - m) acc_w / sum_w 2^(m_w - m) l_w, head h
-//     by wave h.
+//     w = 0..3, o = sum_w 2^(m_w - m) acc_w / sum_w 2^(m_w - m) l_w; wave w
+//     finishes heads w, w + 4, ...
 // Every order is fixed by the split's own token range.
-template <int D>
-__global__ void __launch_bounds__(256) gqa_g4_kernel(GqaLaunch a) {
+template <int D, int G>
+__global__ void __launch_bounds__(256) gqa_tok_kernel(GqaLaunch a) {
   using S = GqaShape<D>;
   constexpr int DPL = S::kDimsPerLane;
   constexpr int kRowsPerWave = kTile / 4;
-  static_assert(kRowsPerWave == 16, "16 rows of a 64-token tile per wave");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[4 * S::kTileBytes + 4 * kRowsPerWave * 4 * 4];
+  constexpr int kSlots = 64 / G;                    // lanes (row slots) per head
+  constexpr int kRowsPerLane = kRowsPerWave / kSlots;
+  static_assert(kRowsPerWave == 16 && (G == 4 || G == 8), "16 rows of a 64-token tile per wave; G = 4 or 8");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[4 * S::kTileBytes + 4 * kRowsPerWave * G * 4];
   ISK_LDS unsigned char* lds = (ISK_LDS unsigned char*)lds_raw;
   ISK_LDS unsigned char* kbufs = lds;                               // [2][tile]
   ISK_LDS unsigned char* vbufs = lds + 2 * S::kTileBytes;           // [2][tile]
   ISK_LDS float* p_lds = (ISK_LDS float*)(lds + 4 * S::kTileBytes); // [wave][row][head]
   // merge area at the end of a split (the tile buffers are free then)
   ISK_LDS float* mg_acc = (ISK_LDS float*)lds;                      // [wave][head][D]
-  ISK_LDS float* mg_ml = mg_acc + 16 * D;                           // [m | l][wave][head]
-  static_assert(16 * D * 4 + 32 * 4 <= 2 * S::kTileBytes, "merge area within the K buffers");
+  ISK_LDS float* mg_ml = mg_acc + 4 * G * D;                        // [m | l][wave][head]
+  static_assert(4 * G * D * 4 + 8 * G * 4 <= 2 * S::kTileBytes, "merge area within the K buffers");
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hh = lane >> 4, tr = lane & 15;           // score lane: head, row slot
-  const int row = kRowsPerWave * wave + tr;           // tile row this lane scores
+  const int hh = lane / kSlots, tr = lane % kSlots;   // score lane: head, row slot
   const int hk = blockIdx.y;
   const int task = blockIdx.x;
   const bool inl = a.inl.n_segs > 0;
   const int seg_first = inl ? task : a.groups[task], seg_last = inl ? task + 1 : a.groups[task + 1];
-  ISK_LDS float* my_p = p_lds + wave * kRowsPerWave * 4;
+  ISK_LDS float* my_p = p_lds + wave * kRowsPerWave * G;
 
   for (int si = seg_first; si < seg_last; ++si) {
     const Seg sg = fetch_seg(a.inl, a.segs, a.lens, si);
     const int b = sg.row;
     __syncthreads();   // LDS of the previous segment is no longer read
 
-    // q of head 4 hk + hh as packed bf16 pairs (the 16 lanes of a head load
-    // the same row)
+    // q of head G hk + hh as packed bf16 pairs (the lanes of a head load the
+    // same row)
     uint32_t qv[D / 2];
     {
-      const uint4* qrow = (const uint4*)(a.q + ((size_t)b * a.hq + 4 * hk + hh) * D);
+      const uint4* qrow = (const uint4*)(a.q + ((size_t)b * a.hq + G * hk + hh) * D);
 #pragma unroll
       for (int c = 0; c < D / 8; ++c) {
         const uint4 w = qrow[c];
         qv[4 * c + 0] = w.x; qv[4 * c + 1] = w.y; qv[4 * c + 2] = w.z; qv[4 * c + 3] = w.w;
       }
     }
-    float m_mine = -INFINITY, l_lane = 0.f;   // running max and normaliser of head hh (this lane's slot)
-    float acc[4][DPL];
+    float m_mine = -INFINITY, l_lane = 0.f;   // running max and normaliser of head hh (this lane's rows)
+    float acc[G][DPL];
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int j = 0; j < DPL; ++j) acc[h][j] = 0.f;
 
@@ -329,10 +332,14 @@ __global__ void __launch_bounds__(256) gqa_g4_kernel(GqaLaunch a) {
         mask_next = gqa_stage<D>(a, b, hk, sg.begin + (it + 1) * kTile, sg.end, kbufs + (cur ^ 1) * S::kTileBytes,
                                  vbufs + (cur ^ 1) * S::kTileBytes, wave, 4, lane);
 
-      // ---- score of (row, head hh)
-      float sc = 0.f;
-      {
+      // ---- scores of (rows of this lane, head hh), log2 domain
+      float x[kRowsPerLane];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < kRowsPerLane; ++r) {
+        const int row = kRowsPerWave * wave + kSlots * r + tr;
         const ISK_LDS unsigned char* krow = K + row * (D * 2);
+        float sc = 0.f;
 #pragma unroll
         for (int c = 0; c < S::kPieces; ++c) {
           const u32x4 kp = *(const ISK_LDS u32x4*)(krow + ((c ^ (row & 7)) * 16));
@@ -341,24 +348,28 @@ __global__ void __launch_bounds__(256) gqa_g4_kernel(GqaLaunch a) {
           sc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[4 * c + 2]), as_bf16x2(kp[2]), sc, false);
           sc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[4 * c + 3]), as_bf16x2(kp[3]), sc, false);
         }
+        x[r] = (mask >> row) & 1ull ? sc * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[r]);
       }
-      // ---- softmax of head hh over the wave's rows (log2 domain)
-      const bool valid = (mask >> row) & 1ull;
-      const float x = valid ? sc * a.scale_log2 : -INFINITY;
-      float mx = x;
+      // ---- softmax of head hh over the wave's rows
 #pragma unroll
-      for (int sh = 1; sh < kRowsPerWave; sh <<= 1) mx = wave_max_xor(mx, sh);
+      for (int sh = 1; sh < kSlots; sh <<= 1) mx = wave_max_xor(mx, sh);
       const float m_new = fmaxf(m_mine, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m_mine - m_use);
       m_mine = m_new;
-      const float p = fast_exp2(x - m_use);
-      l_lane = l_lane * alpha + p;
-      my_p[tr * 4 + hh] = p;
-      // every head's alpha, from lane 16 h (uniform within the head's lanes)
+      float psum = 0.f;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float al = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 16 * h));
+      for (int r = 0; r < kRowsPerLane; ++r) {
+        const float p = fast_exp2(x[r] - m_use);
+        psum += p;
+        my_p[(kSlots * r + tr) * G + hh] = p;
+      }
+      l_lane = l_lane * alpha + psum;
+      // every head's alpha, from its first lane (uniform within the head's lanes)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float al = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), kSlots * h));
 #pragma unroll
         for (int j = 0; j < DPL; ++j) acc[h][j] *= al;
       }
@@ -374,79 +385,84 @@ __global__ void __launch_bounds__(256) gqa_g4_kernel(GqaLaunch a) {
 #pragma unroll
         for (int u = 0; u < kRowsPerWave; ++u) {
           const int t = kRowsPerWave * wave + u;
-          const f32x4 pw = *(const ISK_LDS f32x4*)(my_p + u * 4);
+          f32x4 pw[G / 4];
+#pragma unroll
+          for (int c = 0; c < G / 4; ++c) pw[c] = *(const ISK_LDS f32x4*)(my_p + u * G + 4 * c);
           const ISK_LDS unsigned char* vp = V + t * (D * 2) + ((vpiece ^ (t & 7)) * 16) + vin;
           if constexpr (DPL == 2) {
             const uint32_t w = *(const ISK_LDS uint32_t*)vp;
             const float v0 = bf16_lo(w), v1 = bf16_hi(w);
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              acc[h][0] = fmaf(pw[h], v0, acc[h][0]);
-              acc[h][1] = fmaf(pw[h], v1, acc[h][1]);
+            for (int h = 0; h < G; ++h) {
+              acc[h][0] = fmaf(pw[h >> 2][h & 3], v0, acc[h][0]);
+              acc[h][1] = fmaf(pw[h >> 2][h & 3], v1, acc[h][1]);
             }
           } else {
             const float v0 = __uint_as_float((uint32_t)(*(const ISK_LDS uint16_t*)vp) << 16);
 #pragma unroll
-            for (int h = 0; h < 4; ++h) acc[h][0] = fmaf(pw[h], v0, acc[h][0]);
+            for (int h = 0; h < G; ++h) acc[h][0] = fmaf(pw[h >> 2][h & 3], v0, acc[h][0]);
           }
         }
       }
     }
 
-    // ---- merge of the four waves' states, head h by wave h
+    // ---- merge of the four waves' states; wave w finishes heads w, w + 4, ...
     float l_h = l_lane;
 #pragma unroll
-    for (int sh = 1; sh < kRowsPerWave; sh <<= 1) l_h = wave_add_xor(l_h, sh);
+    for (int sh = 1; sh < kSlots; sh <<= 1) l_h = wave_add_xor(l_h, sh);
     __syncthreads();   // every wave is done with the tile buffers
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) mg_acc[(wave * 4 + h) * D + DPL * lane + j] = acc[h][j];
+      for (int j = 0; j < DPL; ++j) mg_acc[(wave * G + h) * D + DPL * lane + j] = acc[h][j];
     if (tr == 0) {
-      mg_ml[wave * 4 + hh] = m_mine;
-      mg_ml[16 + wave * 4 + hh] = l_h;
+      mg_ml[wave * G + hh] = m_mine;
+      mg_ml[4 * G + wave * G + hh] = l_h;
     }
     __syncthreads();
-    const int h = wave, head = 4 * hk + h;
-    float m = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) m = fmaxf(m, mg_ml[w * 4 + h]);
-    float l_tot = 0.f, o[DPL];
+    for (int c = 0; c < G / 4; ++c) {
+      const int h = wave + 4 * c, head = G * hk + h;
+      float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) o[j] = 0.f;
+      for (int w = 0; w < 4; ++w) m = fmaxf(m, mg_ml[w * G + h]);
+      float l_tot = 0.f, o[DPL];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = mg_ml[w * 4 + h];
-      const float sw = mw == -INFINITY ? 0.f : fast_exp2(mw - m);
-      l_tot = fmaf(sw, mg_ml[16 + w * 4 + h], l_tot);
+      for (int j = 0; j < DPL; ++j) o[j] = 0.f;
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) o[j] = fmaf(sw, mg_acc[(w * 4 + h) * D + DPL * lane + j], o[j]);
-    }
-    const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : 1.f / l_tot;
-    const float lse_v = empty ? -INFINITY : (m + fast_log2(l_tot)) * kLn2;
+      for (int w = 0; w < 4; ++w) {
+        const float mw = mg_ml[w * G + h];
+        const float sw = mw == -INFINITY ? 0.f : fast_exp2(mw - m);
+        l_tot = fmaf(sw, mg_ml[4 * G + w * G + h], l_tot);
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) o[j] *= inv;
-    if (sg.part >= 0) {
-      float* po = a.part_o + ((size_t)sg.part * a.hq + head) * D + DPL * lane;
-      if constexpr (DPL == 2) *(f32x2*)po = f32x2{o[0], o[1]};
-      else po[0] = o[0];
-      if (lane == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
-    } else {
-      const size_t ob = ((size_t)b * a.hq + head) * D + DPL * lane;
-      if (a.out_f32) {
-        float* op = (float*)a.out + ob;
-        if constexpr (DPL == 2) *(f32x2*)op = f32x2{o[0], o[1]};
-        else op[0] = o[0];
-      } else {
-        uint16_t* op = (uint16_t*)a.out + ob;
-        if constexpr (DPL == 2) {
-          *(uint32_t*)op = pack_bf16x2(o[0], o[1]);
-        } else {
-          op[0] = (uint16_t)(pack_bf16x2(o[0], 0.f) & 0xffffu);
-        }
+        for (int j = 0; j < DPL; ++j) o[j] = fmaf(sw, mg_acc[(w * G + h) * D + DPL * lane + j], o[j]);
       }
-      if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
+      const bool empty = !(l_tot > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_tot;
+      const float lse_v = empty ? -INFINITY : (m + fast_log2(l_tot)) * kLn2;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[j] *= inv;
+      if (sg.part >= 0) {
+        float* po = a.part_o + ((size_t)sg.part * a.hq + head) * D + DPL * lane;
+        if constexpr (DPL == 2) *(f32x2*)po = f32x2{o[0], o[1]};
+        else po[0] = o[0];
+        if (lane == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
+      } else {
+        const size_t ob = ((size_t)b * a.hq + head) * D + DPL * lane;
+        if (a.out_f32) {
+          float* op = (float*)a.out + ob;
+          if constexpr (DPL == 2) *(f32x2*)op = f32x2{o[0], o[1]};
+          else op[0] = o[0];
+        } else {
+          uint16_t* op = (uint16_t*)a.out + ob;
+          if constexpr (DPL == 2) {
+            *(uint32_t*)op = pack_bf16x2(o[0], o[1]);
+          } else {
+            op[0] = (uint16_t)(pack_bf16x2(o[0], 0.f) & 0xffffu);
+          }
+        }
+        if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
+      }
     }
   }
 }
@@ -458,8 +474,8 @@ hipError_t launch_d(const GqaLaunch& a, hipStream_t s, const LaunchEvents& ev) {
   switch (g) {
     case 1: return launch_one(gqa_split_kernel<D, 1>, grid, dim3(64), s, a, ev);
     case 2: return launch_one(gqa_split_kernel<D, 1>, grid, dim3(128), s, a, ev);
-    case 4: return launch_one(gqa_g4_kernel<D>, grid, dim3(256), s, a, ev);
-    case 8: return launch_one(gqa_split_kernel<D, 2>, grid, dim3(256), s, a, ev);
+    case 4: return launch_one(gqa_tok_kernel<D, 4>, grid, dim3(256), s, a, ev);
+    case 8: return launch_one(gqa_tok_kernel<D, 8>, grid, dim3(256), s, a, ev);
     case 16: return launch_one(gqa_split_kernel<D, 4>, grid, dim3(256), s, a, ev);
     default: return hipErrorInvalidValue;
   }

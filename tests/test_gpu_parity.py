@@ -75,7 +75,7 @@ def test_balanced_mode_parity(mode):
 EDGE_LENS = [0, 1, 2, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 2100]
 
 
-@pytest.mark.parametrize("g,d", [(4, 128), (1, 64), (2, 128), (8, 64), (16, 128)])
+@pytest.mark.parametrize("g,d", [(4, 128), (1, 64), (2, 128), (8, 64), (8, 128), (16, 128)])
 def test_gqa_edges_and_group_sizes(g, d):
     hkv = 2
     case = synth.gqa_case(EDGE_LENS, g * hkv, hkv, d, 1.0 / math.sqrt(d), 16, structure_seed=30 + g)
