@@ -14,6 +14,9 @@
 //     direct loads, double buffered.  Piece c (8 dims) of tile row t is stored
 //     at piece (c ^ (t & 7)) of that row, so that 8 lanes reading the same
 //     column of 8 consecutive rows hit distinct banks.
+// Two layouts share that staging.  With G = 4, 8 or 16 the four waves split
+// each tile by tokens (gqa_tok_kernel, described there).  With G < 4
+// (gqa_split_kernel) the workgroup has G waves of one head each:
 //   * Scores: lane t owns token t of the tile and accumulates the dot product
 //     with packed bf16 pairs (v_dot2_f32_bf16, fp32 accumulate), in a fixed
 //     dimension order.
@@ -22,9 +25,6 @@
 //     butterfly at the end of the segment.
 //   * PV: lane l owns D/64 output dims and accumulates p_t * v_t[d] in fp32
 //     over the tile's tokens in order.
-// Heads: with G = 4 or 8 the four waves split each tile by tokens instead
-// (gqa_tok_kernel below); with G = 16 each of the four waves owns four
-// heads; with G < 4 the workgroup has G waves of one head each.
 
 #include "device.hpp"
 #include "isk_internal.hpp"
@@ -77,9 +77,11 @@ __device__ __forceinline__ uint64_t gqa_stage(const GqaLaunch& a, int b, int hk,
   return mask;
 }
 
-template <int D, int HPW>
+// One or two query heads per kv head (G < 4): G waves of one head each.
+template <int D>
 __global__ void __launch_bounds__(256) gqa_split_kernel(GqaLaunch a) {
   using S = GqaShape<D>;
+  constexpr int HPW = 1;   // heads per wave
   constexpr int DPL = S::kDimsPerLane;
   __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[4 * S::kTileBytes + 4 * HPW * kTile * 4];
   ISK_LDS unsigned char* lds = (ISK_LDS unsigned char*)lds_raw;
@@ -251,8 +253,8 @@ __global__ void __launch_bounds__(256) gqa_split_kernel(GqaLaunch a) {
   }
 }
 
-// Four or eight query heads per kv head (G = 4, 8): the four waves split each
-// 64-token tile by tokens instead of by heads.  Wave w takes tile rows
+// Four, eight or sixteen query heads per kv head (G = 4, 8, 16): the four
+// waves split each 64-token tile by tokens instead of by heads.  Wave w takes tile rows
 // 16w..16w+15 for all G heads, so a tile's K and V rows are each read and
 // converted by one wave only, and every wave keeps its own online-softmax
 // state:
@@ -276,7 +278,7 @@ __global__ void __launch_bounds__(256) gqa_tok_kernel(GqaLaunch a) {
   constexpr int kRowsPerWave = kTile / 4;
   constexpr int kSlots = 64 / G;                    // lanes (row slots) per head
   constexpr int kRowsPerLane = kRowsPerWave / kSlots;
-  static_assert(kRowsPerWave == 16 && (G == 4 || G == 8), "16 rows of a 64-token tile per wave; G = 4 or 8");
+  static_assert(kRowsPerWave == 16 && (G == 4 || G == 8 || G == 16), "16 rows of a 64-token tile per wave; G = 4, 8, 16");
   __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[4 * S::kTileBytes + 4 * kRowsPerWave * G * 4];
   ISK_LDS unsigned char* lds = (ISK_LDS unsigned char*)lds_raw;
   ISK_LDS unsigned char* kbufs = lds;                               // [2][tile]
@@ -285,7 +287,7 @@ __global__ void __launch_bounds__(256) gqa_tok_kernel(GqaLaunch a) {
   // merge area at the end of a split (the tile buffers are free then)
   ISK_LDS float* mg_acc = (ISK_LDS float*)lds;                      // [wave][head][D]
   ISK_LDS float* mg_ml = mg_acc + 4 * G * D;                        // [m | l][wave][head]
-  static_assert(4 * G * D * 4 + 8 * G * 4 <= 2 * S::kTileBytes, "merge area within the K buffers");
+  static_assert(4 * G * D * 4 + 8 * G * 4 <= 4 * S::kTileBytes, "merge area within the tile buffers");
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hh = lane / kSlots, tr = lane % kSlots;   // score lane: head, row slot
@@ -472,11 +474,11 @@ hipError_t launch_d(const GqaLaunch& a, hipStream_t s, const LaunchEvents& ev) {
   const int g = a.hq / a.hkv;
   const dim3 grid(a.n_groups, a.hkv);
   switch (g) {
-    case 1: return launch_one(gqa_split_kernel<D, 1>, grid, dim3(64), s, a, ev);
-    case 2: return launch_one(gqa_split_kernel<D, 1>, grid, dim3(128), s, a, ev);
+    case 1: return launch_one(gqa_split_kernel<D>, grid, dim3(64), s, a, ev);
+    case 2: return launch_one(gqa_split_kernel<D>, grid, dim3(128), s, a, ev);
     case 4: return launch_one(gqa_tok_kernel<D, 4>, grid, dim3(256), s, a, ev);
     case 8: return launch_one(gqa_tok_kernel<D, 8>, grid, dim3(256), s, a, ev);
-    case 16: return launch_one(gqa_split_kernel<D, 4>, grid, dim3(256), s, a, ev);
+    case 16: return launch_one(gqa_tok_kernel<D, 16>, grid, dim3(256), s, a, ev);
     default: return hipErrorInvalidValue;
   }
 }
