@@ -349,11 +349,11 @@ const char* isk_last_error(void) { return g_err.c_str(); }
 const char* isk_numerics_id(void) {
   static const std::string id = [] {
     std::ostringstream s;
-    s << "isk-1 arch=gfx950"
+    s << "isk-2 arch=gfx950"
       << " gqa_tile=" << isk::kGqaTile
       << " split_gqa=" << isk::kGqaSplitDefault << " split_mla=" << isk::kMlaSplitDefault
       << " split_topk=" << isk::kSparseSplitDefault
-      << " gqa=vdot2-bf16/fp32-pv"
+      << " gqa=vdot2-bf16/fp32-pv(g>=4:4-wave-token-split,wave-order-merge)"
       << " mla(hq%128=0)=qk:mfma32x32x16-bf16/pv:mfma32x32x16-f16(p-fp16-rne-x2^7,v-bf16-to-fp16-rtz)/tile32/rescale-thr8"
       << "/partials-fp16-rne(bf16-out)"
       << " mla(other)=mfma16x16x32-bf16/tile64/p-hi+lo-bf16/rescale-thr8 combine=fixed-order-fp32"
