@@ -21,11 +21,16 @@ max exceeds it by more than 2^8).  Every order is fixed by the segment's own
 token range.  What differs is the schedule:
   * step it computes S^T of tile it+1 and, in the shadows of those MFMAs,
     the exponentials, fp16 P and row sums of tile it, the vote on the
-    rescale of tile it and the loads of tile it+3;
+    rescale of tile it and the loads of tile it+3; as its last four MFMAs
+    free the K operand slots, the V^T (dt, 1) fragments of tile it are read
+    into them and stay in flight across the barrier;
   * PV of tile it runs j-major (each P fragment is read from LDS once per
-    wave, this wave's own fragment straight from registers) and carries the
-    row max and reference move of tile it+1, so the alphas of tile it+1 are
-    in LDS before the next step starts and the vote never waits;
+    wave, into one of four slots, this wave's own fragment straight from
+    registers) and carries the row max and reference move of tile it+1, so
+    the alphas of tile it+1 are in LDS before the next step starts and the
+    vote never waits;
+  * hooks are placed by their measured issue cost in an MFMA's shadow
+    (ins_cost), at most four vector-ALU units per MFMA;
   * masked rows (past the split's end, or a whole tile whose page is not in
     the pool) are streamed from a valid page and then cleared in LDS, so
     every tile load takes the same scalar-base form.
@@ -46,7 +51,8 @@ Registers (one wave per SIMD, 256 VGPRs + 256 AGPRs):
   a0..a255   output block O^T; tile T = 4 dt + g holds dims 32 dt.. of the
              wave's 128 and head tile (g + wave) & 3
   v0..v143   query slice of the wave's 32 heads (36 B operands)
-  v144..v175 two score blocks (current tile, next tile)
+  v144..v175 two score blocks (current tile, next tile); during PV the
+             upper half of the current tile's block holds two P^T slots
   v176..v191 V^T fragments (dt, j=0), fp16
   v192..v207 V^T fragments (dt, j=1); during S^T the K operand ring
   v208..v215 two P^T fragment slots; during S^T the vote's alphas
