@@ -87,11 +87,21 @@ def test_cold_and_warm_cache_give_the_same_bits():
     assert np.array_equal(warm_b, warm2_b)
 
 
-@pytest.mark.parametrize("which", ["config1", "config2", "config3", "config4", "config4_extra"])
+GQA_GROUP_LENS = [1, 17, 64, 65, 500, 511, 512, 513, 1300, 2047, 3000, 4100]
+
+
+def gqa_group_case(g, d):
+    """GQA rows across split and tile edges with G query heads per kv head
+    (the token-split kernel's G = 8 and 16 layouts)."""
+    return synth.gqa_case(GQA_GROUP_LENS, 2 * g, 2, d, 1.0 / math.sqrt(d), 16, structure_seed=60 + g)
+
+
+@pytest.mark.parametrize("which", ["config1", "config2", "config3", "config4", "config4_extra", "gqa_g8", "gqa_g16"])
 def test_every_row_solo_equals_batched(which):
     case = {"config1": synth.config1_gqa_tiny, "config2": synth.config2_gqa,
             "config3": synth.config3_mla, "config4": synth.config4_sparse,
-            "config4_extra": synth.config4_sparse_extra}[which]()
+            "config4_extra": synth.config4_sparse_extra,
+            "gqa_g8": lambda: gqa_group_case(8, 128), "gqa_g16": lambda: gqa_group_case(16, 64)}[which]()
     _, _, bits, lbits = run_bits(case)
     mism = []
     for b in range(case.batch):
