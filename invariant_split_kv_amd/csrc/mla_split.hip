@@ -156,16 +156,21 @@ constexpr float kRescaleThreshold = 8.0f;
 // Prefetch distance (in MFMA steps) of the V^T operand reads.
 constexpr int kVDepth = 4;
 
-// Heads: each wave owns 16 query heads; a workgroup of up to four waves (one
-// per SIMD) owns up to 64 heads.  With more heads the split runs as several
-// workgroups ("head blocks") that read the same KV tiles; their block ids are
-// g + 8*hb so that they land on the same XCD (workgroups are dealt to the 8
-// XCDs round-robin by id) one right after the other and the second read of a
-// tile is served by that XCD's L2.
+// Heads: each wave computes the scores and softmax of 16 query heads; a
+// workgroup of up to four waves (one per SIMD) owns up to 64 heads.  With
+// fewer than 64 heads (16 or 32) the four waves still run, KDS = 64 / Hq
+// waves per head group: they compute the same scores and softmax (the same
+// operations, so the same bits) and split the 32 output dim tiles between
+// them, each doing 32 / KDS of the PV product.  With more than 64 heads the
+// split runs as several workgroups ("head blocks") that read the same KV
+// tiles; their block ids are g + 8*hb so that they land on the same XCD
+// (workgroups are dealt to the 8 XCDs round-robin by id) one right after the
+// other and the second read of a tile is served by that XCD's L2.
 constexpr int kH2 = 1;
 
-template <bool kSparse>
+template <bool kSparse, int KDS>
 __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
+  constexpr int kNt = kDvTiles / KDS;   // output dim tiles of this wave
   __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[2 * kTileBytes];
   ISK_LDS unsigned char* lds = (ISK_LDS unsigned char*)lds_raw;
 
@@ -173,12 +178,14 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
   const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int i16 = lane & 15, g16 = lane >> 4;
   // block id -> (task g, head block hb); see the comment above the kernel.
-  const int n_hb = a.hq / (nw * 16);
+  const int n_groups16 = nw / KDS;   // head groups of 16 in this workgroup
+  const int n_hb = a.hq / (n_groups16 * 16);
   const int bid = blockIdx.x;
   const int g = (bid / (8 * n_hb)) * 8 + (bid & 7);
   const int hb = (bid >> 3) % n_hb;
   if (g >= a.n_groups) return;
-  const int head0 = hb * nw * 16 + wave * 16 + i16;
+  const int hg = wave % n_groups16, dpart = wave / n_groups16;   // head group, part of the dims
+  const int head0 = hb * n_groups16 * 16 + hg * 16 + i16;
   const bool inl = a.inl.n_segs > 0;   // segments by value: one per task
   const int seg_first = inl ? g : a.groups[g], seg_last = inl ? g + 1 : a.groups[g + 1];
   const unsigned char* kv = (const unsigned char*)a.kv;
@@ -200,7 +207,7 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       v_lane_off[m] = kRowBytes * (8 * g16 + ts) + 64 * (((m >> 1) & 1) ^ (ts >> 1)) + 32 * ((m & 1) ^ (g16 >> 1)) +
-                      16 * ((q >> 1) ^ (g16 & 1)) + 8 * (q & 1);
+                      16 * ((q >> 1) ^ (g16 & 1)) + 8 * (q & 1) + 128 * (kNt / 4) * dpart;
   }
   StageOffsets so;
   if (nw == 4) so.init(wave, lane);
@@ -209,8 +216,10 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
   auto k_tile_off = [](int tau, int kk) {
     return kRowBytes * (32 * (tau >> 1) + 4 * (tau & 1)) + 128 * (kk >> 1);
   };
+  // step j: k-step kap = j / kNt, this wave's dim tile nt = j % kNt (dim
+  // tile kNt*dpart + nt of the row; its part of the offset is in v_lane_off)
   auto v_read = [&](const ISK_LDS unsigned char* T, int j, s16x4* dst) {
-    const int kap = j / kDvTiles, nt = j % kDvTiles;
+    const int kap = j / kNt, nt = j % kNt;
     const ISK_LDS unsigned char* vb = T + v_lane_off[nt & 3];
     dst[0] = lds_read_tr16(vb + kRowBytes * 32 * kap + 128 * (nt >> 2));
     dst[1] = lds_read_tr16(vb + kRowBytes * (32 * kap + 4) + 128 * (nt >> 2));
@@ -250,13 +259,13 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
     }
 
     float m_ref[kH2], l_run[kH2];
-    f32x4 acc[kH2][kDvTiles];
+    f32x4 acc[kH2][kNt];
 #pragma unroll
     for (int h2 = 0; h2 < kH2; ++h2) {
       m_ref[h2] = -INFINITY;
       l_run[h2] = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < kDvTiles; ++nt) acc[h2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < kNt; ++nt) acc[h2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     const int n_tiles = (sg.end - sg.begin + kMlaTile - 1) / kMlaTile;
@@ -369,22 +378,22 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
 #pragma unroll
         for (int h2 = 0; h2 < kH2; ++h2)
 #pragma unroll
-          for (int nt = 0; nt < kDvTiles; ++nt) acc[h2][nt] *= alpha[h2];
+          for (int nt = 0; nt < kNt; ++nt) acc[h2][nt] *= alpha[h2];
       }
 
       // ---- O^T += V^T * P^T; V^T operand via transposing LDS reads.
       // For k-step kap and dim tile nt, lane (i16, g16) addresses 4 dims of
       // tile rows 32*kap + 8*g16 + (i16 >> 2) (+4 for the second read).
       {
-        // 64 steps (kap, nt); the two transposing reads of step j + kVDepth
+        // 2 kNt steps (kap, nt); the two transposing reads of step j + kVDepth
         // are issued before the MFMAs of step j.
-        constexpr int kSteps = 2 * kDvTiles;
+        constexpr int kSteps = 2 * kNt;
         s16x4 vr[kVDepth][2];
 #pragma unroll
         for (int j = 0; j < kVDepth; ++j) v_read(T, j, vr[j]);
 #pragma unroll
         for (int j = 0; j < kSteps; ++j) {
-          const int kap = j / kDvTiles, nt = j % kDvTiles;
+          const int kap = j / kNt, nt = j % kNt;
           const bf16x8 vf = __builtin_bit_cast(
               bf16x8, __builtin_shufflevector(vr[j % kVDepth][0], vr[j % kVDepth][1], 0, 1, 2, 3, 4, 5, 6, 7));
           if (j + kVDepth < kSteps) v_read(T, j + kVDepth, vr[j % kVDepth]);
@@ -407,21 +416,23 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
       const bool empty = !(l_tot > 0.f);
       const float inv = empty ? 0.f : 1.f / l_tot;
       const float lse_v = empty ? -INFINITY : (m_ref[h2] + fast_log2(l_tot)) * kLn2;
+      // this wave's dims: dim tiles kNt*dpart .. ; the LSE from the first part
+      const int d0 = 16 * kNt * dpart;
       if (sg.part >= 0) {
-        float* po = a.part_o + ((size_t)sg.part * a.hq + head) * kMlaDv + 4 * g16;
+        float* po = a.part_o + ((size_t)sg.part * a.hq + head) * kMlaDv + d0 + 4 * g16;
 #pragma unroll
-        for (int nt = 0; nt < kDvTiles; ++nt) *(f32x4*)(po + 16 * nt) = acc[h2][nt] * inv;
-        if (g16 == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
+        for (int nt = 0; nt < kNt; ++nt) *(f32x4*)(po + 16 * nt) = acc[h2][nt] * inv;
+        if (g16 == 0 && dpart == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
       } else {
-        const size_t ob = ((size_t)b * a.hq + head) * kMlaDv + 4 * g16;
+        const size_t ob = ((size_t)b * a.hq + head) * kMlaDv + d0 + 4 * g16;
         if (a.out_f32) {
           float* o = (float*)a.out + ob;
 #pragma unroll
-          for (int nt = 0; nt < kDvTiles; ++nt) *(f32x4*)(o + 16 * nt) = acc[h2][nt] * inv;
+          for (int nt = 0; nt < kNt; ++nt) *(f32x4*)(o + 16 * nt) = acc[h2][nt] * inv;
         } else {
           uint16_t* o = (uint16_t*)a.out + ob;
 #pragma unroll
-          for (int nt = 0; nt < kDvTiles; ++nt) {
+          for (int nt = 0; nt < kNt; ++nt) {
             const f32x4 r = acc[h2][nt] * inv;
             uint2 w;
             w.x = pack_bf16x2(r[0], r[1]);
@@ -429,7 +440,7 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
             *(uint2*)(o + 16 * nt) = w;
           }
         }
-        if (a.lse != nullptr && g16 == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
+        if (a.lse != nullptr && g16 == 0 && dpart == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
       }
     }
   }
@@ -440,13 +451,22 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaLaunch a) {
 hipError_t launch_mla_split(const MlaLaunch& a, hipStream_t s, const LaunchEvents& ev) {
   if (a.n_groups == 0) return hipSuccess;
   // Heads per workgroup: all of them up to 64, else 64 (hq % 64 == 0 is
-  // checked by the planner).
+  // checked by the planner).  16 and 32 heads run four waves that split the
+  // output dims; 48 heads run three waves.
   const int hw = a.hq <= 64 ? a.hq : 64;
   const int n_hb = a.hq / hw;
   const int n_blocks = ((a.n_groups + 7) / 8) * 8 * n_hb;
-  const dim3 grid(n_blocks), block(hw * 4);
-  if (a.topk_idx != nullptr) return launch_one(mla_split_kernel<true>, grid, block, s, a, ev);
-  return launch_one(mla_split_kernel<false>, grid, block, s, a, ev);
+  const dim3 grid(n_blocks);
+  const bool sp = a.topk_idx != nullptr;
+  if (hw == 16)
+    return sp ? launch_one(mla_split_kernel<true, 4>, grid, dim3(256), s, a, ev)
+              : launch_one(mla_split_kernel<false, 4>, grid, dim3(256), s, a, ev);
+  if (hw == 32)
+    return sp ? launch_one(mla_split_kernel<true, 2>, grid, dim3(256), s, a, ev)
+              : launch_one(mla_split_kernel<false, 2>, grid, dim3(256), s, a, ev);
+  const dim3 block(hw * 4);
+  return sp ? launch_one(mla_split_kernel<true, 1>, grid, block, s, a, ev)
+            : launch_one(mla_split_kernel<false, 1>, grid, block, s, a, ev);
 }
 
 }  // namespace isk

@@ -84,7 +84,7 @@ def test_gqa_edges_and_group_sizes(g, d):
     parity(out, lse, ro, rl, False, f"gqa edges g={g} d={d}")
 
 
-@pytest.mark.parametrize("hq", [128, 256, 64, 16])
+@pytest.mark.parametrize("hq", [128, 256, 64, 48, 32, 16])
 def test_mla_edges_and_head_counts(hq):
     case = synth.mla_case(EDGE_LENS, hq, 1.0 / math.sqrt(192.0), 64, structure_seed=40 + hq)
     out, lse, _, _ = run_case(case, fill=GARBAGE)
