@@ -16,15 +16,15 @@
 //     column of 8 consecutive rows hit distinct banks.
 // Two layouts share that staging.  With G = 4, 8 or 16 the four waves split
 // each tile by tokens (gqa_tok_kernel, described there).  With G < 4
-// (gqa_split_kernel) the workgroup has G waves of one head each:
+// (gqa_split_kernel) 4/G waves take each head and split its output dims:
 //   * Scores: lane t owns token t of the tile and accumulates the dot product
 //     with packed bf16 pairs (v_dot2_f32_bf16, fp32 accumulate), in a fixed
 //     dimension order.
 //   * Softmax per head: wave-wide butterfly max, p = 2^(x - m) in fp32; each
 //     lane keeps a partial normaliser for its token slot, summed by a fixed
 //     butterfly at the end of the segment.
-//   * PV: lane l owns D/64 output dims and accumulates p_t * v_t[d] in fp32
-//     over the tile's tokens in order.
+//   * PV: each lane owns one output dim and accumulates p_t * v_t[d] in
+//     fp32 over the tile's tokens in order.
 
 #include "device.hpp"
 #include "isk_internal.hpp"
@@ -77,56 +77,56 @@ __device__ __forceinline__ uint64_t gqa_stage(const GqaLaunch& a, int b, int hk,
   return mask;
 }
 
-// One or two query heads per kv head (G < 4): G waves of one head each.
-template <int D>
+// One or two query heads per kv head (G < 4): four waves, 4/G of them per
+// head.  The waves of a head compute its scores and softmax with the same
+// operations (so the same bits) and split its D output dims, D/(4/G) each,
+// one dim per lane (lanes past the wave's dims compute a copy of one and do
+// not store it).
+template <int D, int G>
 __global__ void __launch_bounds__(256) gqa_split_kernel(GqaLaunch a) {
   using S = GqaShape<D>;
-  constexpr int HPW = 1;   // heads per wave
-  constexpr int DPL = S::kDimsPerLane;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[4 * S::kTileBytes + 4 * HPW * kTile * 4];
+  constexpr int kParts = 4 / G;        // waves per head
+  constexpr int DW = D / kParts;       // dims of a wave
+  static_assert(G == 1 || G == 2, "one or two heads per kv head");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[4 * S::kTileBytes + 4 * kTile * 4];
   ISK_LDS unsigned char* lds = (ISK_LDS unsigned char*)lds_raw;
   ISK_LDS unsigned char* kbufs = lds;                               // [2][tile]
   ISK_LDS unsigned char* vbufs = lds + 2 * S::kTileBytes;           // [2][tile]
-  ISK_LDS float* p_lds = (ISK_LDS float*)(lds + 4 * S::kTileBytes); // [wave][HPW][64]
+  ISK_LDS float* p_lds = (ISK_LDS float*)(lds + 4 * S::kTileBytes); // [wave][64]
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int g = a.hq / a.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = wave % G, dp = wave / G;   // head of the wave, part of its dims
   const int hk = blockIdx.y;
   const int task = blockIdx.x;
   const bool inl = a.inl.n_segs > 0;   // segments by value: one per task
   const int seg_first = inl ? task : a.groups[task], seg_last = inl ? task + 1 : a.groups[task + 1];
-  ISK_LDS float* my_p = p_lds + wave * HPW * kTile;
+  ISK_LDS float* my_p = p_lds + wave * kTile;
+  // PV: lane owns dim d of the head (a copy of dim dp*DW for lanes >= DW)
+  const bool owner = lane < DW;
+  const int d = dp * DW + (owner ? lane : 0);
+  const int vpiece = d / 8, vin = (d % 8) * 2;
 
   for (int si = seg_first; si < seg_last; ++si) {
     const Seg sg = fetch_seg(a.inl, a.segs, a.lens, si);
     const int b = sg.row;
     __syncthreads();   // LDS tiles of the previous segment are no longer read
 
-    // Query heads of this wave: hk*G + wave*HPW + hh.  q as packed bf16 pairs.
-    uint32_t qv[HPW][D / 2];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const int head = hk * g + wave * HPW + hh;
+    // q of head G hk + h as packed bf16 pairs
+    const int head = hk * G + h;
+    uint32_t qv[D / 2];
+    {
       const uint4* qrow = (const uint4*)(a.q + ((size_t)b * a.hq + head) * D);
 #pragma unroll
       for (int c = 0; c < D / 8; ++c) {
         const uint4 w = qrow[c];
-        qv[hh][4 * c + 0] = w.x; qv[hh][4 * c + 1] = w.y;
-        qv[hh][4 * c + 2] = w.z; qv[hh][4 * c + 3] = w.w;
+        qv[4 * c + 0] = w.x; qv[4 * c + 1] = w.y;
+        qv[4 * c + 2] = w.z; qv[4 * c + 3] = w.w;
       }
     }
-
-    float m_run[HPW], l_lane[HPW], acc[HPW][DPL];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      m_run[hh] = -INFINITY;
-      l_lane[hh] = 0.f;
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) acc[hh][j] = 0.f;
-    }
+    float m_run = -INFINITY, l_lane = 0.f, acc = 0.f;
 
     const int n_tiles = (sg.end - sg.begin + kTile - 1) / kTile;
-    uint64_t mask_next = n_tiles > 0 ? gqa_stage<D>(a, b, hk, sg.begin, sg.end, kbufs, vbufs, wave, nw, lane) : 0ull;
+    uint64_t mask_next = n_tiles > 0 ? gqa_stage<D>(a, b, hk, sg.begin, sg.end, kbufs, vbufs, wave, 4, lane) : 0ull;
 
     for (int it = 0; it < n_tiles; ++it) {
       wait_vmem_all();
@@ -137,118 +137,73 @@ __global__ void __launch_bounds__(256) gqa_split_kernel(GqaLaunch a) {
       ISK_LDS unsigned char* V = vbufs + cur * S::kTileBytes;
       if (it + 1 < n_tiles)
         mask_next = gqa_stage<D>(a, b, hk, sg.begin + (it + 1) * kTile, sg.end, kbufs + (cur ^ 1) * S::kTileBytes,
-                                 vbufs + (cur ^ 1) * S::kTileBytes, wave, nw, lane);
+                                 vbufs + (cur ^ 1) * S::kTileBytes, wave, 4, lane);
 
       // ---- scores: lane = token
-      float sc[HPW];
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) sc[hh] = 0.f;
+      float sc = 0.f;
       {
         const ISK_LDS unsigned char* krow = K + lane * (D * 2);
 #pragma unroll
         for (int c = 0; c < S::kPieces; ++c) {
           const u32x4 kp = *(const ISK_LDS u32x4*)(krow + ((c ^ (lane & 7)) * 16));
-          const uint32_t k0 = kp[0], k1 = kp[1], k2 = kp[2], k3 = kp[3];
-#pragma unroll
-          for (int hh = 0; hh < HPW; ++hh) {
-            float s = sc[hh];
-            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[hh][4 * c + 0]), as_bf16x2(k0), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[hh][4 * c + 1]), as_bf16x2(k1), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[hh][4 * c + 2]), as_bf16x2(k2), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[hh][4 * c + 3]), as_bf16x2(k3), s, false);
-            sc[hh] = s;
-          }
+          sc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[4 * c + 0]), as_bf16x2(kp[0]), sc, false);
+          sc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[4 * c + 1]), as_bf16x2(kp[1]), sc, false);
+          sc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[4 * c + 2]), as_bf16x2(kp[2]), sc, false);
+          sc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[4 * c + 3]), as_bf16x2(kp[3]), sc, false);
         }
       }
 
-      // ---- softmax per head (log2 domain)
+      // ---- softmax of the head (log2 domain)
       const bool valid = (mask >> lane) & 1ull;
+      const float x = valid ? sc * a.scale_log2 : -INFINITY;
+      float mx = x;
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        const float x = valid ? sc[hh] * a.scale_log2 : -INFINITY;
-        float mx = x;
-#pragma unroll
-        for (int sh = 1; sh < 64; sh <<= 1) mx = wave_max_xor(mx, sh);
-        const float m_new = fmaxf(m_run[hh], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[hh] - m_use);
-        m_run[hh] = m_new;
-        const float p = fast_exp2(x - m_use);
-        l_lane[hh] = l_lane[hh] * alpha + p;
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) acc[hh][j] *= alpha;
-        my_p[hh * kTile + lane] = p;
-      }
-      // p of this wave's heads is read back by the same wave only.
+      for (int sh = 1; sh < 64; sh <<= 1) mx = wave_max_xor(mx, sh);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      const float p = fast_exp2(x - m_use);
+      l_lane = l_lane * alpha + p;
+      acc *= alpha;
+      my_p[lane] = p;
+      // p of this wave is read back by the same wave only.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-      // ---- PV: lane owns dims [DPL*lane, DPL*lane + DPL)
-      {
-        const int vpiece = (DPL * lane) / 8;
-        const int vin = (DPL * lane * 2) % 16;
+      // ---- PV: dim d over the tile's tokens in order
 #pragma unroll 4
-        for (int t4 = 0; t4 < kTile; t4 += 4) {
-          f32x4 pw[HPW];
+      for (int t4 = 0; t4 < kTile; t4 += 4) {
+        const f32x4 pw = *(const ISK_LDS f32x4*)(my_p + t4);
 #pragma unroll
-          for (int hh = 0; hh < HPW; ++hh) pw[hh] = *(const ISK_LDS f32x4*)(my_p + hh * kTile + t4);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int t = t4 + u;
-            const ISK_LDS unsigned char* vp = V + t * (D * 2) + ((vpiece ^ (t & 7)) * 16) + vin;
-            if constexpr (DPL == 2) {
-              const uint32_t w = *(const ISK_LDS uint32_t*)vp;
-              const float v0 = bf16_lo(w), v1 = bf16_hi(w);
-#pragma unroll
-              for (int hh = 0; hh < HPW; ++hh) {
-                acc[hh][0] = fmaf(pw[hh][u], v0, acc[hh][0]);
-                acc[hh][1] = fmaf(pw[hh][u], v1, acc[hh][1]);
-              }
-            } else {
-              const float v0 = __uint_as_float((uint32_t)(*(const ISK_LDS uint16_t*)vp) << 16);
-#pragma unroll
-              for (int hh = 0; hh < HPW; ++hh) acc[hh][0] = fmaf(pw[hh][u], v0, acc[hh][0]);
-            }
-          }
+        for (int u = 0; u < 4; ++u) {
+          const int t = t4 + u;
+          const ISK_LDS unsigned char* vp = V + t * (D * 2) + ((vpiece ^ (t & 7)) * 16) + vin;
+          const float v = __uint_as_float((uint32_t)(*(const ISK_LDS uint16_t*)vp) << 16);
+          acc = fmaf(pw[u], v, acc);
         }
       }
     }
 
     // ---- epilogue
+    float l_tot = l_lane;
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const int head = hk * g + wave * HPW + hh;
-      float l_tot = l_lane[hh];
-#pragma unroll
-      for (int sh = 1; sh < 64; sh <<= 1) l_tot = wave_add_xor(l_tot, sh);
-      const bool empty = !(l_tot > 0.f);
-      const float inv = empty ? 0.f : 1.f / l_tot;
-      const float lse_v = empty ? -INFINITY : (m_run[hh] + fast_log2(l_tot)) * kLn2;
-      float o[DPL];
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) o[j] = acc[hh][j] * inv;
-      if (sg.part >= 0) {
-        float* po = a.part_o + ((size_t)sg.part * a.hq + head) * D + DPL * lane;
-        if constexpr (DPL == 2) *(f32x2*)po = f32x2{o[0], o[1]};
-        else po[0] = o[0];
-        if (lane == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
-      } else {
-        const size_t ob = ((size_t)b * a.hq + head) * D + DPL * lane;
-        if (a.out_f32) {
-          float* op = (float*)a.out + ob;
-          if constexpr (DPL == 2) *(f32x2*)op = f32x2{o[0], o[1]};
-          else op[0] = o[0];
-        } else {
-          uint16_t* op = (uint16_t*)a.out + ob;
-          if constexpr (DPL == 2) {
-            *(uint32_t*)op = pack_bf16x2(o[0], o[1]);
-          } else {
-            op[0] = (uint16_t)(pack_bf16x2(o[0], 0.f) & 0xffffu);
-          }
-        }
-        if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
+    for (int sh = 1; sh < 64; sh <<= 1) l_tot = wave_add_xor(l_tot, sh);
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float lse_v = empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
+    const float o = acc * inv;
+    if (sg.part >= 0) {
+      if (owner) a.part_o[((size_t)sg.part * a.hq + head) * D + d] = o;
+      if (lane == 0 && dp == 0) a.part_lse[(size_t)sg.part * a.hq + head] = lse_v;
+    } else {
+      const size_t ob = ((size_t)b * a.hq + head) * D + d;
+      if (owner) {
+        if (a.out_f32) ((float*)a.out)[ob] = o;
+        else ((uint16_t*)a.out)[ob] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xffffu);
       }
+      if (a.lse != nullptr && lane == 0 && dp == 0) a.lse[(size_t)b * a.hq + head] = lse_v;
     }
   }
 }
@@ -474,8 +429,8 @@ hipError_t launch_d(const GqaLaunch& a, hipStream_t s, const LaunchEvents& ev) {
   const int g = a.hq / a.hkv;
   const dim3 grid(a.n_groups, a.hkv);
   switch (g) {
-    case 1: return launch_one(gqa_split_kernel<D>, grid, dim3(64), s, a, ev);
-    case 2: return launch_one(gqa_split_kernel<D>, grid, dim3(128), s, a, ev);
+    case 1: return launch_one(gqa_split_kernel<D, 1>, grid, dim3(256), s, a, ev);
+    case 2: return launch_one(gqa_split_kernel<D, 2>, grid, dim3(256), s, a, ev);
     case 4: return launch_one(gqa_tok_kernel<D, 4>, grid, dim3(256), s, a, ev);
     case 8: return launch_one(gqa_tok_kernel<D, 8>, grid, dim3(256), s, a, ev);
     case 16: return launch_one(gqa_tok_kernel<D, 16>, grid, dim3(256), s, a, ev);
