@@ -11,8 +11,9 @@
 // they compute every output element with the same instructions.
 //   * Rows <= 32 (decode-sized, weight-bandwidth bound): one 16- or 32-row
 //     tile, so the weights are read once.  Rows <= 256: 64-row tiles, which
-//     reuse each weight fragment for four row tiles.  More rows: 128 x 128
-//     tiles staged through LDS (below).
+//     reuse each weight fragment for four row tiles.  More rows: 256 x 128
+//     tiles staged through LDS when K is a multiple of 256, else 128 x 128
+//     tiles (below).
 //   * All take bf16 activations.  The four waves of a workgroup each own a
 //     quarter of K and run v_mfma_f32_16x16x32_bf16 over it in ascending k
 //     from zero; the partial sums are added in wave order,
@@ -217,6 +218,146 @@ __global__ void __launch_bounds__(256) linear_tiled_kernel(LinearLaunch a) {
     }
 }
 
+
+// Large row counts with K a multiple of 256: 256 x 128 output tiles.  Wave
+// (wm, wn) computes rows 128*wm .. +127 and columns 64*wn .. +63 as 8 x 4
+// MFMA tiles, so each 16-byte fragment read from LDS feeds four or eight
+// MFMAs (the 128 x 128 tiles above feed four), which keeps the LDS port
+// below the matrix cores' rate.  K is staged 64 wide through a ring of three
+// 48 KB buffers, two stages in flight while one is consumed.  A staged row
+// is 128 bytes; its eight 16-byte chunks are stored XOR-permuted by the row
+// index (chunk c of row r at slot c ^ (r mod 8)), so the 16 rows that one
+// fragment read touches spread over all banks.  The per-element arithmetic
+// (quarters of K, each a fresh chain in ascending k, added in order) is the
+// same as in the kernels above.
+constexpr int kGM = 256, kGN = 128, kGK = 64;
+constexpr int kGRowBytes = kGK * 2;                          // 128
+constexpr int kGBufBytes = (kGM + kGN) * kGRowBytes;         // 48 KB
+constexpr int kGLoads = kGBufBytes / (256 * 16);             // 12 per thread per stage
+
+// A 16-byte-per-lane global -> LDS load written as inline assembly: issued
+// through the builtin, the compiler's wait insertion falls back to waiting
+// for every LDS read before each use, which would stall the MFMA stream.  It
+// has no vector register outputs (the kernel's own vmcnt waits cover its
+// data) and puts M0, which holds the LDS address, back as it found it.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_off) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(gsrc), "s"(lds_off) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | 0x0F70);
+}
+
+__global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * kGBufBytes];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g16 = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = blockIdx.y * kGM, n0 = blockIdx.x * kGN;
+
+  // Staging: 48 wave-wide 16-byte loads per stage, 12 per wave.  Load
+  // i = wave + 4 j fills LDS bytes [1024 i, 1024 i + 1024) of the buffer,
+  // staged rows 8 i .. 8 i + 7 (rows 0..255: x, 256..383: w); lane L writes
+  // slot L mod 8 of row 8 i + L / 8 and so fetches chunk (L mod 8) ^ (L / 8).
+  // Rows past m or n read the last valid row (their results are not stored).
+  const unsigned char* src[kGLoads];
+  const int chunk = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+  for (int j = 0; j < kGLoads; ++j) {
+    const int r = 8 * (wave + 4 * j) + (lane >> 3);
+    if (j < 8) {
+      const int m = min(m0 + r, a.m - 1);
+      src[j] = (const unsigned char*)(a.x + (size_t)m * a.k) + 16 * chunk;
+    } else {
+      const int n = min(n0 + r - kGM, a.n - 1);
+      src[j] = (const unsigned char*)(a.w + (size_t)n * a.k) + 16 * chunk;
+    }
+  }
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds_base = (uint32_t)(size_t)(ISK_LDS unsigned char*)lds;
+  auto stage = [&](int s, int buf) {
+#pragma unroll
+    for (int j = 0; j < kGLoads; ++j)
+      dma16(src[j] + (size_t)s * kGRowBytes, lds_base + buf * kGBufBytes + 1024 * (wave_s + 4 * j));
+  };
+  // Fragment reads: row 16 t + i16 of a 16-row tile, k chunk 4 h + g16 of
+  // substep h, found at slot (4 h + g16) ^ (i16 mod 8).
+  const int slot0 = 16 * (g16 ^ (i16 & 7)), slot1 = 16 * ((4 + g16) ^ (i16 & 7));
+  const int a_row = (128 * wm + i16) * kGRowBytes, b_row = (kGM + 64 * wn + i16) * kGRowBytes;
+
+  f32x4 acc[8][4], total[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = total[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The two k32 halves of a stage are each one scheduling region: the
+  // four B fragments and the first two A fragments are read, then each
+  // group of four MFMAs (one A fragment against the four B fragments) is
+  // preceded by the read of the A fragment two groups ahead, so that LDS
+  // latency hides behind 128 cycles of MFMAs.
+  const int n_stages = a.k / kGK, per_quarter = n_stages / 4;
+  stage(0, 0);
+  stage(1, 1);
+  int buf = 0, s = 0;
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < per_quarter; ++t, ++s) {
+      if (s + 1 < n_stages) wait_vmem_le<kGLoads>();   // this wave's loads of stage s landed
+      else wait_vmem_le<0>();
+      asm volatile("s_barrier" ::: "memory");   // ... and every wave's; every wave is done with buffer (s + 2) mod 3
+      if (s + 2 < n_stages) stage(s + 2, buf == 0 ? 2 : buf - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const ISK_LDS unsigned char* base = (const ISK_LDS unsigned char*)lds + buf * kGBufBytes;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int slot = h == 0 ? slot0 : slot1;
+        bf16x8 af[8], bf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = *(const ISK_LDS bf16x8*)(base + b_row + 16 * j * kGRowBytes + slot);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af[i] = *(const ISK_LDS bf16x8*)(base + a_row + 16 * i * kGRowBytes + slot);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // DS reads: B0..B3, A0, A1
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // A[i + 2]
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMAs of A[i]
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // MFMAs of A6, A7
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      buf = buf == 2 ? 0 : buf + 1;
+    }
+    // End of quarter q: total = c0, then total + c1, + c2, + c3.
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) total[i][j] = q == 0 ? acc[i][j] : total[i][j] + acc[i][j];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 64 * wn + 16 * j + i16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 128 * wm + 16 * i + 4 * g16 + r;
+        if (m < a.m && n < a.n) a.y[(size_t)m * a.n + n] = total[i][j][r];
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_linear(const LinearLaunch& a, hipStream_t s) {
@@ -227,6 +368,8 @@ hipError_t launch_linear(const LinearLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL(linear_kernel<32>, dim3(a.n / 16, 1), dim3(256), 0, s, a);
   } else if (a.m <= kLinearTiledRows) {
     hipLaunchKernelGGL(linear_kernel<64>, dim3(a.n / 16, (a.m + 63) / 64), dim3(256), 0, s, a);
+  } else if (a.k % 256 == 0) {
+    hipLaunchKernelGGL(linear_big_kernel, dim3((a.n + kGN - 1) / kGN, (a.m + kGM - 1) / kGM), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(linear_tiled_kernel, dim3((a.n + kBN - 1) / kBN, (a.m + kBM - 1) / kBM), dim3(256), 0, s, a);
   }

@@ -1,6 +1,7 @@
 """Batch-invariant linear layer (isk_linear_bf16) on the GPU: parity with the
 fp64 oracle and bit equality of a row across row counts that cross the
-tile-shape switches at 16, 32 and 256 rows.
+tile-shape switches at 16, 32 and 256 rows (above 256 rows: 256 x 128 tiles when
+K is a multiple of 256, 128 x 128 tiles otherwise, so K = 640 covers the latter).
 
 Bar: bf16 x bf16 products are exact in fp32, so the only errors are the
 fp32 additions of the K products; whatever their order, the error of an
@@ -53,7 +54,7 @@ def test_integer_inputs_are_exact(m):
 
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (16, 256, 4096), (17, 96, 2048), (32, 64, 1024), (33, 128, 4096),
                                    (256, 48, 512), (257, 48, 512), (64, 4096, 1024), (300, 256, 1024),
-                                   (1000, 400, 4096)])
+                                   (1000, 400, 4096), (300, 160, 640)])
 def test_linear_parity(m, n, k):
     xb, wb = rows(m, k, 40 + m), rows(n, k, 41, std=0.05)
     y = run(xb, wb).astype(np.float64)
@@ -65,7 +66,7 @@ def test_linear_parity(m, n, k):
     assert np.all(err <= bound)
 
 
-@pytest.mark.parametrize("k", [1024, 4096])
+@pytest.mark.parametrize("k", [640, 1024, 4096])
 def test_row_bits_do_not_depend_on_the_row_count(k):
     n = 256
     wb = rows(n, k, 51, std=0.05)
