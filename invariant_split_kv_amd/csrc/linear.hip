@@ -295,14 +295,33 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = total[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // The two k32 halves of a stage are each one scheduling region: the
-  // four B fragments and the first two A fragments are read, then each
-  // group of four MFMAs (one A fragment against the four B fragments) is
-  // preceded by the read of the A fragment two groups ahead, so that LDS
-  // latency hides behind 128 cycles of MFMAs.
+  // Each k32 half of a stage is eight groups of four MFMAs (one A fragment
+  // against four B fragments), each group its own scheduling region that
+  // also reads the A fragment two groups ahead.  The first half's groups
+  // issue the next-but-one stage's loads, two per group; its last two groups
+  // read the second half's B fragments and first A fragments.  In the
+  // second half, once every read of the stage has landed (after group 5),
+  // the waves barrier -- the next stage is in LDS, this one's buffer is free
+  // -- and its last two groups read the next stage's first fragments, so a
+  // stage starts with no barrier and no read latency.
   const int n_stages = a.k / kGK, per_quarter = n_stages / 4;
+  bf16x8 af[2][8], bf[2][4];
+  auto read_b = [&](const ISK_LDS unsigned char* base, int h, int j) {
+    bf[h][j] = *(const ISK_LDS bf16x8*)(base + b_row + 16 * j * kGRowBytes + (h == 0 ? slot0 : slot1));
+  };
+  auto read_a = [&](const ISK_LDS unsigned char* base, int h, int i) {
+    af[h][i] = *(const ISK_LDS bf16x8*)(base + a_row + 16 * i * kGRowBytes + (h == 0 ? slot0 : slot1));
+  };
   stage(0, 0);
   stage(1, 1);
+  wait_vmem_le<kGLoads>();
+  asm volatile("s_barrier" ::: "memory");
+  {
+    const ISK_LDS unsigned char* base = (const ISK_LDS unsigned char*)lds;
+    for (int j = 0; j < 4; ++j) read_b(base, 0, j);
+    read_a(base, 0, 0);
+    read_a(base, 0, 1);
+  }
   int buf = 0, s = 0;
   for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -310,34 +329,48 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int t = 0; t < per_quarter; ++t, ++s) {
-      if (s + 1 < n_stages) wait_vmem_le<kGLoads>();   // this wave's loads of stage s landed
-      else wait_vmem_le<0>();
-      asm volatile("s_barrier" ::: "memory");   // ... and every wave's; every wave is done with buffer (s + 2) mod 3
-      if (s + 2 < n_stages) stage(s + 2, buf == 0 ? 2 : buf - 1);
-      __builtin_amdgcn_sched_barrier(0);
+      // Stage s + 2 goes to the buffer read in stage s - 1.  The last two
+      // stages load stage n - 1 again into a buffer that is not read again,
+      // so the loop has no branch; the wait after the loop drains them.
+      const int fill = min(s + 2, n_stages - 1);
+      const int fill_buf = buf == 0 ? 2 : buf - 1;
+      const int next_buf = buf == 2 ? 0 : buf + 1;
       const ISK_LDS unsigned char* base = (const ISK_LDS unsigned char*)lds + buf * kGBufBytes;
+      const ISK_LDS unsigned char* next = (const ISK_LDS unsigned char*)lds + next_buf * kGBufBytes;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int slot = h == 0 ? slot0 : slot1;
-        bf16x8 af[8], bf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bf[j] = *(const ISK_LDS bf16x8*)(base + b_row + 16 * j * kGRowBytes + slot);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) af[i] = *(const ISK_LDS bf16x8*)(base + a_row + 16 * i * kGRowBytes + slot);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // DS reads: B0..B3, A0, A1
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // A[i + 2]
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMAs of A[i]
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // MFMAs of A6, A7
+      for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_barrier(0);
+        if (i < 6) {
+          read_a(base, 0, i + 2);
+          dma16(src[2 * i] + (size_t)fill * kGRowBytes, lds_base + fill_buf * kGBufBytes + 1024 * (wave_s + 8 * i));
+          dma16(src[2 * i + 1] + (size_t)fill * kGRowBytes, lds_base + fill_buf * kGBufBytes + 1024 * (wave_s + 8 * i + 4));
+        } else if (i == 6) {
+          read_b(base, 1, 0); read_b(base, 1, 1); read_b(base, 1, 2);
+        } else {
+          read_b(base, 1, 3); read_a(base, 1, 0); read_a(base, 1, 1);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][i], bf[0][j], acc[i][j], 0, 0, 0);
       }
-      buf = buf == 2 ? 0 : buf + 1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < 6) {
+          read_a(base, 1, i + 2);
+        } else if (i == 6) {
+          // Every read of stage s landed (lgkmcnt 0) and this wave's loads of
+          // stage s + 1 too (vmcnt: stage s + 2's may still be in flight).
+          __builtin_amdgcn_s_waitcnt(kGLoads | 0x70);
+          asm volatile("s_barrier" ::: "memory");
+          read_b(next, 0, 0); read_b(next, 0, 1); read_b(next, 0, 2);
+        } else {
+          read_b(next, 0, 3); read_a(next, 0, 0); read_a(next, 0, 1);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][i], bf[1][j], acc[i][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      buf = next_buf;
     }
     // End of quarter q: total = c0, then total + c1, + c2, + c3.
 #pragma unroll
@@ -345,6 +378,7 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) total[i][j] = q == 0 ? acc[i][j] : total[i][j] + acc[i][j];
   }
+  wait_vmem_le<0>();   // no load into this workgroup's LDS outlives it
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
