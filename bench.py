@@ -478,8 +478,9 @@ def rmsnorm_extras(isk, torch, calls=200):
 
 def linear_extras(isk, torch, calls=50):
     """Batch-invariant linear layer at n = k = 7168 (weights 103 MB, bf16):
-    decode-sized rows (1, 8, 32: the 16-row tile shape, bound by the weight
-    read) and 4096 rows (the 64-row shape, bound by the matrix cores)."""
+    decode-sized rows (1, 8: one 16-row tile, bound by the weight read; 32:
+    one 32-row tile, bound by the activation reads from L2) and 4096 rows
+    (256 x 128 LDS-staged tiles, bound by the LDS port and matrix cores)."""
     res = {}
     stream = torch.cuda.current_stream()
     n = k = 7168

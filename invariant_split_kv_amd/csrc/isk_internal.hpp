@@ -229,7 +229,7 @@ hipError_t launch_hbm_gather(const void* src, const int32_t* rows, int n_rows, i
 
 // Batch-invariant linear layer: tile shape chosen by row count, same bits.
 constexpr int kLinearSmallRows = 32;    // up to here: 16-row tiles
-constexpr int kLinearTiledRows = 256;   // up to here: 64-row tiles; above: 256 x 128 (K % 256 == 0) or 128 x 128 LDS tiles
+constexpr int kLinearTiledRows = 64;    // up to here: one 64-row tile; above: 256 x 128 (K % 256 == 0) or 128 x 128 LDS tiles
 struct LinearLaunch {
   const uint16_t* x; const uint16_t* w; float* y;
   int32_t m, n, k;

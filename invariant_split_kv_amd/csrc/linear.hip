@@ -10,10 +10,13 @@
 // speed only.  This library's tile shapes follow that rule and go further:
 // they compute every output element with the same instructions.
 //   * Rows <= 32 (decode-sized, weight-bandwidth bound): one 16- or 32-row
-//     tile, so the weights are read once.  Rows <= 256: 64-row tiles, which
-//     reuse each weight fragment for four row tiles.  More rows: 256 x 128
-//     tiles staged through LDS when K is a multiple of 256, else 128 x 128
-//     tiles (below).
+//     tile, so the weights are read once.  Rows <= 64: one 64-row tile,
+//     which reuses each weight fragment for four row tiles.  More rows:
+//     256 x 128 tiles staged through LDS when K is a multiple of 256, else
+//     128 x 128 tiles (below).  (Every workgroup of the row-tile kernels
+//     re-reads all of its activation rows from L2 for only 16 output
+//     columns, so from 65 rows on the LDS-tiled kernels are faster even
+//     with a single, partly empty block of rows.)
 //   * All take bf16 activations.  The four waves of a workgroup each own a
 //     quarter of K and run v_mfma_f32_16x16x32_bf16 over it in ascending k
 //     from zero; the partial sums are added in wave order,

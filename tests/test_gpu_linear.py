@@ -1,6 +1,6 @@
 """Batch-invariant linear layer (isk_linear_bf16) on the GPU: parity with the
 fp64 oracle and bit equality of a row across row counts that cross the
-tile-shape switches at 16, 32 and 256 rows (above 256 rows: 256 x 128 tiles when
+tile-shape switches at 16, 32 and 64 rows (above 64 rows: 256 x 128 tiles when
 K is a multiple of 256, 128 x 128 tiles otherwise, so K = 640 covers the latter).
 
 Bar: bf16 x bf16 products are exact in fp32, so the only errors are the
@@ -72,7 +72,7 @@ def test_row_bits_do_not_depend_on_the_row_count(k):
     wb = rows(n, k, 51, std=0.05)
     probe = rows(1, k, 52)[0]
     solo = run(probe[None, :], wb)[0]
-    for m in (2, 16, 17, 31, 32, 33, 64, 100, 256, 257, 1000):
+    for m in (2, 16, 17, 31, 32, 33, 64, 65, 100, 256, 257, 1000):
         xb = rows(m, k, 53 + m)
         pos = (5 * m) // 7
         xb[pos] = probe
