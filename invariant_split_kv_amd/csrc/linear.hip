@@ -11,7 +11,9 @@
 // they compute every output element with the same instructions.
 //   * Rows <= 32 (decode-sized, weight-bandwidth bound): one 16- or 32-row
 //     tile, so the weights are read once.  Rows <= 64: one 64-row tile,
-//     which reuses each weight fragment for four row tiles.  More rows:
+//     which reuses each weight fragment for four row tiles.  In these
+//     shapes a wave covers two 16-column fragments, so each activation
+//     fragment feeds two MFMAs.  More rows:
 //     256 x 128 tiles staged through LDS when K is a multiple of 256, else
 //     128 x 128 tiles (below).  (Every workgroup of the row-tile kernels
 //     re-reads all of its activation rows from L2 for only 16 output
@@ -31,18 +33,22 @@
 namespace isk {
 namespace {
 
-template <int TM>
+template <int TM, int NB>
 __global__ void __launch_bounds__(256) linear_kernel(LinearLaunch a) {
   constexpr int T = TM / 16;   // 16-row MFMA tiles per workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g16 = lane >> 4;
-  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * TM;
+  const int n0 = blockIdx.x * 16 * NB, m0 = blockIdx.y * TM;
   const int kq = a.k / 4;      // K range of this wave: [wave * kq, (wave + 1) * kq)
   const size_t kb = (size_t)wave * kq + 8 * g16;
 
   // Operand fragments: lane (i16, g16) holds 8 consecutive k of one row.
-  // A = x rows m0 + 16t + i16, B = w row n0 + i16 (the output column).
-  const bf16x8* wp = (const bf16x8*)(a.w + (size_t)(n0 + i16) * a.k + kb);
+  // A = x rows m0 + 16t + i16, B = w rows n0 + 16u + i16 (the output
+  // columns; NB of them per lane, so each x fragment feeds NB MFMAs).
+  // Columns past n read the last row of w and are not stored.
+  const bf16x8* wp[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) wp[u] = (const bf16x8*)(a.w + (size_t)min(n0 + 16 * u + i16, a.n - 1) * a.k + kb);
   const bf16x8* xp[T];
   bool xok[T];
 #pragma unroll
@@ -52,29 +58,46 @@ __global__ void __launch_bounds__(256) linear_kernel(LinearLaunch a) {
     xp[t] = (const bf16x8*)(a.x + (size_t)(xok[t] ? m : 0) * a.k + kb);
   }
   const bf16x8 zero = {};
-  f32x4 acc[T];
+  f32x4 acc[T][NB];
 #pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int u = 0; u < NB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // k-steps of 32 through a register ring of D steps: step s's fragments are
-  // loaded D steps ahead, so D loads per operand are in flight per wave (the
-  // weight stream is what bounds the few-row shapes).  The MFMA chain itself
-  // still runs over s in ascending order.
+  // loaded D steps ahead, so D loads per operand fragment are in flight per
+  // wave.  Each MFMA chain still runs over s in ascending order.
   constexpr int D = T == 1 ? 8 : (T == 2 ? 4 : 2);
   const int steps = kq / 32;
-  bf16x8 bq[D], aq[T][D];
+  bf16x8 bq[NB][D], aq[T][D];
   // Prologue in the main loop's load order, unconditional (slots past the
   // last step reload it and are never used).
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     const int st = min(j, steps - 1);
-    bq[j] = wp[4 * st];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) bq[u][j] = wp[u][4 * st];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const bf16x8 v = xp[t][4 * st];
       aq[t][j] = xok[t] ? v : zero;
     }
   }
+  auto mfmas = [&](int j) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int u = 0; u < NB; ++u) acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[t][j], bq[u][j], acc[t][u], 0, 0, 0);
+  };
+  auto refill = [&](int j, int st) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) bq[u][j] = wp[u][4 * st];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const bf16x8 v = xp[t][4 * st];
+      aq[t][j] = xok[t] ? v : zero;
+    }
+  };
   // Main loop: every refill is in range, so the body is straight-line code and
   // the loads of one pass stay in flight while the next pass's MFMAs run.
   // (Rows past m read row 0 and are replaced by zeros.)
@@ -82,14 +105,8 @@ __global__ void __launch_bounds__(256) linear_kernel(LinearLaunch a) {
   for (; s0 + 2 * D <= steps; s0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-#pragma unroll
-      for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[t][j], bq[j], acc[t], 0, 0, 0);
-      bq[j] = wp[4 * (s0 + j + D)];
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const bf16x8 v = xp[t][4 * (s0 + j + D)];
-        aq[t][j] = xok[t] ? v : zero;
-      }
+      mfmas(j);
+      refill(j, s0 + j + D);
     }
   }
   // Tail: the last (fewer than 2 D) steps, refilling only in range.
@@ -98,38 +115,38 @@ __global__ void __launch_bounds__(256) linear_kernel(LinearLaunch a) {
     for (int j = 0; j < D; ++j) {
       const int st = s0 + j;
       if (st < steps) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[t][j], bq[j], acc[t], 0, 0, 0);
-        if (st + D < steps) {
-          bq[j] = wp[4 * (st + D)];
-#pragma unroll
-          for (int t = 0; t < T; ++t) aq[t][j] = xok[t] ? xp[t][4 * (st + D)] : zero;
-        }
+        mfmas(j);
+        if (st + D < steps) refill(j, st + D);
       }
     }
   }
 
   // Partial sums of waves 1..3 through LDS; wave 0 adds them in wave order.
-  __shared__ f32x4 part[3][T][64];
+  __shared__ f32x4 part[3][T][NB][64];
   if (wave > 0) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) part[wave - 1][t][lane] = acc[t];
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int u = 0; u < NB; ++u) part[wave - 1][t][u][lane] = acc[t][u];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    f32x4 sum = acc[t];
-    sum = sum + part[0][t][lane];
-    sum = sum + part[1][t][lane];
-    sum = sum + part[2][t][lane];
-    // lane (i16, g16) holds rows m0 + 16t + 4*g16 + r, column n0 + i16
+  for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 16 * t + 4 * g16 + r;
-      if (m < a.m) a.y[(size_t)m * a.n + n0 + i16] = sum[r];
+    for (int u = 0; u < NB; ++u) {
+      f32x4 sum = acc[t][u];
+      sum = sum + part[0][t][u][lane];
+      sum = sum + part[1][t][u][lane];
+      sum = sum + part[2][t][u][lane];
+      // lane (i16, g16) holds rows m0 + 16t + 4*g16 + r, column n0 + 16u + i16
+      const int n = n0 + 16 * u + i16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * t + 4 * g16 + r;
+        if (m < a.m && n < a.n) a.y[(size_t)m * a.n + n] = sum[r];
+      }
     }
-  }
 }
 
 // Large row counts: 128 x 128 output tiles staged through LDS.  Wave
@@ -397,14 +414,20 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
 
 }  // namespace
 
+// Output-column fragments per wave in the row-tile kernels: two, so each
+// activation fragment feeds two MFMAs per row tile and a workgroup covers 32
+// columns.  (One: 32 rows took 39 us at n = k = 7168, bound by the
+// activation re-reads from L2; two: 27 us; four: 40 us, too few
+// workgroups to keep the weight stream busy.)
+constexpr int kNB = 2;
 hipError_t launch_linear(const LinearLaunch& a, hipStream_t s) {
   if (a.m == 0) return hipSuccess;
   if (a.m <= 16) {
-    hipLaunchKernelGGL(linear_kernel<16>, dim3(a.n / 16, 1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((linear_kernel<16, kNB>), dim3((a.n + 16 * kNB - 1) / (16 * kNB), 1), dim3(256), 0, s, a);
   } else if (a.m <= kLinearSmallRows) {
-    hipLaunchKernelGGL(linear_kernel<32>, dim3(a.n / 16, 1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((linear_kernel<32, kNB>), dim3((a.n + 16 * kNB - 1) / (16 * kNB), 1), dim3(256), 0, s, a);
   } else if (a.m <= kLinearTiledRows) {
-    hipLaunchKernelGGL(linear_kernel<64>, dim3(a.n / 16, (a.m + 63) / 64), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((linear_kernel<64, kNB>), dim3((a.n + 16 * kNB - 1) / (16 * kNB), (a.m + 63) / 64), dim3(256), 0, s, a);
   } else if (a.k % 256 == 0) {
     hipLaunchKernelGGL(linear_big_kernel, dim3((a.n + kGN - 1) / kGN, (a.m + kGM - 1) / kGM), dim3(256), 0, s, a);
   } else {

@@ -54,7 +54,7 @@ def test_integer_inputs_are_exact(m):
 
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (16, 256, 4096), (17, 96, 2048), (32, 64, 1024), (33, 128, 4096),
                                    (256, 48, 512), (257, 48, 512), (64, 4096, 1024), (300, 256, 1024),
-                                   (1000, 400, 4096), (300, 160, 640)])
+                                   (1000, 400, 4096), (300, 160, 640), (40, 48, 1024), (9, 80, 512)])
 def test_linear_parity(m, n, k):
     xb, wb = rows(m, k, 40 + m), rows(n, k, 41, std=0.05)
     y = run(xb, wb).astype(np.float64)
