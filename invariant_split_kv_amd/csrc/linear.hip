@@ -13,12 +13,13 @@
 //     tile, so the weights are read once.  Rows <= 64: one 64-row tile,
 //     which reuses each weight fragment for four row tiles.  In these
 //     shapes a wave covers two 16-column fragments, so each activation
-//     fragment feeds two MFMAs.  More rows:
-//     256 x 128 tiles staged through LDS when K is a multiple of 256, else
-//     128 x 128 tiles (below).  (Every workgroup of the row-tile kernels
-//     re-reads all of its activation rows from L2 for only 16 output
-//     columns, so from 65 rows on the LDS-tiled kernels are faster even
-//     with a single, partly empty block of rows.)
+//     fragment feeds two MFMAs.  More rows: tiles staged through LDS --
+//     with K a multiple of 256, 128 x 128 tiles while one round of them
+//     covers the call and 256 x 128 beyond, both with 64-wide K stages;
+//     other K, 128 x 128 tiles with 32-wide K stages (below).  (Every
+//     workgroup of the row-tile kernels re-reads all of its activation rows
+//     from L2 for only 32 output columns, so from 65 rows on the LDS-tiled
+//     kernels are faster even with a single, partly empty block of rows.)
 //   * All take bf16 activations.  The four waves of a workgroup each own a
 //     quarter of K and run v_mfma_f32_16x16x32_bf16 over it in ascending k
 //     from zero; the partial sums are added in wave order,
@@ -239,21 +240,20 @@ __global__ void __launch_bounds__(256) linear_tiled_kernel(LinearLaunch a) {
 }
 
 
-// Large row counts with K a multiple of 256: 256 x 128 output tiles.  Wave
-// (wm, wn) computes rows 128*wm .. +127 and columns 64*wn .. +63 as 8 x 4
-// MFMA tiles, so each 16-byte fragment read from LDS feeds four or eight
-// MFMAs (the 128 x 128 tiles above feed four), which keeps the LDS port
-// below the matrix cores' rate.  K is staged 64 wide through a ring of three
-// 48 KB buffers, two stages in flight while one is consumed.  A staged row
+// Large row counts with K a multiple of 256: kGM x 128 output tiles, kGM =
+// 256 or 128.  Wave (wm, wn) computes rows kGM/2*wm .. +kGM/2-1 and columns
+// 64*wn .. +63 as 8 x 4 (or 4 x 4) MFMA tiles; with 256-row tiles each
+// 16-byte fragment read from LDS feeds four or eight MFMAs (the 128 x 128
+// tiles above feed four), which keeps the LDS port near the matrix cores'
+// rate.  K is staged 64 wide through a ring of three 48 KB (32 KB)
+// buffers, two stages in flight while one is consumed.  A staged row
 // is 128 bytes; its eight 16-byte chunks are stored XOR-permuted by the row
 // index (chunk c of row r at slot c ^ (r mod 8)), so the 16 rows that one
 // fragment read touches spread over all banks.  The per-element arithmetic
 // (quarters of K, each a fresh chain in ascending k, added in order) is the
 // same as in the kernels above.
-constexpr int kGM = 256, kGN = 128, kGK = 64;
+constexpr int kGN = 128, kGK = 64;
 constexpr int kGRowBytes = kGK * 2;                          // 128
-constexpr int kGBufBytes = (kGM + kGN) * kGRowBytes;         // 48 KB
-constexpr int kGLoads = kGBufBytes / (256 * 16);             // 12 per thread per stage
 
 // A 16-byte-per-lane global -> LDS load written as inline assembly: issued
 // through the builtin, the compiler's wait insertion falls back to waiting
@@ -272,7 +272,11 @@ __device__ __forceinline__ void wait_vmem_le() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | 0x0F70);
 }
 
+template <int kGM>
 __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
+  constexpr int kGBufBytes = (kGM + kGN) * kGRowBytes;       // 48 KB (256 rows) or 32 KB (128)
+  constexpr int kGLoads = kGBufBytes / (256 * 16);           // 12 or 8 per thread per stage
+  constexpr int kAT = kGM / 32;                              // A fragments per wave: 8 or 4
   __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * kGBufBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g16 = lane >> 4;
@@ -289,7 +293,7 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
 #pragma unroll
   for (int j = 0; j < kGLoads; ++j) {
     const int r = 8 * (wave + 4 * j) + (lane >> 3);
-    if (j < 8) {
+    if (j < kGM / 32) {
       const int m = min(m0 + r, a.m - 1);
       src[j] = (const unsigned char*)(a.x + (size_t)m * a.k) + 16 * chunk;
     } else {
@@ -307,11 +311,11 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
   // Fragment reads: row 16 t + i16 of a 16-row tile, k chunk 4 h + g16 of
   // substep h, found at slot (4 h + g16) ^ (i16 mod 8).
   const int slot0 = 16 * (g16 ^ (i16 & 7)), slot1 = 16 * ((4 + g16) ^ (i16 & 7));
-  const int a_row = (128 * wm + i16) * kGRowBytes, b_row = (kGM + 64 * wn + i16) * kGRowBytes;
+  const int a_row = (kGM / 2 * wm + i16) * kGRowBytes, b_row = (kGM + 64 * wn + i16) * kGRowBytes;
 
-  f32x4 acc[8][4], total[8][4];
+  f32x4 acc[kAT][4], total[kAT][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kAT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = total[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -325,7 +329,7 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
   // -- and its last two groups read the next stage's first fragments, so a
   // stage starts with no barrier and no read latency.
   const int n_stages = a.k / kGK, per_quarter = n_stages / 4;
-  bf16x8 af[2][8], bf[2][4];
+  bf16x8 af[2][kAT], bf[2][4];
   auto read_b = [&](const ISK_LDS unsigned char* base, int h, int j) {
     bf[h][j] = *(const ISK_LDS bf16x8*)(base + b_row + 16 * j * kGRowBytes + (h == 0 ? slot0 : slot1));
   };
@@ -345,7 +349,7 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
   int buf = 0, s = 0;
   for (int q = 0; q < 4; ++q) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kAT; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int t = 0; t < per_quarter; ++t, ++s) {
@@ -358,32 +362,32 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
       const ISK_LDS unsigned char* base = (const ISK_LDS unsigned char*)lds + buf * kGBufBytes;
       const ISK_LDS unsigned char* next = (const ISK_LDS unsigned char*)lds + next_buf * kGBufBytes;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kAT; ++i) {
         __builtin_amdgcn_sched_barrier(0);
-        if (i < 6) {
-          read_a(base, 0, i + 2);
+        if (i + 2 < kAT) read_a(base, 0, i + 2);
+        if (i < kGLoads / 2) {   // stage s + 2, two loads per MFMA group
           dma16(src[2 * i] + (size_t)fill * kGRowBytes, lds_base + fill_buf * kGBufBytes + 1024 * (wave_s + 8 * i));
           dma16(src[2 * i + 1] + (size_t)fill * kGRowBytes, lds_base + fill_buf * kGBufBytes + 1024 * (wave_s + 8 * i + 4));
-        } else if (i == 6) {
+        }
+        if (i == kAT - 2) {
           read_b(base, 1, 0); read_b(base, 1, 1); read_b(base, 1, 2);
-        } else {
+        } else if (i == kAT - 1) {
           read_b(base, 1, 3); read_a(base, 1, 0); read_a(base, 1, 1);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][i], bf[0][j], acc[i][j], 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kAT; ++i) {
         __builtin_amdgcn_sched_barrier(0);
-        if (i < 6) {
-          read_a(base, 1, i + 2);
-        } else if (i == 6) {
+        if (i + 2 < kAT) read_a(base, 1, i + 2);
+        if (i == kAT - 2) {
           // Every read of stage s landed (lgkmcnt 0) and this wave's loads of
           // stage s + 1 too (vmcnt: stage s + 2's may still be in flight).
           __builtin_amdgcn_s_waitcnt(kGLoads | 0x70);
           asm volatile("s_barrier" ::: "memory");
           read_b(next, 0, 0); read_b(next, 0, 1); read_b(next, 0, 2);
-        } else {
+        } else if (i == kAT - 1) {
           read_b(next, 0, 3); read_a(next, 0, 0); read_a(next, 0, 1);
         }
 #pragma unroll
@@ -394,19 +398,19 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
     }
     // End of quarter q: total = c0, then total + c1, + c2, + c3.
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kAT; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) total[i][j] = q == 0 ? acc[i][j] : total[i][j] + acc[i][j];
   }
   wait_vmem_le<0>();   // no load into this workgroup's LDS outlives it
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kAT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + 64 * wn + 16 * j + i16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 128 * wm + 16 * i + 4 * g16 + r;
+        const int m = m0 + kGM / 2 * wm + 16 * i + 4 * g16 + r;
         if (m < a.m && n < a.n) a.y[(size_t)m * a.n + n] = total[i][j][r];
       }
     }
@@ -429,7 +433,19 @@ hipError_t launch_linear(const LinearLaunch& a, hipStream_t s) {
   } else if (a.m <= kLinearTiledRows) {
     hipLaunchKernelGGL((linear_kernel<64, kNB>), dim3((a.n + 16 * kNB - 1) / (16 * kNB), (a.m + 63) / 64), dim3(256), 0, s, a);
   } else if (a.k % 256 == 0) {
-    hipLaunchKernelGGL(linear_big_kernel, dim3((a.n + kGN - 1) / kGN, (a.m + kGM - 1) / kGM), dim3(256), 0, s, a);
+    // 128-row tiles (waves of 64 x 64) when one round of them covers the
+    // call: they do half the work of a 256-row tile for two thirds of its
+    // LDS traffic; otherwise 256-row tiles, the better ratio at full load.
+    static int cus = 0;
+    if (cus == 0) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    }
+    const long nb = (a.n + kGN - 1) / kGN, mb128 = (a.m + 127) / 128;
+    if (mb128 * nb <= cus)
+      hipLaunchKernelGGL(linear_big_kernel<128>, dim3(nb, mb128), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(linear_big_kernel<256>, dim3(nb, (a.m + 255) / 256), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(linear_tiled_kernel, dim3((a.n + kBN - 1) / kBN, (a.m + kBM - 1) / kBM), dim3(256), 0, s, a);
   }

@@ -1,7 +1,9 @@
 """Batch-invariant linear layer (isk_linear_bf16) on the GPU: parity with the
 fp64 oracle and bit equality of a row across row counts that cross the
-tile-shape switches at 16, 32 and 64 rows (above 64 rows: 256 x 128 tiles when
-K is a multiple of 256, 128 x 128 tiles otherwise, so K = 640 covers the latter).
+tile-shape switches at 16, 32 and 64 rows.  Above 64 rows, with K a multiple of
+256, tiles are 128 x 128 while one round of them covers the call (at most
+256 tiles: n = 4096 and 1100 rows take 256 x 128 tiles) and 256 x 128
+beyond; other K take 128 x 128 tiles with 32-wide K stages (K = 640).
 
 Bar: bf16 x bf16 products are exact in fp32, so the only errors are the
 fp32 additions of the K products; whatever their order, the error of an
@@ -54,7 +56,7 @@ def test_integer_inputs_are_exact(m):
 
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (16, 256, 4096), (17, 96, 2048), (32, 64, 1024), (33, 128, 4096),
                                    (256, 48, 512), (257, 48, 512), (64, 4096, 1024), (300, 256, 1024),
-                                   (1000, 400, 4096), (300, 160, 640), (40, 48, 1024), (9, 80, 512)])
+                                   (1000, 400, 4096), (300, 160, 640), (40, 48, 1024), (9, 80, 512), (1100, 4096, 256)])
 def test_linear_parity(m, n, k):
     xb, wb = rows(m, k, 40 + m), rows(n, k, 41, std=0.05)
     y = run(xb, wb).astype(np.float64)
@@ -75,6 +77,22 @@ def test_row_bits_do_not_depend_on_the_row_count(k):
     for m in (2, 16, 17, 31, 32, 33, 64, 65, 100, 256, 257, 1000):
         xb = rows(m, k, 53 + m)
         pos = (5 * m) // 7
+        xb[pos] = probe
+        y = run(xb, wb)
+        assert np.array_equal(y[pos], solo), f"m={m}: probe row bits differ"
+
+
+def test_row_bits_across_lds_tile_heights():
+    """n = 4096 (32 column blocks): 300 rows take 128-row tiles (96 tiles),
+    1100 rows 256-row tiles (9 x 32 = 288 tiles of 128 rows would not fit
+    one round on 256 CUs); a probe row's bits match its solo run."""
+    n, k = 4096, 256
+    wb = rows(n, k, 61, std=0.05)
+    probe = rows(1, k, 62)[0]
+    solo = run(probe[None, :], wb)[0]
+    for m in (300, 1100):
+        xb = rows(m, k, 63 + m)
+        pos = (3 * m) // 5
         xb[pos] = probe
         y = run(xb, wb)
         assert np.array_equal(y[pos], solo), f"m={m}: probe row bits differ"
