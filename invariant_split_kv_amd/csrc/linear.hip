@@ -244,8 +244,7 @@ __global__ void __launch_bounds__(256) linear_tiled_kernel(LinearLaunch a) {
 // 256 or 128.  Wave (wm, wn) computes rows kGM/2*wm .. +kGM/2-1 and columns
 // 64*wn .. +63 as 8 x 4 (or 4 x 4) MFMA tiles; with 256-row tiles each
 // 16-byte fragment read from LDS feeds four or eight MFMAs (the 128 x 128
-// tiles above feed four), which keeps the LDS port near the matrix cores'
-// rate.  K is staged 64 wide through a ring of three 48 KB (32 KB)
+// tiles above feed four), a third fewer LDS reads per MFMA.  K is staged 64 wide through a ring of three 48 KB (32 KB)
 // buffers, two stages in flight while one is consumed.  A staged row
 // is 128 bytes; its eight 16-byte chunks are stored XOR-permuted by the row
 // index (chunk c of row r at slot c ^ (r mod 8)), so the 16 rows that one
