@@ -422,8 +422,9 @@ ISK_API int isk_rmsnorm(const void* x, const void* w, void* y, int32_t rows, int
  * and "Next steps") traces batch dependence to a kernel switch by row count
  * whose two sides round activations differently.  This entry point also
  * switches tile shapes by row count (one 16- or 32-row tile up to 32 rows,
- * one 64-row tile up to 64, LDS-staged tiles above: 128 x 128 or 256 x 128,
- * by row count, when k is a multiple of 256, else 128 x 128), but every shape takes
+ * one 64-row tile up to 64, LDS-staged tiles above: 128 x 64, 128 x 128 or
+ * 256 x 128 by tile count when k is a multiple of 256, else 128 x 128), but
+ * every shape takes
  * bf16 activations and computes each element with the same arithmetic (K
  * split in four fixed quarters, each an MFMA chain in ascending k from
  * zero, the quarters added in order), so the switch changes speed only: a

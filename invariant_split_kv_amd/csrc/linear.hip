@@ -14,8 +14,8 @@
 //     which reuses each weight fragment for four row tiles.  In these
 //     shapes a wave covers two 16-column fragments, so each activation
 //     fragment feeds two MFMAs.  More rows: tiles staged through LDS --
-//     with K a multiple of 256, 128 x 128 tiles while one round of them
-//     covers the call and 256 x 128 beyond, both with 64-wide K stages;
+//     with K a multiple of 256, the smallest of 128 x 64, 128 x 128 and
+//     256 x 128 whose count fits one round on the CUs, 64-wide K stages;
 //     other K, 128 x 128 tiles with 32-wide K stages (below).  (Every
 //     workgroup of the row-tile kernels re-reads all of its activation rows
 //     from L2 for only 32 output columns, so from 65 rows on the LDS-tiled
@@ -240,9 +240,10 @@ __global__ void __launch_bounds__(256) linear_tiled_kernel(LinearLaunch a) {
 }
 
 
-// Large row counts with K a multiple of 256: kGM x 128 output tiles, kGM =
-// 256 or 128.  Wave (wm, wn) computes rows kGM/2*wm .. +kGM/2-1 and columns
-// 64*wn .. +63 as 8 x 4 (or 4 x 4) MFMA tiles; with 256-row tiles each
+// Large row counts with K a multiple of 256: kGM x kTN output tiles, 256 x
+// 128, 128 x 128 or 128 x 64.  Wave (wm, wn) computes rows kGM/2*wm ..
+// +kGM/2-1 and columns kTN/2*wn .. +kTN/2-1 as 8 x 4, 4 x 4 or 4 x 2 MFMA
+// tiles; with 256-row tiles each
 // 16-byte fragment read from LDS feeds four or eight MFMAs (the 128 x 128
 // tiles above feed four), a third fewer LDS reads per MFMA.  K is staged 64 wide through a ring of three 48 KB (32 KB)
 // buffers, two stages in flight while one is consumed.  A staged row
@@ -271,18 +272,21 @@ __device__ __forceinline__ void wait_vmem_le() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | 0x0F70);
 }
 
-template <int kGM>
+template <int kGM, int kTN>
 __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
-  constexpr int kGBufBytes = (kGM + kGN) * kGRowBytes;       // 48 KB (256 rows) or 32 KB (128)
-  constexpr int kGLoads = kGBufBytes / (256 * 16);           // 12 or 8 per thread per stage
+  constexpr int kGBufBytes = (kGM + kTN) * kGRowBytes;       // 48, 32 or 24 KB
+  constexpr int kGLoads = kGBufBytes / (256 * 16);           // 12, 8 or 6 per thread per stage
   constexpr int kAT = kGM / 32;                              // A fragments per wave: 8 or 4
+  constexpr int kBT = kTN / 32;                              // B fragments per wave: 4 or 2
+  constexpr int kB1 = kBT == 4 ? 3 : kBT;                    // of which read in the first pre-read group
+  static_assert(kGLoads % 2 == 0 && kGLoads / 2 <= kAT && kAT >= 4, "group schedule");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * kGBufBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g16 = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
-  const int m0 = blockIdx.y * kGM, n0 = blockIdx.x * kGN;
+  const int m0 = blockIdx.y * kGM, n0 = blockIdx.x * kTN;
 
-  // Staging: 48 wave-wide 16-byte loads per stage, 12 per wave.  Load
+  // Staging: 4 kGLoads wave-wide 16-byte loads per stage, kGLoads per wave.  Load
   // i = wave + 4 j fills LDS bytes [1024 i, 1024 i + 1024) of the buffer,
   // staged rows 8 i .. 8 i + 7 (rows 0..255: x, 256..383: w); lane L writes
   // slot L mod 8 of row 8 i + L / 8 and so fetches chunk (L mod 8) ^ (L / 8).
@@ -310,13 +314,13 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
   // Fragment reads: row 16 t + i16 of a 16-row tile, k chunk 4 h + g16 of
   // substep h, found at slot (4 h + g16) ^ (i16 mod 8).
   const int slot0 = 16 * (g16 ^ (i16 & 7)), slot1 = 16 * ((4 + g16) ^ (i16 & 7));
-  const int a_row = (kGM / 2 * wm + i16) * kGRowBytes, b_row = (kGM + 64 * wn + i16) * kGRowBytes;
+  const int a_row = (kGM / 2 * wm + i16) * kGRowBytes, b_row = (kGM + kTN / 2 * wn + i16) * kGRowBytes;
 
-  f32x4 acc[kAT][4], total[kAT][4];
+  f32x4 acc[kAT][kBT], total[kAT][kBT];
 #pragma unroll
   for (int i = 0; i < kAT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = total[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kBT; ++j) acc[i][j] = total[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Each k32 half of a stage is eight groups of four MFMAs (one A fragment
   // against four B fragments), each group its own scheduling region that
@@ -328,7 +332,7 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
   // -- and its last two groups read the next stage's first fragments, so a
   // stage starts with no barrier and no read latency.
   const int n_stages = a.k / kGK, per_quarter = n_stages / 4;
-  bf16x8 af[2][kAT], bf[2][4];
+  bf16x8 af[2][kAT], bf[2][kBT];
   auto read_b = [&](const ISK_LDS unsigned char* base, int h, int j) {
     bf[h][j] = *(const ISK_LDS bf16x8*)(base + b_row + 16 * j * kGRowBytes + (h == 0 ? slot0 : slot1));
   };
@@ -341,7 +345,7 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
   asm volatile("s_barrier" ::: "memory");
   {
     const ISK_LDS unsigned char* base = (const ISK_LDS unsigned char*)lds;
-    for (int j = 0; j < 4; ++j) read_b(base, 0, j);
+    for (int j = 0; j < kBT; ++j) read_b(base, 0, j);
     read_a(base, 0, 0);
     read_a(base, 0, 1);
   }
@@ -350,7 +354,7 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
 #pragma unroll
     for (int i = 0; i < kAT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kBT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int t = 0; t < per_quarter; ++t, ++s) {
       // Stage s + 2 goes to the buffer read in stage s - 1.  The last two
       // stages load stage n - 1 again into a buffer that is not read again,
@@ -369,12 +373,13 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
           dma16(src[2 * i + 1] + (size_t)fill * kGRowBytes, lds_base + fill_buf * kGBufBytes + 1024 * (wave_s + 8 * i + 4));
         }
         if (i == kAT - 2) {
-          read_b(base, 1, 0); read_b(base, 1, 1); read_b(base, 1, 2);
+          for (int j = 0; j < kB1; ++j) read_b(base, 1, j);
         } else if (i == kAT - 1) {
-          read_b(base, 1, 3); read_a(base, 1, 0); read_a(base, 1, 1);
+          for (int j = kB1; j < kBT; ++j) read_b(base, 1, j);
+          read_a(base, 1, 0); read_a(base, 1, 1);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][i], bf[0][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < kBT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][i], bf[0][j], acc[i][j], 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < kAT; ++i) {
@@ -385,12 +390,13 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
           // stage s + 1 too (vmcnt: stage s + 2's may still be in flight).
           __builtin_amdgcn_s_waitcnt(kGLoads | 0x70);
           asm volatile("s_barrier" ::: "memory");
-          read_b(next, 0, 0); read_b(next, 0, 1); read_b(next, 0, 2);
+          for (int j = 0; j < kB1; ++j) read_b(next, 0, j);
         } else if (i == kAT - 1) {
-          read_b(next, 0, 3); read_a(next, 0, 0); read_a(next, 0, 1);
+          for (int j = kB1; j < kBT; ++j) read_b(next, 0, j);
+          read_a(next, 0, 0); read_a(next, 0, 1);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][i], bf[1][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < kBT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][i], bf[1][j], acc[i][j], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       buf = next_buf;
@@ -399,14 +405,14 @@ __global__ void __launch_bounds__(256) linear_big_kernel(LinearLaunch a) {
 #pragma unroll
     for (int i = 0; i < kAT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) total[i][j] = q == 0 ? acc[i][j] : total[i][j] + acc[i][j];
+      for (int j = 0; j < kBT; ++j) total[i][j] = q == 0 ? acc[i][j] : total[i][j] + acc[i][j];
   }
   wait_vmem_le<0>();   // no load into this workgroup's LDS outlives it
 #pragma unroll
   for (int i = 0; i < kAT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + 64 * wn + 16 * j + i16;
+    for (int j = 0; j < kBT; ++j) {
+      const int n = n0 + kTN / 2 * wn + 16 * j + i16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + kGM / 2 * wm + 16 * i + 4 * g16 + r;
@@ -432,19 +438,21 @@ hipError_t launch_linear(const LinearLaunch& a, hipStream_t s) {
   } else if (a.m <= kLinearTiledRows) {
     hipLaunchKernelGGL((linear_kernel<64, kNB>), dim3((a.n + 16 * kNB - 1) / (16 * kNB), (a.m + 63) / 64), dim3(256), 0, s, a);
   } else if (a.k % 256 == 0) {
-    // 128-row tiles (waves of 64 x 64) when one round of them covers the
-    // call: they do half the work of a 256-row tile for two thirds of its
-    // LDS traffic; otherwise 256-row tiles, the better ratio at full load.
+    // The smallest tile whose count fits one round on the CUs: 128 x 64,
+    // then 128 x 128 (half and a quarter of a 256 x 128 tile's work); else
+    // 256 x 128 tiles, the best LDS ratio at full load.
     static int cus = 0;
     if (cus == 0) {
       int dev = 0;
       if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     }
-    const long nb = (a.n + kGN - 1) / kGN, mb128 = (a.m + 127) / 128;
-    if (mb128 * nb <= cus)
-      hipLaunchKernelGGL(linear_big_kernel<128>, dim3(nb, mb128), dim3(256), 0, s, a);
+    const long nb = (a.n + kGN - 1) / kGN, nb64 = (a.n + 63) / 64, mb128 = (a.m + 127) / 128;
+    if (mb128 * nb64 <= cus)
+      hipLaunchKernelGGL((linear_big_kernel<128, 64>), dim3(nb64, mb128), dim3(256), 0, s, a);
+    else if (mb128 * nb <= cus)
+      hipLaunchKernelGGL((linear_big_kernel<128, 128>), dim3(nb, mb128), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL(linear_big_kernel<256>, dim3(nb, (a.m + 255) / 256), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((linear_big_kernel<256, 128>), dim3(nb, (a.m + 255) / 256), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(linear_tiled_kernel, dim3((a.n + kBN - 1) / kBN, (a.m + kBM - 1) / kBM), dim3(256), 0, s, a);
   }

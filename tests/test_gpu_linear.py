@@ -1,9 +1,10 @@
 """Batch-invariant linear layer (isk_linear_bf16) on the GPU: parity with the
 fp64 oracle and bit equality of a row across row counts that cross the
 tile-shape switches at 16, 32 and 64 rows.  Above 64 rows, with K a multiple of
-256, tiles are 128 x 128 while one round of them covers the call (at most
-256 tiles: n = 4096 and 1100 rows take 256 x 128 tiles) and 256 x 128
-beyond; other K take 128 x 128 tiles with 32-wide K stages (K = 640).
+256, tiles are the smallest of 128 x 64, 128 x 128 and 256 x 128 whose count
+fits one round on 256 CUs (n = 4096: 300 rows take 128 x 64, 600 rows 128 x 128,
+1100 rows 256 x 128); other K take 128 x 128 tiles with 32-wide K stages
+(K = 640).
 
 Bar: bf16 x bf16 products are exact in fp32, so the only errors are the
 fp32 additions of the K products; whatever their order, the error of an
@@ -56,7 +57,7 @@ def test_integer_inputs_are_exact(m):
 
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (16, 256, 4096), (17, 96, 2048), (32, 64, 1024), (33, 128, 4096),
                                    (256, 48, 512), (257, 48, 512), (64, 4096, 1024), (300, 256, 1024),
-                                   (1000, 400, 4096), (300, 160, 640), (40, 48, 1024), (9, 80, 512), (1100, 4096, 256)])
+                                   (1000, 400, 4096), (300, 160, 640), (40, 48, 1024), (9, 80, 512), (600, 4096, 256), (1100, 4096, 256)])
 def test_linear_parity(m, n, k):
     xb, wb = rows(m, k, 40 + m), rows(n, k, 41, std=0.05)
     y = run(xb, wb).astype(np.float64)
@@ -83,14 +84,15 @@ def test_row_bits_do_not_depend_on_the_row_count(k):
 
 
 def test_row_bits_across_lds_tile_heights():
-    """n = 4096 (32 column blocks): 300 rows take 128-row tiles (96 tiles),
-    1100 rows 256-row tiles (9 x 32 = 288 tiles of 128 rows would not fit
-    one round on 256 CUs); a probe row's bits match its solo run."""
+    """n = 4096: 300 rows take 128 x 64 tiles (3 x 64 = 192), 600 rows
+    128 x 128 (5 x 64 = 320 tiles of 128 x 64 would not fit one round on 256
+    CUs, 5 x 32 = 160 do), 1100 rows 256 x 128 (9 x 32 = 288 would not); a
+    probe row's bits match its solo run."""
     n, k = 4096, 256
     wb = rows(n, k, 61, std=0.05)
     probe = rows(1, k, 62)[0]
     solo = run(probe[None, :], wb)[0]
-    for m in (300, 1100):
+    for m in (300, 600, 1100):
         xb = rows(m, k, 63 + m)
         pos = (3 * m) // 5
         xb[pos] = probe
