@@ -479,14 +479,15 @@ def rmsnorm_extras(isk, torch, calls=200):
 def linear_extras(isk, torch, calls=50):
     """Batch-invariant linear layer at n = k = 7168 (weights 103 MB, bf16):
     decode-sized rows (1, 8: one 16-row tile, bound by the weight read; 32:
-    one 32-row tile, bound by the activation reads from L2) and 4096 rows
-    (256 x 128 LDS-staged tiles, bound by the LDS port and matrix cores)."""
+    one 32-row tile, bound by the activation reads from L2), 256 rows (128 x
+    64 LDS-staged tiles, one round on the CUs) and 4096 rows (256 x 128
+    LDS-staged tiles, bound by the matrix cores' issue)."""
     res = {}
     stream = torch.cuda.current_stream()
     n = k = 7168
     g = torch.Generator(device="cuda").manual_seed(7)
     w = (0.02 * torch.randn((n, k), generator=g, device="cuda")).to(torch.bfloat16)
-    for m in (1, 8, 32, 4096):
+    for m in (1, 8, 32, 256, 4096):
         x = torch.randn((m, k), generator=g, device="cuda").to(torch.bfloat16)
         y = torch.empty((m, n), dtype=torch.float32, device="cuda")
         for _ in range(5):
